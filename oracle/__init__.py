@@ -1,0 +1,36 @@
+"""fp64 CPU oracle of joint text+image attention with 2D-axial RoPE.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import or call anything in this package.  The product
+path (the HIP library and its Python binding) never does, and shares no code,
+table or constant with it.
+
+What is computed, and where it comes from ("Speed Up Image Generation with
+FLUX 3 Image Klein on NVIDIA Blackwell GPUs"):
+
+* joint attention over the concatenated text / noisy-target / reference
+  streams (section "FLUX 3 inference with TensorRT LLM VisualGen"): dense,
+  bidirectional softmax(Q K^T / sqrt(D)) V over the whole joint sequence;
+* RoPE applied to Q and K where they are produced, i.e. before attention
+  (section "GEMM kernel optimization": the QKV projection epilogue carries
+  query/key normalization and rotary position embeddings);
+* FP8 Q/K and V (section "Quantized and sparse attention", qk_dtype and
+  v_dtype fp8).
+
+The pages state none of the arithmetic; the readings taken where they are
+silent (2D-axial frequencies, pair convention, bf16 rounding point of the
+rotated Q/K, FP8 scale granularity, e4m3 format) are documented at each
+function.  Every function here is pinned by tests in `tests/test_oracle_*.py`
+against closed forms, brute force and library routines.
+"""
+from .rope import rope_angles, apply_rope, rope_table_fp32
+from .attention import attention, joint_attention, brute_force_attention
+from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, quant_rope_fp8,
+                  dequantize, fp8_attention)
+
+__all__ = [
+    "rope_angles", "apply_rope", "rope_table_fp32",
+    "attention", "joint_attention", "brute_force_attention",
+    "e4m3_round", "e4m3_encode", "e4m3_decode", "quant_rope_fp8",
+    "dequantize", "fp8_attention",
+]

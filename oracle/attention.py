@@ -1,0 +1,110 @@
+"""Dense joint attention, fp64 (oracle; test infrastructure only).
+
+Joint attention ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
+Blackwell GPUs", section "FLUX 3 inference with TensorRT LLM VisualGen"): the
+text, noisy-target and reference-image tokens form one sequence and every
+query attends to every key of it, with no mask.  Per batch row b and head h
+
+    O[b, i, h] = sum_j softmax_j(Q[b,i,h] . K[b,j,h] / sqrt(D)) V[b, j, h]
+    LSE[b, h, i] = log sum_j exp(Q[b,i,h] . K[b,j,h] / sqrt(D))
+
+Written as the textbook definition: scores, max-shifted exponentials,
+normalisation.  Query rows are independent, so `rows` evaluates just those
+rows exactly (used for spot checks at full size); chunking over query rows is
+only there to bound memory and changes nothing in the arithmetic of a row.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from .rope import apply_rope
+
+_CHUNK = 2048
+
+
+def attention(q, k, v, scale: float | None = None, rows=None):
+    """softmax(Q K^T * scale) V in fp64.
+
+    q, k, v: [B, S, H, D] tensors of any float dtype (converted exactly to
+    fp64).  scale defaults to 1/sqrt(D).  rows: optional 1-D index array of
+    query rows to evaluate.  Returns (O [B, R, H, D] fp64, LSE [B, H, R] fp64)
+    where R = S or len(rows).
+    """
+    q = torch.as_tensor(q).to(torch.float64)
+    k = torch.as_tensor(k).to(torch.float64)
+    v = torch.as_tensor(v).to(torch.float64)
+    b, s, h, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if rows is not None:
+        q = q[:, torch.as_tensor(np.asarray(rows), dtype=torch.int64)]
+    r = q.shape[1]
+    o = torch.empty((b, r, h, d), dtype=torch.float64)
+    lse = torch.empty((b, h, r), dtype=torch.float64)
+    for bi in range(b):
+        for hi in range(h):
+            kt = k[bi, :, hi, :].T.contiguous()            # [D, S]
+            vb = v[bi, :, hi, :].contiguous()              # [S, D]
+            for c0 in range(0, r, _CHUNK):
+                qc = q[bi, c0:c0 + _CHUNK, hi, :]          # [c, D]
+                sc = (qc @ kt) * scale                     # [c, S]
+                m = sc.max(dim=1, keepdim=True).values
+                p = torch.exp(sc - m)
+                l = p.sum(dim=1, keepdim=True)
+                o[bi, c0:c0 + _CHUNK, hi, :] = (p @ vb) / l
+                lse[bi, hi, c0:c0 + _CHUNK] = (m + torch.log(l))[:, 0]
+    return o, lse
+
+
+def joint_attention(q, k, v, pos=None, theta: float = 10000.0,
+                    scale: float | None = None, round_rotated: bool = True,
+                    rows=None):
+    """The bf16 hot path's reference: RoPE on Q and K, then attention.
+
+    Reading of where the rotated Q/K are rounded: the pages place RoPE in the
+    epilogue of the QKV projection, so attention consumes Q and K that were
+    rotated and then stored in the model's working precision.  With
+    round_rotated=True (the default) the fp64-rotated Q and K are rounded
+    once to bf16 (round to nearest even) before Q K^T.  round_rotated=False
+    gives the unrounded variant for information.  pos=None means no RoPE.
+    """
+    q = torch.as_tensor(q)
+    k = torch.as_tensor(k)
+    if pos is not None:
+        q = apply_rope(q, pos, theta)
+        k = apply_rope(k, pos, theta)
+        if round_rotated:
+            q = q.to(torch.bfloat16)
+            k = k.to(torch.bfloat16)
+    return attention(q, k, v, scale=scale, rows=rows)
+
+
+def brute_force_attention(q, k, v, scale: float | None = None):
+    """Pure-Python triple loop over (b, h, i); for tiny shapes only.
+
+    Uses math.fsum so the reductions are exactly rounded; it is the
+    independent check of the vectorised `attention`.
+    """
+    q = torch.as_tensor(q).to(torch.float64).tolist()
+    k = torch.as_tensor(k).to(torch.float64).tolist()
+    v = torch.as_tensor(v).to(torch.float64).tolist()
+    b_n, s_n, h_n, d_n = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_n)
+    o = [[[[0.0] * d_n for _ in range(h_n)] for _ in range(s_n)] for _ in range(b_n)]
+    lse = [[[0.0] * s_n for _ in range(h_n)] for _ in range(b_n)]
+    for b in range(b_n):
+        for h in range(h_n):
+            for i in range(s_n):
+                sc = [math.fsum(q[b][i][h][t] * k[b][j][h][t] for t in range(d_n)) * scale
+                      for j in range(s_n)]
+                m = max(sc)
+                e = [math.exp(x - m) for x in sc]
+                z = math.fsum(e)
+                for t in range(d_n):
+                    o[b][i][h][t] = math.fsum(e[j] * v[b][j][h][t] for j in range(s_n)) / z
+                lse[b][h][i] = m + math.log(z)
+    return torch.tensor(o, dtype=torch.float64), torch.tensor(lse, dtype=torch.float64)
