@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of the joint-attention forward on one MI355X.
+
+One step = one pass of the bf16 hot path over the 2048x2048 T2I step shape
+(B=1, 24 heads x 128, 512 text + 128x128 image tokens = 16896 tokens): build
+the 2D-axial RoPE table from the token positions, then the fused RoPE +
+attention forward.  Inputs are seeded synthetic tensors resident in HBM before
+the timed region.  Throughput is 4*B*H*S^2*D flops per step (QK^T + PV).
+
+Also reported on the same JSON line:
+  roofline      the forward kernel's own average duration (HIP events on the
+                launch stream) against the bf16 dense MFMA peak;
+  fp8           the FP8 path (RoPE+quantize pass, FP8 forward) timed the same
+                way, against the fp8 MFMA peak and HBM bandwidth;
+  cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
+                sample of query rows (scaled to TFLOP/s), plus the parity of
+                the GPU output on those rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "joint-attention fwd TFLOP/s and % of MFMA peak at 2048x2048 (16896 tok)"
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_t2i_2048.json")
+BF16_SOURCE = os.path.join(ROOT, "joint_attention_attn_amd", "csrc", "attn_bf16.hip")
+
+
+def _log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="t2i_2048")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def _traffic_for_current_kernel():
+    """HBM bytes per launch from committed rocprofv3 counters, only if they
+    were taken on the kernel source as it is now."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    with open(BF16_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _time_launches(fn, n):
+    """Run fn() n times with a HIP event pair around each launch on the
+    current (launch) stream; returns per-launch ms."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def main() -> int:
+    args = _parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU joint-attention kernel; runs on more than "
+              "one GPU are not part of this build (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import torch
+    import joint_attention_attn_amd as ja
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = "cuda:0"
+    w = synth.WORKLOADS[args.config]
+    B, S, H, D = w.shape
+    flops = w.flops()
+    _log(f"[bench] workload {w.name}: B={B} S={S} H={H} D={D}, {flops / 1e12:.4f} TFLOP/step")
+
+    q, k, v, outl = synth.make_qkv(w, args.seed)
+    pos = synth.positions(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    pos_d = torch.from_numpy(pos).to(dev)
+    out = torch.empty_like(qd)
+    torch.cuda.synchronize()
+
+    rope_holder = {}
+
+    def step():
+        rope = ja.rope_table_2d(pos_d, D, w.theta)
+        ja.fwd_bf16(qd, kd, vd, rope, out=out)
+        rope_holder["rope"] = rope
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _log(f"[bench] warmup {args.warmup} done")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    _log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # dominant kernel: the fused RoPE + attention forward, timed per launch
+    rope = rope_holder["rope"]
+    kms = _time_launches(lambda: ja.fwd_bf16(qd, kd, vd, rope, out=out), max(args.steps, 5))
+    k_avg = sum(kms) / len(kms)
+    achieved = flops / (k_avg * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic_for_current_kernel(),
+                "kernel": "attn_fwd_bf16_kernel<128>", "kernel_ms": round(k_avg, 4),
+                "kernel_ms_min": round(min(kms), 4)}
+    _log(f"[bench] fwd kernel avg {k_avg:.3f} ms -> {achieved:.1f} TFLOP/s "
+         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+
+    fp8 = None
+    if not args.no_fp8:
+        q8, k8, v8, sq, sk, sv = ja.quant_rope_fp8(qd, kd, vd, rope)
+        out8 = torch.empty_like(out)
+        for _ in range(2):
+            ja.quant_rope_fp8(qd, kd, vd, rope)
+            ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8)
+        torch.cuda.synchronize()
+        n = max(args.steps, 5)
+        qms = _time_launches(lambda: ja.quant_rope_fp8(qd, kd, vd, rope), n)
+        fms = _time_launches(lambda: ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8), n)
+        q_avg, f_avg = sum(qms) / n, sum(fms) / n
+        elems = B * S * H * D
+        q_bytes = 3 * elems * 2 + S * (D // 2) * 8 + 3 * elems + 3 * B * H * S * 4
+        f_tf = flops / (f_avg * 1e-3) / 1e12
+        fp8 = {"fwd_ms": round(f_avg, 4), "fwd_tflops": round(f_tf, 2),
+               "fwd_frac_of_fp8_peak": round(f_tf / PEAK_FP8_TFLOPS, 4),
+               "quant_ms": round(q_avg, 4),
+               "quant_gbs": round(q_bytes / (q_avg * 1e-3) / 1e9, 1),
+               "quant_frac_of_hbm": round(q_bytes / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "path_tflops": round(flops / ((f_avg + q_avg) * 1e-3) / 1e12, 2)}
+        _log(f"[bench] fp8: fwd {f_avg:.3f} ms ({f_tf:.1f} TFLOP/s), quant {q_avg:.3f} ms "
+             f"({fp8['quant_gbs']} GB/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = _cpu_baseline(w, q, k, v, pos, outl, out, args.cpu_seconds)
+
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"{w.name}: joint text+image attention fwd, "
+                                  f"{w.n_text} text + {w.grid}x{w.grid} image tokens"
+                                  + (f" + {w.n_ref} reference grid(s)" if w.n_ref else "")
+                                  + ", 2D-axial RoPE, N(0,1) bf16 with "
+                                  f"{100 * w.outlier_frac:g}% x{w.outlier_scale:g} outlier tokens",
+                      "batch": B, "seq_len": S, "heads": H, "head_dim": D,
+                      "flops_per_step": flops},
+           "roofline": roofline, "cpu_baseline": cpu, "fp8": fp8}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s):
+    """The fp64 oracle on this host's cores over a bounded sample of query
+    rows (all keys, all heads), scaled to TFLOP/s; plus parity on those rows."""
+    import numpy as np
+    import torch
+    import oracle
+
+    threads = torch.get_num_threads()
+    B, S, H, D = w.shape
+    rng = np.random.default_rng(7)
+    order = rng.permutation(S)
+    done_rows, spent, chunk = [], 0.0, 64
+    got_all = out_gpu.cpu()
+    errs_num, errs_den = 0.0, 0.0
+    while spent < target_s and len(done_rows) < S:
+        rows = np.sort(order[len(done_rows):len(done_rows) + chunk])
+        t0 = time.perf_counter()
+        ref, _ = oracle.joint_attention(q, k, v, pos, w.theta, rows=rows)
+        spent += time.perf_counter() - t0
+        got = got_all[:, rows].double()
+        errs_num += float(((got - ref) ** 2).sum())
+        errs_den += float((ref ** 2).sum())
+        done_rows.extend(rows.tolist())
+        chunk = min(chunk * 2, 1024)
+    n = len(done_rows)
+    sample_flops = 4.0 * B * H * n * S * D
+    tflops = sample_flops / spent / 1e12
+    _log(f"[bench] cpu oracle: {n} query rows x {H} heads in {spent:.1f} s on {threads} "
+         f"threads -> {tflops * 1e3:.2f} GFLOP/s")
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} random query rows x {B * H} (batch, head) pairs x all {S} keys "
+                      f"({sample_flops / 1e9:.1f} GFLOP) of {w.name}, fp64 torch-CPU",
+            "seconds": round(spent, 2),
+            "gpu_rel_l2_on_sample": round(math.sqrt(errs_num / errs_den), 6)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

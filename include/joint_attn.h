@@ -1,0 +1,156 @@
+/*
+ * joint_attn.h - C ABI of the MI355X (gfx950) joint text+image attention
+ * forward library, libjoint_attn.so.
+ *
+ * The operation is the joint attention of a DiT block: text tokens, noisy
+ * target-image latent tokens and optional reference-image tokens form ONE
+ * sequence and every query attends to every key of it, with no mask
+ * ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA Blackwell
+ * GPUs", section "FLUX 3 inference with TensorRT LLM VisualGen").  Q and K
+ * carry rotary position embeddings applied where they are produced (same
+ * page, section "GEMM kernel optimization"), here fused into the attention's
+ * Q/K load; the FP8 path quantizes Q, K and V to FP8 (same page, section
+ * "Quantized and sparse attention", qk_dtype / v_dtype fp8).
+ *
+ *   O[b,i,h,:] = sum_j softmax_j( <R_i q[b,i,h], R_j k[b,j,h]> * scale ) v[b,j,h,:]
+ *
+ * with R_t the rotation of token t (a 2x2 rotation of every adjacent pair
+ * (2p, 2p+1) of the head vector by the angle whose cos/sin the RoPE table
+ * holds) and scale = 1/sqrt(D) unless given.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device.
+ *     The caller allocates and owns every buffer; the library allocates no
+ *     device or host memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *     enqueue work: they return after the launch, inputs must stay unchanged
+ *     and outputs unread until the stream reaches the call.  Calls are
+ *     thread-safe.
+ *   - Validation happens on the host before anything is enqueued; on any
+ *     error nothing is launched and no output is written.  Faults inside a
+ *     kernel are asynchronous and surface at the caller's next
+ *     synchronisation of the stream.
+ *   - bf16 is bfloat16 (1-8-7, round to nearest even); e4m3 is the OCP 8-bit
+ *     floating point E4M3 format (bias 7, no infinities, max 448).
+ */
+#ifndef JOINT_ATTN_H
+#define JOINT_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JA_OK = 0,
+  JA_ERR_INVALID_ARG = 1,  /* null pointer, size < 1, bad stride or alignment */
+  JA_ERR_UNSUPPORTED = 2,  /* head_dim not 64 or 128, grid too large          */
+  JA_ERR_HIP = 3           /* the HIP runtime refused the launch               */
+} ja_status;
+
+/*
+ * Shape and layout of one attention call.
+ *   batch, seq_len, heads >= 1; head_dim in {64, 128}.
+ *   Q/K/V/O are addressed as x[b*x_sb + s*x_ss + h*x_sh + d] (strides in
+ *   ELEMENTS, the D stride is 1).  A contiguous [B, S, H, D] tensor has
+ *   x_ss = H*D, x_sh = D, x_sb = S*H*D; [B, H, S, D] works too.  Strides must
+ *   be multiples of 8 and base pointers 16-byte aligned (16-byte vector
+ *   loads).  softmax_scale = 0 selects 1/sqrt(head_dim).
+ */
+typedef struct {
+  int32_t batch, seq_len, heads, head_dim;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  float softmax_scale;
+} ja_params;
+
+/*
+ * joint_attn_rope_table_2d - cos/sin of every rotation angle of 2D-axial
+ * RoPE (the position encoding of the image latent grid; the pages fuse RoPE
+ * into the QKV epilogue, section "GEMM kernel optimization").
+ *   pos    device int32 [seq_len][2]: (row, col) grid position of each token
+ *          (text tokens conventionally at (0, 0)); any int32 values.
+ *   table  device float [seq_len][head_dim/2][2]: written with
+ *          (cos a, sin a) of pair p's angle a, computed in fp64 and rounded
+ *          once to fp32.  Pair p < head_dim/4 rotates by the row with
+ *          frequency w_p; pair p >= head_dim/4 by the column with w_(p-D/4);
+ *          w_k = theta^(-4k/head_dim) (the 1-D RoPE of dimension D/2 on each
+ *          axis).
+ *   theta  > 0 (10000 in the FLUX-style DiT).
+ * The table depends only on positions, head_dim and theta: build it once per
+ * forward pass and pass it to every layer's attention call.
+ */
+ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len,
+                                   int32_t head_dim, float theta, float *table,
+                                   void *stream);
+
+/*
+ * joint_attn_fwd_bf16 - BF16 joint attention with RoPE fused into the Q/K
+ * load.
+ *   q, k, v  device bf16, layout per ja_params.
+ *   rope     device float [seq_len][head_dim/2][2] (cos, sin) table, e.g.
+ *            from joint_attn_rope_table_2d; NULL = no rotation.  Q and K are
+ *            rotated in fp32, pair (x, y) -> (fma(x, c, -fl(y s)),
+ *            fma(x, s, fl(y c))), and rounded to bf16 before Q K^T.
+ *   o        device bf16, layout per ja_params (o_* strides); must not alias
+ *            q, k or v.
+ *   lse      device float [batch][heads][seq_len], nullable: natural-log
+ *            log-sum-exp of each query row's scaled scores.
+ * Softmax statistics and both products accumulate in fp32; P is rounded to
+ * bf16 for the P.V product.
+ */
+ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
+                              const void *v, const float *rope, void *o,
+                              float *lse, void *stream);
+
+/*
+ * joint_attn_quant_rope_fp8 - RoPE on Q and K, then per-token FP8
+ * quantization of Q, K and V (the pages' fp8 qk_dtype / v_dtype).
+ *   q, k, v     device bf16, layout per ja_params (its Q, K, V strides).
+ *   rope        as for joint_attn_fwd_bf16 (NULL = no rotation).
+ *   q8, k8, v8  device e4m3 (1 byte each), written contiguous
+ *               [batch][seq_len][heads][head_dim].
+ *   sq, sk, sv  device float [batch][heads][seq_len]: one scale per (b, token,
+ *               head).  For each head vector x (after RoPE, computed in fp32
+ *               as (fma(x, c, -fl(y s)), fma(x, s, fl(y c)))): amax = max|x|;
+ *               scale = amax/448 (1 if amax = 0);
+ *               code = e4m3_rne(clamp(fl(x/scale), -448, 448)).
+ */
+ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,
+                                    const void *k, const void *v,
+                                    const float *rope, void *q8, void *k8,
+                                    void *v8, float *sq, float *sk, float *sv,
+                                    void *stream);
+
+/*
+ * joint_attn_fwd_fp8 - joint attention on FP8 inputs produced by
+ * joint_attn_quant_rope_fp8 (RoPE already applied).
+ *   q8, k8, v8  device e4m3, contiguous [batch][seq_len][heads][head_dim]
+ *               (the Q, K and V strides of p are ignored).
+ *   sq, sk, sv  device float [batch][heads][seq_len] dequantization scales,
+ *               16-byte aligned.
+ *   o           device bf16, layout per ja_params (o_* strides).
+ *   lse         device float [batch][heads][seq_len], nullable.
+ * Q K^T and P.V run on FP8 MFMA; the scales are applied in fp32; softmax
+ * statistics and accumulation are fp32; the output is bf16.
+ */
+ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
+                             const void *v8, const float *sq, const float *sk,
+                             const float *sv, void *o, float *lse,
+                             void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *joint_attn_status_string(ja_status s);
+
+/* Message of the last HIP error seen by this thread's library calls
+ * (static per-thread buffer; "" if none). */
+const char *joint_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JOINT_ATTN_H */

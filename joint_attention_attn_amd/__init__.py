@@ -1,0 +1,180 @@
+"""Python binding of libjoint_attn.so (MI355X joint text+image attention).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/joint_attn.h.  PyTorch supplies
+device memory and the current stream.  There is no fallback: if the shared
+library is missing or a call fails, a RuntimeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "JointAttnError", "library_path", "load", "rope_table_2d", "fwd_bf16",
+    "quant_rope_fp8", "fwd_fp8", "Params",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libjoint_attn.so")
+_LIB = None
+
+JA_OK, JA_ERR_INVALID_ARG, JA_ERR_UNSUPPORTED, JA_ERR_HIP = 0, 1, 2, 3
+
+
+class JointAttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(what)
+
+
+class Params(ctypes.Structure):
+    """Mirror of ja_params."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("q_sb", ctypes.c_int64), ("q_ss", ctypes.c_int64), ("q_sh", ctypes.c_int64),
+        ("k_sb", ctypes.c_int64), ("k_ss", ctypes.c_int64), ("k_sh", ctypes.c_int64),
+        ("v_sb", ctypes.c_int64), ("v_ss", ctypes.c_int64), ("v_sh", ctypes.c_int64),
+        ("o_sb", ctypes.c_int64), ("o_ss", ctypes.c_int64), ("o_sh", ctypes.c_int64),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libjoint_attn.so (built by __graft_entry__.build()); raise if absent."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, st = ctypes.c_void_p, ctypes.c_int
+    pp = ctypes.POINTER(Params)
+    lib.joint_attn_rope_table_2d.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp]
+    lib.joint_attn_fwd_bf16.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+    lib.joint_attn_quant_rope_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    for fn in ("joint_attn_rope_table_2d", "joint_attn_fwd_bf16",
+               "joint_attn_quant_rope_fp8", "joint_attn_fwd_fp8"):
+        getattr(lib, fn).restype = st
+    lib.joint_attn_status_string.argtypes = [st]
+    lib.joint_attn_status_string.restype = ctypes.c_char_p
+    lib.joint_attn_last_error.argtypes = []
+    lib.joint_attn_last_error.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, fn: str) -> None:
+    if status != JA_OK:
+        lib = load()
+        msg = lib.joint_attn_status_string(status).decode()
+        extra = lib.joint_attn_last_error().decode() if status == JA_ERR_HIP else ""
+        raise JointAttnError(status, f"{fn}: {msg} {extra}".strip())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bshd(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, S, H, D], got {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name} must have a unit stride along D")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.stride(0), t.stride(1), t.stride(2)
+
+
+def _params(q, k, v, o, softmax_scale):
+    b, s, h, d = q.shape
+    for t, n in ((k, "k"), (v, "v"), (o, "out")):
+        if tuple(t.shape) != (b, s, h, d):
+            raise ValueError(f"{n} shape {tuple(t.shape)} != q shape {(b, s, h, d)}")
+    p = Params(b, s, h, d)
+    p.q_sb, p.q_ss, p.q_sh = _bshd(q, "q")
+    p.k_sb, p.k_ss, p.k_sh = _bshd(k, "k")
+    p.v_sb, p.v_ss, p.v_sh = _bshd(v, "v")
+    p.o_sb, p.o_ss, p.o_sh = _bshd(o, "out")
+    p.softmax_scale = float(softmax_scale or 0.0)
+    return p
+
+
+def rope_table_2d(pos: torch.Tensor, head_dim: int, theta: float = 10000.0) -> torch.Tensor:
+    """(cos, sin) table [S, head_dim/2, 2] fp32 of 2D-axial RoPE for int32 pos [S, 2]."""
+    if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[1] != 2 or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 [S, 2] device tensor")
+    table = torch.empty((pos.shape[0], head_dim // 2, 2), dtype=torch.float32, device=pos.device)
+    st = load().joint_attn_rope_table_2d(_ptr(pos), pos.shape[0], head_dim, float(theta),
+                                         _ptr(table), _stream(pos.device))
+    _check(st, "joint_attn_rope_table_2d")
+    return table
+
+
+def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_lse: bool = False):
+    """Joint attention on bf16 [B, S, H, D] tensors; RoPE from `rope` (or none)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bfloat16")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    p = _params(q, k, v, out, softmax_scale)
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    st = load().joint_attn_fwd_bf16(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
+                                    _ptr(out), _ptr(lse), _stream(q.device))
+    _check(st, "joint_attn_fwd_bf16")
+    return (out, lse) if return_lse else out
+
+
+def quant_rope_fp8(q, k, v, rope=None):
+    """RoPE on Q/K + per-token e4m3 quantization.  Returns (q8, k8, v8, sq, sk, sv):
+    uint8 codes [B, S, H, D] and fp32 scales [B, H, S]."""
+    b, s, h, d = q.shape
+    dev = q.device
+    q8, k8, v8 = (torch.empty((b, s, h, d), dtype=torch.uint8, device=dev) for _ in range(3))
+    sq, sk, sv = (torch.empty((b, h, s), dtype=torch.float32, device=dev) for _ in range(3))
+    p = _params(q, k, v, q, 0.0)
+    st = load().joint_attn_quant_rope_fp8(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
+                                          _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk),
+                                          _ptr(sv), _stream(dev))
+    _check(st, "joint_attn_quant_rope_fp8")
+    return q8, k8, v8, sq, sk, sv
+
+
+def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return_lse: bool = False):
+    """Joint attention on contiguous e4m3 codes [B, S, H, D] with fp32 scales [B, H, S]."""
+    b, s, h, d = q8.shape
+    for t in (q8, k8, v8):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous() \
+                or tuple(t.shape) != (b, s, h, d):
+            raise ValueError("q8/k8/v8 must be contiguous 1-byte [B, S, H, D] tensors")
+    for t in (sq, sk, sv):
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (b, h, s):
+            raise ValueError("sq/sk/sv must be contiguous fp32 [B, H, S] tensors")
+    if out is None:
+        out = torch.empty((b, s, h, d), dtype=torch.bfloat16, device=q8.device)
+    p = Params(b, s, h, d)
+    p.o_sb, p.o_ss, p.o_sh = _bshd(out, "out")
+    p.softmax_scale = float(softmax_scale or 0.0)
+    lse = None
+    if return_lse:
+        lse = torch.empty((b, h, s), dtype=torch.float32, device=q8.device)
+    st = load().joint_attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq),
+                                   _ptr(sk), _ptr(sv), _ptr(out), _ptr(lse), _stream(q8.device))
+    _check(st, "joint_attn_fwd_fp8")
+    return (out, lse) if return_lse else out

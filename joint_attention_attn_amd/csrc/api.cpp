@@ -1,0 +1,154 @@
+// C ABI of libjoint_attn.so: argument validation, status codes and launch.
+// Every check runs on the host before anything is enqueued, so an invalid
+// call never touches the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/joint_attn.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+ja_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return JA_OK;
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", hipGetErrorName(e),
+                hipGetErrorString(e));
+  return JA_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool shape_ok(const ja_params *p) {
+  return p->batch >= 1 && p->seq_len >= 1 && p->heads >= 1;
+}
+
+bool dim_supported(int d) { return d == 64 || d == 128; }
+
+// Strides of a bf16 tensor: multiples of 8 elements (16-byte vector access)
+// and non-negative.
+bool strides_ok(int64_t sb, int64_t ss, int64_t sh) {
+  return sb >= 0 && ss >= 0 && sh >= 0 && sb % 8 == 0 && ss % 8 == 0 && sh % 8 == 0;
+}
+
+// Grid limits: x = query blocks, y = heads, z = batch.
+bool grid_ok(const ja_params *p, int block_rows) {
+  const int64_t nx = ((int64_t)p->seq_len + block_rows - 1) / block_rows;
+  return nx <= 0x7fffffff && p->heads <= 65535 && p->batch <= 65535;
+}
+
+ja::AttnLayout layout(const ja_params *p) {
+  ja::AttnLayout L;
+  L.B = p->batch; L.S = p->seq_len; L.H = p->heads; L.D = p->head_dim;
+  L.q_sb = p->q_sb; L.q_ss = p->q_ss; L.q_sh = p->q_sh;
+  L.k_sb = p->k_sb; L.k_ss = p->k_ss; L.k_sh = p->k_sh;
+  L.v_sb = p->v_sb; L.v_ss = p->v_ss; L.v_sh = p->v_sh;
+  L.o_sb = p->o_sb; L.o_ss = p->o_ss; L.o_sh = p->o_sh;
+  const float scale = p->softmax_scale != 0.f ? p->softmax_scale
+                                              : 1.f / std::sqrt((float)p->head_dim);
+  L.scale_log2 = scale * 1.4426950408889634f;
+  return L;
+}
+
+// Common checks of the Q/K/V/O description.  `qkv_strided` is false for the
+// FP8 forward, whose inputs are contiguous by contract.
+ja_status check_params(const ja_params *p, bool qkv_strided, int block_rows) {
+  if (!p) return JA_ERR_INVALID_ARG;
+  if (!shape_ok(p)) return JA_ERR_INVALID_ARG;
+  if (!dim_supported(p->head_dim)) return JA_ERR_UNSUPPORTED;
+  if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f) return JA_ERR_INVALID_ARG;
+  if (qkv_strided &&
+      (!strides_ok(p->q_sb, p->q_ss, p->q_sh) || !strides_ok(p->k_sb, p->k_ss, p->k_sh) ||
+       !strides_ok(p->v_sb, p->v_ss, p->v_sh)))
+    return JA_ERR_INVALID_ARG;
+  if (block_rows > 0) {
+    if (!strides_ok(p->o_sb, p->o_ss, p->o_sh)) return JA_ERR_INVALID_ARG;
+    if (!grid_ok(p, block_rows)) return JA_ERR_UNSUPPORTED;
+  }
+  return JA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *joint_attn_status_string(ja_status s) {
+  switch (s) {
+    case JA_OK: return "JA_OK";
+    case JA_ERR_INVALID_ARG: return "JA_ERR_INVALID_ARG: invalid argument";
+    case JA_ERR_UNSUPPORTED: return "JA_ERR_UNSUPPORTED: unsupported shape";
+    case JA_ERR_HIP: return "JA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown ja_status";
+}
+
+const char *joint_attn_last_error(void) { return g_last_error; }
+
+ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len,
+                                   int32_t head_dim, float theta, float *table,
+                                   void *stream) {
+  if (!pos || !table || seq_len < 1) return JA_ERR_INVALID_ARG;
+  if (!(theta > 0.f) || !std::isfinite(theta)) return JA_ERR_INVALID_ARG;
+  if (!dim_supported(head_dim)) return JA_ERR_UNSUPPORTED;
+  if (!aligned16(table) || (reinterpret_cast<uintptr_t>(pos) & 3u)) return JA_ERR_INVALID_ARG;
+  if ((int64_t)seq_len * (head_dim / 2) > 0x7fffffffLL * 256) return JA_ERR_UNSUPPORTED;
+  return hip_status(ja::launch_rope_table_2d(pos, seq_len, head_dim, theta, table,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
+                              const void *v, const float *rope, void *o,
+                              float *lse, void *stream) {
+  if (!p || !q || !k || !v || !o) return JA_ERR_INVALID_ARG;
+  const ja_status st = check_params(p, true, ja::fwd_bf16_block_rows(p->head_dim));
+  if (st != JA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (rope && !aligned16(rope)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return JA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v) return JA_ERR_INVALID_ARG;
+  return hip_status(ja::launch_fwd_bf16(layout(p), q, k, v, rope, o, lse,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,
+                                    const void *k, const void *v,
+                                    const float *rope, void *q8, void *k8,
+                                    void *v8, float *sq, float *sk, float *sv,
+                                    void *stream) {
+  if (!p || !q || !k || !v || !q8 || !k8 || !v8 || !sq || !sk || !sv)
+    return JA_ERR_INVALID_ARG;
+  const ja_status st = check_params(p, true, 0);
+  if (st != JA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) ||
+      !aligned16(k8) || !aligned16(v8) || (rope && !aligned16(rope)) ||
+      (reinterpret_cast<uintptr_t>(sq) & 3u) || (reinterpret_cast<uintptr_t>(sk) & 3u) ||
+      (reinterpret_cast<uintptr_t>(sv) & 3u))
+    return JA_ERR_INVALID_ARG;
+  const int64_t threads = (int64_t)p->batch * p->seq_len * p->heads * (p->head_dim / 8);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return JA_ERR_UNSUPPORTED;
+  return hip_status(ja::launch_quant_rope_fp8(layout(p), q, k, v, rope, q8, k8, v8,
+                                              sq, sk, sv,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
+                             const void *v8, const float *sq, const float *sk,
+                             const float *sv, void *o, float *lse,
+                             void *stream) {
+  if (!p || !q8 || !k8 || !v8 || !sq || !sk || !sv || !o) return JA_ERR_INVALID_ARG;
+  const ja_status st = check_params(p, false, ja::fwd_fp8_block_rows(p->head_dim));
+  if (st != JA_OK) return st;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) ||
+      !aligned16(sq) || !aligned16(sk) || !aligned16(sv) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return JA_ERR_INVALID_ARG;
+  return hip_status(ja::launch_fwd_fp8(layout(p), q8, k8, v8, sq, sk, sv, o, lse,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Device-side vocabulary shared by the gfx950 kernels: vector types,
+// bf16 packing and the RoPE pair rotation.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ja {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+template <typename To, typename From>
+__device__ __forceinline__ To bit_cast(const From &f) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  return __builtin_bit_cast(To, f);
+}
+
+// Two fp32 -> packed bf16x2 (round to nearest even; low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return bit_cast<uint32_t>(__builtin_convertvector(v, bf16x2));
+}
+
+// The two bf16 of a packed word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// RoPE of one adjacent pair (x, y) by the angle whose (cos, sin) is cs:
+// (x c - y s, x s + y c) in fp32 with a fixed operation order, the y term
+// rounded on its own and the x term fused onto it:
+//   rx = fma(x, c, -fl(y s)),  ry = fma(x, s, fl(y c)).
+// The result is later rounded to bf16 or e4m3, so the order is pinned down
+// (no compiler contraction) to make those rounding decisions reproducible.
+__device__ __forceinline__ void rope_pair_f32(float x, float y, float2 cs, float &rx,
+                                              float &ry) {
+#pragma clang fp contract(off)
+  const float ys = y * cs.y;
+  const float yc = y * cs.x;
+  rx = __builtin_fmaf(x, cs.x, -ys);
+  ry = __builtin_fmaf(x, cs.y, yc);
+}
+
+// The same rotation of a packed bf16 pair, rounded back to packed bf16.
+__device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t w, float2 cs) {
+  float rx, ry;
+  rope_pair_f32(bf16_lo(w), bf16_hi(w), cs, rx, ry);
+  return pack_bf16x2(rx, ry);
+}
+
+// Rotate the 8 bf16 (4 pairs) of a 16-byte chunk with 4 consecutive table
+// entries.
+__device__ __forceinline__ u32x4 rope_chunk_bf16(u32x4 w, const float2 *cs) {
+  const float4 t01 = reinterpret_cast<const float4 *>(cs)[0];
+  const float4 t23 = reinterpret_cast<const float4 *>(cs)[1];
+  u32x4 r;
+  r.x = rope_pair_bf16(w.x, make_float2(t01.x, t01.y));
+  r.y = rope_pair_bf16(w.y, make_float2(t01.z, t01.w));
+  r.z = rope_pair_bf16(w.z, make_float2(t23.x, t23.y));
+  r.w = rope_pair_bf16(w.w, make_float2(t23.z, t23.w));
+  return r;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace ja

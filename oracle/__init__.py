@@ -13,23 +13,28 @@ FLUX 3 Image Klein on NVIDIA Blackwell GPUs"):
   bidirectional softmax(Q K^T / sqrt(D)) V over the whole joint sequence;
 * RoPE applied to Q and K where they are produced, i.e. before attention
   (section "GEMM kernel optimization": the QKV projection epilogue carries
-  query/key normalization and rotary position embeddings);
+  query/key normalization and rotary position embeddings); attention then
+  consumes rotated Q and K stored in bf16;
 * FP8 Q/K and V (section "Quantized and sparse attention", qk_dtype and
   v_dtype fp8).
 
 The pages state none of the arithmetic; the readings taken where they are
 silent (2D-axial frequencies, pair convention, bf16 rounding point of the
 rotated Q/K, FP8 scale granularity, e4m3 format) are documented at each
-function.  Every function here is pinned by tests in `tests/test_oracle_*.py`
-against closed forms, brute force and library routines.
+function.  The arithmetic is fp64 throughout, except where a floating-point
+value decides a rounded code (the bf16 of a rotated Q/K element, an e4m3
+code): there the value is computed in fp32 with the kernels' fixed operation
+order (`rotate_fp32`), so both sides take the same decision.  Every function
+here is pinned by tests in `tests/test_oracle_*.py` against closed forms,
+brute force, exact rational arithmetic and library routines.
 """
-from .rope import rope_angles, apply_rope, rope_table_fp32
+from .rope import rope_angles, apply_rope, rope_table_fp32, rotate_fp32, fma32
 from .attention import attention, joint_attention, brute_force_attention
 from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, quant_rope_fp8,
                   dequantize, fp8_attention)
 
 __all__ = [
-    "rope_angles", "apply_rope", "rope_table_fp32",
+    "rope_angles", "apply_rope", "rope_table_fp32", "rotate_fp32", "fma32",
     "attention", "joint_attention", "brute_force_attention",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "quant_rope_fp8",
     "dequantize", "fp8_attention",

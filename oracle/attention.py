@@ -20,7 +20,9 @@ import math
 import numpy as np
 import torch
 
-from .rope import apply_rope
+import numpy as _np
+
+from .rope import apply_rope, rope_table_fp32, rotate_fp32
 
 _CHUNK = 2048
 
@@ -67,18 +69,22 @@ def joint_attention(q, k, v, pos=None, theta: float = 10000.0,
     Reading of where the rotated Q/K are rounded: the pages place RoPE in the
     epilogue of the QKV projection, so attention consumes Q and K that were
     rotated and then stored in the model's working precision.  With
-    round_rotated=True (the default) the fp64-rotated Q and K are rounded
-    once to bf16 (round to nearest even) before Q K^T.  round_rotated=False
-    gives the unrounded variant for information.  pos=None means no RoPE.
+    round_rotated=True (the default) Q and K are rotated in fp32
+    (`rotate_fp32`, the kernels' operation order, since the result decides a
+    bf16 code) and rounded once to bf16 (round to nearest even) before
+    Q K^T; attention itself is fp64.  round_rotated=False rotates in fp64
+    and keeps the result unrounded, for information.  pos=None: no RoPE.
     """
     q = torch.as_tensor(q)
     k = torch.as_tensor(k)
     if pos is not None:
-        q = apply_rope(q, pos, theta)
-        k = apply_rope(k, pos, theta)
         if round_rotated:
-            q = q.to(torch.bfloat16)
-            k = k.to(torch.bfloat16)
+            table = rope_table_fp32(pos, q.shape[-1], theta)
+            q = torch.from_numpy(rotate_fp32(q.to(torch.float32).numpy(), table)).to(torch.bfloat16)
+            k = torch.from_numpy(rotate_fp32(k.to(torch.float32).numpy(), table)).to(torch.bfloat16)
+        else:
+            q = apply_rope(q, pos, theta)
+            k = apply_rope(k, pos, theta)
     return attention(q, k, v, scale=scale, rows=rows)
 
 

@@ -12,9 +12,10 @@ Up Image Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", section
   that head vector ("per token"), scale = amax / 448, and scale = 1 when the
   vector is all zeros; Q and K are quantized after RoPE, V as given;
 * precision of the decision: the quantizer rounds values that were computed
-  in fp32 with a fixed operation order (below), so the codes it produces are
-  a deterministic function of the inputs that any fp32 implementation with
-  the same order reproduces bit for bit.
+  in fp32 with a fixed operation order (`oracle.rope.rotate_fp32`, then
+  fl(x / scale)), so the codes it produces are a deterministic function of
+  the inputs that any fp32 implementation with the same order reproduces bit
+  for bit.
 
 The attention reference for this path is plain fp64 attention on the
 dequantized tensors (code value x scale), with no further RoPE.
@@ -25,7 +26,7 @@ import numpy as np
 import torch
 
 from .attention import attention
-from .rope import rope_table_fp32
+from .rope import rope_table_fp32, rotate_fp32
 
 E4M3_MAX = 448.0
 
@@ -74,19 +75,6 @@ def e4m3_decode(code) -> np.ndarray:
     return s * val
 
 
-def _rotate_fp32(x: np.ndarray, table: np.ndarray) -> np.ndarray:
-    """RoPE in fp32 with every product and sum rounded to fp32 separately:
-    (x, y) -> (fl(fl(x c) - fl(y s)), fl(fl(x s) + fl(y c)))."""
-    c = table[None, :, None, :, 0]
-    s = table[None, :, None, :, 1]
-    xe = x[..., 0::2]
-    xo = x[..., 1::2]
-    out = np.empty_like(x)
-    out[..., 0::2] = (xe * c) - (xo * s)
-    out[..., 1::2] = (xe * s) + (xo * c)
-    return out
-
-
 def _quantize_rows(r: np.ndarray):
     """Per-(b, s, h) e4m3 quantization of fp32 r [B, S, H, D].
 
@@ -104,7 +92,7 @@ def _quantize_rows(r: np.ndarray):
 
 
 def quant_rope_fp8(q, k, v, pos, theta: float = 10000.0):
-    """RoPE on Q and K (fp32, fixed order), then per-token e4m3 quantization
+    """RoPE on Q and K (fp32, `rotate_fp32` order), then per-token e4m3 quantization
     of Q, K and V.  Returns (q8, k8, v8, sq, sk, sv): uint8 codes
     [B, S, H, D] and fp32 scales [B, H, S].  pos=None skips the rotation."""
     q = torch.as_tensor(q).to(torch.float32).numpy()
@@ -112,8 +100,8 @@ def quant_rope_fp8(q, k, v, pos, theta: float = 10000.0):
     v = torch.as_tensor(v).to(torch.float32).numpy()
     if pos is not None:
         table = rope_table_fp32(pos, q.shape[-1], theta)
-        q = _rotate_fp32(q, table)
-        k = _rotate_fp32(k, table)
+        q = rotate_fp32(q, table)
+        k = rotate_fp32(k, table)
     q8, sq = _quantize_rows(q)
     k8, sk = _quantize_rows(k)
     v8, sv = _quantize_rows(v)

@@ -50,7 +50,50 @@ def apply_rope(x, pos, theta: float = 10000.0) -> torch.Tensor:
 
 def rope_table_fp32(pos, head_dim: int, theta: float = 10000.0) -> np.ndarray:
     """(cos, sin) of every pair angle, computed in fp64 and rounded once to
-    fp32: float32 [S, D/2, 2].  This is the precision at which the FP8
-    quantizer takes its rounding decisions (see `oracle.fp8`)."""
+    fp32: float32 [S, D/2, 2]."""
     ang = rope_angles(pos, head_dim, theta)
     return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+
+
+def fma32(a, b, c) -> np.ndarray:
+    """Correctly rounded fp32 fused multiply-add a*b + c of fp32 arrays.
+
+    The product of two fp32 values is exact in fp64; the fp64 sum s = p + c
+    is rounded once, and TwoSum recovers its exact error e (p + c = s + e).
+    Rounding s to fp32 can only differ from rounding p + c when s lies
+    exactly halfway between two fp32 values and e != 0; then the exact value
+    is on e's side of the midpoint.
+    """
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    c = np.asarray(c, np.float32)
+    p = a.astype(np.float64) * b.astype(np.float64)
+    c64 = c.astype(np.float64)
+    s = p + c64
+    bb = s - p
+    e = (p - (s - bb)) + (c64 - bb)
+    r = s.astype(np.float32)
+    r64 = r.astype(np.float64)
+    toward_s = np.nextafter(r, np.where(s > r64, np.float32(np.inf), np.float32(-np.inf)))
+    tie = (r64 != s) & ((r64 + toward_s.astype(np.float64)) * 0.5 == s) & (e != 0)
+    # at a tie the exact value is above s when e > 0: pick the neighbour above
+    above = np.where(r64 > s, r, toward_s)
+    below = np.where(r64 > s, toward_s, r)
+    return np.where(tie, np.where(e > 0, above, below), r).astype(np.float32)
+
+
+def rotate_fp32(x, table) -> np.ndarray:
+    """RoPE of fp32 x [B, S, H, D] with an fp32 (cos, sin) table [S, D/2, 2],
+    in the operation order both kernels use, so that every rounding decision
+    taken on the result (bf16 operands, e4m3 codes) is reproducible:
+        x' = fma(x, cos, -fl(y sin)),   y' = fma(x, sin, fl(y cos)).
+    """
+    x = np.asarray(x, np.float32)
+    c = table[None, :, None, :, 0]
+    s = table[None, :, None, :, 1]
+    xe = x[..., 0::2]
+    xo = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = fma32(xe, c, -(xo * s))
+    out[..., 1::2] = fma32(xe, s, xo * c)
+    return out

@@ -1,0 +1,112 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/joint_attn.h declares, and rejects invalid calls on the host
+before anything is enqueued (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import joint_attention_attn_amd as ja
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "joint_attn.h")
+FAKE = 0x10000  # 16-byte aligned stand-in address; validation fails before use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ja.library_path()):
+        pytest.fail("libjoint_attn.so is not built (run __graft_entry__.build())")
+    return ja.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(joint_attn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"joint_attn_fwd_bf16", "joint_attn_fwd_fp8", "joint_attn_quant_rope_fp8",
+            "joint_attn_rope_table_2d", "joint_attn_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(4):
+        assert lib.joint_attn_status_string(code).startswith(b"JA_")
+    assert lib.joint_attn_status_string(99) == b"unknown ja_status"
+
+
+def _p(b=1, s=80, h=2, d=64):
+    p = ja.Params(b, s, h, d)
+    for x in "qkvo":
+        setattr(p, f"{x}_sb", s * h * d)
+        setattr(p, f"{x}_ss", h * d)
+        setattr(p, f"{x}_sh", d)
+    return p
+
+
+def _fwd(lib, p, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, rope=None, lse=None):
+    vp = ctypes.c_void_p
+    return lib.joint_attn_fwd_bf16(ctypes.byref(p) if p is not None else None, vp(q), vp(k),
+                                   vp(v), vp(rope), vp(o), vp(lse), None)
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda p: setattr(p, "batch", 0), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "seq_len", 0), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "heads", -1), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "head_dim", 96), ja.JA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "head_dim", 256), ja.JA_ERR_UNSUPPORTED),
+    (lambda p: setattr(p, "q_ss", 100), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "k_sh", 4), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "o_sb", -8), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "softmax_scale", float("nan")), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "softmax_scale", -1.0), ja.JA_ERR_INVALID_ARG),
+    (lambda p: setattr(p, "heads", 70000), ja.JA_ERR_UNSUPPORTED),
+])
+def test_fwd_bf16_rejects_bad_params(lib, mutate, expect):
+    p = _p()
+    mutate(p)
+    assert _fwd(lib, p) == expect
+
+
+def test_fwd_bf16_rejects_bad_pointers(lib):
+    assert _fwd(lib, None) == ja.JA_ERR_INVALID_ARG
+    assert _fwd(lib, _p(), q=0) == ja.JA_ERR_INVALID_ARG
+    assert _fwd(lib, _p(), o=0) == ja.JA_ERR_INVALID_ARG
+    assert _fwd(lib, _p(), k=FAKE + 2) == ja.JA_ERR_INVALID_ARG         # misaligned
+    assert _fwd(lib, _p(), rope=FAKE + 8) == ja.JA_ERR_INVALID_ARG      # misaligned table
+    assert _fwd(lib, _p(), lse=FAKE + 2) == ja.JA_ERR_INVALID_ARG
+    assert _fwd(lib, _p(), o=FAKE) == ja.JA_ERR_INVALID_ARG             # o aliases q
+
+
+def test_rope_table_validation(lib):
+    vp = ctypes.c_void_p
+    f = lib.joint_attn_rope_table_2d
+    assert f(vp(0), 10, 64, 10000.0, vp(FAKE), None) == ja.JA_ERR_INVALID_ARG
+    assert f(vp(FAKE), 0, 64, 10000.0, vp(FAKE), None) == ja.JA_ERR_INVALID_ARG
+    assert f(vp(FAKE), 10, 64, 0.0, vp(FAKE), None) == ja.JA_ERR_INVALID_ARG
+    assert f(vp(FAKE), 10, 64, float("inf"), vp(FAKE), None) == ja.JA_ERR_INVALID_ARG
+    assert f(vp(FAKE), 10, 48, 10000.0, vp(FAKE), None) == ja.JA_ERR_UNSUPPORTED
+    assert f(vp(FAKE), 10, 64, 10000.0, vp(FAKE + 4), None) == ja.JA_ERR_INVALID_ARG
+
+
+def test_quant_and_fp8_validation(lib):
+    vp = ctypes.c_void_p
+    p = _p()
+    ptrs = [vp(FAKE + 0x1000 * i) for i in range(10)]
+    bad = _p()
+    bad.head_dim = 32
+    assert lib.joint_attn_quant_rope_fp8(ctypes.byref(bad), *ptrs[:3], None, *ptrs[3:6],
+                                         *ptrs[6:9], None) == ja.JA_ERR_UNSUPPORTED
+    assert lib.joint_attn_quant_rope_fp8(ctypes.byref(p), vp(0), *ptrs[1:3], None, *ptrs[3:6],
+                                         *ptrs[6:9], None) == ja.JA_ERR_INVALID_ARG
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(bad), *ptrs[:3], *ptrs[3:6], ptrs[6], None,
+                                  None) == ja.JA_ERR_UNSUPPORTED
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], vp(FAKE + 4), *ptrs[4:6],
+                                  ptrs[6], None, None) == ja.JA_ERR_INVALID_ARG
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], vp(0), None,
+                                  None) == ja.JA_ERR_INVALID_ARG

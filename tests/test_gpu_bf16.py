@@ -1,0 +1,172 @@
+"""GPU parity of the RoPE table and the BF16 joint-attention forward against
+the fp64 oracle (calls go through the C ABI via the Python binding)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_attn_amd as ja
+import oracle
+import synth
+from parity_util import (BF16_MAX_ABS, BF16_REL_L2, max_abs, rel_l2,
+                         row_scaled_max_abs, sample_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _gpu_inputs(w, seed):
+    q, k, v, idx = synth.make_qkv(w, seed)
+    pos = synth.positions(w)
+    return q, k, v, idx, pos
+
+
+def _run_bf16(q, k, v, pos, theta=10000.0, **kw):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    rope = None
+    if pos is not None:
+        rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), q.shape[-1], theta)
+    out = ja.fwd_bf16(qd, kd, vd, rope, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,d", [("tiny", 64), ("t2i_2048", 128), ("i2i_2048", 128)])
+def test_rope_table_bit_exact(name, d):
+    w = synth.WORKLOADS[name].replace(head_dim=d)
+    pos = synth.positions(w)
+    _say(f"rope table {name} D={d} S={w.seq_len}")
+    got = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), d).cpu().numpy()
+    ref = oracle.rope_table_fp32(pos, d)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_tiny_full_parity():
+    w = synth.WORKLOADS["tiny"]
+    q, k, v, _, pos = _gpu_inputs(w, 0)
+    _say("bf16 tiny")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos)
+    assert rel_l2(out, ref) <= BF16_REL_L2
+    assert max_abs(out, ref) <= BF16_MAX_ABS
+    assert max_abs(lse, ref_lse) <= 1e-2
+
+
+@pytest.mark.parametrize("s,d", [(1, 64), (2, 128), (63, 64), (64, 128), (65, 64),
+                                 (127, 128), (129, 128), (200, 64), (1037, 128)])
+def test_ragged_lengths(s, d):
+    w = synth.Workload("ragged", 2, 3, d, n_text=s, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=s)
+    rng = np.random.default_rng(s)
+    pos = rng.integers(0, 200, size=(s, 2)).astype(np.int32)
+    _say(f"bf16 ragged S={s} D={d}")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos)
+    assert rel_l2(out, ref) <= BF16_REL_L2
+    assert max_abs(out, ref) <= BF16_MAX_ABS
+    assert max_abs(lse, ref_lse) <= 1e-2
+
+
+def test_no_rope_and_custom_scale():
+    w = synth.Workload("norope", 1, 2, 128, n_text=300, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=11)
+    _say("bf16 no-rope scale=0.05")
+    out = _run_bf16(q, k, v, None, softmax_scale=0.05)
+    ref, _ = oracle.joint_attention(q, k, v, None, scale=0.05)
+    assert rel_l2(out, ref) <= BF16_REL_L2 and max_abs(out, ref) <= BF16_MAX_ABS
+
+
+def test_strided_bhsd_layout():
+    # Q/K/V/O as [B, H, S, D] memory viewed as [B, S, H, D].
+    w = synth.Workload("strided", 2, 4, 64, n_text=8, grid=10)
+    q, k, v, _ = synth.make_qkv(w, seed=12)
+    pos = synth.positions(w)
+    qd, kd, vd = (t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3) for t in (q, k, v))
+    out = torch.empty((2, 4, w.seq_len, 64), dtype=torch.bfloat16, device=DEV).permute(0, 2, 1, 3)
+    rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), 64)
+    _say("bf16 strided BHSD")
+    ja.fwd_bf16(qd, kd, vd, rope, out=out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.joint_attention(q, k, v, pos)
+    assert rel_l2(out, ref) <= BF16_REL_L2 and max_abs(out, ref) <= BF16_MAX_ABS
+
+
+def test_closed_forms_on_gpu():
+    _say("bf16 closed forms")
+    # single key: O = V exactly
+    w = synth.Workload("one", 1, 2, 128, n_text=1, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=13)
+    out = _run_bf16(q, k, v, np.array([[5, 7]], np.int32))
+    assert torch.equal(out.cpu(), v)
+    # Q = 0: O = mean(V); V = 1: O = 1
+    w = synth.Workload("mean", 1, 2, 64, n_text=333, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=14)
+    pos = np.zeros((333, 2), np.int32)
+    out = _run_bf16(torch.zeros_like(q), k, v, pos)
+    mean = v.to(torch.float64).mean(dim=1, keepdim=True).expand(v.shape)
+    assert max_abs(out, mean) <= 4e-3
+    out = _run_bf16(q, k, torch.ones_like(v), pos)
+    assert torch.equal(out.cpu(), torch.ones_like(v))
+
+
+def test_deterministic_and_fully_written():
+    w = synth.WORKLOADS["t2i_1024"].replace(heads=4)
+    q, k, v, _, pos = _gpu_inputs(w, 3)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), 128)
+    _say("bf16 determinism")
+    outs = []
+    for _ in range(3):
+        o = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+        ja.fwd_bf16(qd, kd, vd, rope, out=o)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert not torch.isnan(outs[0]).any()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("name", ["t2i_1024", "t2i_1024_clean"])
+def test_1024_full_parity(name):
+    w = synth.WORKLOADS[name]
+    q, k, v, idx, pos = _gpu_inputs(w, 0)
+    _say(f"bf16 {name} full")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos)
+    err = rel_l2(out, ref)
+    _say(f"  rel_l2={err:.3e} max_abs={max_abs(out, ref):.3e} "
+         f"row_scaled={row_scaled_max_abs(out, ref):.3e}")
+    assert err <= BF16_REL_L2
+    if w.outlier_frac == 0:
+        assert max_abs(out, ref) <= BF16_MAX_ABS
+    else:
+        assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
+    assert max_abs(lse, ref_lse) <= 2e-2
+
+
+@pytest.mark.parametrize("name,n_rows", [("t2i_2048", 256), ("t2i_2048_clean", 256),
+                                         ("i2i_2048", 96)])
+def test_2048_sampled_parity(name, n_rows):
+    # Full-size launch (the benchmarked configuration); the oracle evaluates a
+    # seeded sample of query rows exactly (rows are independent).
+    w = synth.WORKLOADS[name]
+    q, k, v, idx, pos = _gpu_inputs(w, 0)
+    rows = sample_rows(w.seq_len, w.n_text, idx, n_rows, seed=1)
+    _say(f"bf16 {name} sampled rows={len(rows)}")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    out = out.cpu()[:, rows]
+    lse = lse.cpu()[:, :, rows]
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos, rows=rows)
+    err = rel_l2(out, ref)
+    _say(f"  rel_l2={err:.3e} max_abs={max_abs(out, ref):.3e} "
+         f"row_scaled={row_scaled_max_abs(out, ref):.3e}")
+    assert err <= BF16_REL_L2
+    if w.outlier_frac == 0:
+        assert max_abs(out, ref) <= BF16_MAX_ABS
+    else:
+        assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
+    assert max_abs(lse, ref_lse) <= 2e-2

@@ -79,17 +79,6 @@ def test_quantizer_properties():
     assert np.all(err <= half_ulp * (1 + 1e-6) + 1e-6)
 
 
-def test_fp32_rotation_close_to_fp64():
-    w = synth.WORKLOADS["tiny"]
-    q, _, _, _ = synth.make_qkv(w, seed=2)
-    pos = synth.positions(w)
-    tab = oracle.rope_table_fp32(pos, w.head_dim)
-    from oracle.fp8 import _rotate_fp32
-    r32 = _rotate_fp32(q.to(torch.float32).numpy(), tab)
-    r64 = oracle.apply_rope(q, pos).numpy()
-    assert np.allclose(r32, r64, rtol=0, atol=4e-6 * np.abs(r64).max())
-
-
 def test_fp8_attention_on_exact_inputs_is_plain_attention():
     # Inputs that are already e4m3 values with amax 448 quantize to scale 1
     # and themselves, so the FP8 reference must equal plain attention.
