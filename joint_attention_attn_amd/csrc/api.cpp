@@ -36,10 +36,12 @@ bool strides_ok(int64_t sb, int64_t ss, int64_t sh) {
   return sb >= 0 && ss >= 0 && sh >= 0 && sb % 8 == 0 && ss % 8 == 0 && sh % 8 == 0;
 }
 
-// Grid limits: x = query blocks, y = heads, z = batch.
+// Grid limits: the forward kernels launch one workgroup per
+// (query block, head, batch row) on a 1-D grid indexed with 32-bit ints.
 bool grid_ok(const ja_params *p, int block_rows) {
   const int64_t nx = ((int64_t)p->seq_len + block_rows - 1) / block_rows;
-  return nx <= 0x7fffffff && p->heads <= 65535 && p->batch <= 65535;
+  return nx * p->heads * p->batch <= 0x7fffffffLL && p->heads <= 65535 &&
+         p->batch <= 65535;
 }
 
 ja::AttnLayout layout(const ja_params *p) {

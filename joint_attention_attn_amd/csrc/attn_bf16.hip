@@ -7,16 +7,23 @@
 // "GEMM kernel optimization"); here it is applied in fp32 while Q and K are
 // loaded and the rotated values are rounded to bf16 for the MFMA.
 //
-// Work decomposition: one workgroup per (128-query block, head, batch row),
-// four wave64s of 32 query rows each.  Both products are computed transposed
+// Work decomposition: one workgroup per (256-query block, head, batch row),
+// eight wave64s of 32 query rows each.  Both products are computed transposed
 // so that a lane owns one query row throughout:
-//   S^T[key][q]  = K . Q^T      (v_mfma_f32_32x32x16_bf16, A = K from LDS,
-//                                B = rotated Q kept in registers)
-//   O^T[d][q]   += V^T . P^T    (A = V^T from LDS, B = P straight from the
+//   S^T[key][q]  = K . Q^T      (v_mfma_f32_32x32x16_bf16, A = rotated K from
+//                                LDS, B = rotated Q kept in registers)
+//   O^T[d][q]   += V^T . P^T    (A = V^T read from row-major V in LDS with
+//                                ds_read_b64_tr_b16, B = P straight from the
 //                                S^T accumulators)
 // With that orientation the online-softmax state (running max m and sum l,
-// fp32, exp2 domain) is per lane, the row max needs one cross-half exchange
-// and the O rescale is one multiply per accumulator.
+// fp32) is per lane, the row max needs one cross-half exchange and the O
+// rescale is one multiply per accumulator.
+//
+// K/V tiles of 64 keys are double-buffered in LDS: the next tile is loaded
+// from global memory into registers while the current one is consumed, then
+// K is rotated (fp32, rounded to bf16) and both are stored to the other
+// buffer; one barrier per tile.  Every K tile is rotated once per workgroup,
+// shared by its 256 query rows.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -24,9 +31,14 @@ namespace ja {
 
 namespace {
 
-constexpr int BM = 128;     // query rows per workgroup
+constexpr int BM = 256;     // query rows per workgroup
 constexpr int BN = 64;      // keys per K/V tile
-constexpr int VT_PAD = 8;   // bf16 padding of each transposed-V row in LDS
+constexpr int NT = 512;     // threads per workgroup (8 waves)
+
+// Rescale the output accumulator only when the running row max grows by more
+// than 2^8 in the exp2 domain; until then P may exceed 1 by up to 2^8, which
+// fp32 and bf16 carry exactly as well as values below 1.
+constexpr float kRescaleLog2 = 8.f;
 
 struct FwdArgs {
   const bf16 *q, *k, *v;
@@ -34,25 +46,69 @@ struct FwdArgs {
   bf16 *o;
   float *lse;
   int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_ss, o_sh;
-  int S, H;
+  int S, H, B, n_qblk;
   float scale_log2;
 };
 
+// LDS placement of 16-byte chunk c of key row r.
+// K rows are read by the QK^T operand load: 32 rows at one chunk per
+// instruction, so the chunk index is XOR-ed with r mod 8.
+__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 7); }
+// V rows are read by ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive
+// rows x 2 adjacent chunks, so the chunk index is XOR-ed with 2 (r mod 4).
+__device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 1); }
+
+// Max and sum of x over the two lanes l and l ^ 32 that share a query row.
+// v_permlane32_swap hands each lane the other half's value in one of its two
+// results and keeps its own in the other, so a symmetric combination of both
+// results is the cross-half reduction.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16 *p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p));
+  return bit_cast<u32x2>(v);
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int KCH = D / 8;              // 16-byte chunks per head vector
-  constexpr int VT_STRIDE = BN + VT_PAD;  // bf16 per transposed-V row
-  __shared__ __attribute__((aligned(16))) bf16 Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * VT_STRIDE];
+__global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int CH = D / 8;             // 16-byte chunks per head vector
+  constexpr int ROWS_PER_PASS = NT / CH;
+  constexpr int PASSES = BN / ROWS_PER_PASS;
+  constexpr int TILE = BN * D;          // bf16 elements per K or V tile
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int h = blockIdx.y, b = blockIdx.z;
+
+  // XCD-aware placement: workgroups are dispatched round-robin over the 8
+  // XCDs, so give each XCD a contiguous range of (q-block, head) work items;
+  // the workgroups resident on one XCD then stream the same head's K/V
+  // through that XCD's L2.
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = nwg >> 3, rem = nwg & 7;
+  const int item = xcd * per + min(xcd, rem) + slot;
+  const int qblk = item % a.n_qblk;
+  const int bh = item / a.n_qblk;
+  const int h = bh % a.H, b = bh / a.H;
   const int S = a.S;
 
   // ---- Q rows of this lane: rotate, round to bf16, keep in registers ----
-  const int qi = blockIdx.x * BM + wave * 32 + l32;
+  const int qi = qblk * BM + wave * 32 + l32;
   const int qs = qi < S ? qi : S - 1;
   const bf16 *qrow = a.q + b * a.q_sb + (int64_t)qs * a.q_ss + h * a.q_sh;
   bf16x8 qreg[D / 16];
@@ -65,41 +121,76 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
     qreg[kk] = bit_cast<bf16x8>(w);
   }
 
+  const bf16 *kbase = a.k + b * a.k_sb + h * a.k_sh;
+  const bf16 *vbase = a.v + b * a.v_sb + h * a.v_sh;
+  const int st_c = tid % CH;            // chunk this thread stages
+  const int st_r = tid / CH;            // first row this thread stages
+
+  // global -> registers for tile j0 (rows past S read as zeros)
+  u32x4 kreg[PASSES], vreg[PASSES];
+  float4 treg[PASSES][2];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int key = j0 + st_r + p * ROWS_PER_PASS;
+      kreg[p] = u32x4{0, 0, 0, 0};
+      vreg[p] = u32x4{0, 0, 0, 0};
+      if (key < S) {
+        kreg[p] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)key * a.k_ss + st_c * 8);
+        vreg[p] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * a.v_ss + st_c * 8);
+        if (a.rope) {
+          const float4 *t = reinterpret_cast<const float4 *>(a.rope + (int64_t)key * (D / 2) + st_c * 4);
+          treg[p][0] = t[0];
+          treg[p][1] = t[1];
+        }
+      }
+    }
+  };
+  // registers -> LDS buffer, rotating K on the way
+  auto store_tile = [&](int j0, int buf) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = st_r + p * ROWS_PER_PASS;
+      u32x4 kw = kreg[p];
+      if (a.rope && j0 + r < S) {
+        kw.x = rope_pair_bf16(kw.x, make_float2(treg[p][0].x, treg[p][0].y));
+        kw.y = rope_pair_bf16(kw.y, make_float2(treg[p][0].z, treg[p][0].w));
+        kw.z = rope_pair_bf16(kw.z, make_float2(treg[p][1].x, treg[p][1].y));
+        kw.w = rope_pair_bf16(kw.w, make_float2(treg[p][1].z, treg[p][1].w));
+      }
+      *reinterpret_cast<u32x4 *>(&Ks[buf][r * D + k_chunk(r, st_c) * 8]) = kw;
+      *reinterpret_cast<u32x4 *>(&Vs[buf][r * D + v_chunk(r, st_c) * 8]) = vreg[p];
+    }
+  };
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+  const float thresh = kRescaleLog2 / c;    // in raw score units
+  const uint32_t ones_bf16x2 = 0x3f803f80u;
 
-  const bf16 *kbase = a.k + b * a.k_sb + h * a.k_sh;
-  const bf16 *vbase = a.v + b * a.v_sb + h * a.v_sh;
+  // per-lane constants of the transposed V read: lane i of its 16-lane group
+  // addresses key row (i / 4) and d column 4 (i % 4) of a 4 x 16 block.
+  const int tr_i = lane & 15, tr_g = lane >> 4;
+  const int tr_row = tr_i >> 2;
+  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_i & 3);
 
-  for (int j0 = 0; j0 < S; j0 += BN) {
-    // ---- stage K (rotated) and V^T of this tile in LDS ----
-    for (int c = tid; c < BN * KCH; c += 256) {
-      const int r = c / KCH, ch = c % KCH;
-      const int key = j0 + r;
-      u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
-      if (key < S) {
-        kw = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)key * a.k_ss + ch * 8);
-        if (a.rope) kw = rope_chunk_bf16(kw, a.rope + (int64_t)key * (D / 2) + ch * 4);
-        vw = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * a.v_ss + ch * 8);
-      }
-      // 16-byte chunks of a K row are XOR-swizzled by the row index so that
-      // the 32 rows read by one MFMA operand load hit distinct banks.
-      *reinterpret_cast<u32x4 *>(Ks + r * D + ((ch ^ (r & 7)) * 8)) = kw;
-      uint16_t *vt = reinterpret_cast<uint16_t *>(Vt) + (ch * 8) * VT_STRIDE + r;
-      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[(2 * e) * VT_STRIDE] = (uint16_t)(vv[e] & 0xffffu);
-        vt[(2 * e + 1) * VT_STRIDE] = (uint16_t)(vv[e] >> 16);
-      }
-    }
-    __syncthreads();
+  load_tile(0);
+  store_tile(0, 0);
+  __syncthreads();
 
-    // ---- S^T = K . Q^T for this wave's 32 queries and the tile's 64 keys ----
+  const int ntiles = (S + BN - 1) / BN;
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BN;
+    const int buf = t & 1;
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) load_tile(j0 + BN);
+
+    // ---- S^T = K . Q^T: 32 queries of this wave x 64 keys ----
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -108,35 +199,41 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
       const int r = kb * 32 + l32;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        const int ch = 2 * kk + hf;
-        const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(Ks + r * D + ((ch ^ (r & 7)) * 8));
+        const bf16x8 kv =
+            *reinterpret_cast<const bf16x8 *>(&Ks[buf][r * D + k_chunk(r, 2 * kk + hf) * 8]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[kk], sacc[kb], 0, 0, 0);
       }
     }
 
-    // ---- online softmax (exp2 domain); accumulator row i of block kb is
-    //      key kb*32 + 8*(i/4) + 4*hf + i%4 ----
-    float mloc = -INFINITY;
-    const bool tail = j0 + BN > S;
+    // ---- online softmax; accumulator row i of block kb is key
+    //      kb*32 + 8*(i/4) + 4*hf + i%4 ----
+    if (j0 + BN > S) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (j0 + kb * 32 + 8 * (i / 4) + 4 * hf + (i % 4) >= S) sacc[kb][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = sacc[kb][i] * a.scale_log2;
-        if (tail) {
-          const int key = j0 + kb * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
-          if (key >= S) s = -INFINITY;
-        }
-        sacc[kb][i] = s;
-        mloc = fmaxf(mloc, s);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = half_max(mx);
+    const bool grow = mx > m_run + thresh;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+    }
+    const float mc = m_run * c;
 
     bf16x8 pb[2][2];
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -144,41 +241,41 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[kb][g * 8 + 2 * e] - m_new);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[kb][g * 8 + 2 * e + 1] - m_new);
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e + 1], c, -mc));
           w[e] = pack_bf16x2(p0, p1);
           // the normaliser sums the same bf16-rounded P that feeds P.V
-          psum += bf16_lo(w[e]) + bf16_hi(w[e]);
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(bit_cast<bf16x2>(w[e]),
+                                                  bit_cast<bf16x2>(ones_bf16x2), l_run, false);
         }
         pb[kb][g] = bit_cast<bf16x8>(u32x4{w[0], w[1], w[2], w[3]});
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 
     // ---- O^T += V^T . P^T ; P operand slot j of half hf (block kb, group g)
-    //      is key kb*32 + 16g + 4hf + (j<4 ? j : j+4) ----
+    //      is key 16(2kb+g) + 4hf + (j<4 ? j : j+4) ----
+    const bf16 *vt = Vs[buf];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint16_t *vrow = reinterpret_cast<const uint16_t *>(Vt) + (db * 32 + l32) * VT_STRIDE;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const int base = kb * 32 + g * 16 + 4 * hf;
-          const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + base);
-          const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + base + 8);
+          const int key0 = 16 * (2 * kb + g) + 4 * hf + tr_row;
+          const int dcol = 32 * db + tr_col;
+          const u32x2 lo = lds_read_tr16(vt + key0 * D + v_chunk(key0, dcol >> 3) * 8 + (dcol & 7));
+          const int key1 = key0 + 8;
+          const u32x2 hi = lds_read_tr16(vt + key1 * D + v_chunk(key1, dcol >> 3) * 8 + (dcol & 7));
           const bf16x8 va = bit_cast<bf16x8>(u32x4{lo.x, lo.y, hi.x, hi.y});
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][g], oacc[db], 0, 0, 0);
         }
     }
+
+    if (has_next) store_tile(j0 + BN, buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, bf16; LSE in natural log ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_sum(l_run);
   if (qi < S) {
     const float inv = 1.f / l_tot;
     bf16 *orow = a.o + b * a.o_sb + (int64_t)qi * a.o_ss + h * a.o_sh;
@@ -193,7 +290,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(FwdArgs a) {
         *reinterpret_cast<u32x2 *>(orow + d) = w;
       }
     if (a.lse && hf == 0)
-      a.lse[((int64_t)b * a.H + h) * S + qi] = (m_run + __log2f(l_tot)) * kLn2;
+      a.lse[((int64_t)b * a.H + h) * S + qi] = (m_run * c + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -217,12 +314,15 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
   a.o_sb = L.o_sb; a.o_ss = L.o_ss; a.o_sh = L.o_sh;
   a.S = L.S;
   a.H = L.H;
+  a.B = L.B;
+  a.n_qblk = (L.S + BM - 1) / BM;
   a.scale_log2 = L.scale_log2;
-  const dim3 grid((L.S + BM - 1) / BM, L.H, L.B);
+  const int64_t nwg = (int64_t)a.n_qblk * L.H * L.B;
+  const dim3 grid((unsigned)nwg);
   if (L.D == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
