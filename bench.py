@@ -54,6 +54,9 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain elementwise kernel that reads and writes BYTES "
+                         "(fp32 negation), to calibrate HBM byte counters, then exit")
     return ap.parse_args()
 
 
@@ -101,6 +104,15 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     dev = "cuda:0"
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n}))
+        return 0
     w = synth.WORKLOADS[args.config]
     B, S, H, D = w.shape
     flops = w.flops()

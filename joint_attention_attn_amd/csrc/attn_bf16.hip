@@ -21,9 +21,13 @@
 //
 // K/V tiles of 64 keys are double-buffered in LDS: the next tile is loaded
 // from global memory into registers while the current one is consumed, then
-// K is rotated (fp32, rounded to bf16) and both are stored to the other
-// buffer; one barrier per tile.  Every K tile is rotated once per workgroup,
-// shared by its 256 query rows.
+// K is rotated (fp32, rounded to bf16) and both are stored row-major to the
+// other buffer; one barrier per tile.  Every K tile is rotated once per
+// workgroup, shared by its 256 query rows.  V^T operands come from row-major V
+// through ds_read_b64_tr_b16 (a 16-lane group reads 4 key rows x 16 columns
+// and each lane receives one column's 4 keys).  Rows are padded (K by 16
+// bytes, V by 32 bytes) so that the lanes served together hit distinct banks
+// and every LDS address is a per-lane base plus a compile-time offset.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -50,14 +54,6 @@ struct FwdArgs {
   float scale_log2;
 };
 
-// LDS placement of 16-byte chunk c of key row r.
-// K rows are read by the QK^T operand load: 32 rows at one chunk per
-// instruction, so the chunk index is XOR-ed with r mod 8.
-__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 7); }
-// V rows are read by ds_read_b64_tr_b16: a 16-lane group reads 4 consecutive
-// rows x 2 adjacent chunks, so the chunk index is XOR-ed with 2 (r mod 4).
-__device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 1); }
-
 // Max and sum of x over the two lanes l and l ^ 32 that share a query row.
 // v_permlane32_swap hands each lane the other half's value in one of its two
 // results and keeps its own in the other, so a symmetric combination of both
@@ -82,13 +78,23 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const bf16 *p) {
 }
 
 template <int D>
+struct Lds {
+  static constexpr int KSTR = D + 8;        // bf16 per K row (16-byte pad)
+  static constexpr int VSTR = D + 16;       // bf16 per V row (32-byte pad)
+  static constexpr int KTILE = BN * KSTR;
+  static constexpr int VTILE = BN * VSTR;
+  static constexpr int BYTES = 2 * (KTILE + VTILE) * 2;
+};
+
+template <int D, bool ROPE>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;             // 16-byte chunks per head vector
   constexpr int ROWS_PER_PASS = NT / CH;
   constexpr int PASSES = BN / ROWS_PER_PASS;
-  constexpr int TILE = BN * D;          // bf16 elements per K or V tile
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][TILE];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][TILE];
+  constexpr int KSTR = Lds<D>::KSTR, VSTR = Lds<D>::VSTR;
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  auto Kbuf = [&](int buf) { return smem + buf * Lds<D>::KTILE; };
+  auto Vbuf = [&](int buf) { return smem + 2 * Lds<D>::KTILE + buf * Lds<D>::VTILE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   for (int kk = 0; kk < D / 16; ++kk) {
     const int d0 = 16 * kk + 8 * hf;
     u32x4 w = *reinterpret_cast<const u32x4 *>(qrow + d0);
-    if (a.rope) w = rope_chunk_bf16(w, a.rope + (int64_t)qs * (D / 2) + d0 / 2);
+    if constexpr (ROPE) w = rope_chunk_bf16(w, a.rope + (int64_t)qs * (D / 2) + d0 / 2);
     if (qi >= S) w = u32x4{0, 0, 0, 0};
     qreg[kk] = bit_cast<bf16x8>(w);
   }
@@ -126,72 +132,55 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int st_c = tid % CH;            // chunk this thread stages
   const int st_r = tid / CH;            // first row this thread stages
 
-  // global -> registers for tile j0 (rows past S read as zeros)
+  // ---- staging: global -> registers, then registers -> LDS (K rotated on
+  //      the way).  Rows past the end of the sequence load the last row
+  //      instead: their scores are masked to -inf and their P is 0, so any
+  //      finite values do, and the loads need no per-lane branch. ----
   u32x4 kreg[PASSES], vreg[PASSES];
   float4 treg[PASSES][2];
-  auto load_tile = [&](int j0) {
+  auto load_k = [&](int j0) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const int key = j0 + st_r + p * ROWS_PER_PASS;
-      kreg[p] = u32x4{0, 0, 0, 0};
-      vreg[p] = u32x4{0, 0, 0, 0};
-      if (key < S) {
-        kreg[p] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)key * a.k_ss + st_c * 8);
-        vreg[p] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * a.v_ss + st_c * 8);
-        if (a.rope) {
-          const float4 *t = reinterpret_cast<const float4 *>(a.rope + (int64_t)key * (D / 2) + st_c * 4);
-          treg[p][0] = t[0];
-          treg[p][1] = t[1];
-        }
+      const int key = min(j0 + st_r + p * ROWS_PER_PASS, S - 1);
+      kreg[p] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)key * a.k_ss + st_c * 8);
+      if constexpr (ROPE) {
+        const float4 *t = reinterpret_cast<const float4 *>(a.rope + (int64_t)key * (D / 2) + st_c * 4);
+        treg[p][0] = t[0];
+        treg[p][1] = t[1];
       }
     }
   };
-  // registers -> LDS buffer, rotating K on the way
-  auto store_tile = [&](int j0, int buf) {
+  auto load_v = [&](int j0) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int key = min(j0 + st_r + p * ROWS_PER_PASS, S - 1);
+      vreg[p] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * a.v_ss + st_c * 8);
+    }
+  };
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int r = st_r + p * ROWS_PER_PASS;
       u32x4 kw = kreg[p];
-      if (a.rope && j0 + r < S) {
+      if constexpr (ROPE) {
         kw.x = rope_pair_bf16(kw.x, make_float2(treg[p][0].x, treg[p][0].y));
         kw.y = rope_pair_bf16(kw.y, make_float2(treg[p][0].z, treg[p][0].w));
         kw.z = rope_pair_bf16(kw.z, make_float2(treg[p][1].x, treg[p][1].y));
         kw.w = rope_pair_bf16(kw.w, make_float2(treg[p][1].z, treg[p][1].w));
       }
-      *reinterpret_cast<u32x4 *>(&Ks[buf][r * D + k_chunk(r, st_c) * 8]) = kw;
-      *reinterpret_cast<u32x4 *>(&Vs[buf][r * D + v_chunk(r, st_c) * 8]) = vreg[p];
+      *reinterpret_cast<u32x4 *>(Kbuf(buf) + r * KSTR + st_c * 8) = kw;
+    }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int r = st_r + p * ROWS_PER_PASS;
+      *reinterpret_cast<u32x4 *>(Vbuf(buf) + r * VSTR + st_c * 8) = vreg[p];
     }
   };
 
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c = a.scale_log2;
-  const float thresh = kRescaleLog2 / c;    // in raw score units
-  const uint32_t ones_bf16x2 = 0x3f803f80u;
-
-  // per-lane constants of the transposed V read: lane i of its 16-lane group
-  // addresses key row (i / 4) and d column 4 (i % 4) of a 4 x 16 block.
-  const int tr_i = lane & 15, tr_g = lane >> 4;
-  const int tr_row = tr_i >> 2;
-  const int tr_col = 16 * (tr_g & 1) + 4 * (tr_i & 3);
-
-  load_tile(0);
-  store_tile(0, 0);
-  __syncthreads();
-
-  const int ntiles = (S + BN - 1) / BN;
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * BN;
-    const int buf = t & 1;
-    const bool has_next = t + 1 < ntiles;
-    if (has_next) load_tile(j0 + BN);
-
-    // ---- S^T = K . Q^T: 32 queries of this wave x 64 keys ----
-    f32x16 sacc[2];
+  // ---- S^T = K . Q^T for this wave's 32 queries and the 64 keys of a tile ----
+  auto qk = [&](int buf, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -200,14 +189,77 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         const bf16x8 kv =
-            *reinterpret_cast<const bf16x8 *>(&Ks[buf][r * D + k_chunk(r, 2 * kk + hf) * 8]);
+            *reinterpret_cast<const bf16x8 *>(Kbuf(buf) + r * KSTR + (2 * kk + hf) * 8);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[kk], sacc[kb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- online softmax; accumulator row i of block kb is key
-    //      kb*32 + 8*(i/4) + 4*hf + i%4 ----
-    if (j0 + BN > S) {
+  // per-lane part of the transposed V read: lane i of its 16-lane group
+  // addresses key row i / 4 and columns 4 (i % 4) .. +3 of a 4 x 16 block;
+  // groups 1 and 3 take the upper 16 columns of each 32-column block and
+  // lane half hf the keys 4 hf .. 4 hf + 3 of each group of 8.
+  const int tr_i = lane & 15;
+  const int tr_off = (4 * hf + (tr_i >> 2)) * VSTR + 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
+
+  // ---- O^T += V^T . P^T ; P operand slot j of half hf (block kb, group g)
+  //      is key 16(2kb+g) + 4hf + (j<4 ? j : j+4) ----
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  auto pv = [&](int buf, const bf16x8 (&pb)[2][2]) {
+    const bf16 *vt = Vbuf(buf) + tr_off;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const bf16 *p0 = vt + 16 * (2 * kb + g) * VSTR + 32 * db;
+          const u32x2 lo = lds_read_tr16(p0);
+          const u32x2 hi = lds_read_tr16(p0 + 8 * VSTR);
+          const bf16x8 va = bit_cast<bf16x8>(u32x4{lo.x, lo.y, hi.x, hi.y});
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][g], oacc[db], 0, 0, 0);
+        }
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+  const float thresh = kRescaleLog2 / c;    // in raw score units
+  const uint32_t ones_bf16x2 = 0x3f803f80u;
+
+  // ---- online softmax of one tile (scores in sacc; accumulator row i of
+  //      block kb is key kb*32 + 8*(i/4) + 4*hf + i%4).  P is first computed
+  //      against the running max m_run: that is exact and bounded by 2^8
+  //      unless some row's tile max exceeds m_run by the threshold, which is
+  //      rare after the first tile.  Then the slow path rescales O and l and
+  //      recomputes P against the new max. ----
+  auto exp_tile = [&](const f32x16 (&sacc)[2], float mref, bf16x8 (&pb)[2][2]) -> float {
+    const float mc = mref * c;
+    float lt = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e + 1], c, -mc));
+          w[e] = pack_bf16x2(p0, p1);
+          // the normaliser sums the same bf16-rounded P that feeds P.V
+          lt = __builtin_amdgcn_fdot2_f32_bf16(bit_cast<bf16x2>(w[e]),
+                                               bit_cast<bf16x2>(ones_bf16x2), lt, false);
+        }
+        pb[kb][g] = bit_cast<bf16x8>(u32x4{w[0], w[1], w[2], w[3]});
+      }
+    return lt;
+  };
+  auto softmax = [&]<bool TAIL>(f32x16 (&sacc)[2], int j0, bf16x8 (&pb)[2][2]) {
+    if constexpr (TAIL) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -221,7 +273,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = half_max(mx);
     const bool grow = mx > m_run + thresh;
+    float lt = exp_tile(sacc, m_run, pb);
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      // keep the speculative P computed before the branch (it is the result
+      // on the common path); here it is replaced
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 2; ++g) asm volatile("" ::"v"(pb[kb][g]));
       const float m_new = grow ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       m_run = m_new;
@@ -230,49 +289,52 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      lt = exp_tile(sacc, m_new, pb);
     }
-    const float mc = m_run * c;
+    l_run += lt;
+  };
 
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e + 1], c, -mc));
-          w[e] = pack_bf16x2(p0, p1);
-          // the normaliser sums the same bf16-rounded P that feeds P.V
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(bit_cast<bf16x2>(w[e]),
-                                                  bit_cast<bf16x2>(ones_bf16x2), l_run, false);
-        }
-        pb[kb][g] = bit_cast<bf16x8>(u32x4{w[0], w[1], w[2], w[3]});
-      }
-
-    // ---- O^T += V^T . P^T ; P operand slot j of half hf (block kb, group g)
-    //      is key 16(2kb+g) + 4hf + (j<4 ? j : j+4) ----
-    const bf16 *vt = Vs[buf];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int key0 = 16 * (2 * kb + g) + 4 * hf + tr_row;
-          const int dcol = 32 * db + tr_col;
-          const u32x2 lo = lds_read_tr16(vt + key0 * D + v_chunk(key0, dcol >> 3) * 8 + (dcol & 7));
-          const int key1 = key0 + 8;
-          const u32x2 hi = lds_read_tr16(vt + key1 * D + v_chunk(key1, dcol >> 3) * 8 + (dcol & 7));
-          const bf16x8 va = bit_cast<bf16x8>(u32x4{lo.x, lo.y, hi.x, hi.y});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][g], oacc[db], 0, 0, 0);
-        }
-    }
-
-    if (has_next) store_tile(j0 + BN, buf ^ 1);
-    __syncthreads();
+  // ---- software pipeline over key tiles.  K tile x lives in K buffer x%2
+  //      and V tile x in V buffer x%2.  Iteration t computes Q K^T of tile
+  //      t+1 while it runs the softmax of tile t, then P.V of tile t while it
+  //      rotates and stores K of tile t+2 and V of tile t+1 (both into the
+  //      buffers freed by iteration t-1); one barrier per iteration. ----
+  const int ntiles = (S + BN - 1) / BN;
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (ntiles > 1) {
+    load_k(BN);
+    store_k(1);
   }
+  __syncthreads();
+  f32x16 s_cur[2];
+  qk(0, s_cur);
+
+  // NEXT: a tile t+1 exists (Q K^T of it, V of it staged); K2: a tile t+2
+  // exists (its K staged).  Only the last tile can be partial.
+  auto iteration = [&]<bool NEXT, bool K2>(int t) {
+    const int j0 = t * BN;
+    if constexpr (K2) load_k(j0 + 2 * BN);
+    if constexpr (NEXT) load_v(j0 + BN);
+    f32x16 s_next[2];
+    if constexpr (NEXT) qk((t + 1) & 1, s_next);
+    bf16x8 pb[2][2];
+    softmax.template operator()<!NEXT>(s_cur, j0, pb);
+    pv(t & 1, pb);
+    if constexpr (K2) store_k(t & 1);
+    if constexpr (NEXT) store_v((t + 1) & 1);
+    __syncthreads();
+    if constexpr (NEXT) {
+      s_cur[0] = s_next[0];
+      s_cur[1] = s_next[1];
+    }
+  };
+  int t = 0;
+  for (; t + 2 < ntiles; ++t) iteration.template operator()<true, true>(t);
+  if (t + 1 < ntiles) iteration.template operator()<true, false>(t++);
+  iteration.template operator()<false, false>(t);
 
   // ---- epilogue: O = acc / l, bf16; LSE in natural log ----
   const float l_tot = half_sum(l_run);
@@ -319,10 +381,24 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
   a.scale_log2 = L.scale_log2;
   const int64_t nwg = (int64_t)a.n_qblk * L.H * L.B;
   const dim3 grid((unsigned)nwg);
-  if (L.D == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, dim3(NT), 0, st, a);
+  const bool rope_on = rope != nullptr;
+  if (L.D == 64) {
+    auto kern = rope_on ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(NT), Lds<64>::BYTES, st, a);
+  } else {
+    static const hipError_t attr = []() {
+      hipError_t e = hipFuncSetAttribute(
+          reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<128, true>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::BYTES);
+      if (e != hipSuccess) return e;
+      return hipFuncSetAttribute(
+          reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<128, false>),
+          hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::BYTES);
+    }();
+    if (attr != hipSuccess) return attr;
+    auto kern = rope_on ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(NT), Lds<128>::BYTES, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libjoint_attn.so")
 SOURCES = ["api.cpp", "rope_table.hip", "attn_bf16.hip", "quant_fp8.hip", "attn_fp8.hip"]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are left to nobody: the compiler may not emit them.
-FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-command-line-argument"]
 
