@@ -113,6 +113,14 @@ ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
       (rope && !aligned16(rope)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return JA_ERR_INVALID_ARG;
   if (o == q || o == k || o == v) return JA_ERR_INVALID_ARG;
+  // K, V and the RoPE table of one (batch, head) are addressed with 32-bit
+  // byte offsets
+  const int64_t span_k = ((int64_t)(p->seq_len - 1) * p->k_ss + p->head_dim) * 2;
+  const int64_t span_v = ((int64_t)(p->seq_len - 1) * p->v_ss + p->head_dim) * 2;
+  const int64_t span_t = (int64_t)p->seq_len * p->head_dim * 4;
+  if (span_k > 0x7fffffffLL || span_v > 0x7fffffffLL || span_t > 0x7fffffffLL ||
+      64 * p->k_ss * 2 > 0x7fffffffLL || 64 * p->v_ss * 2 > 0x7fffffffLL)
+    return JA_ERR_UNSUPPORTED;
   return hip_status(ja::launch_fwd_bf16(layout(p), q, k, v, rope, o, lse,
                                         static_cast<hipStream_t>(stream)));
 }

@@ -44,6 +44,10 @@ constexpr int NT = 512;     // threads per workgroup (8 waves)
 // fp32 and bf16 carry exactly as well as values below 1.
 constexpr float kRescaleLog2 = 8.f;
 
+// Buffer-resource word 3 for raw (unswizzled, unformatted 32-bit) buffer
+// access on gfx950: out-of-range reads return zeros.
+constexpr int kBufferFlags = 0x00020000;
+
 struct FwdArgs {
   const bf16 *q, *k, *v;
   const float2 *rope;
@@ -132,30 +136,42 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int st_c = tid % CH;            // chunk this thread stages
   const int st_r = tid / CH;            // first row this thread stages
 
-  // ---- staging: global -> registers, then registers -> LDS (K rotated on
-  //      the way).  Rows past the end of the sequence load the last row
-  //      instead: their scores are masked to -inf and their P is 0, so any
-  //      finite values do, and the loads need no per-lane branch. ----
+  // ---- staging: global -> registers through buffer resources, then
+  //      registers -> LDS (K rotated on the way).  Each lane's byte offset
+  //      inside a tile is fixed; the tile offset is a scalar.  The resource
+  //      ends after row S-1, so rows past the end of the sequence read as
+  //      zeros (their scores are masked, their P is 0). ----
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16 *>(kbase), 0, (int)(((int64_t)(S - 1) * a.k_ss + D) * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16 *>(vbase), 0, (int)(((int64_t)(S - 1) * a.v_ss + D) * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float2 *>(a.rope), 0, ROPE ? S * D * 4 : 0, kBufferFlags);
+  int koff[PASSES], voff[PASSES], toff[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int r = st_r + p * ROWS_PER_PASS;
+    koff[p] = (int)(r * a.k_ss * 2) + st_c * 16;
+    voff[p] = (int)(r * a.v_ss * 2) + st_c * 16;
+    toff[p] = r * D * 4 + st_c * 32;
+  }
+  const int ktile_bytes = (int)(BN * a.k_ss * 2), vtile_bytes = (int)(BN * a.v_ss * 2);
   u32x4 kreg[PASSES], vreg[PASSES];
   float4 treg[PASSES][2];
-  auto load_k = [&](int j0) {
+  auto load_k = [&](int t) {
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-      const int key = min(j0 + st_r + p * ROWS_PER_PASS, S - 1);
-      kreg[p] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)key * a.k_ss + st_c * 8);
+      kreg[p] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(krs, koff[p], t * ktile_bytes, 0));
       if constexpr (ROPE) {
-        const float4 *t = reinterpret_cast<const float4 *>(a.rope + (int64_t)key * (D / 2) + st_c * 4);
-        treg[p][0] = t[0];
-        treg[p][1] = t[1];
+        treg[p][0] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff[p], t * BN * D * 4, 0));
+        treg[p][1] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff[p] + 16, t * BN * D * 4, 0));
       }
     }
   };
-  auto load_v = [&](int j0) {
+  auto load_v = [&](int t) {
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int key = min(j0 + st_r + p * ROWS_PER_PASS, S - 1);
-      vreg[p] = *reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * a.v_ss + st_c * 8);
-    }
+    for (int p = 0; p < PASSES; ++p)
+      vreg[p] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(vrs, voff[p], t * vtile_bytes, 0));
   };
   auto store_k = [&](int buf) {
 #pragma unroll
@@ -305,36 +321,40 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   store_k(0);
   store_v(0);
   if (ntiles > 1) {
-    load_k(BN);
+    load_k(1);
     store_k(1);
   }
   __syncthreads();
-  f32x16 s_cur[2];
-  qk(0, s_cur);
+  f32x16 s_a[2], s_b[2];
+  qk(0, s_a);
 
-  // NEXT: a tile t+1 exists (Q K^T of it, V of it staged); K2: a tile t+2
-  // exists (its K staged).  Only the last tile can be partial.
-  auto iteration = [&]<bool NEXT, bool K2>(int t) {
+  // One pipeline step: softmax of tile t from `cur`, Q K^T of tile t+1 into
+  // `nxt`.  NEXT: a tile t+1 exists (its Q K^T computed, its V staged); K2: a
+  // tile t+2 exists (its K staged).  Only the last tile can be partial.
+  auto iteration = [&]<bool NEXT, bool K2>(int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     const int j0 = t * BN;
-    if constexpr (K2) load_k(j0 + 2 * BN);
-    if constexpr (NEXT) load_v(j0 + BN);
-    f32x16 s_next[2];
-    if constexpr (NEXT) qk((t + 1) & 1, s_next);
+    if constexpr (K2) load_k(t + 2);
+    if constexpr (NEXT) load_v(t + 1);
+    if constexpr (NEXT) qk((t + 1) & 1, nxt);
     bf16x8 pb[2][2];
-    softmax.template operator()<!NEXT>(s_cur, j0, pb);
+    softmax.template operator()<!NEXT>(cur, j0, pb);
     pv(t & 1, pb);
     if constexpr (K2) store_k(t & 1);
     if constexpr (NEXT) store_v((t + 1) & 1);
     __syncthreads();
-    if constexpr (NEXT) {
-      s_cur[0] = s_next[0];
-      s_cur[1] = s_next[1];
-    }
   };
   int t = 0;
-  for (; t + 2 < ntiles; ++t) iteration.template operator()<true, true>(t);
-  if (t + 1 < ntiles) iteration.template operator()<true, false>(t++);
-  iteration.template operator()<false, false>(t);
+  for (; t + 2 < ntiles; ++t) {
+    iteration.template operator()<true, true>(t, s_a, s_b);
+    s_a[0] = s_b[0];
+    s_a[1] = s_b[1];
+  }
+  if (t + 1 < ntiles) {
+    iteration.template operator()<true, false>(t, s_a, s_b);
+    iteration.template operator()<false, false>(t + 1, s_b, s_a);
+  } else {
+    iteration.template operator()<false, false>(t, s_a, s_b);
+  }
 
   // ---- epilogue: O = acc / l, bf16; LSE in natural log ----
   const float l_tot = half_sum(l_run);
