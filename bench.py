@@ -35,7 +35,7 @@ METRIC = "joint-attention fwd TFLOP/s and % of MFMA peak at 2048x2048 (16896 tok
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_bf16_t2i_2048.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_t2i_2048_traffic.txt")
 BF16_SOURCE = os.path.join(ROOT, "joint_attention_attn_amd", "csrc", "attn_bf16.hip")
 
 
@@ -65,13 +65,17 @@ def _traffic_for_current_kernel():
     were taken on the kernel source as it is now."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
+    rec = {}
     with open(TRAFFIC_FILE) as f:
-        rec = json.load(f)
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
     with open(BF16_SOURCE, "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != sha or "hbm_bytes_per_launch" not in rec:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return float(rec["hbm_bytes_per_launch"])
 
 
 def _time_launches(fn, n):
