@@ -12,22 +12,23 @@
 // so that a lane owns one query row throughout:
 //   S^T[key][q]  = K . Q^T      (v_mfma_f32_32x32x16_bf16, A = rotated K from
 //                                LDS, B = rotated Q kept in registers)
-//   O^T[d][q]   += V^T . P^T    (A = V^T read from row-major V in LDS with
-//                                ds_read_b64_tr_b16, B = P straight from the
-//                                S^T accumulators)
+//   O^T[d][q]   += V^T . P^T    (A = V^T from LDS, B = P straight from the S^T
+//                                accumulators)
 // With that orientation the online-softmax state (running max m and sum l,
 // fp32) is per lane, the row max needs one cross-half exchange and the O
 // rescale is one multiply per accumulator.
 //
-// K/V tiles of 64 keys are double-buffered in LDS: the next tile is loaded
-// from global memory into registers while the current one is consumed, then
-// K is rotated (fp32, rounded to bf16) and both are stored row-major to the
-// other buffer; one barrier per tile.  Every K tile is rotated once per
-// workgroup, shared by its 256 query rows.  V^T operands come from row-major V
-// through ds_read_b64_tr_b16 (a 16-lane group reads 4 key rows x 16 columns
-// and each lane receives one column's 4 keys).  Rows are padded (K by 16
-// bytes, V by 32 bytes) so that the lanes served together hit distinct banks
-// and every LDS address is a per-lane base plus a compile-time offset.
+// K/V tiles of 32 keys are double-buffered in LDS.  K is staged row-major
+// (rotated in fp32 and rounded to bf16 on the way); V is staged transposed
+// (one row per head-dimension column, the keys of a row in the order in which
+// the P operand holds them), so both MFMA operands are single 16-byte LDS
+// reads.  Rows are padded so that the 16 lanes served together hit distinct
+// banks.
+//
+// Pipeline: iteration t computes Q K^T of tile t+1 in the same basic block as
+// the softmax of tile t, so those MFMAs overlap its VALU work; after the
+// (rare) rescale branch, P.V of tile t overlaps the rotation and staging of K
+// tile t+2 and V tile t+1.  One barrier per iteration.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -35,18 +36,37 @@ namespace ja {
 
 namespace {
 
-constexpr int BM = 256;     // query rows per workgroup
-constexpr int BN = 64;      // keys per K/V tile
-constexpr int NT = 512;     // threads per workgroup (8 waves)
+#ifndef JA_BF16_WAVES
+#define JA_BF16_WAVES 8
+#endif
+#ifndef JA_BF16_STAGE_WAVES
+#define JA_BF16_STAGE_WAVES JA_BF16_WAVES
+#endif
+#ifndef JA_BF16_RW
+#define JA_BF16_RW 1
+#endif
+constexpr int NW = JA_BF16_WAVES;   // waves per workgroup
+constexpr int RW = JA_BF16_RW;      // 32-row query blocks per wave
+constexpr int BM = 32 * RW * NW;    // query rows per workgroup
+constexpr int BN = 32;              // keys per K/V tile
+constexpr int NT = 64 * NW;         // threads per workgroup
+constexpr int NS = 64 * JA_BF16_STAGE_WAVES;   // threads that stage K/V tiles
+// Workgroups resident per CU: two waves per SIMD in total, so that while one
+// waits on memory or on its workgroup's barrier the other one issues.
+constexpr int WG_PER_CU = 8 / (NW * RW) > 0 ? 8 / (NW * RW) : 1;
 
 // Rescale the output accumulator only when the running row max grows by more
-// than 2^8 in the exp2 domain; until then P may exceed 1 by up to 2^8, which
-// fp32 and bf16 carry exactly as well as values below 1.
-constexpr float kRescaleLog2 = 8.f;
+// than 2^24 in the exp2 domain.  Until then P may exceed 1 by up to 2^24;
+// fp32 and bf16 carry such values with the same relative precision as values
+// below 1, and the sums stay far below the fp32 range.
+constexpr float kRescaleLog2 = 24.f;
 
 // Buffer-resource word 3 for raw (unswizzled, unformatted 32-bit) buffer
-// access on gfx950: out-of-range reads return zeros.
+// access on gfx950: reads outside [0, num_records) return zeros (the check
+// covers the scalar offset too).
 constexpr int kBufferFlags = 0x00020000;
+
+#define JA_INLINE __attribute__((always_inline))
 
 struct FwdArgs {
   const bf16 *q, *k, *v;
@@ -73,32 +93,38 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ u32x2 lds_read_tr16(const bf16 *p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(p));
-  return bit_cast<u32x2>(v);
-}
-
 template <int D>
 struct Lds {
   static constexpr int KSTR = D + 8;        // bf16 per K row (16-byte pad)
-  static constexpr int VSTR = D + 16;       // bf16 per V row (32-byte pad)
+  static constexpr int VTSTR = BN + 8;      // bf16 per V^T row (16-byte pad)
   static constexpr int KTILE = BN * KSTR;
-  static constexpr int VTILE = BN * VSTR;
+  static constexpr int VTILE = D * VTSTR;
   static constexpr int BYTES = 2 * (KTILE + VTILE) * 2;
 };
 
+// Position, inside a 16-key group of a V^T row, of key k: the P operand of
+// lane half hf holds keys 4hf + {0..3} and 4hf + {8..11} of the group in its
+// eight slots, so V^T stores them at 8hf + slot.
+__host__ __device__ constexpr int vt_key_of_slot(int p) {
+  return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
+}
+
 template <int D, bool ROPE>
-__global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int CH = D / 8;             // 16-byte chunks per head vector
-  constexpr int ROWS_PER_PASS = NT / CH;
-  constexpr int PASSES = BN / ROWS_PER_PASS;
-  constexpr int KSTR = Lds<D>::KSTR, VSTR = Lds<D>::VSTR;
+__global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int CH = D / 8;                  // 16-byte chunks per K row
+  constexpr int K_CHUNKS = BN * CH;          // 16-byte K chunks per tile
+  constexpr int V_SLOTS = D * (BN / 8);      // 8-key V^T slots per tile
+  constexpr int KP = (K_CHUNKS + NS - 1) / NS;   // K chunks per staging thread
+  constexpr int VP = (V_SLOTS + NS - 1) / NS;    // V^T slots per staging thread
+  static_assert(K_CHUNKS % NS == 0 || K_CHUNKS < NS, "staging layout");
+  static_assert(V_SLOTS % NS == 0 || V_SLOTS < NS, "staging layout");
+  static_assert(NS % D == 0, "V^T slot groups must be wave-uniform");
+  constexpr int K_THREADS = K_CHUNKS < NS ? K_CHUNKS : NS;
+  constexpr int V_THREADS = V_SLOTS < NS ? V_SLOTS : NS;
+  constexpr int KSTR = Lds<D>::KSTR, VTSTR = Lds<D>::VTSTR;
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-  auto Kbuf = [&](int buf) { return smem + buf * Lds<D>::KTILE; };
-  auto Vbuf = [&](int buf) { return smem + 2 * Lds<D>::KTILE + buf * Lds<D>::VTILE; };
+  auto Kbuf = [&](int buf) JA_INLINE { return smem + buf * Lds<D>::KTILE; };
+  auto Vbuf = [&](int buf) JA_INLINE { return smem + 2 * Lds<D>::KTILE + buf * Lds<D>::VTILE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -117,66 +143,82 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int h = bh % a.H, b = bh / a.H;
   const int S = a.S;
 
-  // ---- Q rows of this lane: rotate, round to bf16, keep in registers ----
-  const int qi = qblk * BM + wave * 32 + l32;
-  const int qs = qi < S ? qi : S - 1;
-  const bf16 *qrow = a.q + b * a.q_sb + (int64_t)qs * a.q_ss + h * a.q_sh;
-  bf16x8 qreg[D / 16];
+  // ---- Q rows of this lane (one per 32-row block): rotate, round to bf16,
+  //      keep in registers ----
+  int qi[RW];
+  bf16x8 qreg[RW][D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const int d0 = 16 * kk + 8 * hf;
-    u32x4 w = *reinterpret_cast<const u32x4 *>(qrow + d0);
-    if constexpr (ROPE) w = rope_chunk_bf16(w, a.rope + (int64_t)qs * (D / 2) + d0 / 2);
-    if (qi >= S) w = u32x4{0, 0, 0, 0};
-    qreg[kk] = bit_cast<bf16x8>(w);
+  for (int r = 0; r < RW; ++r) {
+    qi[r] = qblk * BM + (wave * RW + r) * 32 + l32;
+    const int qs = qi[r] < S ? qi[r] : S - 1;
+    const bf16 *qrow = a.q + b * a.q_sb + (int64_t)qs * a.q_ss + h * a.q_sh;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int d0 = 16 * kk + 8 * hf;
+      u32x4 w = *reinterpret_cast<const u32x4 *>(qrow + d0);
+      if constexpr (ROPE) w = rope_chunk_bf16(w, a.rope + (int64_t)qs * (D / 2) + d0 / 2);
+      if (qi[r] >= S) w = u32x4{0, 0, 0, 0};
+      qreg[r][kk] = bit_cast<bf16x8>(w);
+    }
   }
 
+  // ---- staging: global -> registers through buffer resources, then
+  //      registers -> LDS.  Per-lane offsets inside a tile are fixed; the
+  //      tile offset is scalar.  Each resource ends after row S-1, so rows
+  //      past the end of the sequence read as zeros (their scores are masked
+  //      and their P is 0). ----
   const bf16 *kbase = a.k + b * a.k_sb + h * a.k_sh;
   const bf16 *vbase = a.v + b * a.v_sb + h * a.v_sh;
-  const int st_c = tid % CH;            // chunk this thread stages
-  const int st_r = tid / CH;            // first row this thread stages
-
-  // ---- staging: global -> registers through buffer resources, then
-  //      registers -> LDS (K rotated on the way).  Each lane's byte offset
-  //      inside a tile is fixed; the tile offset is a scalar.  The resource
-  //      ends after row S-1, so rows past the end of the sequence read as
-  //      zeros (their scores are masked, their P is 0). ----
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16 *>(kbase), 0, (int)(((int64_t)(S - 1) * a.k_ss + D) * 2), kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16 *>(vbase), 0, (int)(((int64_t)(S - 1) * a.v_ss + D) * 2), kBufferFlags);
   const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float2 *>(a.rope), 0, ROPE ? S * D * 4 : 0, kBufferFlags);
-  int koff[PASSES], voff[PASSES], toff[PASSES];
+
+  // K: pass p of a staging thread stages chunk st_c of row st_r + p * (NS / CH)
+  const int st_r = tid / CH, st_c = tid % CH;
+  const int koff = (int)(st_r * a.k_ss * 2) + st_c * 16;
+  const int toff = st_r * D * 4 + st_c * 32;
+  const int ktile_bytes = (int)(BN * a.k_ss * 2);
+  const int kpass_bytes = (int)((NS / CH) * a.k_ss * 2);
+  // V^T: pass p of a thread stages column vd, slots 8 vc .. 8 vc + 7 with
+  // vc = tid / D + p * (NS / D) (wave-uniform)
+  const int vd = tid % D;
+  const int vc0 = __builtin_amdgcn_readfirstlane(tid / D);
+  const int vrow_bytes = (int)(a.v_ss * 2);
+  u32x4 kreg[KP];
+  float4 treg[KP][2];
+  uint16_t vreg[VP][8];
+  auto load_k = [&](int t) JA_INLINE {
+    if (K_THREADS < NT && tid >= K_THREADS) return;
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int r = st_r + p * ROWS_PER_PASS;
-    koff[p] = (int)(r * a.k_ss * 2) + st_c * 16;
-    voff[p] = (int)(r * a.v_ss * 2) + st_c * 16;
-    toff[p] = r * D * 4 + st_c * 32;
-  }
-  const int ktile_bytes = (int)(BN * a.k_ss * 2), vtile_bytes = (int)(BN * a.v_ss * 2);
-  u32x4 kreg[PASSES], vreg[PASSES];
-  float4 treg[PASSES][2];
-  auto load_k = [&](int t) {
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      kreg[p] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(krs, koff[p], t * ktile_bytes, 0));
+    for (int p = 0; p < KP; ++p) {
+      kreg[p] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
+          krs, koff, t * ktile_bytes + p * kpass_bytes, 0));
       if constexpr (ROPE) {
-        treg[p][0] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff[p], t * BN * D * 4, 0));
-        treg[p][1] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff[p] + 16, t * BN * D * 4, 0));
+        const int tt = (t * BN + p * (NS / CH)) * D * 4;
+        treg[p][0] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff, tt, 0));
+        treg[p][1] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff + 16, tt, 0));
       }
     }
   };
-  auto load_v = [&](int t) {
+  auto load_v = [&](int t) JA_INLINE {
+    if (V_THREADS < NT && tid >= V_THREADS) return;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p)
-      vreg[p] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(vrs, voff[p], t * vtile_bytes, 0));
+    for (int p = 0; p < VP; ++p) {
+      const int vc = vc0 + p * (NS / D);
+      const int key0 = t * BN + 16 * (vc >> 1);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        vreg[p][j] = __builtin_amdgcn_raw_buffer_load_b16(
+            vrs, vd * 2, (key0 + vt_key_of_slot(8 * (vc & 1) + j)) * vrow_bytes, 0);
+    }
   };
-  auto store_k = [&](int buf) {
+  auto store_k = [&](int buf) JA_INLINE {
+    if (K_THREADS < NT && tid >= K_THREADS) return;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int r = st_r + p * ROWS_PER_PASS;
+    for (int p = 0; p < KP; ++p) {
       u32x4 kw = kreg[p];
       if constexpr (ROPE) {
         kw.x = rope_pair_bf16(kw.x, make_float2(treg[p][0].x, treg[p][0].y));
@@ -184,137 +226,146 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         kw.z = rope_pair_bf16(kw.z, make_float2(treg[p][1].x, treg[p][1].y));
         kw.w = rope_pair_bf16(kw.w, make_float2(treg[p][1].z, treg[p][1].w));
       }
-      *reinterpret_cast<u32x4 *>(Kbuf(buf) + r * KSTR + st_c * 8) = kw;
+      *reinterpret_cast<u32x4 *>(Kbuf(buf) + (st_r + p * (NS / CH)) * KSTR + st_c * 8) = kw;
     }
   };
-  auto store_v = [&](int buf) {
+  auto store_v = [&](int buf) JA_INLINE {
+    if (V_THREADS < NT && tid >= V_THREADS) return;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int r = st_r + p * ROWS_PER_PASS;
-      *reinterpret_cast<u32x4 *>(Vbuf(buf) + r * VSTR + st_c * 8) = vreg[p];
+    for (int p = 0; p < VP; ++p) {
+      const int vc = vc0 + p * (NS / D);
+      u32x4 w;
+      w.x = (uint32_t)vreg[p][0] | ((uint32_t)vreg[p][1] << 16);
+      w.y = (uint32_t)vreg[p][2] | ((uint32_t)vreg[p][3] << 16);
+      w.z = (uint32_t)vreg[p][4] | ((uint32_t)vreg[p][5] << 16);
+      w.w = (uint32_t)vreg[p][6] | ((uint32_t)vreg[p][7] << 16);
+      *reinterpret_cast<u32x4 *>(Vbuf(buf) + vd * VTSTR + 8 * vc) = w;
     }
   };
 
-  // ---- S^T = K . Q^T for this wave's 32 queries and the 64 keys of a tile ----
-  auto qk = [&](int buf, f32x16 (&sacc)[2]) {
+  // ---- S^T = K . Q^T for this wave's 32 queries and the 32 keys of a tile,
+  //      in two halves over the head dimension ----
+  auto qk = [&]<int KK0, int KK1>(int buf, f32x16 (&sacc)[RW]) JA_INLINE {
+    if constexpr (KK0 == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int r = 0; r < RW; ++r)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const int r = kb * 32 + l32;
+        for (int i = 0; i < 16; ++i) sacc[r][i] = 0.f;
+    }
+    const bf16 *krow = Kbuf(buf) + l32 * KSTR + 8 * hf;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const bf16x8 kv =
-            *reinterpret_cast<const bf16x8 *>(Kbuf(buf) + r * KSTR + (2 * kk + hf) * 8);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[kk], sacc[kb], 0, 0, 0);
+    for (int kk = KK0; kk < KK1; ++kk) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(krow + 16 * kk);
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+        sacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[r][kk], sacc[r], 0, 0, 0);
+    }
+  };
+
+  // ---- O^T += V^T . P^T ; P operand slot j of half hf (key group g) is key
+  //      16g + 4hf + (j<4 ? j : j+4), which V^T stores at 16g + 8hf + j ----
+  f32x16 oacc[RW][D / 32];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[r][db][i] = 0.f;
+  auto pv = [&](const bf16x8 (&pb)[RW][2], int buf) JA_INLINE {
+    const bf16 *vt = Vbuf(buf) + l32 * VTSTR + 8 * hf;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vt + 32 * db * VTSTR + 16 * g);
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+          oacc[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[r][g], oacc[r][db], 0, 0, 0);
       }
-    }
   };
 
-  // per-lane part of the transposed V read: lane i of its 16-lane group
-  // addresses key row i / 4 and columns 4 (i % 4) .. +3 of a 4 x 16 block;
-  // groups 1 and 3 take the upper 16 columns of each 32-column block and
-  // lane half hf the keys 4 hf .. 4 hf + 3 of each group of 8.
-  const int tr_i = lane & 15;
-  const int tr_off = (4 * hf + (tr_i >> 2)) * VSTR + 16 * ((lane >> 4) & 1) + 4 * (tr_i & 3);
-
-  // ---- O^T += V^T . P^T ; P operand slot j of half hf (block kb, group g)
-  //      is key 16(2kb+g) + 4hf + (j<4 ? j : j+4) ----
-  f32x16 oacc[D / 32];
+  float m_run[RW], l_run[RW];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  auto pv = [&](int buf, const bf16x8 (&pb)[2][2]) {
-    const bf16 *vt = Vbuf(buf) + tr_off;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const bf16 *p0 = vt + 16 * (2 * kb + g) * VSTR + 32 * db;
-          const u32x2 lo = lds_read_tr16(p0);
-          const u32x2 hi = lds_read_tr16(p0 + 8 * VSTR);
-          const bf16x8 va = bit_cast<bf16x8>(u32x4{lo.x, lo.y, hi.x, hi.y});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][g], oacc[db], 0, 0, 0);
-        }
-    }
-  };
-
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int r = 0; r < RW; ++r) {
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
   const float c = a.scale_log2;
   const float thresh = kRescaleLog2 / c;    // in raw score units
   const uint32_t ones_bf16x2 = 0x3f803f80u;
 
-  // ---- online softmax of one tile (scores in sacc; accumulator row i of
-  //      block kb is key kb*32 + 8*(i/4) + 4*hf + i%4).  P is first computed
-  //      against the running max m_run: that is exact and bounded by 2^8
-  //      unless some row's tile max exceeds m_run by the threshold, which is
-  //      rare after the first tile.  Then the slow path rescales O and l and
-  //      recomputes P against the new max. ----
-  auto exp_tile = [&](const f32x16 (&sacc)[2], float mref, bf16x8 (&pb)[2][2]) -> float {
+  // ---- online softmax of one tile (accumulator row i is key
+  //      8*(i/4) + 4*hf + i%4).  P is first computed against the running max
+  //      m_run: that is exact and bounded by 2^24 unless some row's tile max
+  //      exceeds m_run by the threshold, which is rare after the first tile.
+  //      Then the slow path rescales O and l and recomputes P against the new
+  //      max. ----
+  auto exp_tile = [&](const f32x16 &sacc, float mref, bf16x8 (&pb)[2]) JA_INLINE -> float {
     const float mc = mref * c;
     float lt = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int g = 0; g < 2; ++g) {
+      uint32_t w[4];
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][g * 8 + 2 * e + 1], c, -mc));
-          w[e] = pack_bf16x2(p0, p1);
-          // the normaliser sums the same bf16-rounded P that feeds P.V
-          lt = __builtin_amdgcn_fdot2_f32_bf16(bit_cast<bf16x2>(w[e]),
-                                               bit_cast<bf16x2>(ones_bf16x2), lt, false);
-        }
-        pb[kb][g] = bit_cast<bf16x8>(u32x4{w[0], w[1], w[2], w[3]});
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g * 8 + 2 * e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g * 8 + 2 * e + 1], c, -mc));
+        w[e] = pack_bf16x2(p0, p1);
+        // the normaliser sums the same bf16-rounded P that feeds P.V
+        lt = __builtin_amdgcn_fdot2_f32_bf16(bit_cast<bf16x2>(w[e]),
+                                             bit_cast<bf16x2>(ones_bf16x2), lt, false);
       }
+      pb[g] = bit_cast<bf16x8>(u32x4{w[0], w[1], w[2], w[3]});
+    }
     return lt;
   };
-  auto softmax = [&]<bool TAIL>(f32x16 (&sacc)[2], int j0, bf16x8 (&pb)[2][2]) {
-    if constexpr (TAIL) {
+  auto softmax = [&]<bool TAIL>(f32x16 (&sacc)[RW], int j0, bf16x8 (&pb)[RW][2]) JA_INLINE {
+    float mx[RW], lt[RW];
+    bool grow[RW], any = false;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int r = 0; r < RW; ++r) {
+      if constexpr (TAIL) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (j0 + kb * 32 + 8 * (i / 4) + 4 * hf + (i % 4) >= S) sacc[kb][i] = -INFINITY;
+          if (j0 + 8 * (i / 4) + 4 * hf + (i % 4) >= S) sacc[r][i] = -INFINITY;
+      }
+      mx[r] = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx[r] = fmaxf(mx[r], sacc[r][i]);
+      mx[r] = half_max(mx[r]);
+      grow[r] = mx[r] > m_run[r] + thresh;
+      any = any || grow[r];
+      lt[r] = exp_tile(sacc[r], m_run[r], pb[r]);
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = half_max(mx);
-    const bool grow = mx > m_run + thresh;
-    float lt = exp_tile(sacc, m_run, pb);
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    if (__builtin_amdgcn_ballot_w64(any)) {
       // keep the speculative P computed before the branch (it is the result
       // on the common path); here it is replaced
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < RW; ++r)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) asm volatile("" ::"v"(pb[kb][g]));
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      m_run = m_new;
-      l_run *= alpha;
+        for (int g = 0; g < 2; ++g) asm volatile("" ::"v"(pb[r][g]));
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int r = 0; r < RW; ++r) {
+        const float m_new = grow[r] ? mx[r] : m_run[r];
+        const float alpha = __builtin_amdgcn_exp2f((m_run[r] - m_new) * c);
+        m_run[r] = m_new;
+        l_run[r] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      lt = exp_tile(sacc, m_new, pb);
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[r][db][i] *= alpha;
+        lt[r] = exp_tile(sacc[r], m_new, pb[r]);
+      }
     }
-    l_run += lt;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) l_run[r] += lt[r];
   };
 
-  // ---- software pipeline over key tiles.  K tile x lives in K buffer x%2
-  //      and V tile x in V buffer x%2.  Iteration t computes Q K^T of tile
-  //      t+1 while it runs the softmax of tile t, then P.V of tile t while it
-  //      rotates and stores K of tile t+2 and V of tile t+1 (both into the
-  //      buffers freed by iteration t-1); one barrier per iteration. ----
+  // ---- software pipeline over key tiles.  K tile x lives in K buffer x%2,
+  //      V tile x in V buffer x%2.  Iteration t computes Q K^T of tile t+1
+  //      while it runs the softmax of tile t, then P.V of tile t while it
+  //      rotates and stores K of tile t+2 and stores V of tile t+1 (into the
+  //      buffers read by iteration t-1); a barrier closes the iteration. ----
   const int ntiles = (S + BN - 1) / BN;
   load_k(0);
   load_v(0);
@@ -325,31 +376,35 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     store_k(1);
   }
   __syncthreads();
-  f32x16 s_a[2], s_b[2];
-  qk(0, s_a);
+  f32x16 s_a[RW], s_b[RW];
+  qk.template operator()<0, D / 16>(0, s_a);
 
-  // One pipeline step: softmax of tile t from `cur`, Q K^T of tile t+1 into
-  // `nxt`.  NEXT: a tile t+1 exists (its Q K^T computed, its V staged); K2: a
-  // tile t+2 exists (its K staged).  Only the last tile can be partial.
-  auto iteration = [&]<bool NEXT, bool K2>(int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    const int j0 = t * BN;
+  // NEXT: tile t+1 exists; K2: tile t+2 exists.  Only the last tile can be
+  // partial.
+  auto iteration = [&]<bool NEXT, bool K2>(int t, f32x16 (&cur)[RW],
+                                           f32x16 (&nxt)[RW]) JA_INLINE {
     if constexpr (K2) load_k(t + 2);
     if constexpr (NEXT) load_v(t + 1);
-    if constexpr (NEXT) qk((t + 1) & 1, nxt);
-    bf16x8 pb[2][2];
-    softmax.template operator()<!NEXT>(cur, j0, pb);
-    pv(t & 1, pb);
+    if constexpr (NEXT) qk.template operator()<0, D / 16>((t + 1) & 1, nxt);
+    bf16x8 pb[RW][2];
+    softmax.template operator()<!NEXT>(cur, t * BN, pb);
+    pv(pb, t & 1);
     if constexpr (K2) store_k(t & 1);
     if constexpr (NEXT) store_v((t + 1) & 1);
     __syncthreads();
   };
+  // The score registers of tiles t and t+1 swap roles every iteration, so
+  // the steady state runs two iterations per loop trip.
   int t = 0;
-  for (; t + 2 < ntiles; ++t) {
+  for (; t + 3 < ntiles; t += 2) {
     iteration.template operator()<true, true>(t, s_a, s_b);
-    s_a[0] = s_b[0];
-    s_a[1] = s_b[1];
+    iteration.template operator()<true, true>(t + 1, s_b, s_a);
   }
-  if (t + 1 < ntiles) {
+  if (ntiles - t == 3) {
+    iteration.template operator()<true, true>(t, s_a, s_b);
+    iteration.template operator()<true, false>(t + 1, s_b, s_a);
+    iteration.template operator()<false, false>(t + 2, s_a, s_b);
+  } else if (ntiles - t == 2) {
     iteration.template operator()<true, false>(t, s_a, s_b);
     iteration.template operator()<false, false>(t + 1, s_b, s_a);
   } else {
@@ -357,22 +412,25 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: O = acc / l, bf16; LSE in natural log ----
-  const float l_tot = half_sum(l_run);
-  if (qi < S) {
-    const float inv = 1.f / l_tot;
-    bf16 *orow = a.o + b * a.o_sb + (int64_t)qi * a.o_ss + h * a.o_sh;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int r = 0; r < RW; ++r) {
+    const float l_tot = half_sum(l_run[r]);
+    if (qi[r] < S) {
+      const float inv = 1.f / l_tot;
+      bf16 *orow = a.o + b * a.o_sb + (int64_t)qi[r] * a.o_ss + h * a.o_sh;
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        const int d = db * 32 + 8 * grp + 4 * hf;
-        u32x2 w;
-        w.x = pack_bf16x2(oacc[db][4 * grp + 0] * inv, oacc[db][4 * grp + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * grp + 2] * inv, oacc[db][4 * grp + 3] * inv);
-        *reinterpret_cast<u32x2 *>(orow + d) = w;
-      }
-    if (a.lse && hf == 0)
-      a.lse[((int64_t)b * a.H + h) * S + qi] = (m_run * c + __log2f(l_tot)) * kLn2;
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const int d = db * 32 + 8 * grp + 4 * hf;
+          u32x2 w;
+          w.x = pack_bf16x2(oacc[r][db][4 * grp + 0] * inv, oacc[r][db][4 * grp + 1] * inv);
+          w.y = pack_bf16x2(oacc[r][db][4 * grp + 2] * inv, oacc[r][db][4 * grp + 3] * inv);
+          *reinterpret_cast<u32x2 *>(orow + d) = w;
+        }
+      if (a.lse && hf == 0)
+        a.lse[((int64_t)b * a.H + h) * S + qi[r]] = (m_run[r] * c + __log2f(l_tot)) * kLn2;
+    }
   }
 }
 
