@@ -20,8 +20,9 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer on the current HIP device.
- *     The caller allocates and owns every buffer; the library allocates no
- *     device or host memory and keeps no per-call state.
+ *     The caller allocates and owns every buffer, workspaces included; the
+ *     library allocates no device or host memory and keeps no per-call
+ *     state.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *     enqueue work: they return after the launch, inputs must stay unchanged
  *     and outputs unread until the stream reaches the call.  Calls are
@@ -36,6 +37,7 @@
 #ifndef JOINT_ATTN_H
 #define JOINT_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -99,12 +101,28 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len,
  *            q, k or v.
  *   lse      device float [batch][heads][seq_len], nullable: natural-log
  *            log-sum-exp of each query row's scaled scores.
+ *   workspace, workspace_bytes
+ *            optional device scratch (16-byte aligned) of at least
+ *            joint_attn_fwd_bf16_workspace_bytes(p) bytes.  With it, the
+ *            work items of a last, mostly idle round of workgroups are split
+ *            over key ranges and merged exactly (same softmax rescaling as
+ *            between key tiles), which shortens that round; NULL or too
+ *            small = no split.  The scratch must not be used by another call
+ *            that runs concurrently; its contents on return are undefined.
  * Softmax statistics and both products accumulate in fp32; P is rounded to
  * bf16 for the P.V product.
  */
 ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
                               const void *v, const float *rope, void *o,
-                              float *lse, void *stream);
+                              float *lse, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * joint_attn_fwd_bf16_workspace_bytes - bytes of the optional workspace of
+ * joint_attn_fwd_bf16 for this shape on the current device (0: no split
+ * helps, or p is invalid).  Host-only; launches nothing.
+ */
+size_t joint_attn_fwd_bf16_workspace_bytes(const ja_params *p);
 
 /*
  * joint_attn_quant_rope_fp8 - RoPE on Q and K, then per-token FP8

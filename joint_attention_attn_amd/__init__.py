@@ -14,6 +14,7 @@ import torch
 
 __all__ = [
     "JointAttnError", "library_path", "load", "rope_table_2d", "fwd_bf16",
+    "fwd_bf16_workspace_bytes",
     "quant_rope_fp8", "fwd_fp8", "Params",
 ]
 
@@ -59,7 +60,9 @@ def load() -> ctypes.CDLL:
     vp, st = ctypes.c_void_p, ctypes.c_int
     pp = ctypes.POINTER(Params)
     lib.joint_attn_rope_table_2d.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp]
-    lib.joint_attn_fwd_bf16.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
+    lib.joint_attn_fwd_bf16.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.joint_attn_fwd_bf16_workspace_bytes.argtypes = [pp]
+    lib.joint_attn_fwd_bf16_workspace_bytes.restype = ctypes.c_size_t
     lib.joint_attn_quant_rope_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     for fn in ("joint_attn_rope_table_2d", "joint_attn_fwd_bf16",
@@ -124,8 +127,11 @@ def rope_table_2d(pos: torch.Tensor, head_dim: int, theta: float = 10000.0) -> t
     return table
 
 
-def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_lse: bool = False):
-    """Joint attention on bf16 [B, S, H, D] tensors; RoPE from `rope` (or none)."""
+def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
+             split: bool = True):
+    """Joint attention on bf16 [B, S, H, D] tensors; RoPE from `rope` (or none).
+    `split` passes the workspace that lets a mostly idle last round of
+    workgroups be split over key ranges (False: no workspace)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         if t.dtype != torch.bfloat16:
             raise ValueError(f"{n} must be bfloat16")
@@ -135,10 +141,24 @@ def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_ls
     lse = None
     if return_lse:
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
-    st = load().joint_attn_fwd_bf16(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
-                                    _ptr(out), _ptr(lse), _stream(q.device))
+    lib = load()
+    ws_bytes = lib.joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(p)) if split else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    st = lib.joint_attn_fwd_bf16(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
+                                 _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(q.device))
     _check(st, "joint_attn_fwd_bf16")
     return (out, lse) if return_lse else out
+
+
+def fwd_bf16_workspace_bytes(batch: int, seq_len: int, heads: int, head_dim: int) -> int:
+    """Workspace of fwd_bf16 for a contiguous [B, S, H, D] call on the current
+    device (0 when no split of the last round is planned)."""
+    p = Params(batch, seq_len, heads, head_dim)
+    for x in "qkvo":
+        setattr(p, f"{x}_sb", seq_len * heads * head_dim)
+        setattr(p, f"{x}_ss", heads * head_dim)
+        setattr(p, f"{x}_sh", head_dim)
+    return int(load().joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(p)))
 
 
 def quant_rope_fp8(q, k, v, rope=None):

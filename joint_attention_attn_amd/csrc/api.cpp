@@ -3,6 +3,7 @@
 // call never touches the device.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -75,6 +76,37 @@ ja_status check_params(const ja_params *p, bool qkv_strided, int block_rows) {
   return JA_OK;
 }
 
+// Compute units of the current device (cached per device id).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Checks of joint_attn_fwd_bf16 that do not involve device pointers.
+ja_status check_fwd_bf16(const ja_params *p) {
+  const ja_status st = check_params(p, true, ja::fwd_bf16_block_rows(p ? p->head_dim : 0));
+  if (st != JA_OK) return st;
+  // K, V and the RoPE table of one (batch, head) are addressed with 32-bit
+  // byte offsets
+  const int64_t span_k = ((int64_t)(p->seq_len - 1) * p->k_ss + p->head_dim) * 2;
+  const int64_t span_v = ((int64_t)(p->seq_len - 1) * p->v_ss + p->head_dim) * 2;
+  const int64_t span_t = (int64_t)p->seq_len * p->head_dim * 4;
+  if (span_k > 0x7fffffffLL || span_v > 0x7fffffffLL || span_t > 0x7fffffffLL ||
+      64 * p->k_ss * 2 > 0x7fffffffLL || 64 * p->v_ss * 2 > 0x7fffffffLL)
+    return JA_ERR_UNSUPPORTED;
+  return JA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,25 +135,28 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len,
                                              static_cast<hipStream_t>(stream)));
 }
 
+size_t joint_attn_fwd_bf16_workspace_bytes(const ja_params *p) {
+  if (!p || check_fwd_bf16(p) != JA_OK) return 0;
+  return (size_t)ja::plan_fwd_bf16(layout(p), device_cu_count()).ws_bytes;
+}
+
 ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
                               const void *v, const float *rope, void *o,
-                              float *lse, void *stream) {
+                              float *lse, void *workspace, size_t workspace_bytes,
+                              void *stream) {
   if (!p || !q || !k || !v || !o) return JA_ERR_INVALID_ARG;
-  const ja_status st = check_params(p, true, ja::fwd_bf16_block_rows(p->head_dim));
+  const ja_status st = check_fwd_bf16(p);
   if (st != JA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (rope && !aligned16(rope)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+      (rope && !aligned16(rope)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
+      (workspace && !aligned16(workspace)))
     return JA_ERR_INVALID_ARG;
   if (o == q || o == k || o == v) return JA_ERR_INVALID_ARG;
-  // K, V and the RoPE table of one (batch, head) are addressed with 32-bit
-  // byte offsets
-  const int64_t span_k = ((int64_t)(p->seq_len - 1) * p->k_ss + p->head_dim) * 2;
-  const int64_t span_v = ((int64_t)(p->seq_len - 1) * p->v_ss + p->head_dim) * 2;
-  const int64_t span_t = (int64_t)p->seq_len * p->head_dim * 4;
-  if (span_k > 0x7fffffffLL || span_v > 0x7fffffffLL || span_t > 0x7fffffffLL ||
-      64 * p->k_ss * 2 > 0x7fffffffLL || 64 * p->v_ss * 2 > 0x7fffffffLL)
-    return JA_ERR_UNSUPPORTED;
-  return hip_status(ja::launch_fwd_bf16(layout(p), q, k, v, rope, o, lse,
+  const ja::AttnLayout L = layout(p);
+  ja::SplitPlan plan = ja::plan_fwd_bf16(L, device_cu_count());
+  if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
+    plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
+  return hip_status(ja::launch_fwd_bf16(L, q, k, v, rope, o, lse, plan, workspace,
                                         static_cast<hipStream_t>(stream)));
 }
 

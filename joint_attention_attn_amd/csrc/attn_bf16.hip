@@ -76,6 +76,12 @@ struct FwdArgs {
   int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_ss, o_sh;
   int S, H, B, n_qblk;
   float scale_log2;
+  // Split of the last, partial round of workgroups over key ranges: the
+  // first n_direct workgroups each own one (q-block, head, batch) item; the
+  // remaining ones are `parts` workgroups per item, each over a contiguous
+  // range of key tiles, writing unnormalised partial results to `ws`.
+  int n_direct, parts;
+  SplitWorkspace ws;
 };
 
 // Max and sum of x over the two lanes l and l ^ 32 that share a query row.
@@ -134,14 +140,25 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   // XCDs, so give each XCD a contiguous range of (q-block, head) work items;
   // the workgroups resident on one XCD then stream the same head's K/V
   // through that XCD's L2.
-  const int nwg = gridDim.x;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per = nwg >> 3, rem = nwg & 7;
-  const int item = xcd * per + min(xcd, rem) + slot;
+  const int S = a.S;
+  const int ntiles_all = (S + BN - 1) / BN;
+  int item, t0, t1, unit = -1;
+  if ((int)blockIdx.x < a.n_direct) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = a.n_direct >> 3, rem = a.n_direct & 7;
+    item = xcd * per + min(xcd, rem) + slot;
+    t0 = 0;
+    t1 = ntiles_all;
+  } else {
+    unit = blockIdx.x - a.n_direct;
+    const int part = unit % a.parts;
+    item = a.n_direct + unit / a.parts;
+    t0 = (int)((int64_t)part * ntiles_all / a.parts);
+    t1 = (int)((int64_t)(part + 1) * ntiles_all / a.parts);
+  }
   const int qblk = item % a.n_qblk;
   const int bh = item / a.n_qblk;
   const int h = bh % a.H, b = bh / a.H;
-  const int S = a.S;
 
   // ---- Q rows of this lane (one per 32-row block): rotate, round to bf16,
   //      keep in registers ----
@@ -361,54 +378,78 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     for (int r = 0; r < RW; ++r) l_run[r] += lt[r];
   };
 
-  // ---- software pipeline over key tiles.  K tile x lives in K buffer x%2,
-  //      V tile x in V buffer x%2.  Iteration t computes Q K^T of tile t+1
-  //      while it runs the softmax of tile t, then P.V of tile t while it
-  //      rotates and stores K of tile t+2 and stores V of tile t+1 (into the
-  //      buffers read by iteration t-1); a barrier closes the iteration. ----
-  const int ntiles = (S + BN - 1) / BN;
-  load_k(0);
-  load_v(0);
+  // ---- software pipeline over the key tiles t0 .. t1-1 (local index
+  //      i = t - t0).  Local tile i lives in K buffer i%2 and V buffer i%2.
+  //      Iteration i computes Q K^T of tile i+1 while it runs the softmax of
+  //      tile i, then P.V of tile i while it rotates and stores K of tile i+2
+  //      and stores V of tile i+1 (into the buffers read by iteration i-1); a
+  //      barrier closes the iteration. ----
+  const int nt = t1 - t0;
+  load_k(t0);
+  load_v(t0);
   store_k(0);
   store_v(0);
-  if (ntiles > 1) {
-    load_k(1);
+  if (nt > 1) {
+    load_k(t0 + 1);
     store_k(1);
   }
   __syncthreads();
   f32x16 s_a[RW], s_b[RW];
   qk.template operator()<0, D / 16>(0, s_a);
 
-  // NEXT: tile t+1 exists; K2: tile t+2 exists.  Only the last tile can be
-  // partial.
-  auto iteration = [&]<bool NEXT, bool K2>(int t, f32x16 (&cur)[RW],
+  // NEXT: tile i+1 exists; K2: tile i+2 exists.  Only the last tile of the
+  // sequence can be partial (masking a full tile changes nothing).
+  auto iteration = [&]<bool NEXT, bool K2>(int i, f32x16 (&cur)[RW],
                                            f32x16 (&nxt)[RW]) JA_INLINE {
+    const int t = t0 + i;
     if constexpr (K2) load_k(t + 2);
     if constexpr (NEXT) load_v(t + 1);
-    if constexpr (NEXT) qk.template operator()<0, D / 16>((t + 1) & 1, nxt);
+    if constexpr (NEXT) qk.template operator()<0, D / 16>((i + 1) & 1, nxt);
     bf16x8 pb[RW][2];
     softmax.template operator()<!NEXT>(cur, t * BN, pb);
-    pv(pb, t & 1);
-    if constexpr (K2) store_k(t & 1);
-    if constexpr (NEXT) store_v((t + 1) & 1);
+    pv(pb, i & 1);
+    if constexpr (K2) store_k(i & 1);
+    if constexpr (NEXT) store_v((i + 1) & 1);
     __syncthreads();
   };
-  // The score registers of tiles t and t+1 swap roles every iteration, so
+  // The score registers of tiles i and i+1 swap roles every iteration, so
   // the steady state runs two iterations per loop trip.
-  int t = 0;
-  for (; t + 3 < ntiles; t += 2) {
-    iteration.template operator()<true, true>(t, s_a, s_b);
-    iteration.template operator()<true, true>(t + 1, s_b, s_a);
+  int i = 0;
+  for (; i + 3 < nt; i += 2) {
+    iteration.template operator()<true, true>(i, s_a, s_b);
+    iteration.template operator()<true, true>(i + 1, s_b, s_a);
   }
-  if (ntiles - t == 3) {
-    iteration.template operator()<true, true>(t, s_a, s_b);
-    iteration.template operator()<true, false>(t + 1, s_b, s_a);
-    iteration.template operator()<false, false>(t + 2, s_a, s_b);
-  } else if (ntiles - t == 2) {
-    iteration.template operator()<true, false>(t, s_a, s_b);
-    iteration.template operator()<false, false>(t + 1, s_b, s_a);
+  if (nt - i == 3) {
+    iteration.template operator()<true, true>(i, s_a, s_b);
+    iteration.template operator()<true, false>(i + 1, s_b, s_a);
+    iteration.template operator()<false, false>(i + 2, s_a, s_b);
+  } else if (nt - i == 2) {
+    iteration.template operator()<true, false>(i, s_a, s_b);
+    iteration.template operator()<false, false>(i + 1, s_b, s_a);
   } else {
-    iteration.template operator()<false, false>(t, s_a, s_b);
+    iteration.template operator()<false, false>(i, s_a, s_b);
+  }
+
+  // ---- a split part leaves O unnormalised, with its row max (raw score
+  //      units) and row sum, for the merge kernel ----
+  if (unit >= 0) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const float l_tot = half_sum(l_run[r]);
+      const int row = (wave * RW + r) * 32 + l32;
+      float *orow = a.ws.o + ((int64_t)unit * BM + row) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp)
+          *reinterpret_cast<float4 *>(orow + db * 32 + 8 * grp + 4 * hf) =
+              make_float4(oacc[r][db][4 * grp], oacc[r][db][4 * grp + 1],
+                          oacc[r][db][4 * grp + 2], oacc[r][db][4 * grp + 3]);
+      if (hf == 0)
+        *reinterpret_cast<float2 *>(a.ws.ml + ((int64_t)unit * BM + row) * 2) =
+            make_float2(m_run[r], l_tot);
+    }
+    return;
   }
 
   // ---- epilogue: O = acc / l, bf16; LSE in natural log ----
@@ -438,9 +479,15 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
 
 int fwd_bf16_block_rows(int) { return BM; }
 
+SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu) {
+  const int n_items = ((L.S + BM - 1) / BM) * L.H * L.B;
+  return plan_split(n_items, (L.S + BN - 1) / BN, n_cu * WG_PER_CU, BM, L.D);
+}
+
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
                            const void *v, const float *rope, void *o,
-                           float *lse, hipStream_t st) {
+                           float *lse, const SplitPlan &plan, void *workspace,
+                           hipStream_t st) {
   FwdArgs a;
   a.q = static_cast<const bf16 *>(q);
   a.k = static_cast<const bf16 *>(k);
@@ -457,8 +504,10 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
   a.B = L.B;
   a.n_qblk = (L.S + BM - 1) / BM;
   a.scale_log2 = L.scale_log2;
-  const int64_t nwg = (int64_t)a.n_qblk * L.H * L.B;
-  const dim3 grid((unsigned)nwg);
+  a.n_direct = plan.n_direct;
+  a.parts = plan.parts;
+  a.ws = split_workspace(plan, workspace, BM, L.D);
+  const dim3 grid((unsigned)(plan.n_direct + plan.n_units));
   const bool rope_on = rope != nullptr;
   if (L.D == 64) {
     auto kern = rope_on ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>;
@@ -477,7 +526,9 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
     auto kern = rope_on ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>;
     hipLaunchKernelGGL(kern, grid, dim3(NT), Lds<128>::BYTES, st, a);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.n_units == 0) return e;
+  return launch_merge_split(L, plan, a.ws, BM, o, lse, st);
 }
 
 }  // namespace ja

@@ -18,9 +18,35 @@ struct AttnLayout {
 hipError_t launch_rope_table_2d(const int32_t *pos, int S, int D, float theta,
                                 float *table, hipStream_t st);
 
+// Split of the last partial round of workgroups over key ranges.  A forward
+// launch has n_items (query block, head, batch row) work items for `slots`
+// co-resident workgroups.  When the last round would leave more than half of
+// the slots idle, its items are cut into `parts` key ranges each; those
+// workgroups write unnormalised partial results that a merge pass combines.
+struct SplitPlan {
+  int n_direct = 0;     // items computed by one workgroup each
+  int parts = 1;        // key ranges per split item
+  int n_units = 0;      // workgroups over key ranges (split items x parts)
+  int64_t ws_bytes = 0; // workspace the split needs
+};
+// Partial results of the split workgroups: O rows [n_units][block_rows][D]
+// (fp32, unnormalised) and (row max in raw score units, row sum)
+// [n_units][block_rows][2].
+struct SplitWorkspace {
+  float *o = nullptr;
+  float *ml = nullptr;
+};
+SplitPlan plan_split(int n_items, int ntiles, int slots, int block_rows, int D);
+SplitWorkspace split_workspace(const SplitPlan &plan, void *ws, int block_rows, int D);
+hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
+                              const SplitWorkspace &ws, int block_rows, void *o,
+                              float *lse, hipStream_t st);
+
+SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu);
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
                            const void *v, const float *rope, void *o,
-                           float *lse, hipStream_t st);
+                           float *lse, const SplitPlan &plan, void *workspace,
+                           hipStream_t st);
 
 hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
                                  const void *k, const void *v,

@@ -48,10 +48,11 @@ def _p(b=1, s=80, h=2, d=64):
     return p
 
 
-def _fwd(lib, p, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, rope=None, lse=None):
+def _fwd(lib, p, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, rope=None, lse=None,
+         ws=None, ws_bytes=0):
     vp = ctypes.c_void_p
     return lib.joint_attn_fwd_bf16(ctypes.byref(p) if p is not None else None, vp(q), vp(k),
-                                   vp(v), vp(rope), vp(o), vp(lse), None)
+                                   vp(v), vp(rope), vp(o), vp(lse), vp(ws), ws_bytes, None)
 
 
 @pytest.mark.parametrize("mutate,expect", [
@@ -81,6 +82,14 @@ def test_fwd_bf16_rejects_bad_pointers(lib):
     assert _fwd(lib, _p(), rope=FAKE + 8) == ja.JA_ERR_INVALID_ARG      # misaligned table
     assert _fwd(lib, _p(), lse=FAKE + 2) == ja.JA_ERR_INVALID_ARG
     assert _fwd(lib, _p(), o=FAKE) == ja.JA_ERR_INVALID_ARG             # o aliases q
+    assert _fwd(lib, _p(), ws=FAKE + 0x4008, ws_bytes=64) == ja.JA_ERR_INVALID_ARG  # misaligned
+
+
+def test_workspace_bytes_of_invalid_params_is_zero(lib):
+    assert lib.joint_attn_fwd_bf16_workspace_bytes(None) == 0
+    bad = _p()
+    bad.head_dim = 96
+    assert lib.joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(bad)) == 0
 
 
 def test_rope_table_validation(lib):

@@ -170,3 +170,36 @@ def test_2048_sampled_parity(name, n_rows):
     else:
         assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
     assert max_abs(lse, ref_lse) <= 2e-2
+
+
+def test_split_last_round_parity():
+    # A shape whose last round of workgroups is mostly idle, so the forward
+    # splits those work items over key ranges and merges them (the items of
+    # the last head's upper query blocks).  Checked against the oracle on
+    # rows of split items and of whole items, and against the unsplit launch.
+    base = synth.WORKLOADS["t2i_1024"]
+    w = ws = None
+    for heads in range(8, 65):   # first head count for which a split is planned
+        w = base.replace(heads=heads)
+        ws = ja.fwd_bf16_workspace_bytes(w.batch, w.seq_len, heads, 128)
+        if ws:
+            break
+    assert ws, "no split planned for any head count"
+    q, k, v, idx, pos = _gpu_inputs(w, 5)
+    _say(f"bf16 split: S={w.seq_len} H={w.heads} workspace={ws} B")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    out_ns, lse_ns = _run_bf16(q, k, v, pos, return_lse=True, split=False)
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([rng.choice(w.seq_len, 96, replace=False),
+                                     np.arange(w.seq_len - 8, w.seq_len)]))
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos, rows=rows)
+    got, got_lse = out.cpu()[:, rows], lse.cpu()[:, :, rows]
+    _say(f"  rel_l2={rel_l2(got, ref):.3e} vs unsplit {rel_l2(out.cpu(), out_ns.cpu()):.3e}")
+    assert rel_l2(got, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(got, ref) <= BF16_MAX_ABS
+    assert max_abs(got_lse, ref_lse) <= 2e-2
+    # The two launches round P to bf16 against different running maxima (each
+    # key range of a split item has its own), so they differ by bf16 rounding:
+    # about 2^-9 relative in the row sum, a few 1e-3 in the LSE.
+    assert rel_l2(out.cpu(), out_ns.cpu()) <= 2e-3
+    assert max_abs(lse, lse_ns) <= 1e-2
