@@ -152,13 +152,26 @@ ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,
  *               16-byte aligned.
  *   o           device bf16, layout per ja_params (o_* strides).
  *   lse         device float [batch][heads][seq_len], nullable.
- * Q K^T and P.V run on FP8 MFMA; the scales are applied in fp32; softmax
+ *   workspace, workspace_bytes
+ *               optional scratch of joint_attn_fwd_fp8_workspace_bytes(p)
+ *               bytes, as for joint_attn_fwd_bf16.
+ * Q K^T and P.V run on FP8 MFMA.  The K scale multiplies the fp32 scores,
+ * the Q scale joins the softmax scale; V's per-key scale is folded into the
+ * probabilities before they are rounded to e4m3 for P.V
+ * (P' = P * sv[key] * 64 / max(sv), undone in the epilogue).  Softmax
  * statistics and accumulation are fp32; the output is bf16.
  */
 ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
                              const void *v8, const float *sq, const float *sk,
-                             const float *sv, void *o, float *lse,
-                             void *stream);
+                             const float *sv, void *o, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * joint_attn_fwd_fp8_workspace_bytes - bytes of the optional workspace of
+ * joint_attn_fwd_fp8 for this shape on the current device (0: no split
+ * helps, or p is invalid).  Host-only; launches nothing.
+ */
+size_t joint_attn_fwd_fp8_workspace_bytes(const ja_params *p);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *joint_attn_status_string(ja_status s);

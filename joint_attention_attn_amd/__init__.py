@@ -64,7 +64,9 @@ def load() -> ctypes.CDLL:
     lib.joint_attn_fwd_bf16_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_bf16_workspace_bytes.restype = ctypes.c_size_t
     lib.joint_attn_quant_rope_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.joint_attn_fwd_fp8_workspace_bytes.argtypes = [pp]
+    lib.joint_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("joint_attn_rope_table_2d", "joint_attn_fwd_bf16",
                "joint_attn_quant_rope_fp8", "joint_attn_fwd_fp8"):
         getattr(lib, fn).restype = st
@@ -176,8 +178,10 @@ def quant_rope_fp8(q, k, v, rope=None):
     return q8, k8, v8, sq, sk, sv
 
 
-def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return_lse: bool = False):
-    """Joint attention on contiguous e4m3 codes [B, S, H, D] with fp32 scales [B, H, S]."""
+def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
+            split: bool = True):
+    """Joint attention on contiguous e4m3 codes [B, S, H, D] with fp32 scales [B, H, S].
+    `split` as for fwd_bf16."""
     b, s, h, d = q8.shape
     for t in (q8, k8, v8):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous() \
@@ -194,7 +198,11 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return
     lse = None
     if return_lse:
         lse = torch.empty((b, h, s), dtype=torch.float32, device=q8.device)
-    st = load().joint_attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq),
-                                   _ptr(sk), _ptr(sv), _ptr(out), _ptr(lse), _stream(q8.device))
+    lib = load()
+    ws_bytes = lib.joint_attn_fwd_fp8_workspace_bytes(ctypes.byref(p)) if split else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q8.device) if ws_bytes else None
+    st = lib.joint_attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq),
+                                _ptr(sk), _ptr(sv), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
+                                _stream(q8.device))
     _check(st, "joint_attn_fwd_fp8")
     return (out, lse) if return_lse else out

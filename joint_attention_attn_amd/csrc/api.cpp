@@ -107,6 +107,17 @@ ja_status check_fwd_bf16(const ja_params *p) {
   return JA_OK;
 }
 
+// Checks of joint_attn_fwd_fp8 that do not involve device pointers.
+ja_status check_fwd_fp8(const ja_params *p) {
+  const ja_status st = check_params(p, false, ja::fwd_fp8_block_rows(p ? p->head_dim : 0));
+  if (st != JA_OK) return st;
+  // the e4m3 K and V of one (batch, head) are addressed with 32-bit byte
+  // offsets
+  const int64_t span = (int64_t)(p->seq_len - 1) * p->heads * p->head_dim + p->head_dim;
+  if (span > 0x7fffffffLL) return JA_ERR_UNSUPPORTED;
+  return JA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,18 +192,27 @@ ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,
                                               static_cast<hipStream_t>(stream)));
 }
 
+size_t joint_attn_fwd_fp8_workspace_bytes(const ja_params *p) {
+  if (!p || check_fwd_fp8(p) != JA_OK) return 0;
+  return (size_t)ja::plan_fwd_fp8(layout(p), device_cu_count()).ws_bytes;
+}
+
 ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
                              const void *v8, const float *sq, const float *sk,
-                             const float *sv, void *o, float *lse,
-                             void *stream) {
+                             const float *sv, void *o, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream) {
   if (!p || !q8 || !k8 || !v8 || !sq || !sk || !sv || !o) return JA_ERR_INVALID_ARG;
-  const ja_status st = check_params(p, false, ja::fwd_fp8_block_rows(p->head_dim));
+  const ja_status st = check_fwd_fp8(p);
   if (st != JA_OK) return st;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) ||
       !aligned16(sq) || !aligned16(sk) || !aligned16(sv) ||
-      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (workspace && !aligned16(workspace)))
     return JA_ERR_INVALID_ARG;
-  return hip_status(ja::launch_fwd_fp8(layout(p), q8, k8, v8, sq, sk, sv, o, lse,
+  const ja::AttnLayout L = layout(p);
+  ja::SplitPlan plan = ja::plan_fwd_fp8(L, device_cu_count());
+  if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
+    plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
+  return hip_status(ja::launch_fwd_fp8(L, q8, k8, v8, sq, sk, sv, o, lse, plan, workspace,
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -528,7 +528,7 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_units == 0) return e;
-  return launch_merge_split(L, plan, a.ws, BM, o, lse, st);
+  return launch_merge_split(L, plan, a.ws, BM, L.scale_log2, o, lse, st);
 }
 
 }  // namespace ja

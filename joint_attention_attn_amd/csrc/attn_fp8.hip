@@ -4,25 +4,46 @@
 // FP8 attention is the pages' qk_dtype / v_dtype fp8 setting ("Speed Up Image
 // Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", section
 // "Quantized and sparse attention").  Both products run on
-// v_mfma_f32_32x32x64_f8f6f4 with the same transposed orientation as the bf16
-// kernel (a lane owns one query row):
-//   S^T[key][q] = K8 . Q8^T, then s = acc * sk[key] * sq[q] * scale (fp32)
+// v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands, no block scaling) in the
+// transposed orientation of the bf16 kernel, so a lane owns one query row:
+//   S^T[key][q] = K8 . Q8^T, then t = acc * sk[key]; scores = t * sq[q] * scale
 //   O^T[d][q]  += V8^T . P'^T
 // V's scale is per key, i.e. on the reduction index of P.V, so it is folded
-// into P before the e4m3 cast: P'[q][key] = P * sv[key] * 256 / sv_max, where
-// sv_max is the largest V scale of the (batch, head).  P' then lies in
-// [0, 256] and the epilogue multiplies by sv_max / 256.  The softmax
-// normaliser sums the unquantized fp32 P.
+// into P before the e4m3 cast: P'[q][key] = P * sv[key] * 64 / sv_max, where
+// sv_max is the largest V scale of the (batch, head).  P stays below 2^2 (the
+// running max is refreshed whenever a row max grows by more than 2 in the
+// exp2 domain), so P' stays below 256, inside the e4m3 range; the epilogue
+// multiplies by sv_max / 64.  The softmax normaliser sums the unquantized
+// fp32 P.
+//
+// Structure as in the bf16 kernel: one workgroup of eight wave64s per
+// (256-query block, head, batch row), XCD-aware placement, K/V tiles of 64
+// keys double-buffered in LDS with the next tiles loaded while the current
+// one is consumed, one barrier per tile.  K rows are copied as they are; V is
+// staged transposed (one row per head-dimension column, keys in the order in
+// which the P' operand holds them) by a 4 x 4 byte transpose in registers, so
+// both MFMA operands are 16-byte LDS reads.
 #include "common.hpp"
 #include "internal.hpp"
+
+#define JA_INLINE __attribute__((always_inline))
 
 namespace ja {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 64;
-constexpr int VT8_STRIDE = BN + 16;  // bytes per transposed-V row in LDS
+constexpr int NW = 8;               // waves per workgroup, 32 query rows each
+constexpr int BM = 32 * NW;         // query rows per workgroup
+constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
+constexpr int NT = 64 * NW;         // threads per workgroup
+constexpr int VTSTR = BN + 16;      // bytes per V^T row in LDS (16-byte pad)
+
+// P may exceed 1 by up to 2^kRescaleLog2 before the running max is refreshed;
+// kPScale = 256 / 2^kRescaleLog2 keeps P' = P * sv / sv_max * kPScale <= 256.
+constexpr float kRescaleLog2 = 2.f;
+constexpr float kPScale = 64.f;
+
+constexpr int kBufferFlags = 0x00020000;
 
 struct Fp8Args {
   const uint8_t *q, *k, *v;
@@ -30,8 +51,10 @@ struct Fp8Args {
   bf16 *o;
   float *lse;
   int64_t o_sb, o_ss, o_sh;
-  int S, H;
+  int S, H, B, n_qblk;
   float scale_log2;
+  int n_direct, parts;
+  SplitWorkspace ws;
 };
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -39,42 +62,86 @@ __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// Position of key r (0..63) of a tile inside a transposed-V LDS row, chosen so
-// that the 32 keys the P' operand of lane half hf carries are contiguous:
-// key = kb*32 + g*8 + hf*4 + i  ->  hf*32 + kb*16 + g*4 + i.
-__device__ __forceinline__ int vt8_pos(int r) {
-  const int kb = r >> 5, g = (r >> 3) & 3, hf = (r >> 2) & 1, i = r & 3;
-  return hf * 32 + kb * 16 + g * 4 + i;
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Position of key r (0..63) of a tile inside a V^T row: the P' operand of
+// lane half hf holds, in slot kb*16 + g*4 + i, key kb*32 + g*8 + hf*4 + i
+// (the S^T accumulator order), so V^T keeps that key at hf*32 + slot.
+__host__ __device__ constexpr int vt8_pos(int r) {
+  return ((r >> 2) & 1) * 32 + (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3);
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_fp8_kernel(Fp8Args a) {
-  constexpr int KCH = D / 16;  // 16-byte chunks per fp8 head vector
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[BN * D];
-  __shared__ __attribute__((aligned(16))) uint8_t Vt[D * VT8_STRIDE];
-  __shared__ __attribute__((aligned(16))) float sk_t[BN];
-  __shared__ __attribute__((aligned(16))) float wv_t[BN];
-  __shared__ float red[4];
+struct Fp8Lds {
+  static constexpr int KSTR = D + 16;       // bytes per K row (16-byte pad)
+  static constexpr int KTILE = BN * KSTR;
+  static constexpr int VTILE = D * VTSTR;
+};
+
+template <int D>
+__global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
+  constexpr int KSTR = Fp8Lds<D>::KSTR;
+  constexpr int KCH = D / 16;                 // 16-byte chunks per K row
+  constexpr int K_THREADS = BN * KCH;         // one K chunk each
+  constexpr int V_THREADS = D * BN / 16;      // a 4-key x 4-column block each
+  static_assert(K_THREADS <= NT && V_THREADS <= NT, "staging layout");
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][Fp8Lds<D>::KTILE];
+  __shared__ __attribute__((aligned(16))) uint8_t Vt[2][Fp8Lds<D>::VTILE];
+  __shared__ __attribute__((aligned(16))) float sk_t[2][BN];
+  __shared__ __attribute__((aligned(16))) float wv_t[2][BN];
+  __shared__ float red[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int h = blockIdx.y, b = blockIdx.z;
   const int S = a.S;
+  const int ntiles_all = (S + BN - 1) / BN;
+
+  // ---- work item: XCD-aware placement of whole items, then the key-range
+  //      parts of split items (see split.hip) ----
+  int item, t0, t1, unit = -1;
+  if ((int)blockIdx.x < a.n_direct) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = a.n_direct >> 3, rem = a.n_direct & 7;
+    item = xcd * per + min(xcd, rem) + slot;
+    t0 = 0;
+    t1 = ntiles_all;
+  } else {
+    unit = blockIdx.x - a.n_direct;
+    const int part = unit % a.parts;
+    item = a.n_direct + unit / a.parts;
+    t0 = (int)((int64_t)part * ntiles_all / a.parts);
+    t1 = (int)((int64_t)(part + 1) * ntiles_all / a.parts);
+  }
+  const int qblk = item % a.n_qblk;
+  const int bh32 = item / a.n_qblk;
+  const int h = bh32 % a.H, b = bh32 / a.H;
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t row_stride = (int64_t)a.H * D;  // contiguous [B, S, H, D]
 
   // ---- largest V scale of this (b, h) ----
   float vmax = 0.f;
-  for (int s = tid; s < S; s += 256) vmax = fmaxf(vmax, a.sv[bh * S + s]);
+  for (int s = tid; s < S; s += NT) vmax = fmaxf(vmax, a.sv[bh * S + s]);
+#pragma unroll
   for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
   if (lane == 0) red[wave] = vmax;
   __syncthreads();
-  const float sv_max = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float wv_mul = 256.f / sv_max;
+  float sv_max = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) sv_max = fmaxf(sv_max, red[w]);
+  const float wv_mul = kPScale / sv_max;
 
   // ---- Q8 of this lane's query row ----
-  const int qi = blockIdx.x * BM + wave * 32 + l32;
+  const int qi = qblk * BM + wave * 32 + l32;
   const int qs = qi < S ? qi : S - 1;
   const uint8_t *qrow = a.q + ((int64_t)b * S + qs) * row_stride + (int64_t)h * D;
   i32x8 qreg[D / 64];
@@ -87,117 +154,226 @@ __global__ __launch_bounds__(256) void attn_fwd_fp8_kernel(Fp8Args a) {
   }
   const float qmul = a.sq[bh * S + qs] * a.scale_log2;
 
+  // ---- staging through buffer resources (rows past the end read as 0) ----
+  const uint8_t *kbase = a.k + (int64_t)b * S * row_stride + (int64_t)h * D;
+  const uint8_t *vbase = a.v + (int64_t)b * S * row_stride + (int64_t)h * D;
+  const int span = (int)((int64_t)(S - 1) * row_stride + D);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(kbase), 0, span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vbase), 0, span, kBufferFlags);
+  const int tile_bytes = (int)(BN * row_stride);
+  // K: row kr, chunk kc.  V: keys 4vm..4vm+3 of columns 4vn..4vn+3; the 64
+  // lanes of a wave take 16 key groups x 4 column groups, which spreads their
+  // 4-byte V^T writes over all LDS banks.
+  const int kr = tid / KCH, kc = tid % KCH;
+  const int koff = (int)(kr * row_stride) + kc * 16;
+  const int vm = lane & 15, vn = wave * 4 + (lane >> 4);
+  const int voff = (int)(4 * vm * row_stride) + 4 * vn;
+  u32x4 kreg;
+  uint32_t vreg[4];
+  float skreg = 0.f, svreg = 0.f;
+  auto load = [&](int t, bool with_k, bool with_v) JA_INLINE {
+    if (with_k && tid < K_THREADS)
+      kreg = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(krs, koff, t * tile_bytes, 0));
+    if (with_v) {
+      if (tid < V_THREADS) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          vreg[k] = __builtin_amdgcn_raw_buffer_load_b32(vrs, voff + (int)(k * row_stride),
+                                                         t * tile_bytes, 0);
+      }
+      if (tid < BN) {
+        const int key = t * BN + tid;
+        skreg = key < S ? a.sk[bh * S + key] : 0.f;
+        svreg = key < S ? a.sv[bh * S + key] : 0.f;
+      }
+    }
+  };
+  auto store_k = [&](int buf) JA_INLINE {
+    if (tid < K_THREADS) *reinterpret_cast<u32x4 *>(&Ks[buf][kr * KSTR + kc * 16]) = kreg;
+  };
+  auto store_v = [&](int buf) JA_INLINE {
+    if (tid < V_THREADS) {
+      // 4 x 4 byte transpose: vreg[k] holds columns 4vn..+3 of key 4vm+k;
+      // u[j] gets keys 4vm..+3 of column 4vn+j
+      const uint32_t t01l = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x05010400u);
+      const uint32_t t01h = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x07030602u);
+      const uint32_t t23l = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x05010400u);
+      const uint32_t t23h = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x07030602u);
+      const uint32_t u[4] = {__builtin_amdgcn_perm(t23l, t01l, 0x05040100u),
+                             __builtin_amdgcn_perm(t23l, t01l, 0x07060302u),
+                             __builtin_amdgcn_perm(t23h, t01h, 0x05040100u),
+                             __builtin_amdgcn_perm(t23h, t01h, 0x07060302u)};
+      const int pos = vt8_pos(4 * vm);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint32_t *>(&Vt[buf][(4 * vn + j) * VTSTR + pos]) = u[j];
+    }
+    if (tid < BN) {
+      sk_t[buf][tid] = skreg;
+      wv_t[buf][tid] = svreg * wv_mul;
+    }
+  };
+
+  // ---- S^T = K8 . Q8^T for the 64 keys of a tile (two 32-key blocks) ----
+  auto qk = [&](int buf, f32x16 (&sacc)[2]) JA_INLINE {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      const uint8_t *krow = &Ks[buf][(kb * 32 + l32) * KSTR + 32 * hf];
+#pragma unroll
+      for (int kk = 0; kk < D / 64; ++kk) {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(krow + 64 * kk);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(krow + 64 * kk + 16);
+        sacc[kb] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qreg[kk],
+                            sacc[kb]);
+      }
+    }
+  };
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  auto pv = [&](const i32x8 &pb, int buf) JA_INLINE {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const uint8_t *vrow = &Vt[buf][(db * 32 + l32) * VTSTR + 32 * hf];
+      const i32x4 lo = *reinterpret_cast<const i32x4 *>(vrow);
+      const i32x4 hi = *reinterpret_cast<const i32x4 *>(vrow + 16);
+      oacc[db] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, pb, oacc[db]);
+    }
+  };
+
+  // ---- online softmax of one tile; m_run is in the exp2 domain.  As in the
+  //      bf16 kernel, P is first computed against the running max and only
+  //      recomputed (with O and l rescaled) when some row max grew by more
+  //      than the threshold. ----
   float m_run = -INFINITY, l_run = 0.f;
-
-  const uint8_t *kbase = a.k + (int64_t)b * S * row_stride + (int64_t)h * D;
-  const uint8_t *vbase = a.v + (int64_t)b * S * row_stride + (int64_t)h * D;
-
-  for (int j0 = 0; j0 < S; j0 += BN) {
-    for (int c = tid; c < BN * KCH; c += 256) {
-      const int r = c / KCH, ch = c % KCH;
-      const int key = j0 + r;
-      u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
-      if (key < S) {
-        kw = *reinterpret_cast<const u32x4 *>(kbase + key * row_stride + ch * 16);
-        vw = *reinterpret_cast<const u32x4 *>(vbase + key * row_stride + ch * 16);
-      }
-      *reinterpret_cast<u32x4 *>(Ks + r * D + ((ch ^ (r & (KCH - 1))) * 16)) = kw;
-      const int pos = vt8_pos(r);
-      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        Vt[(ch * 16 + e) * VT8_STRIDE + pos] = (uint8_t)(vv[e >> 2] >> (8 * (e & 3)));
-    }
-    if (tid < BN) {
-      const int key = j0 + tid;
-      const float skv = key < S ? a.sk[bh * S + key] : 0.f;
-      const float svv = key < S ? a.sv[bh * S + key] : 0.f;
-      sk_t[tid] = skv;
-      wv_t[tid] = svv * wv_mul;
-    }
-    __syncthreads();
-
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-      const int r = kb * 32 + l32;
-#pragma unroll
-      for (int kk = 0; kk < D / 64; ++kk) {
-        const int c0 = 4 * kk + 2 * hf;
-        const i32x4 lo = *reinterpret_cast<const i32x4 *>(Ks + r * D + ((c0 ^ (r & (KCH - 1))) * 16));
-        const i32x4 hi = *reinterpret_cast<const i32x4 *>(Ks + r * D + (((c0 + 1) ^ (r & (KCH - 1))) * 16));
-        const i32x8 kv = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        sacc[kb] = mfma_fp8(kv, qreg[kk], sacc[kb]);
-      }
-    }
-
-    // t = acc * sk[key]; the row max of t * qmul is qmul * max(t) (qmul > 0)
-    float tmax = -INFINITY;
-    const bool tail = j0 + BN > S;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 skg = *reinterpret_cast<const float4 *>(&sk_t[kb * 32 + g * 8 + hf * 4]);
-        const float skv[4] = {skg.x, skg.y, skg.z, skg.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float t = sacc[kb][4 * g + i] * skv[i];
-          if (tail && j0 + kb * 32 + g * 8 + hf * 4 + i >= S) t = -INFINITY;
-          sacc[kb][4 * g + i] = t;
-          tmax = fmaxf(tmax, t);
-        }
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax * qmul);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    // P = exp2(t * qmul - m); P' = P * w[key] -> e4m3; operand slot order is
-    // kb*16 + g*4 + i, matching vt8_pos.
+  auto exp_tile = [&](const f32x16 (&t)[2], float mref, int buf, float &psum) JA_INLINE -> i32x8 {
     uint32_t pw[8];
-    float psum = 0.f;
+    psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 wg = *reinterpret_cast<const float4 *>(&wv_t[kb * 32 + g * 8 + hf * 4]);
+        const float4 wg = *reinterpret_cast<const float4 *>(&wv_t[buf][kb * 32 + g * 8 + hf * 4]);
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * g + i], qmul, -m_new));
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][4 * g + i], qmul, -mref));
           psum += p[i];
         }
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * wg.x, p[1] * wg.y, 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * wg.z, p[3] * wg.w, w, true);
         pw[kb * 4 + g] = (uint32_t)w;
       }
-    l_run = l_run * alpha + psum;
-    const i32x8 pb = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3],
-                      (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+    return bit_cast<i32x8>(pw);
+  };
+  auto softmax = [&]<bool TAIL>(f32x16 (&sacc)[2], int j0, int buf) JA_INLINE -> i32x8 {
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      const uint8_t *vrow = Vt + (db * 32 + l32) * VT8_STRIDE + 32 * hf;
-      const i32x4 lo = *reinterpret_cast<const i32x4 *>(vrow);
-      const i32x4 hi = *reinterpret_cast<const i32x4 *>(vrow + 16);
-      const i32x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      oacc[db] = mfma_fp8(va, pb, oacc[db]);
+      for (int g = 0; g < 4; ++g) {
+        const float4 skg = *reinterpret_cast<const float4 *>(&sk_t[buf][kb * 32 + g * 8 + hf * 4]);
+        const float skv[4] = {skg.x, skg.y, skg.z, skg.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float t = sacc[kb][4 * g + i] * skv[i];
+          if (TAIL && j0 + kb * 32 + g * 8 + hf * 4 + i >= S) t = -INFINITY;
+          sacc[kb][4 * g + i] = t;
+          tmax = fmaxf(tmax, t);
+        }
+      }
+    // the row max of t * qmul is qmul * max(t) (qmul > 0)
+    const float mx = half_max(tmax) * qmul;
+    const bool grow = mx > m_run + kRescaleLog2;
+    float psum;
+    i32x8 pb = exp_tile(sacc, m_run, buf, psum);
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      asm volatile("" ::"v"(pb));
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      pb = exp_tile(sacc, m_new, buf, psum);
     }
+    l_run += psum;
+    return pb;
+  };
+
+  // ---- software pipeline over the key tiles t0 .. t1-1 (local index i):
+  //      local tile i lives in K buffer i%2 and V buffer i%2 (with its
+  //      scales).  Iteration i computes Q K^T of tile i+1 while it runs the
+  //      softmax of tile i, then P.V of tile i while it stores K of tile i+2
+  //      and V of tile i+1 into the buffers read by iteration i-1. ----
+  const int nt = t1 - t0;
+  load(t0, true, true);
+  store_k(0);
+  store_v(0);
+  if (nt > 1) {
+    load(t0 + 1, true, false);
+    store_k(1);
+  }
+  __syncthreads();
+  f32x16 s_a[2], s_b[2];
+  qk(0, s_a);
+
+  auto iteration = [&]<bool NEXT, bool K2>(int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) JA_INLINE {
+    const int t = t0 + i;
+    if constexpr (K2 || NEXT) load(K2 ? t + 2 : 0, K2, false);
+    if constexpr (NEXT) load(t + 1, false, true);
+    if constexpr (NEXT) qk((i + 1) & 1, nxt);
+    const i32x8 pb = softmax.template operator()<!NEXT>(cur, t * BN, i & 1);
+    pv(pb, i & 1);
+    if constexpr (K2) store_k(i & 1);
+    if constexpr (NEXT) store_v((i + 1) & 1);
     __syncthreads();
+  };
+  int i = 0;
+  for (; i + 3 < nt; i += 2) {
+    iteration.template operator()<true, true>(i, s_a, s_b);
+    iteration.template operator()<true, true>(i + 1, s_b, s_a);
+  }
+  if (nt - i == 3) {
+    iteration.template operator()<true, true>(i, s_a, s_b);
+    iteration.template operator()<true, false>(i + 1, s_b, s_a);
+    iteration.template operator()<false, false>(i + 2, s_a, s_b);
+  } else if (nt - i == 2) {
+    iteration.template operator()<true, false>(i, s_a, s_b);
+    iteration.template operator()<false, false>(i + 1, s_b, s_a);
+  } else {
+    iteration.template operator()<false, false>(i, s_a, s_b);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_sum(l_run);
+  const float o_mul = sv_max / kPScale;
+  if (unit >= 0) {
+    // split part: unnormalised O in true units, row max (exp2 domain), sum
+    const int row = wave * 32 + l32;
+    float *orow = a.ws.o + ((int64_t)unit * BM + row) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp)
+        *reinterpret_cast<float4 *>(orow + db * 32 + 8 * grp + 4 * hf) =
+            make_float4(oacc[db][4 * grp] * o_mul, oacc[db][4 * grp + 1] * o_mul,
+                        oacc[db][4 * grp + 2] * o_mul, oacc[db][4 * grp + 3] * o_mul);
+    if (hf == 0)
+      *reinterpret_cast<float2 *>(a.ws.ml + ((int64_t)unit * BM + row) * 2) =
+          make_float2(m_run, l_tot);
+    return;
+  }
   if (qi < S) {
-    const float inv = sv_max / (256.f * l_tot);
+    const float inv = o_mul / l_tot;
     bf16 *orow = a.o + b * a.o_sb + (int64_t)qi * a.o_ss + h * a.o_sh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -217,9 +393,15 @@ __global__ __launch_bounds__(256) void attn_fwd_fp8_kernel(Fp8Args a) {
 
 int fwd_fp8_block_rows(int) { return BM; }
 
+SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu) {
+  const int n_items = ((L.S + BM - 1) / BM) * L.H * L.B;
+  return plan_split(n_items, (L.S + BN - 1) / BN, n_cu, BM, L.D);
+}
+
 hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
                           const void *v8, const float *sq, const float *sk,
-                          const float *sv, void *o, float *lse, hipStream_t st) {
+                          const float *sv, void *o, float *lse, const SplitPlan &plan,
+                          void *workspace, hipStream_t st) {
   Fp8Args a;
   a.q = static_cast<const uint8_t *>(q8);
   a.k = static_cast<const uint8_t *>(k8);
@@ -232,13 +414,20 @@ hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
   a.o_sb = L.o_sb; a.o_ss = L.o_ss; a.o_sh = L.o_sh;
   a.S = L.S;
   a.H = L.H;
+  a.B = L.B;
+  a.n_qblk = (L.S + BM - 1) / BM;
   a.scale_log2 = L.scale_log2;
-  const dim3 grid((L.S + BM - 1) / BM, L.H, L.B);
+  a.n_direct = plan.n_direct;
+  a.parts = plan.parts;
+  a.ws = split_workspace(plan, workspace, BM, L.D);
+  const dim3 grid((unsigned)(plan.n_direct + plan.n_units));
   if (L.D == 64)
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<64>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<64>, grid, dim3(NT), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<128>, grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+    hipLaunchKernelGGL(attn_fwd_fp8_kernel<128>, grid, dim3(NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.n_units == 0) return e;
+  return launch_merge_split(L, plan, a.ws, BM, 1.f, o, lse, st);
 }
 
 }  // namespace ja

@@ -30,8 +30,8 @@ struct SplitPlan {
   int64_t ws_bytes = 0; // workspace the split needs
 };
 // Partial results of the split workgroups: O rows [n_units][block_rows][D]
-// (fp32, unnormalised) and (row max in raw score units, row sum)
-// [n_units][block_rows][2].
+// (fp32, unnormalised) and (row max, row sum) [n_units][block_rows][2]; the
+// row max times the merge's m_scale is in the exp2 domain.
 struct SplitWorkspace {
   float *o = nullptr;
   float *ml = nullptr;
@@ -39,8 +39,8 @@ struct SplitWorkspace {
 SplitPlan plan_split(int n_items, int ntiles, int slots, int block_rows, int D);
 SplitWorkspace split_workspace(const SplitPlan &plan, void *ws, int block_rows, int D);
 hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
-                              const SplitWorkspace &ws, int block_rows, void *o,
-                              float *lse, hipStream_t st);
+                              const SplitWorkspace &ws, int block_rows, float m_scale,
+                              void *o, float *lse, hipStream_t st);
 
 SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu);
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
@@ -54,9 +54,11 @@ hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
                                  void *v8, float *sq, float *sk, float *sv,
                                  hipStream_t st);
 
+SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu);
 hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
                           const void *v8, const float *sq, const float *sk,
-                          const float *sv, void *o, float *lse, hipStream_t st);
+                          const float *sv, void *o, float *lse, const SplitPlan &plan,
+                          void *workspace, hipStream_t st);
 
 // Query rows per workgroup of each forward kernel (the grid's x extent is
 // ceil(S / rows)).

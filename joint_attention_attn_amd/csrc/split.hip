@@ -26,7 +26,7 @@ struct MergeArgs {
   float *lse;
   int64_t o_sb, o_ss, o_sh;
   int S, H, n_qblk, block_rows, n_direct, parts, n_split;
-  float scale_log2;
+  float scale_log2;   // factor from stored row maxima to the exp2 domain
 };
 
 // One thread per (split item, row, 8-column chunk).
@@ -99,8 +99,8 @@ SplitWorkspace split_workspace(const SplitPlan &plan, void *ws, int block_rows, 
 }
 
 hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
-                              const SplitWorkspace &ws, int block_rows, void *o,
-                              float *lse, hipStream_t st) {
+                              const SplitWorkspace &ws, int block_rows, float m_scale,
+                              void *o, float *lse, hipStream_t st) {
   MergeArgs m;
   m.ws = ws;
   m.o = static_cast<bf16 *>(o);
@@ -113,7 +113,7 @@ hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
   m.n_direct = plan.n_direct;
   m.parts = plan.parts;
   m.n_split = plan.n_units / plan.parts;
-  m.scale_log2 = L.scale_log2;
+  m.scale_log2 = m_scale;
   const int64_t threads = (int64_t)m.n_split * block_rows * (L.D / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (L.D == 64)

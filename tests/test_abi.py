@@ -114,8 +114,11 @@ def test_quant_and_fp8_validation(lib):
     assert lib.joint_attn_quant_rope_fp8(ctypes.byref(p), vp(0), *ptrs[1:3], None, *ptrs[3:6],
                                          *ptrs[6:9], None) == ja.JA_ERR_INVALID_ARG
     assert lib.joint_attn_fwd_fp8(ctypes.byref(bad), *ptrs[:3], *ptrs[3:6], ptrs[6], None,
-                                  None) == ja.JA_ERR_UNSUPPORTED
+                                  None, 0, None) == ja.JA_ERR_UNSUPPORTED
     assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], vp(FAKE + 4), *ptrs[4:6],
-                                  ptrs[6], None, None) == ja.JA_ERR_INVALID_ARG
+                                  ptrs[6], None, None, 0, None) == ja.JA_ERR_INVALID_ARG
     assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], vp(0), None,
-                                  None) == ja.JA_ERR_INVALID_ARG
+                                  None, 0, None) == ja.JA_ERR_INVALID_ARG
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], ptrs[6], None,
+                                  vp(FAKE + 0x9008), 64, None) == ja.JA_ERR_INVALID_ARG
+    assert lib.joint_attn_fwd_fp8_workspace_bytes(ctypes.byref(bad)) == 0
