@@ -382,7 +382,9 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   //      i = t - t0).  Local tile i lives in K buffer i%2 and V buffer i%2.
   //      Iteration i computes Q K^T of tile i+1 while it runs the softmax of
   //      tile i, then P.V of tile i while it rotates and stores K of tile i+2
-  //      and stores V of tile i+1 (into the buffers read by iteration i-1); a
+  //      and stores V of tile i+1 (into the buffers read by iteration i-1);
+  //      right after those stores it issues the global loads of K tile i+3
+  //      and V tile i+2, which then have a whole iteration to arrive; a
   //      barrier closes the iteration. ----
   const int nt = t1 - t0;
   load_k(t0);
@@ -393,6 +395,8 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     load_k(t0 + 1);
     store_k(1);
   }
+  if (nt > 2) load_k(t0 + 2);
+  if (nt > 1) load_v(t0 + 1);
   __syncthreads();
   f32x16 s_a[RW], s_b[RW];
   qk.template operator()<0, D / 16>(0, s_a);
@@ -402,14 +406,16 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   auto iteration = [&]<bool NEXT, bool K2>(int i, f32x16 (&cur)[RW],
                                            f32x16 (&nxt)[RW]) JA_INLINE {
     const int t = t0 + i;
-    if constexpr (K2) load_k(t + 2);
-    if constexpr (NEXT) load_v(t + 1);
     if constexpr (NEXT) qk.template operator()<0, D / 16>((i + 1) & 1, nxt);
     bf16x8 pb[RW][2];
     softmax.template operator()<!NEXT>(cur, t * BN, pb);
     pv(pb, i & 1);
     if constexpr (K2) store_k(i & 1);
     if constexpr (NEXT) store_v((i + 1) & 1);
+    if constexpr (K2) {
+      if (i + 3 < nt) load_k(t + 3);
+      load_v(t + 2);
+    }
     __syncthreads();
   };
   // The score registers of tiles i and i+1 swap roles every iteration, so
