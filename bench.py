@@ -35,8 +35,8 @@ METRIC = "joint-attention fwd TFLOP/s and % of MFMA peak at 2048x2048 (16896 tok
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_t2i_2048_traffic.txt")
-BF16_SOURCE = os.path.join(ROOT, "joint_attention_attn_amd", "csrc", "attn_bf16.hip")
+CSRC = os.path.join(ROOT, "joint_attention_attn_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def _log(msg: str) -> None:
@@ -47,7 +47,8 @@ def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the first launches run while the GPU clock ramps up (see profiles/)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="t2i_2048")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-fp8", action="store_true")
@@ -60,18 +61,20 @@ def _parse():
     return ap.parse_args()
 
 
-def _traffic_for_current_kernel():
-    """HBM bytes per launch from committed rocprofv3 counters, only if they
-    were taken on the kernel source as it is now."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _traffic_for_current_kernel(record: str, source: str):
+    """HBM bytes per launch from a committed rocprofv3 counter record
+    (profiles/<record>), only if it was taken on the kernel source as it is
+    now; None otherwise."""
+    path = os.path.join(PROFILES, record)
+    if not os.path.exists(path):
         return None
     rec = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.lstrip().startswith("#"):
                 key, val = line.split(":", 1)
                 rec[key.strip()] = val.strip()
-    with open(BF16_SOURCE, "rb") as f:
+    with open(os.path.join(CSRC, source), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     if rec.get("source_sha256") != sha or "hbm_bytes_per_launch" not in rec:
         return None
@@ -158,9 +161,11 @@ def main() -> int:
     achieved = flops / (k_avg * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic_for_current_kernel(),
-                "kernel": "attn_fwd_bf16_kernel<128>", "kernel_ms": round(k_avg, 4),
-                "kernel_ms_min": round(min(kms), 4)}
+                "traffic": _traffic_for_current_kernel("attn_fwd_bf16_t2i_2048_traffic.txt",
+                                                       "attn_bf16.hip"),
+                "kernel": "attn_fwd_bf16_kernel<128, true> (+ merge_split_kernel of the split "
+                          "last round)",
+                "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4)}
     _log(f"[bench] fwd kernel avg {k_avg:.3f} ms -> {achieved:.1f} TFLOP/s "
          f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
 
@@ -181,9 +186,13 @@ def main() -> int:
         f_tf = flops / (f_avg * 1e-3) / 1e12
         fp8 = {"fwd_ms": round(f_avg, 4), "fwd_tflops": round(f_tf, 2),
                "fwd_frac_of_fp8_peak": round(f_tf / PEAK_FP8_TFLOPS, 4),
+               "fwd_traffic": _traffic_for_current_kernel("attn_fwd_fp8_t2i_2048_traffic.txt",
+                                                          "attn_fp8.hip"),
                "quant_ms": round(q_avg, 4),
                "quant_gbs": round(q_bytes / (q_avg * 1e-3) / 1e9, 1),
                "quant_frac_of_hbm": round(q_bytes / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "quant_traffic": _traffic_for_current_kernel("quant_rope_fp8_t2i_2048_traffic.txt",
+                                                            "quant_fp8.hip"),
                "path_tflops": round(flops / ((f_avg + q_avg) * 1e-3) / 1e12, 2)}
         _log(f"[bench] fp8: fwd {f_avg:.3f} ms ({f_tf:.1f} TFLOP/s), quant {q_avg:.3f} ms "
              f"({fp8['quant_gbs']} GB/s)")
