@@ -206,7 +206,7 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   const int vrow_bytes = (int)(a.v_ss * 2);
   u32x4 kreg[KP];
   float4 treg[KP][2];
-  uint16_t vreg[VP][8];
+  uint32_t vreg[VP][8];
   auto load_k = [&](int t) JA_INLINE {
     if (K_THREADS < NT && tid >= K_THREADS) return;
 #pragma unroll
@@ -232,10 +232,21 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
             vrs, vd * 2, (key0 + vt_key_of_slot(8 * (vc & 1) + j)) * vrow_bytes, 0);
     }
   };
+  // The empty asm statements in the stores pin the use of the loaded
+  // registers there: otherwise the compiler moves the rotation and packing
+  // (and with them the wait for the loads) up to just after the previous
+  // barrier, where every wave would wait for memory at the same moment.
   auto store_k = [&](int buf) JA_INLINE {
     if (K_THREADS < NT && tid >= K_THREADS) return;
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
+      asm volatile("" : "+v"(kreg[p]));
+      if constexpr (ROPE) {
+        u32x4 c0 = bit_cast<u32x4>(treg[p][0]), c1 = bit_cast<u32x4>(treg[p][1]);
+        asm volatile("" : "+v"(c0), "+v"(c1));
+        treg[p][0] = bit_cast<float4>(c0);
+        treg[p][1] = bit_cast<float4>(c1);
+      }
       u32x4 kw = kreg[p];
       if constexpr (ROPE) {
         kw.x = rope_pair_bf16(kw.x, make_float2(treg[p][0].x, treg[p][0].y));
@@ -251,11 +262,13 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
     for (int p = 0; p < VP; ++p) {
       const int vc = vc0 + p * (NS / D);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(vreg[p][j]));
       u32x4 w;
-      w.x = (uint32_t)vreg[p][0] | ((uint32_t)vreg[p][1] << 16);
-      w.y = (uint32_t)vreg[p][2] | ((uint32_t)vreg[p][3] << 16);
-      w.z = (uint32_t)vreg[p][4] | ((uint32_t)vreg[p][5] << 16);
-      w.w = (uint32_t)vreg[p][6] | ((uint32_t)vreg[p][7] << 16);
+      w.x = vreg[p][0] | (vreg[p][1] << 16);
+      w.y = vreg[p][2] | (vreg[p][3] << 16);
+      w.z = vreg[p][4] | (vreg[p][5] << 16);
+      w.w = vreg[p][6] | (vreg[p][7] << 16);
       *reinterpret_cast<u32x4 *>(Vbuf(buf) + vd * VTSTR + 8 * vc) = w;
     }
   };
