@@ -7,9 +7,9 @@
 // "GEMM kernel optimization"); here it is applied in fp32 while Q and K are
 // loaded and the rotated values are rounded to bf16 for the MFMA.
 //
-// Work decomposition: one workgroup per (256-query block, head, batch row),
-// eight wave64s of 32 query rows each.  Both products are computed transposed
-// so that a lane owns one query row throughout:
+// Work decomposition: one workgroup per (384-query block, head, batch row),
+// twelve wave64s of 32 query rows each, three per SIMD.  Both products are
+// computed transposed so that a lane owns one query row throughout:
 //   S^T[key][q]  = K . Q^T      (v_mfma_f32_32x32x16_bf16, A = rotated K from
 //                                LDS, B = rotated Q kept in registers)
 //   O^T[d][q]   += V^T . P^T    (A = V^T from LDS, B = P straight from the S^T
@@ -25,10 +25,11 @@
 // reads.  Rows are padded so that the 16 lanes served together hit distinct
 // banks.
 //
-// Pipeline: iteration t computes Q K^T of tile t+1 in the same basic block as
-// the softmax of tile t, so those MFMAs overlap its VALU work; after the
-// (rare) rescale branch, P.V of tile t overlaps the rotation and staging of K
-// tile t+2 and V tile t+1.  One barrier per iteration.
+// Each wave runs Q K^T, softmax and P.V of a tile in turn; the three waves of
+// a SIMD overlap one another's MFMA, VALU and memory waits (a wave needs 160
+// VGPRs this way, against more than 168 for a wave that also overlaps the
+// next tile's Q K^T with its own softmax).  The next tiles' global loads are
+// issued one iteration ahead; one barrier per tile.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -37,7 +38,7 @@ namespace ja {
 namespace {
 
 #ifndef JA_BF16_WAVES
-#define JA_BF16_WAVES 8
+#define JA_BF16_WAVES 12
 #endif
 #ifndef JA_BF16_STAGE_WAVES
 #define JA_BF16_STAGE_WAVES JA_BF16_WAVES
@@ -51,9 +52,10 @@ constexpr int BM = 32 * RW * NW;    // query rows per workgroup
 constexpr int BN = 32;              // keys per K/V tile
 constexpr int NT = 64 * NW;         // threads per workgroup
 constexpr int NS = 64 * JA_BF16_STAGE_WAVES;   // threads that stage K/V tiles
-// Workgroups resident per CU: two waves per SIMD in total, so that while one
-// waits on memory or on its workgroup's barrier the other one issues.
-constexpr int WG_PER_CU = 8 / (NW * RW) > 0 ? 8 / (NW * RW) : 1;
+// One workgroup per CU: 12 waves, three per SIMD, at most 168 VGPRs each.
+// Latency is hidden by the three waves of a SIMD rather than by deeper
+// software pipelining inside a wave (which needs more registers).
+constexpr int WG_PER_CU = 1;
 
 // Rescale the output accumulator only when the running row max grows by more
 // than 2^24 in the exp2 domain.  Until then P may exceed 1 by up to 2^24;
@@ -391,13 +393,11 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     for (int r = 0; r < RW; ++r) l_run[r] += lt[r];
   };
 
-  // ---- software pipeline over the key tiles t0 .. t1-1 (local index
-  //      i = t - t0).  Local tile i lives in K buffer i%2 and V buffer i%2.
-  //      Iteration i computes Q K^T of tile i+1 while it runs the softmax of
-  //      tile i, then P.V of tile i while it rotates and stores K of tile i+2
-  //      and stores V of tile i+1 (into the buffers read by iteration i-1);
-  //      right after those stores it issues the global loads of K tile i+3
-  //      and V tile i+2, which then have a whole iteration to arrive; a
+  // ---- loop over the key tiles t0 .. t1-1 (local index i = t - t0).  Local
+  //      tile i lives in K buffer i%2 and V buffer i%2.  Iteration i computes
+  //      Q K^T, the softmax and P.V of tile i, then rotates and stores K and V
+  //      of tile i+1 (into the buffers read by iteration i-1) and issues the
+  //      global loads of tile i+2, which have a whole iteration to arrive; a
   //      barrier closes the iteration. ----
   const int nt = t1 - t0;
   load_k(t0);
@@ -406,48 +406,30 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   store_v(0);
   if (nt > 1) {
     load_k(t0 + 1);
-    store_k(1);
+    load_v(t0 + 1);
   }
-  if (nt > 2) load_k(t0 + 2);
-  if (nt > 1) load_v(t0 + 1);
   __syncthreads();
-  f32x16 s_a[RW], s_b[RW];
-  qk.template operator()<0, D / 16>(0, s_a);
-
-  // NEXT: tile i+1 exists; K2: tile i+2 exists.  Only the last tile of the
-  // sequence can be partial (masking a full tile changes nothing).
-  auto iteration = [&]<bool NEXT, bool K2>(int i, f32x16 (&cur)[RW],
-                                           f32x16 (&nxt)[RW]) JA_INLINE {
+  f32x16 sacc[RW];
+  // NEXT: tile i+1 exists.  Only the last tile of the sequence can be partial
+  // (masking a full tile changes nothing).
+  auto iteration = [&]<bool NEXT>(int i) JA_INLINE {
     const int t = t0 + i;
-    if constexpr (NEXT) qk.template operator()<0, D / 16>((i + 1) & 1, nxt);
+    qk.template operator()<0, D / 16>(i & 1, sacc);
     bf16x8 pb[RW][2];
-    softmax.template operator()<!NEXT>(cur, t * BN, pb);
+    softmax.template operator()<!NEXT>(sacc, t * BN, pb);
     pv(pb, i & 1);
-    if constexpr (K2) store_k(i & 1);
-    if constexpr (NEXT) store_v((i + 1) & 1);
-    if constexpr (K2) {
-      if (i + 3 < nt) load_k(t + 3);
-      load_v(t + 2);
+    if constexpr (NEXT) {
+      store_k((i + 1) & 1);
+      store_v((i + 1) & 1);
+      if (i + 2 < nt) {
+        load_k(t + 2);
+        load_v(t + 2);
+      }
     }
     __syncthreads();
   };
-  // The score registers of tiles i and i+1 swap roles every iteration, so
-  // the steady state runs two iterations per loop trip.
-  int i = 0;
-  for (; i + 3 < nt; i += 2) {
-    iteration.template operator()<true, true>(i, s_a, s_b);
-    iteration.template operator()<true, true>(i + 1, s_b, s_a);
-  }
-  if (nt - i == 3) {
-    iteration.template operator()<true, true>(i, s_a, s_b);
-    iteration.template operator()<true, false>(i + 1, s_b, s_a);
-    iteration.template operator()<false, false>(i + 2, s_a, s_b);
-  } else if (nt - i == 2) {
-    iteration.template operator()<true, false>(i, s_a, s_b);
-    iteration.template operator()<false, false>(i + 1, s_b, s_a);
-  } else {
-    iteration.template operator()<false, false>(i, s_a, s_b);
-  }
+  for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<true>(i);
+  iteration.template operator()<false>(nt - 1);
 
   // ---- a split part leaves O unnormalised, with its row max (raw score
   //      units) and row sum, for the merge kernel ----
