@@ -16,10 +16,10 @@
 // multiplies by sv_max / 64.  The softmax normaliser sums the unquantized
 // fp32 P.
 //
-// Structure as in the bf16 kernel: one workgroup of eight wave64s per
-// (256-query block, head, batch row), XCD-aware placement, K/V tiles of 64
-// keys double-buffered in LDS with the next tiles loaded while the current
-// one is consumed, one barrier per tile.  K rows are copied as they are; V is
+// Structure as in the bf16 kernel: one workgroup of eight wave64s (two per
+// SIMD) per (256-query block, head, batch row), XCD-aware placement, K/V tiles
+// of 64 keys double-buffered in LDS with the next tiles loaded one iteration
+// ahead, one barrier per tile.  K rows are copied as they are; V is
 // staged transposed (one row per head-dimension column, keys in the order in
 // which the P' operand holds them) by a 4 x 4 byte transpose in registers, so
 // both MFMA operands are 16-byte LDS reads.
@@ -32,7 +32,10 @@ namespace ja {
 
 namespace {
 
-constexpr int NW = 8;               // waves per workgroup, 32 query rows each
+// Waves per workgroup, 32 query rows each, two per SIMD: a wave of this
+// kernel needs about 200 VGPRs (three waves per SIMD would allow 168, and the
+// spills that forces cost more than the third wave gains).
+constexpr int NW = 8;
 constexpr int BM = 32 * NW;         // query rows per workgroup
 constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
 constexpr int NT = 64 * NW;         // threads per workgroup
@@ -310,49 +313,32 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     return pb;
   };
 
-  // ---- software pipeline over the key tiles t0 .. t1-1 (local index i):
-  //      local tile i lives in K buffer i%2 and V buffer i%2 (with its
-  //      scales).  Iteration i computes Q K^T of tile i+1 while it runs the
-  //      softmax of tile i, then P.V of tile i while it stores K of tile i+2
-  //      and V of tile i+1 into the buffers read by iteration i-1. ----
+  // ---- loop over the key tiles t0 .. t1-1 (local index i): local tile i
+  //      lives in K buffer i%2 and V buffer i%2 (with its scales).  Iteration
+  //      i computes Q K^T, the softmax and P.V of tile i, then stores K and V
+  //      of tile i+1 (into the buffers read by iteration i-1) and issues the
+  //      loads of tile i+2; a barrier closes the iteration. ----
   const int nt = t1 - t0;
   load(t0, true, true);
   store_k(0);
   store_v(0);
-  if (nt > 1) {
-    load(t0 + 1, true, false);
-    store_k(1);
-  }
+  if (nt > 1) load(t0 + 1, true, true);
   __syncthreads();
-  f32x16 s_a[2], s_b[2];
-  qk(0, s_a);
-
-  auto iteration = [&]<bool NEXT, bool K2>(int i, f32x16 (&cur)[2], f32x16 (&nxt)[2]) JA_INLINE {
+  f32x16 sacc[2];
+  auto iteration = [&]<bool NEXT>(int i) JA_INLINE {
     const int t = t0 + i;
-    if constexpr (K2 || NEXT) load(K2 ? t + 2 : 0, K2, false);
-    if constexpr (NEXT) load(t + 1, false, true);
-    if constexpr (NEXT) qk((i + 1) & 1, nxt);
-    const i32x8 pb = softmax.template operator()<!NEXT>(cur, t * BN, i & 1);
+    qk(i & 1, sacc);
+    const i32x8 pb = softmax.template operator()<!NEXT>(sacc, t * BN, i & 1);
     pv(pb, i & 1);
-    if constexpr (K2) store_k(i & 1);
-    if constexpr (NEXT) store_v((i + 1) & 1);
+    if constexpr (NEXT) {
+      store_k((i + 1) & 1);
+      store_v((i + 1) & 1);
+      if (i + 2 < nt) load(t + 2, true, true);
+    }
     __syncthreads();
   };
-  int i = 0;
-  for (; i + 3 < nt; i += 2) {
-    iteration.template operator()<true, true>(i, s_a, s_b);
-    iteration.template operator()<true, true>(i + 1, s_b, s_a);
-  }
-  if (nt - i == 3) {
-    iteration.template operator()<true, true>(i, s_a, s_b);
-    iteration.template operator()<true, false>(i + 1, s_b, s_a);
-    iteration.template operator()<false, false>(i + 2, s_a, s_b);
-  } else if (nt - i == 2) {
-    iteration.template operator()<true, false>(i, s_a, s_b);
-    iteration.template operator()<false, false>(i + 1, s_b, s_a);
-  } else {
-    iteration.template operator()<false, false>(i, s_a, s_b);
-  }
+  for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<true>(i);
+  iteration.template operator()<false>(nt - 1);
 
   const float l_tot = half_sum(l_run);
   const float o_mul = sv_max / kPScale;
