@@ -16,7 +16,8 @@ FLUX 3 Image Klein on NVIDIA Blackwell GPUs"):
   query/key normalization and rotary position embeddings); attention then
   consumes rotated Q and K stored in bf16;
 * FP8 Q/K and V (section "Quantized and sparse attention", qk_dtype and
-  v_dtype fp8).
+  v_dtype fp8), and the repair of the tokens with the largest quantization
+  error (same section, VC-Attention FP8 with vc_repair_budget).
 
 The pages state none of the arithmetic; the readings taken where they are
 silent (2D-axial frequencies, pair convention, bf16 rounding point of the
@@ -31,11 +32,13 @@ brute force, exact rational arithmetic and library routines.
 from .rope import rope_angles, apply_rope, rope_table_fp32, rotate_fp32, fma32
 from .attention import attention, joint_attention, brute_force_attention
 from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, quant_rope_fp8,
-                  dequantize, fp8_attention)
+                  dequantize, fp8_attention, repair_count, quant_error, repair_errors,
+                  repair_select, repair_values, fp8_repaired_attention)
 
 __all__ = [
     "rope_angles", "apply_rope", "rope_table_fp32", "rotate_fp32", "fma32",
     "attention", "joint_attention", "brute_force_attention",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "quant_rope_fp8",
-    "dequantize", "fp8_attention",
+    "dequantize", "fp8_attention", "repair_count", "quant_error", "repair_errors",
+    "repair_select", "repair_values", "fp8_repaired_attention",
 ]

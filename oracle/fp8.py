@@ -119,3 +119,99 @@ def fp8_attention(q8, k8, v8, sq, sk, sv, scale=None, rows=None):
     """fp64 attention on the dequantized Q/K/V (RoPE already applied)."""
     return attention(dequantize(q8, sq), dequantize(k8, sk), dequantize(v8, sv),
                      scale=scale, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# Repair of the tokens with the largest quantization error (VC-Attention FP8)
+#
+# The pages configure VC-Attention FP8 with a repair budget rho = 0.005 that
+# selects the fraction of tokens with the highest quantization error for
+# residual correction (same page, section "Quantized and sparse attention",
+# vc_repair_budget).  The mechanism is not given beyond that sentence.
+# Reading taken:
+#
+# * a token's error, per (batch, head), is the max-abs quantization error of
+#   its key plus that of its value: e = max_d |k - k^| + max_d |v - v^|, with
+#   k the fp32 rotated key that was quantized, k^ = fl32(code value * scale),
+#   and both maxima and their sum in fp32 (max is order-free, so any fp32
+#   implementation takes the same selection);
+# * the ceil(rho * S) tokens with the largest e are repaired, ties to the
+#   lower token index;
+# * repairing a token adds its residual (k - k^, v - v^) back, i.e. the key
+#   and value of that token enter attention at the precision of the bf16 path
+#   (the bf16-rounded rotated key, the bf16 value).  Queries stay FP8: a
+#   query's error only affects its own row, a key's error every row.
+# ---------------------------------------------------------------------------
+
+def repair_count(budget: float, seq_len: int) -> int:
+    """Repaired tokens per (batch, head): ceil(budget * seq_len)."""
+    return int(np.ceil(np.float64(budget) * seq_len))
+
+
+def _bshd_scales(scales) -> np.ndarray:
+    return np.transpose(np.asarray(scales, dtype=np.float32), (0, 2, 1))[..., None]
+
+
+def quant_error(x32, codes, scales) -> np.ndarray:
+    """max over D of |x - fl32(value(code) * scale)|, all in fp32: float32
+    [B, H, S].  x32: the fp32 values that were quantized, [B, S, H, D]."""
+    deq = e4m3_decode(codes).astype(np.float32) * _bshd_scales(scales)   # one fp32 rounding
+    err = np.abs(np.asarray(x32, np.float32) - deq.astype(np.float32)).astype(np.float32)
+    return np.ascontiguousarray(np.transpose(err.max(axis=-1), (0, 2, 1)))
+
+
+def repair_errors(k, v, pos, k8, v8, sk, sv, theta: float = 10000.0) -> np.ndarray:
+    """Per-(b, h, token) error e = err(K) + err(V) in fp32, float32 [B, H, S]."""
+    k32 = torch.as_tensor(k).to(torch.float32).numpy()
+    v32 = torch.as_tensor(v).to(torch.float32).numpy()
+    if pos is not None:
+        k32 = rotate_fp32(k32, rope_table_fp32(pos, k32.shape[-1], theta))
+    return (quant_error(k32, k8, sk) + quant_error(v32, v8, sv)).astype(np.float32)
+
+
+def repair_select(err, n: int) -> np.ndarray:
+    """Token indices [B, H, n] (ascending) of the n largest errors of each
+    (b, h) row; equal errors are taken in ascending token order."""
+    err = np.asarray(err, np.float32)
+    b, h, s = err.shape
+    out = np.empty((b, h, n), dtype=np.int32)
+    idx = np.arange(s)
+    for bi in range(b):
+        for hi in range(h):
+            order = np.lexsort((idx, -err[bi, hi].astype(np.float64)))
+            out[bi, hi] = np.sort(order[:n])
+    return out
+
+
+def repair_values(k, v, pos, idx, theta: float = 10000.0):
+    """Exact key and value of the repaired tokens: the bf16-rounded rotated
+    key (as on the bf16 path) and the bf16 value, float64 [B, H, n, D]."""
+    k32 = torch.as_tensor(k).to(torch.float32).numpy()
+    if pos is not None:
+        k32 = rotate_fp32(k32, rope_table_fp32(pos, k32.shape[-1], theta))
+    kb = torch.from_numpy(np.ascontiguousarray(k32)).to(torch.bfloat16).to(torch.float64)
+    vb = torch.as_tensor(v).to(torch.float64)
+    idx = np.asarray(idx)
+    b, h, n = idx.shape
+    d = kb.shape[-1]
+    kr = torch.empty((b, h, n, d), dtype=torch.float64)
+    vr = torch.empty((b, h, n, d), dtype=torch.float64)
+    for bi in range(b):
+        for hi in range(h):
+            sel = torch.from_numpy(np.array(idx[bi, hi], dtype=np.int64))
+            kr[bi, hi] = kb[bi, sel, hi]
+            vr[bi, hi] = vb[bi, sel, hi]
+    return kr, vr
+
+
+def fp8_repaired_attention(q8, k8, v8, sq, sk, sv, idx, kr, vr, scale=None, rows=None):
+    """fp64 attention on the dequantized Q/K/V in which the keys and values of
+    the tokens idx[b, h] are replaced by their exact values kr / vr."""
+    qd, kd, vd = dequantize(q8, sq), dequantize(k8, sk), dequantize(v8, sv)
+    idx = np.asarray(idx)
+    for bi in range(idx.shape[0]):
+        for hi in range(idx.shape[1]):
+            sel = torch.from_numpy(np.array(idx[bi, hi], dtype=np.int64))
+            kd[bi, sel, hi] = torch.as_tensor(kr[bi, hi], dtype=torch.float64)
+            vd[bi, sel, hi] = torch.as_tensor(vr[bi, hi], dtype=torch.float64)
+    return attention(qd, kd, vd, scale=scale, rows=rows)

@@ -92,3 +92,82 @@ def test_fp8_attention_on_exact_inputs_is_plain_attention():
     o, _ = oracle.fp8_attention(q8, k8, v8, sq, sk, sv)
     ref, _ = oracle.attention(x, x * 0.5, x)
     assert torch.allclose(o, ref, atol=1e-12)
+
+
+# ---- repair of the tokens with the largest quantization error ----
+
+def test_quant_error_closed_forms():
+    # 1.0625 lies halfway between e4m3 1.0 and 1.125 and rounds to the even
+    # code 1.0: error 0.0625.  Values that are codes times the scale have
+    # error 0.  Scale 2: 3.25 = 2 * 1.625 is exact (1.625 is a code).
+    x = np.zeros((1, 3, 1, 4), np.float32)
+    x[0, 0, 0] = [1.0625, 0.0, 0.0, 448.0]        # amax 448 -> scale 1
+    x[0, 1, 0] = [448.0 * 2, 3.25, 0.0, 0.0]       # scale 2
+    x[0, 2, 0] = [0.0, 0.0, 0.0, 0.0]              # all zero: scale 1, error 0
+    codes, scales = oracle.fp8._quantize_rows(x)
+    err = oracle.quant_error(x, codes, scales)
+    assert err.shape == (1, 1, 3)
+    assert err[0, 0, 0] == np.float32(0.0625)
+    assert err[0, 0, 1] == 0.0 and err[0, 0, 2] == 0.0
+
+
+def test_repair_select_matches_brute_force_with_ties():
+    rng = np.random.default_rng(11)
+    err = rng.integers(0, 6, size=(2, 3, 40)).astype(np.float32)   # many ties
+    for n in (0, 1, 7, 40):
+        got = oracle.repair_select(err, n)
+        for b in range(2):
+            for h in range(3):
+                ranked = sorted(range(40), key=lambda i: (-float(err[b, h, i]), i))
+                assert list(got[b, h]) == sorted(ranked[:n]), (n, b, h)
+
+
+def test_repair_count():
+    assert oracle.repair_count(0.005, 16896) == 85
+    assert oracle.repair_count(0.005, 80) == 1
+    assert oracle.repair_count(0.0, 80) == 0
+    assert oracle.repair_count(1.0, 80) == 80
+
+
+def test_repaired_attention_limits():
+    # no repaired token: plain FP8 attention; every token repaired: attention
+    # on the dequantized queries with the exact (bf16-path) keys and values.
+    w = synth.WORKLOADS["tiny"]
+    q, k, v, _ = synth.make_qkv(w, 2)
+    pos = synth.positions(w)
+    codes = oracle.quant_rope_fp8(q, k, v, pos)
+    q8, k8, v8, sq, sk, sv = codes
+    b, s, h, d = q.shape
+    none = np.zeros((b, h, 0), np.int32)
+    kr, vr = oracle.repair_values(k, v, pos, none)
+    o0, l0 = oracle.fp8_repaired_attention(*codes, none, kr, vr)
+    o1, l1 = oracle.fp8_attention(*codes)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    every = np.broadcast_to(np.arange(s, dtype=np.int32), (b, h, s))
+    kr, vr = oracle.repair_values(k, v, pos, every)
+    oa, la = oracle.fp8_repaired_attention(*codes, every, kr, vr)
+    # reference keys: the rotated keys of the bf16 path (fp32 rotation, bf16)
+    kx = torch.from_numpy(oracle.rotate_fp32(k.float().numpy(),
+                                             oracle.rope_table_fp32(pos, d))).to(torch.bfloat16)
+    ob, lb = oracle.attention(oracle.dequantize(q8, sq), kx, v)
+    assert torch.allclose(oa, ob, rtol=0, atol=1e-12) and torch.allclose(la, lb, rtol=0, atol=1e-12)
+
+
+def test_repair_reduces_error_on_outlier_inputs():
+    # The largest quantization errors sit on the x8 outlier tokens; repairing
+    # them must bring FP8 attention closer to the bf16-path attention.
+    w = synth.WORKLOADS["t2i_1024"].replace(heads=2, n_text=64, grid=24)
+    q, k, v, _ = synth.make_qkv(w, 4)
+    pos = synth.positions(w)
+    codes = oracle.quant_rope_fp8(q, k, v, pos)
+    rows = np.arange(0, w.seq_len, 7)
+    ref, _ = oracle.joint_attention(q, k, v, pos, rows=rows)
+    base, _ = oracle.fp8_attention(*codes, rows=rows)
+    err = oracle.repair_errors(k, v, pos, *codes[1:3], *codes[4:6])
+    n = oracle.repair_count(0.01, w.seq_len)
+    idx = oracle.repair_select(err, n)
+    kr, vr = oracle.repair_values(k, v, pos, idx)
+    rep, _ = oracle.fp8_repaired_attention(*codes, idx, kr, vr, rows=rows)
+    e0 = float((base - ref).norm() / ref.norm())
+    e1 = float((rep - ref).norm() / ref.norm())
+    assert e1 < 0.9 * e0, (e0, e1)
