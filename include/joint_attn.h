@@ -144,12 +144,53 @@ ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,
                                     void *stream);
 
 /*
+ * Repair of the FP8 path (the pages' VC-Attention FP8 with vc_repair_budget:
+ * the fraction of tokens with the highest quantization error gets a residual
+ * correction; section "Quantized and sparse attention").  Reading: per
+ * (batch, head), token t's error is e = max_d |k - k^| + max_d |v - v^| in
+ * fp32 (k the rotated key that was quantized, k^ = fl(value(code) * scale));
+ * the n_rep tokens with the largest e (ties to the lower index) are repaired:
+ * their key and value enter attention at bf16-path precision.
+ *
+ * joint_attn_fp8_repair_plan - selects the repaired tokens and gathers them.
+ *   p           shape and the K/V strides of k and v (Q and O strides unused).
+ *   k, v, rope  as for joint_attn_quant_rope_fp8.
+ *   k8, v8, sk, sv   that call's outputs.
+ *   n_rep       0 <= n_rep <= seq_len (ceil(budget * seq_len) for a budget).
+ *   idx         device int32 [batch][heads][n_rep]: written with the repaired
+ *               token indices, ascending (may be NULL when n_rep = 0).
+ *   kr, vr      device bf16 [batch][heads][n_pad][head_dim], n_pad = n_rep
+ *               rounded up to a multiple of 32: the rotated keys (rotation
+ *               and bf16 rounding as in joint_attn_fwd_bf16) and the values of
+ *               the repaired tokens; rows n_rep .. n_pad-1 are zero.
+ *   kbias       device float [batch][heads][seq_len]: 0, or -inf for a
+ *               repaired token.
+ * seq_len is limited to 39936 (the selection keeps a row's errors in LDS);
+ * larger: JA_ERR_UNSUPPORTED.
+ */
+ja_status joint_attn_fp8_repair_plan(const ja_params *p, const void *k, const void *v,
+                                     const float *rope, const void *k8, const void *v8,
+                                     const float *sk, const float *sv, int32_t n_rep,
+                                     int32_t *idx, void *kr, void *vr, float *kbias,
+                                     void *stream);
+
+/* The repair set passed to joint_attn_fwd_fp8 (n_rep = 0: none). */
+typedef struct {
+  int32_t n_rep;
+  const float *kbias;   /* [batch][heads][seq_len], 16-byte aligned */
+  const void *kr, *vr;  /* [batch][heads][n_pad][head_dim] bf16 */
+} ja_fp8_repair;
+
+/*
  * joint_attn_fwd_fp8 - joint attention on FP8 inputs produced by
  * joint_attn_quant_rope_fp8 (RoPE already applied).
  *   q8, k8, v8  device e4m3, contiguous [batch][seq_len][heads][head_dim]
  *               (the Q, K and V strides of p are ignored).
  *   sq, sk, sv  device float [batch][heads][seq_len] dequantization scales,
  *               16-byte aligned.
+ *   repair      nullable: repaired tokens from joint_attn_fp8_repair_plan.
+ *               Their keys are removed from the FP8 tiles and attended from
+ *               kr / vr (bf16 products) in the same softmax.
  *   o           device bf16, layout per ja_params (o_* strides).
  *   lse         device float [batch][heads][seq_len], nullable.
  *   workspace, workspace_bytes
@@ -163,8 +204,9 @@ ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,
  */
 ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
                              const void *v8, const float *sq, const float *sk,
-                             const float *sv, void *o, float *lse, void *workspace,
-                             size_t workspace_bytes, void *stream);
+                             const float *sv, const ja_fp8_repair *repair, void *o,
+                             float *lse, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * joint_attn_fwd_fp8_workspace_bytes - bytes of the optional workspace of

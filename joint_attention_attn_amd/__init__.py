@@ -8,13 +8,14 @@ library is missing or a call fails, a RuntimeError is raised.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
 
 __all__ = [
     "JointAttnError", "library_path", "load", "rope_table_2d", "fwd_bf16",
-    "fwd_bf16_workspace_bytes",
+    "fwd_bf16_workspace_bytes", "Fp8Repair", "fp8_repair_plan", "repair_count",
     "quant_rope_fp8", "fwd_fp8", "Params",
 ]
 
@@ -44,6 +45,12 @@ class Params(ctypes.Structure):
     ]
 
 
+class Fp8RepairC(ctypes.Structure):
+    """Mirror of ja_fp8_repair."""
+    _fields_ = [("n_rep", ctypes.c_int32), ("kbias", ctypes.c_void_p),
+                ("kr", ctypes.c_void_p), ("vr", ctypes.c_void_p)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -64,7 +71,11 @@ def load() -> ctypes.CDLL:
     lib.joint_attn_fwd_bf16_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_bf16_workspace_bytes.restype = ctypes.c_size_t
     lib.joint_attn_quant_rope_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Fp8RepairC),
+                                       vp, vp, vp, ctypes.c_size_t, vp]
+    lib.joint_attn_fp8_repair_plan.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
+                                               vp, vp, vp, vp, vp]
+    lib.joint_attn_fp8_repair_plan.restype = st
     lib.joint_attn_fwd_fp8_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("joint_attn_rope_table_2d", "joint_attn_fwd_bf16",
@@ -178,10 +189,42 @@ def quant_rope_fp8(q, k, v, rope=None):
     return q8, k8, v8, sq, sk, sv
 
 
+class Fp8Repair:
+    """Repaired tokens of the FP8 path (from fp8_repair_plan): idx [B, H, n]
+    int32, kr / vr [B, H, n_pad, D] bf16, kbias [B, H, S] fp32."""
+
+    def __init__(self, n_rep, idx, kr, vr, kbias):
+        self.n_rep, self.idx, self.kr, self.vr, self.kbias = n_rep, idx, kr, vr, kbias
+
+
+def repair_count(budget: float, seq_len: int) -> int:
+    """Repaired tokens per (batch, head) for a repair budget: ceil(budget * seq_len)."""
+    return int(math.ceil(float(budget) * seq_len))
+
+
+def fp8_repair_plan(k, v, rope, k8, v8, sk, sv, n_rep: int) -> Fp8Repair:
+    """Select the n_rep tokens per (batch, head) with the largest FP8 quantization
+    error of their key and value, and gather their exact rotated keys and values."""
+    b, s, h, d = k.shape
+    dev = k.device
+    n_pad = (n_rep + 31) // 32 * 32
+    idx = torch.empty((b, h, n_rep), dtype=torch.int32, device=dev)
+    kr = torch.empty((b, h, n_pad, d), dtype=torch.bfloat16, device=dev)
+    vr = torch.empty((b, h, n_pad, d), dtype=torch.bfloat16, device=dev)
+    kbias = torch.empty((b, h, s), dtype=torch.float32, device=dev)
+    p = _params(k, k, v, k, 0.0)
+    st = load().joint_attn_fp8_repair_plan(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(rope), _ptr(k8),
+                                           _ptr(v8), _ptr(sk), _ptr(sv), int(n_rep),
+                                           _ptr(idx) if n_rep else None, _ptr(kr), _ptr(vr),
+                                           _ptr(kbias), _stream(dev))
+    _check(st, "joint_attn_fp8_repair_plan")
+    return Fp8Repair(n_rep, idx, kr, vr, kbias)
+
+
 def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
-            split: bool = True):
+            split: bool = True, repair: "Fp8Repair | None" = None):
     """Joint attention on contiguous e4m3 codes [B, S, H, D] with fp32 scales [B, H, S].
-    `split` as for fwd_bf16."""
+    `split` as for fwd_bf16; `repair` from fp8_repair_plan (None: no repair)."""
     b, s, h, d = q8.shape
     for t in (q8, k8, v8):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous() \
@@ -201,8 +244,11 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return
     lib = load()
     ws_bytes = lib.joint_attn_fwd_fp8_workspace_bytes(ctypes.byref(p)) if split else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q8.device) if ws_bytes else None
+    rc = None
+    if repair is not None and repair.n_rep > 0:
+        rc = Fp8RepairC(int(repair.n_rep), _ptr(repair.kbias), _ptr(repair.kr), _ptr(repair.vr))
     st = lib.joint_attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq),
-                                _ptr(sk), _ptr(sv), _ptr(out), _ptr(lse), _ptr(ws), ws_bytes,
-                                _stream(q8.device))
+                                _ptr(sk), _ptr(sv), ctypes.byref(rc) if rc is not None else None,
+                                _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(q8.device))
     _check(st, "joint_attn_fwd_fp8")
     return (out, lse) if return_lse else out

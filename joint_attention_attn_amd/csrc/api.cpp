@@ -197,13 +197,49 @@ size_t joint_attn_fwd_fp8_workspace_bytes(const ja_params *p) {
   return (size_t)ja::plan_fwd_fp8(layout(p), device_cu_count()).ws_bytes;
 }
 
+ja_status joint_attn_fp8_repair_plan(const ja_params *p, const void *k, const void *v,
+                                     const float *rope, const void *k8, const void *v8,
+                                     const float *sk, const float *sv, int32_t n_rep,
+                                     int32_t *idx, void *kr, void *vr, float *kbias,
+                                     void *stream) {
+  if (!p || !k || !v || !k8 || !v8 || !sk || !sv || !kbias || !kr || !vr)
+    return JA_ERR_INVALID_ARG;
+  const ja_status st = check_params(p, true, 0);
+  if (st != JA_OK) return st;
+  if (n_rep < 0 || n_rep > p->seq_len || (n_rep > 0 && !idx)) return JA_ERR_INVALID_ARG;
+  if (p->seq_len > ja::repair_max_seq()) return JA_ERR_UNSUPPORTED;
+  if ((int64_t)p->batch * p->heads > 0x7fffffffLL) return JA_ERR_UNSUPPORTED;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k8) || !aligned16(v8) || !aligned16(kr) ||
+      !aligned16(vr) || (rope && !aligned16(rope)) ||
+      (reinterpret_cast<uintptr_t>(sk) & 3u) || (reinterpret_cast<uintptr_t>(sv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(kbias) & 3u) || (idx && (reinterpret_cast<uintptr_t>(idx) & 3u)))
+    return JA_ERR_INVALID_ARG;
+  const int64_t threads = (int64_t)p->batch * p->seq_len * p->heads * (p->head_dim / 8);
+  if ((threads + 255) / 256 > 0x7fffffffLL) return JA_ERR_UNSUPPORTED;
+  return hip_status(ja::launch_repair_plan(layout(p), k, v, rope, k8, v8, sk, sv, n_rep, idx,
+                                           kr, vr, kbias, static_cast<hipStream_t>(stream)));
+}
+
 ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
                              const void *v8, const float *sq, const float *sk,
-                             const float *sv, void *o, float *lse, void *workspace,
-                             size_t workspace_bytes, void *stream) {
+                             const float *sv, const ja_fp8_repair *repair, void *o,
+                             float *lse, void *workspace, size_t workspace_bytes,
+                             void *stream) {
   if (!p || !q8 || !k8 || !v8 || !sq || !sk || !sv || !o) return JA_ERR_INVALID_ARG;
   const ja_status st = check_fwd_fp8(p);
   if (st != JA_OK) return st;
+  ja::Fp8Repair rp;
+  if (repair && repair->n_rep > 0) {
+    if (repair->n_rep > p->seq_len || !repair->kbias || !repair->kr || !repair->vr ||
+        !aligned16(repair->kr) || !aligned16(repair->vr) || !aligned16(repair->kbias))
+      return JA_ERR_INVALID_ARG;
+    rp.n_rep = repair->n_rep;
+    rp.kbias = repair->kbias;
+    rp.kr = repair->kr;
+    rp.vr = repair->vr;
+  } else if (repair && repair->n_rep < 0) {
+    return JA_ERR_INVALID_ARG;
+  }
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) ||
       !aligned16(sq) || !aligned16(sk) || !aligned16(sv) ||
       (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (workspace && !aligned16(workspace)))
@@ -212,7 +248,7 @@ ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
   ja::SplitPlan plan = ja::plan_fwd_fp8(L, device_cu_count());
   if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
     plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
-  return hip_status(ja::launch_fwd_fp8(L, q8, k8, v8, sq, sk, sv, o, lse, plan, workspace,
+  return hip_status(ja::launch_fwd_fp8(L, q8, k8, v8, sq, sk, sv, o, lse, plan, workspace, rp,
                                        static_cast<hipStream_t>(stream)));
 }
 

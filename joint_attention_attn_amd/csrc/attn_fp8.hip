@@ -58,7 +58,19 @@ struct Fp8Args {
   float scale_log2;
   int n_direct, parts;
   SplitWorkspace ws;
+  // repair of the tokens with the largest quantization error (REPAIR
+  // kernels only): kbias [B][H][S] is 0, or -inf for a repaired key; kr / vr
+  // [B][H][n_pad][D] hold the repaired keys' exact rotated K and V (bf16).
+  const float *kbias;
+  const bf16 *kr, *vr;
+  int n_rep, n_pad;
 };
+
+// Position, inside a 16-key group of a bf16 V^T row, of the key that P operand
+// slot p holds (lane half p/8): keys 4*(p/8) + {0..3, 8..11}.
+__host__ __device__ constexpr int vt_key_of_slot(int p) {
+  return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
+}
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // format 0 = fp8 e4m3 for both operands, no block scaling
@@ -90,7 +102,7 @@ struct Fp8Lds {
   static constexpr int VTILE = D * VTSTR;
 };
 
-template <int D>
+template <int D, bool REPAIR>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   constexpr int KSTR = Fp8Lds<D>::KSTR;
   constexpr int KCH = D / 16;                 // 16-byte chunks per K row
@@ -101,6 +113,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t Vt[2][Fp8Lds<D>::VTILE];
   __shared__ __attribute__((aligned(16))) float sk_t[2][BN];
   __shared__ __attribute__((aligned(16))) float wv_t[2][BN];
+  __shared__ __attribute__((aligned(16))) float kb_t[REPAIR ? 2 : 1][REPAIR ? BN : 4];
   __shared__ float red[NW];
 
   const int tid = threadIdx.x;
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const int voff = (int)(4 * vm * row_stride) + 4 * vn;
   u32x4 kreg;
   uint32_t vreg[4];
-  float skreg = 0.f, svreg = 0.f;
+  float skreg = 0.f, svreg = 0.f, kbreg = 0.f;
   auto load = [&](int t, bool with_k, bool with_v) JA_INLINE {
     if (with_k && tid < K_THREADS)
       kreg = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(krs, koff, t * tile_bytes, 0));
@@ -189,6 +202,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       if (tid < BN) {
         const int key = t * BN + tid;
         skreg = key < S ? a.sk[bh * S + key] : 0.f;
+        if constexpr (REPAIR) kbreg = key < S ? a.kbias[bh * S + key] : 0.f;
         svreg = key < S ? a.sv[bh * S + key] : 0.f;
       }
     }
@@ -215,6 +229,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     }
     if (tid < BN) {
       sk_t[buf][tid] = skreg;
+      if constexpr (REPAIR) kb_t[buf][tid] = kbreg;
       wv_t[buf][tid] = svreg * wv_mul;
     }
   };
@@ -284,9 +299,17 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       for (int g = 0; g < 4; ++g) {
         const float4 skg = *reinterpret_cast<const float4 *>(&sk_t[buf][kb * 32 + g * 8 + hf * 4]);
         const float skv[4] = {skg.x, skg.y, skg.z, skg.w};
+        float kbv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (REPAIR) {
+          const float4 kbg = *reinterpret_cast<const float4 *>(&kb_t[buf][kb * 32 + g * 8 + hf * 4]);
+          kbv[0] = kbg.x; kbv[1] = kbg.y; kbv[2] = kbg.z; kbv[3] = kbg.w;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float t = sacc[kb][4 * g + i] * skv[i];
+          // a repaired key's bias is -inf: it leaves the FP8 tile and is
+          // attended from its exact values after the loop
+          float t = REPAIR ? __builtin_fmaf(sacc[kb][4 * g + i], skv[i], kbv[i])
+                           : sacc[kb][4 * g + i] * skv[i];
           if (TAIL && j0 + kb * 32 + g * 8 + hf * 4 + i >= S) t = -INFINITY;
           sacc[kb][4 * g + i] = t;
           tmax = fmaxf(tmax, t);
@@ -340,6 +363,119 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<true>(i);
   iteration.template operator()<false>(nt - 1);
 
+  // ---- repaired keys: one more pass over them with their exact values, on
+  //      bf16 MFMA (an e4m3 code times its scale is exact in this product:
+  //      the codes are bf16-representable and the scale stays in the exp2
+  //      argument), within the same online softmax.  P.V adds P * 64/sv_max
+  //      times the exact V, the units of the FP8 accumulator.  Only one part
+  //      of a split item runs it. ----
+  if constexpr (REPAIR) {
+    if (a.n_rep > 0 && (unit < 0 || unit % a.parts == 0)) {
+      constexpr int KBS = D + 8;          // bf16 per staged K row (16-byte pad)
+      constexpr int VBS = 32 + 8;         // bf16 per staged V^T row
+      bf16 *kbuf = reinterpret_cast<bf16 *>(&Ks[0][0]);
+      bf16 *vbuf = reinterpret_cast<bf16 *>(&Vt[0][0]);
+      // Q codes in the bf16 operand layout: lane half hf holds d = 16kk + 8hf + 0..7
+      bf16x8 qb[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const u32x2 cw = *reinterpret_cast<const u32x2 *>(qrow + 16 * kk + 8 * hf);
+        float f[8];
+        f[0] = __builtin_amdgcn_cvt_f32_fp8((int)cw.x, 0);
+        f[1] = __builtin_amdgcn_cvt_f32_fp8((int)cw.x, 1);
+        f[2] = __builtin_amdgcn_cvt_f32_fp8((int)cw.x, 2);
+        f[3] = __builtin_amdgcn_cvt_f32_fp8((int)cw.x, 3);
+        f[4] = __builtin_amdgcn_cvt_f32_fp8((int)cw.y, 0);
+        f[5] = __builtin_amdgcn_cvt_f32_fp8((int)cw.y, 1);
+        f[6] = __builtin_amdgcn_cvt_f32_fp8((int)cw.y, 2);
+        f[7] = __builtin_amdgcn_cvt_f32_fp8((int)cw.y, 3);
+        u32x4 w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7])};
+        if (qi >= S) w = u32x4{0, 0, 0, 0};
+        qb[kk] = bit_cast<bf16x8>(w);
+      }
+      const float pmul = kPScale / sv_max;
+      const bf16 *krb = a.kr + bh * a.n_pad * D;
+      const bf16 *vrb = a.vr + bh * a.n_pad * D;
+      for (int r0 = 0; r0 < a.n_pad; r0 += 32) {
+        // stage 32 keys: K row-major, V transposed in the P operand's key order
+        if (tid < 32 * (D / 8)) {
+          const int r = tid / (D / 8), c = tid % (D / 8);
+          *reinterpret_cast<u32x4 *>(kbuf + r * KBS + c * 8) =
+              *reinterpret_cast<const u32x4 *>(krb + (int64_t)(r0 + r) * D + c * 8);
+        }
+        if (tid < D * 4) {
+          const int vd = tid % D, vc = tid / D;
+          uint32_t hv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            hv[j] = *reinterpret_cast<const uint16_t *>(
+                vrb + (int64_t)(r0 + 16 * (vc >> 1) + vt_key_of_slot(8 * (vc & 1) + j)) * D + vd);
+          *reinterpret_cast<u32x4 *>(vbuf + vd * VBS + 8 * vc) =
+              u32x4{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                    hv[6] | (hv[7] << 16)};
+        }
+        __syncthreads();
+        f32x16 st;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(kbuf + l32 * KBS + 16 * kk + 8 * hf);
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[kk], st, 0, 0, 0);
+        }
+        // accumulator row i is key r0 + 8(i/4) + 4hf + i%4; rows past n are padding
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (r0 + 8 * (i / 4) + 4 * hf + (i % 4) >= a.n_rep) st[i] = -INFINITY;
+          tmax = fmaxf(tmax, st[i]);
+        }
+        const float mx = half_max(tmax) * qmul;
+        const bool grow = mx > m_run + kRescaleLog2;
+        auto exp_rep = [&](float mref, bf16x8 (&pbr)[2]) JA_INLINE -> float {
+          float ps = 0.f;
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * g + 2 * e], qmul, -mref));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * g + 2 * e + 1], qmul, -mref));
+              ps += p0 + p1;
+              w[e] = pack_bf16x2(p0 * pmul, p1 * pmul);
+            }
+            pbr[g] = bit_cast<bf16x8>(u32x4{w[0], w[1], w[2], w[3]});
+          }
+          return ps;
+        };
+        bf16x8 pbr[2];
+        float ps = exp_rep(m_run, pbr);
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = grow ? mx : m_run;
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+          ps = exp_rep(m_new, pbr);
+        }
+        l_run += ps;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const bf16x8 va =
+                *reinterpret_cast<const bf16x8 *>(vbuf + (32 * db + l32) * VBS + 16 * g + 8 * hf);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[g], oacc[db], 0, 0, 0);
+          }
+        __syncthreads();
+      }
+    }
+  }
+
   const float l_tot = half_sum(l_run);
   const float o_mul = sv_max / kPScale;
   if (unit >= 0) {
@@ -387,7 +523,7 @@ SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu) {
 hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
                           const void *v8, const float *sq, const float *sk,
                           const float *sv, void *o, float *lse, const SplitPlan &plan,
-                          void *workspace, hipStream_t st) {
+                          void *workspace, const Fp8Repair &repair, hipStream_t st) {
   Fp8Args a;
   a.q = static_cast<const uint8_t *>(q8);
   a.k = static_cast<const uint8_t *>(k8);
@@ -407,10 +543,19 @@ hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
   a.parts = plan.parts;
   a.ws = split_workspace(plan, workspace, BM, L.D);
   const dim3 grid((unsigned)(plan.n_direct + plan.n_units));
-  if (L.D == 64)
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<64>, grid, dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_fp8_kernel<128>, grid, dim3(NT), 0, st, a);
+  const bool rep = repair.n_rep > 0;
+  a.kbias = repair.kbias;
+  a.kr = static_cast<const bf16 *>(repair.kr);
+  a.vr = static_cast<const bf16 *>(repair.vr);
+  a.n_rep = repair.n_rep;
+  a.n_pad = repair_pad(repair.n_rep);
+  if (L.D == 64) {
+    auto kern = rep ? attn_fwd_fp8_kernel<64, true> : attn_fwd_fp8_kernel<64, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(NT), 0, st, a);
+  } else {
+    auto kern = rep ? attn_fwd_fp8_kernel<128, true> : attn_fwd_fp8_kernel<128, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(NT), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.n_units == 0) return e;
   return launch_merge_split(L, plan, a.ws, BM, 1.f, o, lse, st);

@@ -54,11 +54,24 @@ hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
                                  void *v8, float *sq, float *sk, float *sv,
                                  hipStream_t st);
 
+// Repair set of the FP8 forward (see repair_fp8.hip); n_rep = 0: none.
+struct Fp8Repair {
+  int n_rep = 0;
+  const float *kbias = nullptr;
+  const void *kr = nullptr, *vr = nullptr;
+};
+int repair_pad(int n);          // repaired keys rounded up to whole 32-key tiles
+int repair_max_seq();           // longest sequence the selection handles
+hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
+                              const float *rope, const void *k8, const void *v8,
+                              const float *sk, const float *sv, int n, int32_t *idx,
+                              void *kr, void *vr, float *kbias, hipStream_t st);
+
 SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu);
 hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
                           const void *v8, const float *sq, const float *sk,
                           const float *sv, void *o, float *lse, const SplitPlan &plan,
-                          void *workspace, hipStream_t st);
+                          void *workspace, const Fp8Repair &repair, hipStream_t st);
 
 // Query rows per workgroup of each forward kernel (the grid's x extent is
 // ceil(S / rows)).

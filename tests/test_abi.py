@@ -113,12 +113,33 @@ def test_quant_and_fp8_validation(lib):
                                          *ptrs[6:9], None) == ja.JA_ERR_UNSUPPORTED
     assert lib.joint_attn_quant_rope_fp8(ctypes.byref(p), vp(0), *ptrs[1:3], None, *ptrs[3:6],
                                          *ptrs[6:9], None) == ja.JA_ERR_INVALID_ARG
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(bad), *ptrs[:3], *ptrs[3:6], ptrs[6], None,
-                                  None, 0, None) == ja.JA_ERR_UNSUPPORTED
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], vp(FAKE + 4), *ptrs[4:6],
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(bad), *ptrs[:3], *ptrs[3:6], None, ptrs[6],
+                                  None, None, 0, None) == ja.JA_ERR_UNSUPPORTED
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], vp(FAKE + 4), *ptrs[4:6], None,
                                   ptrs[6], None, None, 0, None) == ja.JA_ERR_INVALID_ARG
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], vp(0), None,
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], None, vp(0), None,
                                   None, 0, None) == ja.JA_ERR_INVALID_ARG
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], ptrs[6], None,
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], None, ptrs[6], None,
                                   vp(FAKE + 0x9008), 64, None) == ja.JA_ERR_INVALID_ARG
+    rep_bad = ja.Fp8RepairC(5, None, FAKE, FAKE)           # kbias missing
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], ctypes.byref(rep_bad),
+                                  ptrs[6], None, None, 0, None) == ja.JA_ERR_INVALID_ARG
+    rep_big = ja.Fp8RepairC(81, FAKE, FAKE, FAKE)          # more than seq_len = 80
+    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], ctypes.byref(rep_big),
+                                  ptrs[6], None, None, 0, None) == ja.JA_ERR_INVALID_ARG
+
+
+def test_repair_plan_validation(lib):
+    vp = ctypes.c_void_p
+    p = _p()
+    ptrs = [vp(FAKE + 0x1000 * i) for i in range(12)]
+    f = lib.joint_attn_fp8_repair_plan
+    assert f(ctypes.byref(p), *ptrs[:2], None, *ptrs[2:6], 81, *ptrs[6:10], None) == ja.JA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), *ptrs[:2], None, *ptrs[2:6], -1, *ptrs[6:10], None) == ja.JA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), *ptrs[:2], None, *ptrs[2:6], 4, None, *ptrs[7:10], None) == ja.JA_ERR_INVALID_ARG
+    long = _p(s=40000)
+    assert f(ctypes.byref(long), *ptrs[:2], None, *ptrs[2:6], 4, *ptrs[6:10], None) == ja.JA_ERR_UNSUPPORTED
+    bad = _p()
+    bad.head_dim = 96
+    assert f(ctypes.byref(bad), *ptrs[:2], None, *ptrs[2:6], 4, *ptrs[6:10], None) == ja.JA_ERR_UNSUPPORTED
     assert lib.joint_attn_fwd_fp8_workspace_bytes(ctypes.byref(bad)) == 0

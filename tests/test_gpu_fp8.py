@@ -113,3 +113,114 @@ def test_fp8_2048_sampled():
     err = rel_l2(out, ref)
     _say(f"  rel_l2={err:.3e}")
     assert err <= FP8_REL_L2
+
+
+# ---- repair of the tokens with the largest quantization error ----
+
+def _repair_gpu(q, k, v, pos, n_rep):
+    d = q.shape[-1]
+    rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), d) if pos is not None else None
+    kd, vd = k.to(DEV), v.to(DEV)
+    q8, k8, v8, sq, sk, sv = ja.quant_rope_fp8(q.to(DEV), kd, vd, rope)
+    rep = ja.fp8_repair_plan(kd, vd, rope, k8, v8, sk, sv, n_rep)
+    torch.cuda.synchronize()
+    return (q8, k8, v8, sq, sk, sv), rep
+
+
+@pytest.mark.parametrize("w,budget", [
+    (synth.WORKLOADS["tiny"].replace(outlier_frac=0.05), 0.05),
+    (synth.Workload("ragged", 2, 3, 64, n_text=7, grid=9, outlier_frac=0.03), 0.1),
+    (synth.WORKLOADS["t2i_1024"].replace(heads=4), 0.005),
+    (synth.WORKLOADS["t2i_1024"].replace(heads=2), 0.05),
+], ids=lambda x: getattr(x, "name", str(x)))
+def test_repair_plan_bit_exact(w, budget):
+    # selection, mask and gathered keys/values equal the oracle's exactly
+    q, k, v, _ = synth.make_qkv(w, 1)
+    pos = synth.positions(w)
+    n = oracle.repair_count(budget, w.seq_len)
+    _say(f"repair plan {w.name} S={w.seq_len} H={w.heads} n={n}")
+    codes, rep = _repair_gpu(q, k, v, pos, n)
+    ref_codes = oracle.quant_rope_fp8(q, k, v, pos)
+    err = oracle.repair_errors(k, v, pos, ref_codes[1], ref_codes[2], ref_codes[4], ref_codes[5])
+    idx = oracle.repair_select(err, n)
+    assert np.array_equal(rep.idx.cpu().numpy(), idx)
+    kr, vr = oracle.repair_values(k, v, pos, idx)
+    n_pad = rep.kr.shape[2]
+    assert torch.equal(rep.kr.cpu()[:, :, :n].double(), kr)
+    assert torch.equal(rep.vr.cpu()[:, :, :n].double(), vr)
+    assert not rep.kr.cpu()[:, :, n:n_pad].any() and not rep.vr.cpu()[:, :, n:n_pad].any()
+    mask = np.zeros(err.shape, bool)
+    for b in range(idx.shape[0]):
+        for h in range(idx.shape[1]):
+            mask[b, h, idx[b, h]] = True
+    kb = rep.kbias.cpu().numpy()
+    assert np.all(kb[mask] == -np.inf) and np.all(kb[~mask] == 0)
+
+
+@pytest.mark.parametrize("s,d,budget", [(80, 64, 0.05), (129, 128, 0.02), (700, 64, 0.05),
+                                        (1037, 128, 0.005)])
+def test_repaired_forward_ragged(s, d, budget):
+    w = synth.Workload("ragged", 1, 2, d, n_text=s, grid=0, outlier_frac=0.02)
+    q, k, v, _ = synth.make_qkv(w, seed=s + 1)
+    rng = np.random.default_rng(s)
+    pos = rng.integers(0, 200, size=(s, 2)).astype(np.int32)
+    n = oracle.repair_count(budget, s)
+    _say(f"repaired fp8 fwd S={s} D={d} n={n}")
+    codes, rep = _repair_gpu(q, k, v, pos, n)
+    out = ja.fwd_fp8(*codes, repair=rep)
+    torch.cuda.synchronize()
+    ref_codes = oracle.quant_rope_fp8(q, k, v, pos)
+    idx = rep.idx.cpu().numpy()
+    kr, vr = oracle.repair_values(k, v, pos, idx)
+    ref, _ = oracle.fp8_repaired_attention(*ref_codes, idx, kr, vr)
+    assert not torch.isnan(out).any()
+    err = rel_l2(out, ref)
+    _say(f"  rel_l2={err:.3e}")
+    assert err <= FP8_REL_L2
+
+
+def test_repaired_forward_1024_closer_to_bf16_path():
+    # full t2i_1024 shape with the pages' budget 0.005: parity with the
+    # repaired oracle, and a result closer to the bf16-path attention than
+    # the unrepaired FP8 forward (on sampled rows).
+    w = synth.WORKLOADS["t2i_1024"]
+    q, k, v, oidx = synth.make_qkv(w, 0)
+    pos = synth.positions(w)
+    n = oracle.repair_count(0.005, w.seq_len)
+    _say(f"repaired fp8 t2i_1024 n={n}")
+    codes, rep = _repair_gpu(q, k, v, pos, n)
+    out_r, lse_r = ja.fwd_fp8(*codes, repair=rep, return_lse=True)
+    out_0 = ja.fwd_fp8(*codes)
+    torch.cuda.synchronize()
+    ref_codes = oracle.quant_rope_fp8(q, k, v, pos)
+    idx = rep.idx.cpu().numpy()
+    kr, vr = oracle.repair_values(k, v, pos, idx)
+    rows = sample_rows(w.seq_len, w.n_text, oidx, 192, seed=3)
+    ref_r, ref_lse = oracle.fp8_repaired_attention(*ref_codes, idx, kr, vr, rows=rows)
+    exact, _ = oracle.joint_attention(q, k, v, pos, rows=rows)
+    got_r, got_0 = out_r.cpu()[:, rows], out_0.cpu()[:, rows]
+    e_par = rel_l2(got_r, ref_r)
+    e_rep, e_fp8 = rel_l2(got_r, exact), rel_l2(got_0, exact)
+    _say(f"  parity rel_l2={e_par:.3e}; vs bf16 path: repaired {e_rep:.3e}, fp8 {e_fp8:.3e}")
+    assert e_par <= FP8_REL_L2
+    assert float((lse_r.cpu()[:, :, rows].double() - ref_lse).abs().max()) <= 5e-2
+    assert e_rep < e_fp8
+
+
+def test_repaired_forward_split_matches_unsplit():
+    base = synth.WORKLOADS["t2i_1024"]
+    w = None
+    for heads in range(8, 65):
+        w = base.replace(heads=heads)
+        p = ja.Params(w.batch, w.seq_len, heads, 128)
+        p.o_sb, p.o_ss, p.o_sh = w.seq_len * heads * 128, heads * 128, 128
+        if ja.load().joint_attn_fwd_fp8_workspace_bytes(ja.ctypes.byref(p)):
+            break
+    q, k, v, _ = synth.make_qkv(w, 6)
+    pos = synth.positions(w)
+    n = oracle.repair_count(0.005, w.seq_len)
+    _say(f"repaired fp8 split H={w.heads} n={n}")
+    codes, rep = _repair_gpu(q, k, v, pos, n)
+    a = ja.fwd_fp8(*codes, repair=rep).cpu()
+    b = ja.fwd_fp8(*codes, repair=rep, split=False).cpu()
+    assert rel_l2(a, b) <= 5e-3
