@@ -11,7 +11,9 @@ Also reported on the same JSON line:
   roofline      the forward kernel's own average duration (HIP events on the
                 launch stream) against the bf16 dense MFMA peak;
   fp8           the FP8 path (RoPE+quantize pass, FP8 forward) timed the same
-                way, against the fp8 MFMA peak and HBM bandwidth;
+                way, against the fp8 MFMA peak and HBM bandwidth, and with the
+                repair of the tokens with the largest quantization error
+                (budget 0.005);
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
                 sample of query rows (scaled to TFLOP/s), plus the parity of
                 the GPU output on those rows.
@@ -35,6 +37,7 @@ METRIC = "joint-attention fwd TFLOP/s and % of MFMA peak at 2048x2048 (16896 tok
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+REPAIR_BUDGET = 0.005        # the pages' vc_repair_budget
 CSRC = os.path.join(ROOT, "joint_attention_attn_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -170,6 +173,7 @@ def main() -> int:
          f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
 
     fp8 = None
+    fp8_outs = None
     if not args.no_fp8:
         q8, k8, v8, sq, sk, sv = ja.quant_rope_fp8(qd, kd, vd, rope)
         out8 = torch.empty_like(out)
@@ -196,10 +200,27 @@ def main() -> int:
                "path_tflops": round(flops / ((f_avg + q_avg) * 1e-3) / 1e12, 2)}
         _log(f"[bench] fp8: fwd {f_avg:.3f} ms ({f_tf:.1f} TFLOP/s), quant {q_avg:.3f} ms "
              f"({fp8['quant_gbs']} GB/s)")
+        # repair of the tokens with the largest quantization error, at the
+        # pages' budget 0.005
+        n_rep = ja.repair_count(REPAIR_BUDGET, S)
+        rp = ja.fp8_repair_plan(kd, vd, rope, k8, v8, sk, sv, n_rep)
+        out8r = torch.empty_like(out)
+        for _ in range(2):
+            ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8r, repair=rp)
+        torch.cuda.synchronize()
+        pms = _time_launches(lambda: ja.fp8_repair_plan(kd, vd, rope, k8, v8, sk, sv, n_rep), n)
+        rms = _time_launches(lambda: ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8r, repair=rp), n)
+        p_avg, r_avg = sum(pms) / n, sum(rms) / n
+        fp8["repair"] = {"budget": REPAIR_BUDGET, "tokens_per_head": n_rep,
+                         "plan_ms": round(p_avg, 4), "fwd_ms": round(r_avg, 4),
+                         "fwd_tflops": round(flops / (r_avg * 1e-3) / 1e12, 2),
+                         "path_tflops": round(flops / ((q_avg + p_avg + r_avg) * 1e-3) / 1e12, 2)}
+        _log(f"[bench] fp8 + repair ({n_rep} tokens/head): plan {p_avg:.3f} ms, fwd {r_avg:.3f} ms")
+        fp8_outs = (out8, out8r)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = _cpu_baseline(w, q, k, v, pos, outl, out, args.cpu_seconds)
+        cpu = _cpu_baseline(w, q, k, v, pos, outl, out, args.cpu_seconds, fp8_outs)
 
     rec = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -217,9 +238,11 @@ def main() -> int:
     return 0
 
 
-def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s):
+def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s, fp8_outs=None):
     """The fp64 oracle on this host's cores over a bounded sample of query
-    rows (all keys, all heads), scaled to TFLOP/s; plus parity on those rows."""
+    rows (all keys, all heads), scaled to TFLOP/s; plus parity on those rows
+    (and, on the same rows, the distance of the FP8 and repaired FP8 outputs
+    from the oracle)."""
     import numpy as np
     import torch
     import oracle
@@ -230,6 +253,8 @@ def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s):
     order = rng.permutation(S)
     done_rows, spent, chunk = [], 0.0, 64
     got_all = out_gpu.cpu()
+    f8_all = [t.cpu() for t in fp8_outs] if fp8_outs else []
+    f8_num = [0.0] * len(f8_all)
     errs_num, errs_den = 0.0, 0.0
     while spent < target_s and len(done_rows) < S:
         rows = np.sort(order[len(done_rows):len(done_rows) + chunk])
@@ -239,6 +264,8 @@ def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s):
         got = got_all[:, rows].double()
         errs_num += float(((got - ref) ** 2).sum())
         errs_den += float((ref ** 2).sum())
+        for i, t in enumerate(f8_all):
+            f8_num[i] += float(((t[:, rows].double() - ref) ** 2).sum())
         done_rows.extend(rows.tolist())
         chunk = min(chunk * 2, 1024)
     n = len(done_rows)
@@ -250,7 +277,10 @@ def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s):
             "sample": f"{n} random query rows x {B * H} (batch, head) pairs x all {S} keys "
                       f"({sample_flops / 1e9:.1f} GFLOP) of {w.name}, fp64 torch-CPU",
             "seconds": round(spent, 2),
-            "gpu_rel_l2_on_sample": round(math.sqrt(errs_num / errs_den), 6)}
+            "gpu_rel_l2_on_sample": round(math.sqrt(errs_num / errs_den), 6),
+            **({"fp8_rel_l2_on_sample": round(math.sqrt(f8_num[0] / errs_den), 6),
+                "fp8_repair_rel_l2_on_sample": round(math.sqrt(f8_num[1] / errs_den), 6)}
+               if f8_all else {})}
 
 
 if __name__ == "__main__":
