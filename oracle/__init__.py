@@ -17,7 +17,9 @@ FLUX 3 Image Klein on NVIDIA Blackwell GPUs"):
   consumes rotated Q and K stored in bf16;
 * FP8 Q/K and V (section "Quantized and sparse attention", qk_dtype and
   v_dtype fp8), and the repair of the tokens with the largest quantization
-  error (same section, VC-Attention FP8 with vc_repair_budget).
+  error (same section, VC-Attention FP8 with vc_repair_budget);
+* block-sparse attention on a given block mask (same section: Sol-Attention
+  runs on a general block-sparse attention kernel).
 
 The pages state none of the arithmetic; the readings taken where they are
 silent (2D-axial frequencies, pair convention, bf16 rounding point of the
@@ -30,14 +32,16 @@ here is pinned by tests in `tests/test_oracle_*.py` against closed forms,
 brute force, exact rational arithmetic and library routines.
 """
 from .rope import rope_angles, apply_rope, rope_table_fp32, rotate_fp32, fma32
-from .attention import attention, joint_attention, brute_force_attention
+from .attention import (attention, joint_attention, brute_force_attention,
+                        block_sparse_attention, QUERY_BLOCK, KEY_BLOCK)
 from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, quant_rope_fp8,
                   dequantize, fp8_attention, repair_count, quant_error, repair_errors,
                   repair_select, repair_values, fp8_repaired_attention)
 
 __all__ = [
     "rope_angles", "apply_rope", "rope_table_fp32", "rotate_fp32", "fma32",
-    "attention", "joint_attention", "brute_force_attention",
+    "attention", "joint_attention", "brute_force_attention", "block_sparse_attention",
+    "QUERY_BLOCK", "KEY_BLOCK",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "quant_rope_fp8",
     "dequantize", "fp8_attention", "repair_count", "quant_error", "repair_errors",
     "repair_select", "repair_values", "fp8_repaired_attention",

@@ -92,12 +92,14 @@ def brute_force_attention(q, k, v, scale: float | None = None):
     """Pure-Python triple loop over (b, h, i); for tiny shapes only.
 
     Uses math.fsum so the reductions are exactly rounded; it is the
-    independent check of the vectorised `attention`.
+    independent check of the vectorised `attention`.  The key count may differ
+    from the query count.
     """
     q = torch.as_tensor(q).to(torch.float64).tolist()
     k = torch.as_tensor(k).to(torch.float64).tolist()
     v = torch.as_tensor(v).to(torch.float64).tolist()
     b_n, s_n, h_n, d_n = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    sk_n = len(k[0])
     if scale is None:
         scale = 1.0 / math.sqrt(d_n)
     o = [[[[0.0] * d_n for _ in range(h_n)] for _ in range(s_n)] for _ in range(b_n)]
@@ -106,11 +108,68 @@ def brute_force_attention(q, k, v, scale: float | None = None):
         for h in range(h_n):
             for i in range(s_n):
                 sc = [math.fsum(q[b][i][h][t] * k[b][j][h][t] for t in range(d_n)) * scale
-                      for j in range(s_n)]
+                      for j in range(sk_n)]
                 m = max(sc)
                 e = [math.exp(x - m) for x in sc]
                 z = math.fsum(e)
                 for t in range(d_n):
-                    o[b][i][h][t] = math.fsum(e[j] * v[b][j][h][t] for j in range(s_n)) / z
+                    o[b][i][h][t] = math.fsum(e[j] * v[b][j][h][t] for j in range(sk_n)) / z
                 lse[b][h][i] = m + math.log(z)
     return torch.tensor(o, dtype=torch.float64), torch.tensor(lse, dtype=torch.float64)
+
+
+# Block granularity of the block-sparse variant (queries x keys).
+QUERY_BLOCK = 128
+KEY_BLOCK = 64
+
+
+def block_sparse_attention(q, k, v, mask, pos=None, theta: float = 10000.0,
+                           scale: float | None = None, rows=None,
+                           q_block: int = QUERY_BLOCK, k_block: int = KEY_BLOCK):
+    """Joint attention restricted by a block mask (the kernel half of the
+    pages' block-sparse attention, section "Quantized and sparse attention":
+    Sol-Attention runs on a general block-sparse attention kernel; how its
+    blocks are chosen is not on the pages, so the mask is an input here).
+
+    mask: [B, H, ceil(S / q_block), ceil(S / k_block)], nonzero = computed.
+    Query i attends key j iff mask[b, h, i // q_block, j // k_block] != 0;
+    the softmax runs over the attended keys only.  A query row with no
+    attended key gets O = 0 and LSE = -inf.  RoPE and the bf16 rounding of the
+    rotated Q/K are those of `joint_attention`; attention itself is fp64.
+    Returns (O [B, R, H, D] fp64, LSE [B, H, R] fp64).
+    """
+    q = torch.as_tensor(q)
+    k = torch.as_tensor(k)
+    if pos is not None:
+        table = rope_table_fp32(pos, q.shape[-1], theta)
+        q = torch.from_numpy(rotate_fp32(q.to(torch.float32).numpy(), table)).to(torch.bfloat16)
+        k = torch.from_numpy(rotate_fp32(k.to(torch.float32).numpy(), table)).to(torch.bfloat16)
+    q = q.to(torch.float64)
+    k = k.to(torch.float64)
+    v = torch.as_tensor(v).to(torch.float64)
+    mask = torch.as_tensor(np.asarray(mask)) != 0
+    b, s, h, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(s) if rows is None else np.asarray(rows)
+    key_blk = torch.arange(s) // k_block
+    o = torch.zeros((b, len(rows), h, d), dtype=torch.float64)
+    lse = torch.full((b, h, len(rows)), -math.inf, dtype=torch.float64)
+    for bi in range(b):
+        for hi in range(h):
+            kt = k[bi, :, hi, :].T.contiguous()
+            vb = v[bi, :, hi, :].contiguous()
+            for c0 in range(0, len(rows), _CHUNK):
+                r = torch.as_tensor(rows[c0:c0 + _CHUNK], dtype=torch.int64)
+                allowed = mask[bi, hi][(r // q_block)[:, None], key_blk[None, :]]   # [c, S]
+                sc = (q[bi, r, hi, :] @ kt) * scale
+                sc = torch.where(allowed, sc, torch.tensor(-math.inf, dtype=torch.float64))
+                m = sc.max(dim=1, keepdim=True).values
+                live = torch.isfinite(m[:, 0])
+                p = torch.where(allowed, torch.exp(sc - torch.where(torch.isfinite(m), m, 0.0)), 0.0)
+                l = p.sum(dim=1, keepdim=True)
+                oc = (p @ vb) / torch.where(l > 0, l, 1.0)
+                o[bi, c0:c0 + len(r), hi, :] = torch.where(live[:, None], oc, 0.0)
+                lse[bi, hi, c0:c0 + len(r)] = torch.where(live, (m + torch.log(l))[:, 0],
+                                                          torch.tensor(-math.inf, dtype=torch.float64))
+    return o, lse

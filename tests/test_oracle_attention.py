@@ -146,3 +146,59 @@ def test_rotated_inputs_are_rounded_to_bf16():
     # bf16 rounding of the rotated operands moves the result, but only at the
     # level of bf16's relative precision (2^-8) times the output scale.
     assert 0 < diff < 5e-2
+
+
+# ---- block-sparse variant ----
+
+def _sparse_case(seed=0, s=300, h=2, d=64):
+    w = synth.Workload("sparse", 1, h, d, n_text=s, grid=0, outlier_frac=0.02)
+    q, k, v, _ = synth.make_qkv(w, seed)
+    rng = np.random.default_rng(seed)
+    pos = rng.integers(0, 50, size=(s, 2)).astype(np.int32)
+    nq = -(-s // oracle.QUERY_BLOCK)
+    nk = -(-s // oracle.KEY_BLOCK)
+    return q, k, v, pos, nq, nk
+
+
+def test_block_sparse_all_ones_is_dense():
+    q, k, v, pos, nq, nk = _sparse_case()
+    mask = np.ones((1, 2, nq, nk), np.uint8)
+    o, l = oracle.block_sparse_attention(q, k, v, mask, pos)
+    od, ld = oracle.joint_attention(q, k, v, pos)
+    assert torch.allclose(o, od, rtol=0, atol=1e-12) and torch.allclose(l, ld, rtol=0, atol=1e-12)
+
+
+def test_block_sparse_equals_attention_on_the_kept_keys():
+    # every query block keeps its own set of key blocks: the result for its
+    # rows is dense attention over exactly those keys (sliced out)
+    q, k, v, pos, nq, nk = _sparse_case(seed=3)
+    rng = np.random.default_rng(5)
+    mask = (rng.random((1, 2, nq, nk)) < 0.4).astype(np.uint8)
+    mask[..., 0] = 1                                  # no empty row
+    o, l = oracle.block_sparse_attention(q, k, v, mask, pos)
+    s = q.shape[1]
+    table = oracle.rope_table_fp32(pos, q.shape[-1])
+    qr = torch.from_numpy(oracle.rotate_fp32(q.float().numpy(), table)).to(torch.bfloat16)
+    kr = torch.from_numpy(oracle.rotate_fp32(k.float().numpy(), table)).to(torch.bfloat16)
+    for h in range(2):
+        for qb in range(nq):
+            r0, r1 = qb * oracle.QUERY_BLOCK, min(s, (qb + 1) * oracle.QUERY_BLOCK)
+            keys = np.concatenate([np.arange(kb * oracle.KEY_BLOCK, min(s, (kb + 1) * oracle.KEY_BLOCK))
+                                   for kb in range(nk) if mask[0, h, qb, kb]])
+            sel = torch.as_tensor(keys, dtype=torch.int64)
+            od, ld = oracle.attention(qr[:, r0:r1, h:h + 1], kr[:, sel, h:h + 1], v[:, sel, h:h + 1])
+            assert torch.allclose(o[:, r0:r1, h:h + 1], od, rtol=0, atol=1e-12)
+            assert torch.allclose(l[:, h:h + 1, r0:r1], ld, rtol=0, atol=1e-12)
+
+
+def test_block_sparse_empty_row_and_brute_force():
+    w = synth.Workload("sparse_tiny", 1, 1, 16, n_text=200, grid=0)
+    q, k, v, _ = synth.make_qkv(w, 9)
+    mask = np.array([[[[1, 0, 1, 0], [0, 0, 0, 0]]]], np.uint8)   # 2 x 4 blocks of 128 x 64
+    o, l = oracle.block_sparse_attention(q, k, v, mask)
+    assert torch.equal(o[:, 128:], torch.zeros_like(o[:, 128:]))
+    assert torch.isinf(l[:, :, 128:]).all() and (l[:, :, 128:] < 0).all()
+    keys = torch.as_tensor(np.r_[0:64, 128:192], dtype=torch.int64)
+    ob, lb = oracle.brute_force_attention(q[:, :128:9], k[:, keys], v[:, keys])
+    assert torch.allclose(o[:, :128:9], ob, rtol=0, atol=1e-12)
+    assert torch.allclose(l[:, :, :128:9], lb, rtol=0, atol=1e-12)
