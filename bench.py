@@ -14,6 +14,9 @@ Also reported on the same JSON line:
                 way, against the fp8 MFMA peak and HBM bandwidth, and with the
                 repair of the tokens with the largest quantization error
                 (budget 0.005);
+  sparse        the block-sparse forward on a seeded mask over 128-query x
+                64-key blocks at the block density of the sparse steps
+                (half the blocks kept), against the flops of the kept blocks;
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
                 sample of query rows (scaled to TFLOP/s), plus the parity of
                 the GPU output on those rows.
@@ -55,6 +58,7 @@ def _parse():
     ap.add_argument("--config", default="t2i_2048")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-sparse", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
@@ -218,6 +222,10 @@ def main() -> int:
         _log(f"[bench] fp8 + repair ({n_rep} tokens/head): plan {p_avg:.3f} ms, fwd {r_avg:.3f} ms")
         fp8_outs = (out8, out8r)
 
+    sparse = None
+    if not args.no_sparse:
+        sparse = _sparse_leg(ja, w, qd, kd, vd, rope, out, k_avg, max(args.steps, 5), args.seed)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = _cpu_baseline(w, q, k, v, pos, outl, out, args.cpu_seconds, fp8_outs)
@@ -233,9 +241,45 @@ def main() -> int:
                                   f"{100 * w.outlier_frac:g}% x{w.outlier_scale:g} outlier tokens",
                       "batch": B, "seq_len": S, "heads": H, "head_dim": D,
                       "flops_per_step": flops},
-           "roofline": roofline, "cpu_baseline": cpu, "fp8": fp8}
+           "roofline": roofline, "cpu_baseline": cpu, "fp8": fp8, "sparse": sparse}
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def _sparse_leg(ja, w, qd, kd, vd, rope, out, dense_ms, n, seed):
+    """Block-sparse forward on the seeded mask of the workload: its kernel
+    time, the flops of the kept blocks per second, and the blocks staged
+    (kept by any of the three query blocks one workgroup covers)."""
+    import numpy as np
+    import torch
+    import synth
+    B, S, H, D = w.shape
+    mask = synth.make_block_mask(w, synth.SPARSE_DENSITY, seed)
+    m = mask.numpy().astype(bool)
+    qb, kb = ja.SPARSE_QUERY_BLOCK, ja.SPARSE_KEY_BLOCK
+    qrows = np.minimum(S - qb * np.arange(m.shape[2]), qb)
+    kcols = np.minimum(S - kb * np.arange(m.shape[3]), kb)
+    pairs = float((m * qrows[:, None] * kcols[None, :]).sum())
+    kept_flops = 4.0 * D * pairs
+    nq3 = -(-m.shape[2] // 3)
+    m3 = np.zeros((B, H, nq3 * 3, m.shape[3]), bool)
+    m3[:, :, :m.shape[2]] = m
+    staged = m3.reshape(B, H, nq3, 3, m.shape[3]).any(axis=3).mean()
+    mask_d = mask.to(qd.device)
+    outs = torch.empty_like(out)
+    for _ in range(3):
+        ja.fwd_bf16_block_sparse(qd, kd, vd, mask_d, rope, out=outs)
+    torch.cuda.synchronize()
+    ms = _time_launches(lambda: ja.fwd_bf16_block_sparse(qd, kd, vd, mask_d, rope, out=outs), n)
+    avg = sum(ms) / n
+    tf = kept_flops / (avg * 1e-3) / 1e12
+    _log(f"[bench] sparse (density {synth.SPARSE_DENSITY}): {avg:.3f} ms, {tf:.1f} TFLOP/s of "
+         f"kept blocks, {dense_ms / avg:.2f}x the dense kernel")
+    return {"mask": f"seeded iid blocks of {qb}x{kb}, kept with p={synth.SPARSE_DENSITY}",
+            "kept_frac": round(float(m.mean()), 4), "staged_frac": round(float(staged), 4),
+            "kept_flops": kept_flops, "fwd_ms": round(avg, 4), "fwd_tflops": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "speedup_vs_dense_kernel": round(dense_ms / avg, 3)}
 
 
 def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s, fp8_outs=None):

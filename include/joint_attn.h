@@ -124,6 +124,36 @@ ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
  */
 size_t joint_attn_fwd_bf16_workspace_bytes(const ja_params *p);
 
+/* Block granularity of joint_attn_fwd_bf16_block_sparse's mask. */
+#define JA_SPARSE_QUERY_BLOCK 128
+#define JA_SPARSE_KEY_BLOCK 64
+
+/*
+ * joint_attn_fwd_bf16_block_sparse - joint_attn_fwd_bf16 restricted to the
+ * blocks of a given block mask: the kernel half of the pages' block-sparse
+ * attention (section "Quantized and sparse attention": Sol-Attention runs on
+ * a general block-sparse attention kernel; how it chooses the blocks is not
+ * on the pages, so the mask is an input).
+ *   block_mask  device uint8 [batch][heads][nqb][nkb], contiguous, with
+ *               nqb = ceil(seq_len / JA_SPARSE_QUERY_BLOCK) and
+ *               nkb = ceil(seq_len / JA_SPARSE_KEY_BLOCK); nonzero = keep.
+ *               Query i attends key j iff
+ *               block_mask[b][h][i / JA_SPARSE_QUERY_BLOCK][j / JA_SPARSE_KEY_BLOCK]
+ *               is nonzero, and its softmax runs over those keys only.  A
+ *               query row that keeps no key gets O = 0 and LSE = -inf.
+ *   Every other argument, the arithmetic and the workspace (same size,
+ *   joint_attn_fwd_bf16_workspace_bytes) are those of joint_attn_fwd_bf16;
+ *   an all-nonzero mask gives the same result as joint_attn_fwd_bf16.
+ *   seq_len up to 1048576 (JA_ERR_UNSUPPORTED above).  Work and time scale
+ *   with the key blocks kept by any of the three consecutive query blocks
+ *   that one workgroup covers.
+ */
+ja_status joint_attn_fwd_bf16_block_sparse(const ja_params *p, const void *q, const void *k,
+                                           const void *v, const float *rope,
+                                           const uint8_t *block_mask, void *o, float *lse,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream);
+
 /*
  * joint_attn_quant_rope_fp8 - RoPE on Q and K, then per-token FP8
  * quantization of Q, K and V (the pages' fp8 qk_dtype / v_dtype).

@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "JointAttnError", "library_path", "load", "rope_table_2d", "fwd_bf16",
     "fwd_bf16_workspace_bytes", "Fp8Repair", "fp8_repair_plan", "repair_count",
-    "quant_rope_fp8", "fwd_fp8", "Params",
+    "quant_rope_fp8", "fwd_fp8", "Params", "fwd_bf16_block_sparse",
+    "SPARSE_QUERY_BLOCK", "SPARSE_KEY_BLOCK", "block_mask_shape",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,6 +25,8 @@ _LIB_PATH = os.path.join(_HERE, "libjoint_attn.so")
 _LIB = None
 
 JA_OK, JA_ERR_INVALID_ARG, JA_ERR_UNSUPPORTED, JA_ERR_HIP = 0, 1, 2, 3
+# block granularity of the block-sparse forward's mask (queries x keys)
+SPARSE_QUERY_BLOCK, SPARSE_KEY_BLOCK = 128, 64
 
 
 class JointAttnError(RuntimeError):
@@ -68,6 +71,8 @@ def load() -> ctypes.CDLL:
     pp = ctypes.POINTER(Params)
     lib.joint_attn_rope_table_2d.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp]
     lib.joint_attn_fwd_bf16.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.joint_attn_fwd_bf16_block_sparse.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                     ctypes.c_size_t, vp]
     lib.joint_attn_fwd_bf16_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_bf16_workspace_bytes.restype = ctypes.c_size_t
     lib.joint_attn_quant_rope_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -78,7 +83,7 @@ def load() -> ctypes.CDLL:
     lib.joint_attn_fp8_repair_plan.restype = st
     lib.joint_attn_fwd_fp8_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
-    for fn in ("joint_attn_rope_table_2d", "joint_attn_fwd_bf16",
+    for fn in ("joint_attn_rope_table_2d", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_block_sparse",
                "joint_attn_quant_rope_fp8", "joint_attn_fwd_fp8"):
         getattr(lib, fn).restype = st
     lib.joint_attn_status_string.argtypes = [st]
@@ -160,6 +165,39 @@ def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_ls
     st = lib.joint_attn_fwd_bf16(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
                                  _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(q.device))
     _check(st, "joint_attn_fwd_bf16")
+    return (out, lse) if return_lse else out
+
+
+def block_mask_shape(batch: int, seq_len: int, heads: int):
+    """Shape [B, H, ceil(S / 128), ceil(S / 64)] of the block-sparse mask."""
+    return (batch, heads, -(-seq_len // SPARSE_QUERY_BLOCK), -(-seq_len // SPARSE_KEY_BLOCK))
+
+
+def fwd_bf16_block_sparse(q, k, v, block_mask, rope=None, softmax_scale: float = 0.0, out=None,
+                          return_lse: bool = False, split: bool = True):
+    """fwd_bf16 restricted to the (128-query x 64-key) blocks where the uint8
+    `block_mask` [B, H, ceil(S/128), ceil(S/64)] is nonzero; query rows that
+    keep no key get O = 0 and LSE = -inf."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{n} must be bfloat16")
+    want = block_mask_shape(q.shape[0], q.shape[1], q.shape[2])
+    if (block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != want
+            or not block_mask.is_contiguous() or block_mask.device != q.device):
+        raise ValueError(f"block_mask must be a contiguous uint8 {want} tensor on {q.device}")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    p = _params(q, k, v, out, softmax_scale)
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    lib = load()
+    ws_bytes = lib.joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(p)) if split else 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    st = lib.joint_attn_fwd_bf16_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(rope), _ptr(block_mask), _ptr(out), _ptr(lse),
+                                              _ptr(ws), ws_bytes, _stream(q.device))
+    _check(st, "joint_attn_fwd_bf16_block_sparse")
     return (out, lse) if return_lse else out
 
 

@@ -167,7 +167,29 @@ ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
   ja::SplitPlan plan = ja::plan_fwd_bf16(L, device_cu_count());
   if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
     plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
-  return hip_status(ja::launch_fwd_bf16(L, q, k, v, rope, o, lse, plan, workspace,
+  return hip_status(ja::launch_fwd_bf16(L, q, k, v, rope, nullptr, o, lse, plan, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+ja_status joint_attn_fwd_bf16_block_sparse(const ja_params *p, const void *q, const void *k,
+                                           const void *v, const float *rope,
+                                           const uint8_t *block_mask, void *o, float *lse,
+                                           void *workspace, size_t workspace_bytes,
+                                           void *stream) {
+  if (!p || !q || !k || !v || !o || !block_mask) return JA_ERR_INVALID_ARG;
+  const ja_status st = check_fwd_bf16(p);
+  if (st != JA_OK) return st;
+  if (p->seq_len > ja::fwd_bf16_sparse_max_seq()) return JA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (rope && !aligned16(rope)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
+      (workspace && !aligned16(workspace)))
+    return JA_ERR_INVALID_ARG;
+  if (o == q || o == k || o == v) return JA_ERR_INVALID_ARG;
+  const ja::AttnLayout L = layout(p);
+  ja::SplitPlan plan = ja::plan_fwd_bf16(L, device_cu_count());
+  if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
+    plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
+  return hip_status(ja::launch_fwd_bf16(L, q, k, v, rope, block_mask, o, lse, plan, workspace,
                                         static_cast<hipStream_t>(stream)));
 }
 

@@ -30,6 +30,15 @@
 // VGPRs this way, against more than 168 for a wave that also overlaps the
 // next tile's Q K^T with its own softmax).  The next tiles' global loads are
 // issued one iteration ahead; one barrier per tile.
+//
+// Block-sparse variant (the kernel half of the pages' sparse attention,
+// section "Quantized and sparse attention": attention restricted to the
+// blocks of a given block mask over 128-query x 64-key blocks).  A workgroup
+// covers three query blocks; it first compacts, in LDS, the list of key
+// blocks that any of the three keeps, with a 3-bit flag per entry, then
+// stages only the tiles of that list.  A wave computes a staged tile only if
+// its own query block keeps it (a wave-uniform branch); staging and the
+// barrier are shared.  Query rows that keep no key get O = 0 and LSE = -inf.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -56,6 +65,17 @@ constexpr int NS = 64 * JA_BF16_STAGE_WAVES;   // threads that stage K/V tiles
 // Latency is hidden by the three waves of a SIMD rather than by deeper
 // software pipelining inside a wave (which needs more registers).
 constexpr int WG_PER_CU = 1;
+
+// Block-mask granularity of the block-sparse variant.
+constexpr int kQueryBlock = 128;
+constexpr int kKeyBlock = 64;
+constexpr int KB_TILES = kKeyBlock / BN;              // key tiles per key block
+constexpr int QB_PER_WG = BM / kQueryBlock;           // query blocks per workgroup
+static_assert(BM % kQueryBlock == 0 && kKeyBlock % BN == 0, "mask blocks");
+static_assert(QB_PER_WG <= 16, "query-block flags");
+// Longest sequence of the block-sparse variant (its key-block list lives in
+// LDS, 4 bytes per key block, and entries hold the key block in 16 bits).
+constexpr int kSparseMaxSeq = 1 << 20;
 
 // Rescale the output accumulator only when the running row max grows by more
 // than 2^24 in the exp2 domain.  Until then P may exceed 1 by up to 2^24;
@@ -84,6 +104,9 @@ struct FwdArgs {
   // range of key tiles, writing unnormalised partial results to `ws`.
   int n_direct, parts;
   SplitWorkspace ws;
+  // block-sparse variant: mask [B][H][nqb][nkb] (nonzero = keep)
+  const uint8_t *mask;
+  int nqb, nkb;
 };
 
 // Max and sum of x over the two lanes l and l ^ 32 that share a query row.
@@ -108,6 +131,9 @@ struct Lds {
   static constexpr int KTILE = BN * KSTR;
   static constexpr int VTILE = D * VTSTR;
   static constexpr int BYTES = 2 * (KTILE + VTILE) * 2;
+  // block-sparse variant: per-wave counts, then the key-block list
+  static constexpr int LIST_OFFSET = BYTES + 64;
+  static constexpr int sparse_bytes(int nkb) { return LIST_OFFSET + 4 * nkb; }
 };
 
 // Position, inside a 16-key group of a V^T row, of key k: the P operand of
@@ -117,7 +143,7 @@ __host__ __device__ constexpr int vt_key_of_slot(int p) {
   return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool SPARSE>
 __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int CH = D / 8;                  // 16-byte chunks per K row
   constexpr int K_CHUNKS = BN * CH;          // 16-byte K chunks per tile
@@ -144,23 +170,84 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   // through that XCD's L2.
   const int S = a.S;
   const int ntiles_all = (S + BN - 1) / BN;
-  int item, t0, t1, unit = -1;
+  int item, part = 0, unit = -1;
   if ((int)blockIdx.x < a.n_direct) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per = a.n_direct >> 3, rem = a.n_direct & 7;
     item = xcd * per + min(xcd, rem) + slot;
-    t0 = 0;
-    t1 = ntiles_all;
   } else {
     unit = blockIdx.x - a.n_direct;
-    const int part = unit % a.parts;
+    part = unit % a.parts;
     item = a.n_direct + unit / a.parts;
-    t0 = (int)((int64_t)part * ntiles_all / a.parts);
-    t1 = (int)((int64_t)(part + 1) * ntiles_all / a.parts);
   }
   const int qblk = item % a.n_qblk;
   const int bh = item / a.n_qblk;
   const int h = bh % a.H, b = bh / a.H;
+
+  // ---- block-sparse variant: compact the key blocks kept by any of this
+  //      workgroup's query blocks into an LDS list (ascending), entry =
+  //      key block | (flags of the query blocks that keep it) << 16.  The
+  //      workgroup's key tiles are then the tiles of the listed blocks that
+  //      lie inside the sequence; the dense kernel's tiles are 0..ntiles-1. ----
+  uint32_t *blist = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(smem) + Lds<D>::LIST_OFFSET);
+  int ntiles = ntiles_all;
+  if constexpr (SPARSE) {
+    int *wcnt = reinterpret_cast<int *>(reinterpret_cast<char *>(smem) + Lds<D>::BYTES);
+    const int qb0 = qblk * QB_PER_WG;
+    const uint8_t *mrow = a.mask + ((int64_t)bh * a.nqb + qb0) * a.nkb;
+    int nact = 0;
+    for (int base = 0; base < a.nkb; base += NT) {
+      const int j = base + tid;
+      uint32_t flags = 0;
+      if (j < a.nkb) {
+#pragma unroll
+        for (int r = 0; r < QB_PER_WG; ++r)
+          if (qb0 + r < a.nqb && mrow[(int64_t)r * a.nkb + j] != 0) flags |= 1u << r;
+      }
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(flags != 0);
+      if (lane == 0) wcnt[wave] = (int)__builtin_popcountll(bal);
+      __syncthreads();
+      int off = nact, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int cw = wcnt[w];
+        off += w < wave ? cw : 0;
+        tot += cw;
+      }
+      if (flags) blist[off + __builtin_popcountll(bal & ((1ull << lane) - 1))] = (uint32_t)j | (flags << 16);
+      nact += tot;
+      __syncthreads();
+    }
+    ntiles = nact * KB_TILES;
+    if (nact > 0) {
+      // tiles of the last key block past the end of the sequence
+      const int kb_last = (int)(blist[nact - 1] & 0xffffu);
+      ntiles -= max(0, (kb_last + 1) * KB_TILES - ntiles_all);
+    }
+  }
+  int t0 = 0, t1 = ntiles;
+  if (unit >= 0) {
+    t0 = (int)((int64_t)part * ntiles / a.parts);
+    t1 = (int)((int64_t)(part + 1) * ntiles / a.parts);
+  }
+  // key tile of list position x, and whether this wave's query block keeps it
+  const int my_qb = (wave * RW * 32) / kQueryBlock;
+  auto tile_of = [&](int x) JA_INLINE -> int {
+    if constexpr (SPARSE) {
+      const uint32_t e = __builtin_amdgcn_readfirstlane(blist[x / KB_TILES]);
+      return (int)(e & 0xffffu) * KB_TILES + x % KB_TILES;
+    } else {
+      return x;
+    }
+  };
+  auto kept = [&](int x) JA_INLINE -> bool {
+    if constexpr (SPARSE) {
+      const uint32_t e = __builtin_amdgcn_readfirstlane(blist[x / KB_TILES]);
+      return (e >> (16 + my_qb)) & 1u;
+    } else {
+      return true;
+    }
+  };
 
   // ---- Q rows of this lane (one per 32-row block): rotate, round to bf16,
   //      keep in registers ----
@@ -400,36 +487,44 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   //      global loads of tile i+2, which have a whole iteration to arrive; a
   //      barrier closes the iteration. ----
   const int nt = t1 - t0;
-  load_k(t0);
-  load_v(t0);
-  store_k(0);
-  store_v(0);
-  if (nt > 1) {
-    load_k(t0 + 1);
-    load_v(t0 + 1);
+  // a dense workgroup always has at least one tile; a sparse one may have none
+  const bool any_tile = !SPARSE || nt > 0;
+  if (any_tile) {
+    load_k(tile_of(t0));
+    load_v(tile_of(t0));
+    store_k(0);
+    store_v(0);
+    if (nt > 1) {
+      load_k(tile_of(t0 + 1));
+      load_v(tile_of(t0 + 1));
+    }
+    __syncthreads();
   }
-  __syncthreads();
   f32x16 sacc[RW];
   // NEXT: tile i+1 exists.  Only the last tile of the sequence can be partial
-  // (masking a full tile changes nothing).
+  // (masking a full tile changes nothing), and it is always the last of the
+  // workgroup's tiles.
   auto iteration = [&]<bool NEXT>(int i) JA_INLINE {
-    const int t = t0 + i;
-    qk.template operator()<0, D / 16>(i & 1, sacc);
-    bf16x8 pb[RW][2];
-    softmax.template operator()<!NEXT>(sacc, t * BN, pb);
-    pv(pb, i & 1);
+    const int t = tile_of(t0 + i);
+    if (kept(t0 + i)) {
+      qk.template operator()<0, D / 16>(i & 1, sacc);
+      bf16x8 pb[RW][2];
+      softmax.template operator()<!NEXT>(sacc, t * BN, pb);
+      pv(pb, i & 1);
+    }
     if constexpr (NEXT) {
       store_k((i + 1) & 1);
       store_v((i + 1) & 1);
       if (i + 2 < nt) {
-        load_k(t + 2);
-        load_v(t + 2);
+        const int t2 = tile_of(t0 + i + 2);
+        load_k(t2);
+        load_v(t2);
       }
     }
     __syncthreads();
   };
   for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<true>(i);
-  iteration.template operator()<false>(nt - 1);
+  if (any_tile) iteration.template operator()<false>(nt - 1);
 
   // ---- a split part leaves O unnormalised, with its row max (raw score
   //      units) and row sum, for the merge kernel ----
@@ -458,7 +553,9 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   for (int r = 0; r < RW; ++r) {
     const float l_tot = half_sum(l_run[r]);
     if (qi[r] < S) {
-      const float inv = 1.f / l_tot;
+      // a row of the block-sparse variant that keeps no key has l = 0 (and
+      // O accumulators 0): O = 0, LSE = -inf
+      const float inv = SPARSE && l_tot == 0.f ? 0.f : 1.f / l_tot;
       bf16 *orow = a.o + b * a.o_sb + (int64_t)qi[r] * a.o_ss + h * a.o_sh;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -476,6 +573,29 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   }
 }
 
+// Dynamic LDS of one instantiation; kernels that need more than the default
+// limit get it raised once per process.
+template <int D, bool ROPE, bool SPARSE>
+hipError_t launch_instance(const FwdArgs &a, dim3 grid, hipStream_t st) {
+  const int bytes = SPARSE ? Lds<D>::sparse_bytes(a.nkb) : Lds<D>::BYTES;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<D, ROPE, SPARSE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      SPARSE ? Lds<D>::sparse_bytes((kSparseMaxSeq + kKeyBlock - 1) / kKeyBlock) : Lds<D>::BYTES);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, ROPE, SPARSE>), grid, dim3(NT), bytes, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dim(const FwdArgs &a, dim3 grid, bool rope_on, hipStream_t st) {
+  if (a.mask)
+    return rope_on ? launch_instance<D, true, true>(a, grid, st)
+                   : launch_instance<D, false, true>(a, grid, st);
+  return rope_on ? launch_instance<D, true, false>(a, grid, st)
+                 : launch_instance<D, false, false>(a, grid, st);
+}
+
 }  // namespace
 
 int fwd_bf16_block_rows(int) { return BM; }
@@ -485,9 +605,11 @@ SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu) {
   return plan_split(n_items, (L.S + BN - 1) / BN, n_cu * WG_PER_CU, BM, L.D);
 }
 
+int fwd_bf16_sparse_max_seq() { return kSparseMaxSeq; }
+
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
-                           const void *v, const float *rope, void *o,
-                           float *lse, const SplitPlan &plan, void *workspace,
+                           const void *v, const float *rope, const uint8_t *mask,
+                           void *o, float *lse, const SplitPlan &plan, void *workspace,
                            hipStream_t st) {
   FwdArgs a;
   a.q = static_cast<const bf16 *>(q);
@@ -508,26 +630,12 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
   a.n_direct = plan.n_direct;
   a.parts = plan.parts;
   a.ws = split_workspace(plan, workspace, BM, L.D);
+  a.mask = mask;
+  a.nqb = (L.S + kQueryBlock - 1) / kQueryBlock;
+  a.nkb = (L.S + kKeyBlock - 1) / kKeyBlock;
   const dim3 grid((unsigned)(plan.n_direct + plan.n_units));
-  const bool rope_on = rope != nullptr;
-  if (L.D == 64) {
-    auto kern = rope_on ? attn_fwd_bf16_kernel<64, true> : attn_fwd_bf16_kernel<64, false>;
-    hipLaunchKernelGGL(kern, grid, dim3(NT), Lds<64>::BYTES, st, a);
-  } else {
-    static const hipError_t attr = []() {
-      hipError_t e = hipFuncSetAttribute(
-          reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<128, true>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::BYTES);
-      if (e != hipSuccess) return e;
-      return hipFuncSetAttribute(
-          reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<128, false>),
-          hipFuncAttributeMaxDynamicSharedMemorySize, Lds<128>::BYTES);
-    }();
-    if (attr != hipSuccess) return attr;
-    auto kern = rope_on ? attn_fwd_bf16_kernel<128, true> : attn_fwd_bf16_kernel<128, false>;
-    hipLaunchKernelGGL(kern, grid, dim3(NT), Lds<128>::BYTES, st, a);
-  }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = L.D == 64 ? launch_dim<64>(a, grid, rope != nullptr, st)
+                                 : launch_dim<128>(a, grid, rope != nullptr, st);
   if (e != hipSuccess || plan.n_units == 0) return e;
   return launch_merge_split(L, plan, a.ws, BM, L.scale_log2, o, lse, st);
 }

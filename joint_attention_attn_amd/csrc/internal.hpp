@@ -43,10 +43,13 @@ hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
                               void *o, float *lse, hipStream_t st);
 
 SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu);
+// mask: NULL = dense; else the block mask of the block-sparse variant,
+// uint8 [B][H][ceil(S/128)][ceil(S/64)] (nonzero = keep).
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
-                           const void *v, const float *rope, void *o,
-                           float *lse, const SplitPlan &plan, void *workspace,
+                           const void *v, const float *rope, const uint8_t *mask,
+                           void *o, float *lse, const SplitPlan &plan, void *workspace,
                            hipStream_t st);
+int fwd_bf16_sparse_max_seq();   // longest sequence of the block-sparse variant
 
 hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
                                  const void *k, const void *v,

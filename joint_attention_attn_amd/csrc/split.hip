@@ -50,7 +50,10 @@ __global__ __launch_bounds__(256) void merge_split_kernel(MergeArgs m) {
   for (int j = 0; j < m.parts; ++j)
     mx = fmaxf(mx, m.ws.ml[((unit0 + j) * m.block_rows + row) * 2]);
   float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < m.parts; ++j) {
+  // a row that no part saw a key for (block-sparse rows that keep no key
+  // block) has every part at max -inf and sum 0: O = 0, LSE = -inf
+  const bool empty = mx == -INFINITY;
+  for (int j = 0; j < m.parts && !empty; ++j) {
     const int64_t r = (unit0 + j) * m.block_rows + row;
     const float2 ml = *reinterpret_cast<const float2 *>(m.ws.ml + r * 2);
     const float w = __builtin_amdgcn_exp2f((ml.x - mx) * c);
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(256) void merge_split_kernel(MergeArgs m) {
     acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
     acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
   }
-  const float inv = 1.f / l;
+  const float inv = empty ? 0.f : 1.f / l;
   u32x4 out;
   out.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   out.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(256) void merge_split_kernel(MergeArgs m) {
   out.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
   *reinterpret_cast<u32x4 *>(m.o + b * m.o_sb + (int64_t)qi * m.o_ss + h * m.o_sh + ch * 8) = out;
   if (m.lse && ch == 0)
-    m.lse[((int64_t)b * m.H + h) * m.S + qi] = (mx * c + __log2f(l)) * kLn2;
+    m.lse[((int64_t)b * m.H + h) * m.S + qi] = empty ? -INFINITY : (mx * c + __log2f(l)) * kLn2;
 }
 
 }  // namespace

@@ -143,3 +143,22 @@ def test_repair_plan_validation(lib):
     bad.head_dim = 96
     assert f(ctypes.byref(bad), *ptrs[:2], None, *ptrs[2:6], 4, *ptrs[6:10], None) == ja.JA_ERR_UNSUPPORTED
     assert lib.joint_attn_fwd_fp8_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_block_sparse_validation(lib):
+    vp = ctypes.c_void_p
+
+    def call(p, mask=FAKE + 0x5000, o=FAKE + 0x3000, q=FAKE):
+        return lib.joint_attn_fwd_bf16_block_sparse(
+            ctypes.byref(p) if p is not None else None, vp(q), vp(FAKE + 0x1000),
+            vp(FAKE + 0x2000), None, vp(mask), vp(o), None, None, 0, None)
+
+    assert call(None) == ja.JA_ERR_INVALID_ARG
+    assert call(_p(), mask=0) == ja.JA_ERR_INVALID_ARG                  # mask required
+    assert call(_p(), o=FAKE) == ja.JA_ERR_INVALID_ARG                  # o aliases q
+    assert call(_p(), q=FAKE + 4) == ja.JA_ERR_INVALID_ARG              # misaligned
+    bad = _p()
+    bad.head_dim = 96
+    assert call(bad) == ja.JA_ERR_UNSUPPORTED
+    assert call(_p(s=(1 << 20) + 1)) == ja.JA_ERR_UNSUPPORTED           # longest sequence
+    assert ja.block_mask_shape(2, 300, 3) == (2, 3, 3, 5)

@@ -1,0 +1,146 @@
+"""GPU parity of the block-sparse BF16 forward against the fp64 oracle
+(calls go through the C ABI via the Python binding)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import joint_attention_attn_amd as ja
+import oracle
+import synth
+from parity_util import (BF16_MAX_ABS, BF16_REL_L2, max_abs, rel_l2,
+                         row_scaled_max_abs, sample_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _rope(pos, d):
+    return None if pos is None else ja.rope_table_2d(torch.from_numpy(pos).to(DEV), d)
+
+
+def _run(q, k, v, mask, pos, **kw):
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    out = ja.fwd_bf16_block_sparse(qd, kd, vd, mask.to(DEV), _rope(pos, q.shape[-1]),
+                                   return_lse=True, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _lse_close(got, ref, tol=1e-2):
+    got = got.detach().cpu().to(torch.float64)
+    ref = ref.to(torch.float64)
+    inf_ref = torch.isinf(ref)
+    assert torch.equal(torch.isinf(got), inf_ref)
+    assert (got[inf_ref] < 0).all()
+    if (~inf_ref).any():
+        assert float((got[~inf_ref] - ref[~inf_ref]).abs().max()) <= tol
+
+
+def _check(out, lse, ref, ref_lse, scaled=False):
+    assert rel_l2(out, ref) <= BF16_REL_L2
+    if scaled:
+        assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
+    else:
+        assert max_abs(out, ref) <= BF16_MAX_ABS
+    _lse_close(lse, ref_lse)
+
+
+@pytest.mark.parametrize("s,d,density", [(80, 64, 0.5), (1000, 128, 0.5), (1100, 64, 0.3),
+                                         (1100, 128, 0.7), (2049, 128, 0.5)])
+def test_ragged_parity(s, d, density):
+    # several workgroups, partial last tile (1000: 8 keys; 1100: a last key
+    # block of 12 keys whose second tile lies past the end)
+    w = synth.Workload("sparse", 2, 3, d, n_text=s, grid=0, outlier_frac=0.01)
+    q, k, v, _ = synth.make_qkv(w, seed=s)
+    pos = np.random.default_rng(s).integers(0, 200, size=(s, 2)).astype(np.int32)
+    mask = synth.make_block_mask(w, density, seed=s + 1)
+    mask[1, 2, 0] = 0                      # a query block that keeps nothing
+    mask[0, 1] = 0                         # a (batch, head) that keeps nothing
+    _say(f"sparse ragged S={s} D={d} density={density}")
+    out, lse = _run(q, k, v, mask, pos)
+    ref, ref_lse = oracle.block_sparse_attention(q, k, v, mask, pos)
+    _check(out, lse, ref, ref_lse, scaled=True)
+    # the empty rows are exactly zero
+    assert not out[1, :128, 2].any() and not out[0, :, 1].any()
+
+
+def test_all_kept_equals_dense_bit_exact():
+    # an all-ones mask stages the same tiles in the same order with the same
+    # split as the dense kernel: identical arithmetic, identical bits
+    w = synth.WORKLOADS["t2i_1024"]
+    q, k, v, _ = synth.make_qkv(w, seed=4)
+    pos = synth.positions(w)
+    mask = torch.ones(ja.block_mask_shape(w.batch, w.seq_len, w.heads), dtype=torch.uint8)
+    _say("sparse all-ones vs dense t2i_1024")
+    out, lse = _run(q, k, v, mask, pos)
+    qd, kd, vd = (t.to(DEV) for t in (q, k, v))
+    dense, dense_lse = ja.fwd_bf16(qd, kd, vd, _rope(pos, w.head_dim), return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), dense.view(torch.int16))
+    assert torch.equal(lse, dense_lse)
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_nothing_kept(split):
+    w = synth.Workload("sparse_empty", 1, 4, 128, n_text=3000, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=2)
+    mask = torch.zeros(ja.block_mask_shape(1, w.seq_len, 4), dtype=torch.uint8)
+    _say(f"sparse empty mask split={split}")
+    out, lse = _run(q, k, v, mask, None, split=split)
+    assert not out.any()
+    assert torch.isinf(lse).all() and (lse < 0).all()
+
+
+def test_single_key_block():
+    # each query block keeps one key block: softmax over 64 keys (the last
+    # one partial for the last query block)
+    w = synth.Workload("sparse_one", 1, 2, 64, n_text=700, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=6)
+    shape = ja.block_mask_shape(1, w.seq_len, 2)
+    mask = torch.zeros(shape, dtype=torch.uint8)
+    for qb in range(shape[2]):
+        mask[0, 0, qb, qb % shape[3]] = 1
+        mask[0, 1, qb, shape[3] - 1] = 1
+    _say("sparse one key block per query block")
+    out, lse = _run(q, k, v, mask, None)
+    ref, ref_lse = oracle.block_sparse_attention(q, k, v, mask)
+    _check(out, lse, ref, ref_lse)
+
+
+def test_split_matches_unsplit():
+    # the split of the last round cuts each item's list of kept tiles; the
+    # merge is exact up to rounding
+    w = synth.WORKLOADS["t2i_1024"]
+    q, k, v, _ = synth.make_qkv(w, seed=8)
+    pos = synth.positions(w)
+    mask = synth.make_block_mask(w, 0.5, seed=9)
+    mask[0, 5, 3] = 0
+    if ja.fwd_bf16_workspace_bytes(w.batch, w.seq_len, w.heads, w.head_dim) == 0:
+        pytest.skip("no split planned for this shape on this device")
+    _say("sparse split vs unsplit t2i_1024")
+    a, la = _run(q, k, v, mask, pos, split=True)
+    b, lb = _run(q, k, v, mask, pos, split=False)
+    assert rel_l2(a, b) <= 2e-3
+    _lse_close(la, lb.cpu().to(torch.float64), tol=1e-2)
+
+
+@pytest.mark.parametrize("name", ["t2i_1024", "t2i_2048"])
+def test_full_size_sampled_rows(name):
+    # the bench workload: seeded mask at the block density of the sparse
+    # steps, sampled query rows computed by the oracle one by one
+    w = synth.WORKLOADS[name]
+    q, k, v, idx = synth.make_qkv(w, seed=0)
+    pos = synth.positions(w)
+    mask = synth.make_block_mask(w, synth.SPARSE_DENSITY, seed=0)
+    _say(f"sparse full size {name}")
+    out, lse = _run(q, k, v, mask, pos)
+    rows = sample_rows(w.seq_len, w.n_text, idx[:8], 24, seed=1)
+    ref, ref_lse = oracle.block_sparse_attention(q, k, v, mask, pos, rows=rows)
+    got = out.cpu()[:, torch.as_tensor(rows)]
+    _check(got, lse.cpu()[:, :, torch.as_tensor(rows)], ref, ref_lse, scaled=True)
