@@ -3,13 +3,15 @@
 
 One step = one pass of the bf16 hot path over the 2048x2048 T2I step shape
 (B=1, 24 heads x 128, 512 text + 128x128 image tokens = 16896 tokens): build
-the 2D-axial RoPE table from the token positions, then the fused RoPE +
-attention forward.  Inputs are seeded synthetic tensors resident in HBM before
+the 2D-axial RoPE table from the token positions, the K/V preparation (K
+rotated, V transposed), then the attention forward with RoPE fused into the
+Q load.  Inputs are seeded synthetic tensors resident in HBM before
 the timed region.  Throughput is 4*B*H*S^2*D flops per step (QK^T + PV).
 
 Also reported on the same JSON line:
-  roofline      the forward kernel's own average duration (HIP events on the
-                launch stream) against the bf16 dense MFMA peak;
+  roofline      the attention forward's own average duration (HIP events on
+                the launch stream, the K/V preparation excluded and reported
+                beside it) against the bf16 dense MFMA peak;
   fp8           the FP8 path (RoPE+quantize pass, FP8 forward) timed the same
                 way, against the fp8 MFMA peak and HBM bandwidth, and with the
                 repair of the tokens with the largest quantization error
@@ -143,8 +145,10 @@ def main() -> int:
 
     def step():
         rope = ja.rope_table_2d(pos_d, D, w.theta)
-        ja.fwd_bf16(qd, kd, vd, rope, out=out)
+        kv = ja.prep_kv_bf16(kd, vd, rope)
+        ja.fwd_bf16_prepared(qd, kv, rope, out=out)
         rope_holder["rope"] = rope
+        rope_holder["kv"] = kv
 
     for _ in range(args.warmup):
         step()
@@ -161,20 +165,29 @@ def main() -> int:
     value = flops / (ms_per_step * 1e-3) / 1e12
     _log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
-    # dominant kernel: the fused RoPE + attention forward, timed per launch
-    rope = rope_holder["rope"]
-    kms = _time_launches(lambda: ja.fwd_bf16(qd, kd, vd, rope, out=out), max(args.steps, 5))
+    # dominant kernel: the attention forward (RoPE fused into the Q load),
+    # timed per launch; the K/V preparation beside it
+    rope, kv = rope_holder["rope"], rope_holder["kv"]
+    kms = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope, out=out), max(args.steps, 5))
     k_avg = sum(kms) / len(kms)
+    pms = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope), max(args.steps, 5))
+    p_avg = sum(pms) / len(pms)
+    # algorithmic bytes of the preparation: read K, V and the table, write both
+    prep_bytes = 4 * B * S * H * D * 2 + S * (D // 2) * 8
     achieved = flops / (k_avg * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": _traffic_for_current_kernel("attn_fwd_bf16_t2i_2048_traffic.txt",
                                                        "attn_bf16.hip"),
-                "kernel": "attn_fwd_bf16_kernel<128, true> (+ merge_split_kernel of the split "
-                          "last round)",
-                "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4)}
+                "kernel": "attn_fwd_bf16_kernel<128, true, false> (+ merge_split_kernel of the "
+                          "split last round)",
+                "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4),
+                "prep_kv": {"ms": round(p_avg, 4),
+                            "gbs": round(prep_bytes / (p_avg * 1e-3) / 1e9, 1),
+                            "frac_of_hbm": round(prep_bytes / (p_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                 4)}}
     _log(f"[bench] fwd kernel avg {k_avg:.3f} ms -> {achieved:.1f} TFLOP/s "
-         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak)")
+         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); K/V prep {p_avg:.3f} ms")
 
     fp8 = None
     fp8_outs = None
@@ -224,7 +237,7 @@ def main() -> int:
 
     sparse = None
     if not args.no_sparse:
-        sparse = _sparse_leg(ja, w, qd, kd, vd, rope, out, k_avg, max(args.steps, 5), args.seed)
+        sparse = _sparse_leg(ja, w, qd, kv, rope, out, k_avg, max(args.steps, 5), args.seed)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -246,7 +259,7 @@ def main() -> int:
     return 0
 
 
-def _sparse_leg(ja, w, qd, kd, vd, rope, out, dense_ms, n, seed):
+def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
     """Block-sparse forward on the seeded mask of the workload: its kernel
     time, the flops of the kept blocks per second, and the blocks staged
     (kept by any of the three query blocks one workgroup covers)."""
@@ -268,9 +281,9 @@ def _sparse_leg(ja, w, qd, kd, vd, rope, out, dense_ms, n, seed):
     mask_d = mask.to(qd.device)
     outs = torch.empty_like(out)
     for _ in range(3):
-        ja.fwd_bf16_block_sparse(qd, kd, vd, mask_d, rope, out=outs)
+        ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope, out=outs)
     torch.cuda.synchronize()
-    ms = _time_launches(lambda: ja.fwd_bf16_block_sparse(qd, kd, vd, mask_d, rope, out=outs), n)
+    ms = _time_launches(lambda: ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope, out=outs), n)
     avg = sum(ms) / n
     tf = kept_flops / (avg * 1e-3) / 1e12
     _log(f"[bench] sparse (density {synth.SPARSE_DENSITY}): {avg:.3f} ms, {tf:.1f} TFLOP/s of "

@@ -90,15 +90,37 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len,
                                    void *stream);
 
 /*
- * joint_attn_fwd_bf16 - BF16 joint attention with RoPE fused into the Q/K
- * load.
- *   q, k, v  device bf16, layout per ja_params.
- *   rope     device float [seq_len][head_dim/2][2] (cos, sin) table, e.g.
- *            from joint_attn_rope_table_2d; NULL = no rotation.  Q and K are
- *            rotated in fp32, pair (x, y) -> (fma(x, c, -fl(y s)),
- *            fma(x, s, fl(y c))), and rounded to bf16 before Q K^T.
+ * joint_attn_prep_kv_bf16 - K/V preparation of the BF16 forward: RoPE fused
+ * into the single load of K (same page, section "GEMM kernel optimization",
+ * where RoPE is fused into the epilogue that produces K), V transposed.
+ *   k, v     device bf16, layout per ja_params (its K and V strides).
+ *   rope     as for joint_attn_fwd_bf16 (NULL = no rotation).  K is rotated
+ *            in fp32, pair (x, y) -> (fma(x, c, -fl(y s)), fma(x, s, fl(y c))),
+ *            and rounded to bf16.
+ *   kv       device buffer (16-byte aligned) of kv_bytes >=
+ *            joint_attn_prep_kv_bf16_bytes(p), written with
+ *              Kr [batch*heads][S_pad][head_dim]  rotated K,
+ *              Vt [batch*heads][head_dim][S_pad]  V transposed, the keys of
+ *                   every 16-key group in the order p -> 4*(p/8) + (p%8 < 4 ?
+ *                   p%8 : p%8 + 4) (the P operand order of the forward),
+ *            S_pad = seq_len rounded up to 64, zeros past seq_len.
+ * The buffer depends only on K, V and the table: when several calls share
+ * them, prepare once.
+ */
+size_t joint_attn_prep_kv_bf16_bytes(const ja_params *p);
+ja_status joint_attn_prep_kv_bf16(const ja_params *p, const void *k, const void *v,
+                                  const float *rope, void *kv, size_t kv_bytes, void *stream);
+
+/*
+ * joint_attn_fwd_bf16 - BF16 joint attention on K/V prepared by
+ * joint_attn_prep_kv_bf16 (with the same p and rope), with RoPE fused into
+ * the load of Q.
+ *   q        device bf16, layout per ja_params.
+ *   kv, kv_bytes  the prepared K/V buffer.
+ *   rope     the table the K/V were prepared with (NULL = no rotation); Q is
+ *            rotated as K was and rounded to bf16 before Q K^T.
  *   o        device bf16, layout per ja_params (o_* strides); must not alias
- *            q, k or v.
+ *            q or kv.
  *   lse      device float [batch][heads][seq_len], nullable: natural-log
  *            log-sum-exp of each query row's scaled scores.
  *   workspace, workspace_bytes
@@ -112,15 +134,15 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len,
  * Softmax statistics and both products accumulate in fp32; P is rounded to
  * bf16 for the P.V product.
  */
-ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
-                              const void *v, const float *rope, void *o,
-                              float *lse, void *workspace, size_t workspace_bytes,
-                              void *stream);
+ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *kv,
+                              size_t kv_bytes, const float *rope, void *o, float *lse,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * joint_attn_fwd_bf16_workspace_bytes - bytes of the optional workspace of
- * joint_attn_fwd_bf16 for this shape on the current device (0: no split
- * helps, or p is invalid).  Host-only; launches nothing.
+ * joint_attn_fwd_bf16 (and joint_attn_fwd_bf16_block_sparse) for this shape
+ * on the current device (0: no split helps, or p is invalid).  Host-only;
+ * launches nothing.
  */
 size_t joint_attn_fwd_bf16_workspace_bytes(const ja_params *p);
 
@@ -148,8 +170,8 @@ size_t joint_attn_fwd_bf16_workspace_bytes(const ja_params *p);
  *   with the key blocks kept by any of the three consecutive query blocks
  *   that one workgroup covers.
  */
-ja_status joint_attn_fwd_bf16_block_sparse(const ja_params *p, const void *q, const void *k,
-                                           const void *v, const float *rope,
+ja_status joint_attn_fwd_bf16_block_sparse(const ja_params *p, const void *q, const void *kv,
+                                           size_t kv_bytes, const float *rope,
                                            const uint8_t *block_mask, void *o, float *lse,
                                            void *workspace, size_t workspace_bytes,
                                            void *stream);

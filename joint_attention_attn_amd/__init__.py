@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "JointAttnError", "library_path", "load", "rope_table_2d", "fwd_bf16",
-    "fwd_bf16_workspace_bytes", "Fp8Repair", "fp8_repair_plan", "repair_count",
+    "fwd_bf16_workspace_bytes", "prep_kv_bf16", "fwd_bf16_prepared",
+    "fwd_bf16_block_sparse_prepared", "Fp8Repair", "fp8_repair_plan", "repair_count",
     "quant_rope_fp8", "fwd_fp8", "Params", "fwd_bf16_block_sparse",
     "SPARSE_QUERY_BLOCK", "SPARSE_KEY_BLOCK", "block_mask_shape",
 ]
@@ -70,9 +71,12 @@ def load() -> ctypes.CDLL:
     vp, st = ctypes.c_void_p, ctypes.c_int
     pp = ctypes.POINTER(Params)
     lib.joint_attn_rope_table_2d.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp]
-    lib.joint_attn_fwd_bf16.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.joint_attn_fwd_bf16_block_sparse.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                                     ctypes.c_size_t, vp]
+    sz = ctypes.c_size_t
+    lib.joint_attn_prep_kv_bf16_bytes.argtypes = [pp]
+    lib.joint_attn_prep_kv_bf16_bytes.restype = sz
+    lib.joint_attn_prep_kv_bf16.argtypes = [pp, vp, vp, vp, vp, sz, vp]
+    lib.joint_attn_fwd_bf16.argtypes = [pp, vp, vp, sz, vp, vp, vp, vp, sz, vp]
+    lib.joint_attn_fwd_bf16_block_sparse.argtypes = [pp, vp, vp, sz, vp, vp, vp, vp, vp, sz, vp]
     lib.joint_attn_fwd_bf16_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_bf16_workspace_bytes.restype = ctypes.c_size_t
     lib.joint_attn_quant_rope_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -83,7 +87,8 @@ def load() -> ctypes.CDLL:
     lib.joint_attn_fp8_repair_plan.restype = st
     lib.joint_attn_fwd_fp8_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
-    for fn in ("joint_attn_rope_table_2d", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_block_sparse",
+    for fn in ("joint_attn_rope_table_2d", "joint_attn_prep_kv_bf16", "joint_attn_fwd_bf16",
+               "joint_attn_fwd_bf16_block_sparse",
                "joint_attn_quant_rope_fp8", "joint_attn_fwd_fp8"):
         getattr(lib, fn).restype = st
     lib.joint_attn_status_string.argtypes = [st]
@@ -145,27 +150,67 @@ def rope_table_2d(pos: torch.Tensor, head_dim: int, theta: float = 10000.0) -> t
     return table
 
 
-def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
-             split: bool = True):
-    """Joint attention on bf16 [B, S, H, D] tensors; RoPE from `rope` (or none).
-    `split` passes the workspace that lets a mostly idle last round of
-    workgroups be split over key ranges (False: no workspace)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+def _check_bf16(**tensors):
+    for n, t in tensors.items():
         if t.dtype != torch.bfloat16:
             raise ValueError(f"{n} must be bfloat16")
+
+
+def prep_kv_bf16(k, v, rope=None):
+    """Prepared K/V buffer of the bf16 forward (uint8 device tensor): K rotated
+    with `rope` (or not), V transposed."""
+    _check_bf16(k=k, v=v)
+    p = _params(k, k, v, k, 0.0)
+    lib = load()
+    n = int(lib.joint_attn_prep_kv_bf16_bytes(ctypes.byref(p)))
+    if n == 0:
+        raise JointAttnError(JA_ERR_UNSUPPORTED, "joint_attn_prep_kv_bf16: unsupported shape")
+    kv = torch.empty(n, dtype=torch.uint8, device=k.device)
+    st = lib.joint_attn_prep_kv_bf16(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(rope), _ptr(kv), n,
+                                     _stream(k.device))
+    _check(st, "joint_attn_prep_kv_bf16")
+    return kv
+
+
+def _fwd_prepared(fn, name, q, kv, rope, mask, softmax_scale, out, return_lse, split):
+    _check_bf16(q=q)
+    if kv.dtype != torch.uint8 or kv.dim() != 1 or kv.device != q.device:
+        raise ValueError("kv must be the uint8 buffer from prep_kv_bf16 on q's device")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    p = _params(q, k, v, out, softmax_scale)
+    p = _params(q, q, q, out, softmax_scale)
     lse = None
     if return_lse:
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
     lib = load()
     ws_bytes = lib.joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(p)) if split else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
-    st = lib.joint_attn_fwd_bf16(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
-                                 _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(q.device))
-    _check(st, "joint_attn_fwd_bf16")
+    args = [ctypes.byref(p), _ptr(q), _ptr(kv), kv.numel(), _ptr(rope)]
+    if mask is not None:
+        args.append(_ptr(mask))
+    st = fn(*args, _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(q.device))
+    _check(st, name)
     return (out, lse) if return_lse else out
+
+
+def fwd_bf16_prepared(q, kv, rope=None, softmax_scale: float = 0.0, out=None,
+                      return_lse: bool = False, split: bool = True):
+    """Joint attention of bf16 Q [B, S, H, D] on K/V prepared by prep_kv_bf16
+    (with the same `rope`).  `split` passes the workspace that lets a mostly
+    idle last round of workgroups be split over key ranges."""
+    return _fwd_prepared(load().joint_attn_fwd_bf16, "joint_attn_fwd_bf16", q, kv, rope, None,
+                         softmax_scale, out, return_lse, split)
+
+
+def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
+             split: bool = True):
+    """Joint attention on bf16 [B, S, H, D] tensors; RoPE from `rope` (or none):
+    prep_kv_bf16 then fwd_bf16_prepared."""
+    _check_bf16(q=q, k=k, v=v)
+    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError("q, k, v must have the same [B, S, H, D] shape")
+    kv = prep_kv_bf16(k, v, rope)
+    return fwd_bf16_prepared(q, kv, rope, softmax_scale, out, return_lse, split)
 
 
 def block_mask_shape(batch: int, seq_len: int, heads: int):
@@ -173,42 +218,44 @@ def block_mask_shape(batch: int, seq_len: int, heads: int):
     return (batch, heads, -(-seq_len // SPARSE_QUERY_BLOCK), -(-seq_len // SPARSE_KEY_BLOCK))
 
 
-def fwd_bf16_block_sparse(q, k, v, block_mask, rope=None, softmax_scale: float = 0.0, out=None,
-                          return_lse: bool = False, split: bool = True):
-    """fwd_bf16 restricted to the (128-query x 64-key) blocks where the uint8
-    `block_mask` [B, H, ceil(S/128), ceil(S/64)] is nonzero; query rows that
-    keep no key get O = 0 and LSE = -inf."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{n} must be bfloat16")
+def fwd_bf16_block_sparse_prepared(q, kv, block_mask, rope=None, softmax_scale: float = 0.0,
+                                   out=None, return_lse: bool = False, split: bool = True):
+    """fwd_bf16_prepared restricted to the (128-query x 64-key) blocks where the
+    uint8 `block_mask` [B, H, ceil(S/128), ceil(S/64)] is nonzero; query rows
+    that keep no key get O = 0 and LSE = -inf."""
     want = block_mask_shape(q.shape[0], q.shape[1], q.shape[2])
     if (block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != want
             or not block_mask.is_contiguous() or block_mask.device != q.device):
         raise ValueError(f"block_mask must be a contiguous uint8 {want} tensor on {q.device}")
-    if out is None:
-        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    p = _params(q, k, v, out, softmax_scale)
-    lse = None
-    if return_lse:
-        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
-    lib = load()
-    ws_bytes = lib.joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(p)) if split else 0
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
-    st = lib.joint_attn_fwd_bf16_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
-                                              _ptr(rope), _ptr(block_mask), _ptr(out), _ptr(lse),
-                                              _ptr(ws), ws_bytes, _stream(q.device))
-    _check(st, "joint_attn_fwd_bf16_block_sparse")
-    return (out, lse) if return_lse else out
+    return _fwd_prepared(load().joint_attn_fwd_bf16_block_sparse,
+                         "joint_attn_fwd_bf16_block_sparse", q, kv, rope, block_mask,
+                         softmax_scale, out, return_lse, split)
 
 
-def fwd_bf16_workspace_bytes(batch: int, seq_len: int, heads: int, head_dim: int) -> int:
-    """Workspace of fwd_bf16 for a contiguous [B, S, H, D] call on the current
-    device (0 when no split of the last round is planned)."""
+def fwd_bf16_block_sparse(q, k, v, block_mask, rope=None, softmax_scale: float = 0.0, out=None,
+                          return_lse: bool = False, split: bool = True):
+    """prep_kv_bf16 then fwd_bf16_block_sparse_prepared."""
+    _check_bf16(q=q, k=k, v=v)
+    if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
+        raise ValueError("q, k, v must have the same [B, S, H, D] shape")
+    kv = prep_kv_bf16(k, v, rope)
+    return fwd_bf16_block_sparse_prepared(q, kv, block_mask, rope, softmax_scale, out,
+                                          return_lse, split)
+
+
+def _contiguous_params(batch, seq_len, heads, head_dim):
     p = Params(batch, seq_len, heads, head_dim)
     for x in "qkvo":
         setattr(p, f"{x}_sb", seq_len * heads * head_dim)
         setattr(p, f"{x}_ss", heads * head_dim)
         setattr(p, f"{x}_sh", head_dim)
+    return p
+
+
+def fwd_bf16_workspace_bytes(batch: int, seq_len: int, heads: int, head_dim: int) -> int:
+    """Workspace of fwd_bf16 for a contiguous [B, S, H, D] call on the current
+    device (0 when no split of the last round is planned)."""
+    p = _contiguous_params(batch, seq_len, heads, head_dim)
     return int(load().joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(p)))
 
 

@@ -96,13 +96,11 @@ int device_cu_count() {
 ja_status check_fwd_bf16(const ja_params *p) {
   const ja_status st = check_params(p, true, ja::fwd_bf16_block_rows(p ? p->head_dim : 0));
   if (st != JA_OK) return st;
-  // K, V and the RoPE table of one (batch, head) are addressed with 32-bit
-  // byte offsets
-  const int64_t span_k = ((int64_t)(p->seq_len - 1) * p->k_ss + p->head_dim) * 2;
-  const int64_t span_v = ((int64_t)(p->seq_len - 1) * p->v_ss + p->head_dim) * 2;
-  const int64_t span_t = (int64_t)p->seq_len * p->head_dim * 4;
-  if (span_k > 0x7fffffffLL || span_v > 0x7fffffffLL || span_t > 0x7fffffffLL ||
-      64 * p->k_ss * 2 > 0x7fffffffLL || 64 * p->v_ss * 2 > 0x7fffffffLL)
+  // the prepared K and V^T of one (batch, head) are addressed with 32-bit
+  // byte offsets; the preparation pass has one workgroup per 64 keys and head
+  const int64_t s_pad = ((int64_t)p->seq_len + 63) / 64 * 64;
+  if (s_pad * p->head_dim * 2 > 0x7fffffffLL ||
+      s_pad / 64 * p->batch * p->heads > 0x7fffffffLL)
     return JA_ERR_UNSUPPORTED;
   return JA_OK;
 }
@@ -146,51 +144,64 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len,
                                              static_cast<hipStream_t>(stream)));
 }
 
+size_t joint_attn_prep_kv_bf16_bytes(const ja_params *p) {
+  if (!p || check_fwd_bf16(p) != JA_OK) return 0;
+  return (size_t)ja::prep_kv_bytes(layout(p));
+}
+
+ja_status joint_attn_prep_kv_bf16(const ja_params *p, const void *k, const void *v,
+                                  const float *rope, void *kv, size_t kv_bytes, void *stream) {
+  if (!p || !k || !v || !kv) return JA_ERR_INVALID_ARG;
+  const ja_status st = check_fwd_bf16(p);
+  if (st != JA_OK) return st;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(kv) || (rope && !aligned16(rope)))
+    return JA_ERR_INVALID_ARG;
+  const ja::AttnLayout L = layout(p);
+  if (kv_bytes < (size_t)ja::prep_kv_bytes(L)) return JA_ERR_INVALID_ARG;
+  return hip_status(ja::launch_prep_kv_bf16(L, k, v, rope, kv, static_cast<hipStream_t>(stream)));
+}
+
 size_t joint_attn_fwd_bf16_workspace_bytes(const ja_params *p) {
   if (!p || check_fwd_bf16(p) != JA_OK) return 0;
   return (size_t)ja::plan_fwd_bf16(layout(p), device_cu_count()).ws_bytes;
 }
 
-ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *k,
-                              const void *v, const float *rope, void *o,
-                              float *lse, void *workspace, size_t workspace_bytes,
-                              void *stream) {
-  if (!p || !q || !k || !v || !o) return JA_ERR_INVALID_ARG;
+// Shared checks and launch of the dense and block-sparse BF16 forwards.
+static ja_status fwd_bf16_call(const ja_params *p, const void *q, const void *kv, size_t kv_bytes,
+                        const float *rope, const uint8_t *mask, void *o, float *lse,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  if (!p || !q || !kv || !o) return JA_ERR_INVALID_ARG;
   const ja_status st = check_fwd_bf16(p);
   if (st != JA_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (rope && !aligned16(rope)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
-      (workspace && !aligned16(workspace)))
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o) || (rope && !aligned16(rope)) ||
+      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (workspace && !aligned16(workspace)))
     return JA_ERR_INVALID_ARG;
-  if (o == q || o == k || o == v) return JA_ERR_INVALID_ARG;
+  if (o == q || o == kv) return JA_ERR_INVALID_ARG;
   const ja::AttnLayout L = layout(p);
+  if (kv_bytes < (size_t)ja::prep_kv_bytes(L)) return JA_ERR_INVALID_ARG;
   ja::SplitPlan plan = ja::plan_fwd_bf16(L, device_cu_count());
   if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
     plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
-  return hip_status(ja::launch_fwd_bf16(L, q, k, v, rope, nullptr, o, lse, plan, workspace,
+  return hip_status(ja::launch_fwd_bf16(L, q, kv, rope, mask, o, lse, plan, workspace,
                                         static_cast<hipStream_t>(stream)));
 }
 
-ja_status joint_attn_fwd_bf16_block_sparse(const ja_params *p, const void *q, const void *k,
-                                           const void *v, const float *rope,
+ja_status joint_attn_fwd_bf16(const ja_params *p, const void *q, const void *kv,
+                              size_t kv_bytes, const float *rope, void *o, float *lse,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  return fwd_bf16_call(p, q, kv, kv_bytes, rope, nullptr, o, lse, workspace, workspace_bytes,
+                       stream);
+}
+
+ja_status joint_attn_fwd_bf16_block_sparse(const ja_params *p, const void *q, const void *kv,
+                                           size_t kv_bytes, const float *rope,
                                            const uint8_t *block_mask, void *o, float *lse,
                                            void *workspace, size_t workspace_bytes,
                                            void *stream) {
-  if (!p || !q || !k || !v || !o || !block_mask) return JA_ERR_INVALID_ARG;
-  const ja_status st = check_fwd_bf16(p);
-  if (st != JA_OK) return st;
-  if (p->seq_len > ja::fwd_bf16_sparse_max_seq()) return JA_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (rope && !aligned16(rope)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
-      (workspace && !aligned16(workspace)))
-    return JA_ERR_INVALID_ARG;
-  if (o == q || o == k || o == v) return JA_ERR_INVALID_ARG;
-  const ja::AttnLayout L = layout(p);
-  ja::SplitPlan plan = ja::plan_fwd_bf16(L, device_cu_count());
-  if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
-    plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
-  return hip_status(ja::launch_fwd_bf16(L, q, k, v, rope, block_mask, o, lse, plan, workspace,
-                                        static_cast<hipStream_t>(stream)));
+  if (!block_mask) return JA_ERR_INVALID_ARG;
+  if (p && p->seq_len > ja::fwd_bf16_sparse_max_seq()) return JA_ERR_UNSUPPORTED;
+  return fwd_bf16_call(p, q, kv, kv_bytes, rope, block_mask, o, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,

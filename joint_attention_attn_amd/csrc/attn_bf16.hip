@@ -18,18 +18,21 @@
 // fp32) is per lane, the row max needs one cross-half exchange and the O
 // rescale is one multiply per accumulator.
 //
-// K/V tiles of 32 keys are double-buffered in LDS.  K is staged row-major
-// (rotated in fp32 and rounded to bf16 on the way); V is staged transposed
-// (one row per head-dimension column, the keys of a row in the order in which
-// the P operand holds them), so both MFMA operands are single 16-byte LDS
-// reads.  Rows are padded so that the 16 lanes served together hit distinct
-// banks.
+// K and V arrive from the preparation pass (prep_kv.hip) as rotated K rows
+// and as V^T rows whose keys are in the order in which the P operand holds
+// them, so both MFMA operands are single 16-byte LDS reads.  Tiles of 32 keys
+// go from HBM straight into a four-stage LDS ring with buffer loads to LDS:
+// no registers, no VALU work, and the loads of a tile are issued three tiles
+// ahead of its use.  K rows are padded by one 16-byte granule (the lanes that
+// would fill a pad load a dummy chunk) and V^T rows are XOR-swizzled, so that
+// the 16 lanes served together by a fragment read hit distinct banks.
 //
 // Each wave runs Q K^T, softmax and P.V of a tile in turn; the three waves of
-// a SIMD overlap one another's MFMA, VALU and memory waits (a wave needs 160
-// VGPRs this way, against more than 168 for a wave that also overlaps the
-// next tile's Q K^T with its own softmax).  The next tiles' global loads are
-// issued one iteration ahead; one barrier per tile.
+// a SIMD overlap one another's MFMA, VALU and memory waits (a wave fits in
+// 168 VGPRs this way, which a wave that also overlapped the next tile's Q K^T
+// with its own softmax would not).  Inside Q K^T and P.V the LDS fragment
+// reads run four MFMAs ahead.  One barrier per tile; it waits only for the
+// loads of the next tile, never for the ones still in flight behind it.
 //
 // Block-sparse variant (the kernel half of the pages' sparse attention,
 // section "Quantized and sparse attention": attention restricted to the
@@ -49,9 +52,6 @@ namespace {
 #ifndef JA_BF16_WAVES
 #define JA_BF16_WAVES 12
 #endif
-#ifndef JA_BF16_STAGE_WAVES
-#define JA_BF16_STAGE_WAVES JA_BF16_WAVES
-#endif
 #ifndef JA_BF16_RW
 #define JA_BF16_RW 1
 #endif
@@ -60,7 +60,7 @@ constexpr int RW = JA_BF16_RW;      // 32-row query blocks per wave
 constexpr int BM = 32 * RW * NW;    // query rows per workgroup
 constexpr int BN = 32;              // keys per K/V tile
 constexpr int NT = 64 * NW;         // threads per workgroup
-constexpr int NS = 64 * JA_BF16_STAGE_WAVES;   // threads that stage K/V tiles
+constexpr int NSTAGE = 4;           // K/V tiles in the LDS ring
 // One workgroup per CU: 12 waves, three per SIMD, at most 168 VGPRs each.
 // Latency is hidden by the three waves of a SIMD rather than by deeper
 // software pipelining inside a wave (which needs more registers).
@@ -83,6 +83,9 @@ constexpr int kSparseMaxSeq = 1 << 20;
 // below 1, and the sums stay far below the fp32 range.
 constexpr float kRescaleLog2 = 24.f;
 
+// LDS fragment reads in flight ahead of the MFMA that consumes them.
+constexpr int kPrefetch = 4;
+
 // Buffer-resource word 3 for raw (unswizzled, unformatted 32-bit) buffer
 // access on gfx950: reads outside [0, num_records) return zeros (the check
 // covers the scalar offset too).
@@ -91,12 +94,13 @@ constexpr int kBufferFlags = 0x00020000;
 #define JA_INLINE __attribute__((always_inline))
 
 struct FwdArgs {
-  const bf16 *q, *k, *v;
+  const bf16 *q;
+  const bf16 *kr, *vt;      // prepared K and V^T (prep_kv.hip), S_pad keys
   const float2 *rope;
   bf16 *o;
   float *lse;
-  int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_ss, o_sh;
-  int S, H, B, n_qblk;
+  int64_t q_sb, q_ss, q_sh, o_sb, o_ss, o_sh;
+  int S, S_pad, H, B, n_qblk;
   float scale_log2;
   // Split of the last, partial round of workgroups over key ranges: the
   // first n_direct workgroups each own one (q-block, head, batch) item; the
@@ -124,44 +128,68 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS ring: NSTAGE stages of [K tile | V^T tile].  A K row is D bf16 plus a
+// 16-byte pad; the K part is rounded up to whole 1 KB loads (one wave's 64
+// lanes x 16 bytes), the slack taking the dummy chunks.  A V^T row is the 32
+// keys of one head-dimension column, 64 bytes, granule g stored at g ^ vswz.
+// Granule position of V^T row d's granule g is g ^ vswz(d): the 16 rows read
+// together by a fragment read then cover all 16 bank groups of 16 bytes.
+__host__ __device__ constexpr int vswz(int d) { return (d / 4) % 4; }
+
 template <int D>
 struct Lds {
-  static constexpr int KSTR = D + 8;        // bf16 per K row (16-byte pad)
-  static constexpr int VTSTR = BN + 8;      // bf16 per V^T row (16-byte pad)
-  static constexpr int KTILE = BN * KSTR;
-  static constexpr int VTILE = D * VTSTR;
-  static constexpr int BYTES = 2 * (KTILE + VTILE) * 2;
+  static constexpr int CH = D / 8;                    // 16-byte chunks per K row
+  static constexpr int KSTR = D + 8;                  // bf16 per K row
+  static constexpr int K_GRANULES = BN * (CH + 1);    // K part incl. pads
+  static constexpr int K_LOADS = (K_GRANULES + 63) / 64;
+  static constexpr int V_LOADS = D * (BN / 8) / 64;   // V^T part: 4 granules per row
+  static constexpr int LOADS = K_LOADS + V_LOADS;     // 1 KB loads per tile
+  static constexpr int KBYTES = K_LOADS * 1024;
+  static constexpr int STAGE = LOADS * 1024;
+  static constexpr int BYTES = NSTAGE * STAGE;
   // block-sparse variant: per-wave counts, then the key-block list
   static constexpr int LIST_OFFSET = BYTES + 64;
   static constexpr int sparse_bytes(int nkb) { return LIST_OFFSET + 4 * nkb; }
 };
 
-// Position, inside a 16-key group of a V^T row, of key k: the P operand of
-// lane half hf holds keys 4hf + {0..3} and 4hf + {8..11} of the group in its
-// eight slots, so V^T stores them at 8hf + slot.
-__host__ __device__ constexpr int vt_key_of_slot(int p) {
-  return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
+// vmcnt-only wait (gfx9 s_waitcnt encoding: expcnt and lgkmcnt at their
+// maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
 }
+
+// Workgroup barrier with no memory fence: a fence would make the compiler
+// wait for every load to LDS in flight, including the ones for later tiles.
+// The visibility that matters is ordered by hand (each wave waits for its own
+// loads of the next tile before the barrier); the empty asm statements keep
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+#define JA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 template <int D, bool ROPE, bool SPARSE>
 __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int CH = D / 8;                  // 16-byte chunks per K row
-  constexpr int K_CHUNKS = BN * CH;          // 16-byte K chunks per tile
-  constexpr int V_SLOTS = D * (BN / 8);      // 8-key V^T slots per tile
-  constexpr int KP = (K_CHUNKS + NS - 1) / NS;   // K chunks per staging thread
-  constexpr int VP = (V_SLOTS + NS - 1) / NS;    // V^T slots per staging thread
-  static_assert(K_CHUNKS % NS == 0 || K_CHUNKS < NS, "staging layout");
-  static_assert(V_SLOTS % NS == 0 || V_SLOTS < NS, "staging layout");
-  static_assert(NS % D == 0, "V^T slot groups must be wave-uniform");
-  constexpr int K_THREADS = K_CHUNKS < NS ? K_CHUNKS : NS;
-  constexpr int V_THREADS = V_SLOTS < NS ? V_SLOTS : NS;
-  constexpr int KSTR = Lds<D>::KSTR, VTSTR = Lds<D>::VTSTR;
+  constexpr int CH = Lds<D>::CH;
+  constexpr int KSTR = Lds<D>::KSTR;
+  constexpr int LOADS = Lds<D>::LOADS, K_LOADS = Lds<D>::K_LOADS;
+  static_assert(LOADS <= 2 * NW, "at most two tile loads per wave");
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-  auto Kbuf = [&](int buf) JA_INLINE { return smem + buf * Lds<D>::KTILE; };
-  auto Vbuf = [&](int buf) JA_INLINE { return smem + 2 * Lds<D>::KTILE + buf * Lds<D>::VTILE; };
+  auto Kst = [&](int st) JA_INLINE { return smem + st * (Lds<D>::STAGE / 2); };
+  auto Vst = [&](int st) JA_INLINE {
+    return smem + st * (Lds<D>::STAGE / 2) + Lds<D>::KBYTES / 2;
+  };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
 
   // XCD-aware placement: workgroups are dispatched round-robin over the 8
@@ -268,102 +296,54 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     }
   }
 
-  // ---- staging: global -> registers through buffer resources, then
-  //      registers -> LDS.  Per-lane offsets inside a tile are fixed; the
-  //      tile offset is scalar.  Each resource ends after row S-1, so rows
-  //      past the end of the sequence read as zeros (their scores are masked
-  //      and their P is 0). ----
-  const bf16 *kbase = a.k + b * a.k_sb + h * a.k_sh;
-  const bf16 *vbase = a.v + b * a.v_sb + h * a.v_sh;
+  // ---- tile loads: load j (0 <= j < LOADS) of a tile fills LDS bytes
+  //      [j KB, (j+1) KB) of its stage, lane i the 16 bytes at 16 i.  Loads
+  //      below K_LOADS carry the K rows: granule G = 64 j + i is chunk
+  //      G % (CH+1) of row G / (CH+1), and pad or slack granules take a dummy
+  //      chunk.  The others carry V^T rows, 16 per load: row
+  //      d = 16 (j - K_LOADS) + i / 4, position i % 4 holding granule
+  //      (i % 4) ^ vswz(d) of the row.  Wave w issues loads w and w + NW.
+  //      The lane offsets are fixed; the tile offset is scalar. ----
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16 *>(kbase), 0, (int)(((int64_t)(S - 1) * a.k_ss + D) * 2), kBufferFlags);
+      const_cast<bf16 *>(a.kr + (int64_t)bh * a.S_pad * D), 0, a.S_pad * D * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16 *>(vbase), 0, (int)(((int64_t)(S - 1) * a.v_ss + D) * 2), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float2 *>(a.rope), 0, ROPE ? S * D * 4 : 0, kBufferFlags);
-
-  // K: pass p of a staging thread stages chunk st_c of row st_r + p * (NS / CH)
-  const int st_r = tid / CH, st_c = tid % CH;
-  const int koff = (int)(st_r * a.k_ss * 2) + st_c * 16;
-  const int toff = st_r * D * 4 + st_c * 32;
-  const int ktile_bytes = (int)(BN * a.k_ss * 2);
-  const int kpass_bytes = (int)((NS / CH) * a.k_ss * 2);
-  // V^T: pass p of a thread stages column vd, slots 8 vc .. 8 vc + 7 with
-  // vc = tid / D + p * (NS / D) (wave-uniform)
-  const int vd = tid % D;
-  const int vc0 = __builtin_amdgcn_readfirstlane(tid / D);
-  const int vrow_bytes = (int)(a.v_ss * 2);
-  u32x4 kreg[KP];
-  float4 treg[KP][2];
-  uint32_t vreg[VP][8];
-  auto load_k = [&](int t) JA_INLINE {
-    if (K_THREADS < NT && tid >= K_THREADS) return;
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-      kreg[p] = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(
-          krs, koff, t * ktile_bytes + p * kpass_bytes, 0));
-      if constexpr (ROPE) {
-        const int tt = (t * BN + p * (NS / CH)) * D * 4;
-        treg[p][0] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff, tt, 0));
-        treg[p][1] = bit_cast<float4>(__builtin_amdgcn_raw_buffer_load_b128(trs, toff + 16, tt, 0));
-      }
+      const_cast<bf16 *>(a.vt + (int64_t)bh * D * a.S_pad), 0, a.S_pad * D * 2, kBufferFlags);
+  auto load_offset = [&](int j) JA_INLINE -> int {
+    if (j < K_LOADS) {
+      const int g = 64 * j + lane;
+      const int r = g / (CH + 1), c = g % (CH + 1);
+      return (r < BN && c < CH) ? (r * D + 8 * c) * 2 : 0;
     }
+    const int d = 16 * (j - K_LOADS) + lane / 4;
+    return (d * a.S_pad + 8 * ((lane % 4) ^ vswz(d))) * 2;
   };
-  auto load_v = [&](int t) JA_INLINE {
-    if (V_THREADS < NT && tid >= V_THREADS) return;
-#pragma unroll
-    for (int p = 0; p < VP; ++p) {
-      const int vc = vc0 + p * (NS / D);
-      const int key0 = t * BN + 16 * (vc >> 1);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        vreg[p][j] = __builtin_amdgcn_raw_buffer_load_b16(
-            vrs, vd * 2, (key0 + vt_key_of_slot(8 * (vc & 1) + j)) * vrow_bytes, 0);
-    }
+  const int j0 = wave, j1 = wave + NW;
+  const int voff0 = j0 < LOADS ? load_offset(j0) : 0;
+  const int voff1 = j1 < LOADS ? load_offset(j1) : 0;
+  auto issue_one = [&](int j, int voff, int t, int st) JA_INLINE {
+    char *dst = reinterpret_cast<char *>(smem) + st * Lds<D>::STAGE + j * 1024;
+    if (j < K_LOADS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, JA_LDS_PTR(dst), 16, voff, t * (BN * D * 2), 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, JA_LDS_PTR(dst), 16, voff, t * (BN * 2), 0, 0);
   };
-  // The empty asm statements in the stores pin the use of the loaded
-  // registers there: otherwise the compiler moves the rotation and packing
-  // (and with them the wait for the loads) up to just after the previous
-  // barrier, where every wave would wait for memory at the same moment.
-  auto store_k = [&](int buf) JA_INLINE {
-    if (K_THREADS < NT && tid >= K_THREADS) return;
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-      asm volatile("" : "+v"(kreg[p]));
-      if constexpr (ROPE) {
-        u32x4 c0 = bit_cast<u32x4>(treg[p][0]), c1 = bit_cast<u32x4>(treg[p][1]);
-        asm volatile("" : "+v"(c0), "+v"(c1));
-        treg[p][0] = bit_cast<float4>(c0);
-        treg[p][1] = bit_cast<float4>(c1);
-      }
-      u32x4 kw = kreg[p];
-      if constexpr (ROPE) {
-        kw.x = rope_pair_bf16(kw.x, make_float2(treg[p][0].x, treg[p][0].y));
-        kw.y = rope_pair_bf16(kw.y, make_float2(treg[p][0].z, treg[p][0].w));
-        kw.z = rope_pair_bf16(kw.z, make_float2(treg[p][1].x, treg[p][1].y));
-        kw.w = rope_pair_bf16(kw.w, make_float2(treg[p][1].z, treg[p][1].w));
-      }
-      *reinterpret_cast<u32x4 *>(Kbuf(buf) + (st_r + p * (NS / CH)) * KSTR + st_c * 8) = kw;
-    }
+  // loads of key tile t into stage st
+  auto issue = [&](int t, int st) JA_INLINE {
+    if (j0 < LOADS) issue_one(j0, voff0, t, st);
+    if (j1 < LOADS) issue_one(j1, voff1, t, st);
   };
-  auto store_v = [&](int buf) JA_INLINE {
-    if (V_THREADS < NT && tid >= V_THREADS) return;
-#pragma unroll
-    for (int p = 0; p < VP; ++p) {
-      const int vc = vc0 + p * (NS / D);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(vreg[p][j]));
-      u32x4 w;
-      w.x = vreg[p][0] | (vreg[p][1] << 16);
-      w.y = vreg[p][2] | (vreg[p][3] << 16);
-      w.z = vreg[p][4] | (vreg[p][5] << 16);
-      w.w = vreg[p][6] | (vreg[p][7] << 16);
-      *reinterpret_cast<u32x4 *>(Vbuf(buf) + vd * VTSTR + 8 * vc) = w;
-    }
+  // wait until at most `ahead` later tiles' loads of this wave are in flight
+  auto wait_tiles = [&]<int AHEAD>() JA_INLINE {
+    if (j1 < LOADS)
+      wait_vmcnt<2 * AHEAD>();
+    else
+      wait_vmcnt<AHEAD>();
   };
 
-  // ---- S^T = K . Q^T for this wave's 32 queries and the 32 keys of a tile,
-  //      in two halves over the head dimension ----
+  // ---- S^T = K . Q^T for this wave's 32 queries and the 32 keys of a tile.
+  //      The K fragments are read kPrefetch steps ahead of their MFMA (left
+  //      to itself the compiler reuses one register and every MFMA waits a
+  //      full LDS latency); the scheduling barriers keep that order. ----
   auto qk = [&]<int KK0, int KK1>(int buf, f32x16 (&sacc)[RW]) JA_INLINE {
     if constexpr (KK0 == 0) {
 #pragma unroll
@@ -371,18 +351,30 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[r][i] = 0.f;
     }
-    const bf16 *krow = Kbuf(buf) + l32 * KSTR + 8 * hf;
+    const bf16 *krow = Kst(buf) + l32 * KSTR + 8 * hf;
+    bf16x8 kf[kPrefetch];
+#pragma unroll
+    for (int j = 0; j < kPrefetch && KK0 + j < KK1; ++j)
+      kf[j] = *reinterpret_cast<const bf16x8 *>(krow + 16 * (KK0 + j));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = KK0; kk < KK1; ++kk) {
-      const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(krow + 16 * kk);
 #pragma unroll
       for (int r = 0; r < RW; ++r)
-        sacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[r][kk], sacc[r], 0, 0, 0);
+        sacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[(kk - KK0) % kPrefetch], qreg[r][kk],
+                                                          sacc[r], 0, 0, 0);
+      if (kk + kPrefetch < KK1)
+        kf[(kk - KK0) % kPrefetch] = *reinterpret_cast<const bf16x8 *>(krow + 16 * (kk + kPrefetch));
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // ---- O^T += V^T . P^T ; P operand slot j of half hf (key group g) is key
-  //      16g + 4hf + (j<4 ? j : j+4), which V^T stores at 16g + 8hf + j ----
+  //      16g + 4hf + (j<4 ? j : j+4), which V^T stores in logical granule
+  //      2g + hf of its row.  Step st covers head-dimension block st/2 and key
+  //      group st%2; its V^T fragment is read kPrefetch steps ahead, as in
+  //      Q K^T.  Row l32 of every 32-row block has the same swizzle, so the
+  //      two granules of a lane sit at two fixed offsets. ----
   f32x16 oacc[RW][D / 32];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -391,16 +383,24 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[r][db][i] = 0.f;
   auto pv = [&](const bf16x8 (&pb)[RW][2], int buf) JA_INLINE {
-    const bf16 *vt = Vbuf(buf) + l32 * VTSTR + 8 * hf;
+    const int vy = hf ^ vswz(l32);
+    const bf16 *vt0 = Vst(buf) + l32 * BN + 8 * vy;          // key group 0
+    const bf16 *vt1 = Vst(buf) + l32 * BN + 8 * (vy ^ 2);    // key group 1
+    constexpr int NV = 2 * (D / 32);
+    auto vaddr = [&](int st) JA_INLINE { return (st % 2 ? vt1 : vt0) + 32 * BN * (st / 2); };
+    bf16x8 vf[kPrefetch];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int j = 0; j < kPrefetch && j < NV; ++j) vf[j] = *reinterpret_cast<const bf16x8 *>(vaddr(j));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8 *>(vt + 32 * db * VTSTR + 16 * g);
+    for (int st = 0; st < NV; ++st) {
 #pragma unroll
-        for (int r = 0; r < RW; ++r)
-          oacc[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[r][g], oacc[r][db], 0, 0, 0);
-      }
+      for (int r = 0; r < RW; ++r)
+        oacc[r][st / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % kPrefetch], pb[r][st % 2],
+                                                                  oacc[r][st / 2], 0, 0, 0);
+      if (st + kPrefetch < NV) vf[st % kPrefetch] = *reinterpret_cast<const bf16x8 *>(vaddr(st + kPrefetch));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   float m_run[RW], l_run[RW];
@@ -480,48 +480,44 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     for (int r = 0; r < RW; ++r) l_run[r] += lt[r];
   };
 
-  // ---- loop over the key tiles t0 .. t1-1 (local index i = t - t0).  Local
-  //      tile i lives in K buffer i%2 and V buffer i%2.  Iteration i computes
-  //      Q K^T, the softmax and P.V of tile i, then rotates and stores K and V
-  //      of tile i+1 (into the buffers read by iteration i-1) and issues the
-  //      global loads of tile i+2, which have a whole iteration to arrive; a
-  //      barrier closes the iteration. ----
+  // ---- loop over the workgroup's tiles (local index i, list position
+  //      t0 + i).  Tile i lives in stage i % NSTAGE.  Iteration i first issues
+  //      the loads of tile i + NSTAGE - 1 into the stage that iteration i - 1
+  //      read, then computes Q K^T, the softmax and P.V of tile i; before the
+  //      barrier that closes it, each wave waits for its own loads of tile
+  //      i + 1 only. ----
   const int nt = t1 - t0;
   // a dense workgroup always has at least one tile; a sparse one may have none
   const bool any_tile = !SPARSE || nt > 0;
   if (any_tile) {
-    load_k(tile_of(t0));
-    load_v(tile_of(t0));
-    store_k(0);
-    store_v(0);
-    if (nt > 1) {
-      load_k(tile_of(t0 + 1));
-      load_v(tile_of(t0 + 1));
-    }
-    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NSTAGE - 1; ++p)
+      if (p < nt) issue(tile_of(t0 + p), p);
+    wait_vmcnt<0>();
+    tile_barrier();
   }
   f32x16 sacc[RW];
   // NEXT: tile i+1 exists.  Only the last tile of the sequence can be partial
   // (masking a full tile changes nothing), and it is always the last of the
   // workgroup's tiles.
   auto iteration = [&]<bool NEXT>(int i) JA_INLINE {
-    const int t = tile_of(t0 + i);
-    if (kept(t0 + i)) {
-      qk.template operator()<0, D / 16>(i & 1, sacc);
+    const int x = t0 + i;
+    const bool ahead = i + NSTAGE - 1 < nt;
+    if (ahead) issue(tile_of(x + NSTAGE - 1), (i + NSTAGE - 1) % NSTAGE);
+    if (kept(x)) {
+      const int t = tile_of(x);
+      qk.template operator()<0, D / 16>(i % NSTAGE, sacc);
       bf16x8 pb[RW][2];
       softmax.template operator()<!NEXT>(sacc, t * BN, pb);
-      pv(pb, i & 1);
+      pv(pb, i % NSTAGE);
     }
     if constexpr (NEXT) {
-      store_k((i + 1) & 1);
-      store_v((i + 1) & 1);
-      if (i + 2 < nt) {
-        const int t2 = tile_of(t0 + i + 2);
-        load_k(t2);
-        load_v(t2);
-      }
+      if (ahead)
+        wait_tiles.template operator()<NSTAGE - 2>();
+      else
+        wait_vmcnt<0>();
+      tile_barrier();
     }
-    __syncthreads();
   };
   for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<true>(i);
   if (any_tile) iteration.template operator()<false>(nt - 1);
@@ -607,22 +603,24 @@ SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu) {
 
 int fwd_bf16_sparse_max_seq() { return kSparseMaxSeq; }
 
-hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
-                           const void *v, const float *rope, const uint8_t *mask,
-                           void *o, float *lse, const SplitPlan &plan, void *workspace,
-                           hipStream_t st) {
+hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
+                           const float *rope, const uint8_t *mask, void *o, float *lse,
+                           const SplitPlan &plan, void *workspace, hipStream_t st) {
+  // kv: prepared K | prepared V^T (prep_kv.hip)
+  const int64_t prep_elems = (int64_t)L.B * L.H * prep_pad(L.S) * L.D;
+  const bf16 *kr = static_cast<const bf16 *>(kv);
+  const bf16 *vt = kr + prep_elems;
   FwdArgs a;
   a.q = static_cast<const bf16 *>(q);
-  a.k = static_cast<const bf16 *>(k);
-  a.v = static_cast<const bf16 *>(v);
+  a.kr = kr;
+  a.vt = vt;
   a.rope = reinterpret_cast<const float2 *>(rope);
   a.o = static_cast<bf16 *>(o);
   a.lse = lse;
   a.q_sb = L.q_sb; a.q_ss = L.q_ss; a.q_sh = L.q_sh;
-  a.k_sb = L.k_sb; a.k_ss = L.k_ss; a.k_sh = L.k_sh;
-  a.v_sb = L.v_sb; a.v_ss = L.v_ss; a.v_sh = L.v_sh;
   a.o_sb = L.o_sb; a.o_ss = L.o_ss; a.o_sh = L.o_sh;
   a.S = L.S;
+  a.S_pad = prep_pad(L.S);
   a.H = L.H;
   a.B = L.B;
   a.n_qblk = (L.S + BM - 1) / BM;

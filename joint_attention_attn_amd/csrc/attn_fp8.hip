@@ -66,12 +66,6 @@ struct Fp8Args {
   int n_rep, n_pad;
 };
 
-// Position, inside a 16-key group of a bf16 V^T row, of the key that P operand
-// slot p holds (lane half p/8): keys 4*(p/8) + {0..3, 8..11}.
-__host__ __device__ constexpr int vt_key_of_slot(int p) {
-  return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
-}
-
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   // format 0 = fp8 e4m3 for both operands, no block scaling
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);

@@ -69,6 +69,15 @@ __device__ __forceinline__ u32x4 rope_chunk_bf16(u32x4 w, const float2 *cs) {
   return r;
 }
 
+// Key held by slot p (0..15) of a 16-key group in the P operand of the P.V
+// MFMA: the S^T accumulator gives lane half hf = p / 8 the keys
+// 4hf + {0..3} and 4hf + {8..11} of the group, in that order.  V^T rows store
+// the keys of each group in this slot order so that one 16-byte read is the
+// matching A operand.
+__host__ __device__ constexpr int vt_key_of_slot(int p) {
+  return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

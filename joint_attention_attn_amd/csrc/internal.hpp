@@ -42,13 +42,21 @@ hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
                               const SplitWorkspace &ws, int block_rows, float m_scale,
                               void *o, float *lse, hipStream_t st);
 
+// K/V preparation of the BF16 forward (prep_kv.hip): one buffer of
+// prep_kv_bytes(L) holding rotated K [B*H][S_pad][D], then V^T [B*H][D][S_pad],
+// S_pad = prep_pad(S).
+int prep_pad(int S);
+int64_t prep_kv_bytes(const AttnLayout &L);
+hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v,
+                               const float *rope, void *kv, hipStream_t st);
+
 SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu);
-// mask: NULL = dense; else the block mask of the block-sparse variant,
-// uint8 [B][H][ceil(S/128)][ceil(S/64)] (nonzero = keep).
-hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *k,
-                           const void *v, const float *rope, const uint8_t *mask,
-                           void *o, float *lse, const SplitPlan &plan, void *workspace,
-                           hipStream_t st);
+// kv: the prepared K/V buffer; mask: NULL = dense, else the block mask of the
+// block-sparse variant, uint8 [B][H][ceil(S/128)][ceil(S/64)] (nonzero =
+// keep).  workspace: the split's partial results (plan.ws_bytes).
+hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
+                           const float *rope, const uint8_t *mask, void *o, float *lse,
+                           const SplitPlan &plan, void *workspace, hipStream_t st);
 int fwd_bf16_sparse_max_seq();   // longest sequence of the block-sparse variant
 
 hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,

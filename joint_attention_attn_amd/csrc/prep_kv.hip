@@ -1,0 +1,119 @@
+// K/V preparation pass of the BF16 forward: K rotated once per (batch, head)
+// and V written transposed, both in the layouts that the attention kernel
+// copies into LDS tile by tile without touching them.
+//
+// RoPE on K ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
+// Blackwell GPUs", section "GEMM kernel optimization", where it is fused into
+// the epilogue that produces Q and K): here it is fused into this pass's
+// single load of K, with the same fp32 pair rotation and bf16 rounding as the
+// Q load of the attention kernel.  Every workgroup of the attention kernel
+// reads each K tile once, so rotating there would redo the rotation (and its
+// table reads) once per query block.
+//
+// Layout of the prepared buffer, Kr then Vt (S_pad = S rounded up to 64
+// keys; rows and columns past S are 0):
+//   Kr [B*H][S_pad][D]  rotated K, one row per key;
+//   Vt [B*H][D][S_pad]  V transposed, one row per head-dimension column; in
+//                       every 16-key group the keys are stored in the order
+//                       in which the attention kernel's P operand holds them
+//                       (position p holds key vt_key_of_slot(p)).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace ja {
+
+namespace {
+
+constexpr int PT = 256;       // threads per workgroup
+constexpr int PK = 64;        // keys per workgroup
+
+struct PrepArgs {
+  const bf16 *k, *v;
+  const float2 *rope;
+  bf16 *kr, *vt;
+  int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
+  int S, S_pad, H;
+};
+
+template <int D, bool ROPE>
+__global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int VSTR = D + 8;        // bf16 per staged V row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) bf16 vs[PK * VSTR];
+  const int tid = threadIdx.x;
+  const int nkb = a.S_pad / PK;
+  const int k0 = (blockIdx.x % nkb) * PK;
+  const int bh = blockIdx.x / nkb;
+  const int b = bh / a.H, h = bh % a.H;
+  const bf16 *kb = a.k + b * a.k_sb + h * a.k_sh;
+  const bf16 *vb = a.v + b * a.v_sb + h * a.v_sh;
+  bf16 *krb = a.kr + (int64_t)bh * a.S_pad * D;
+  bf16 *vtb = a.vt + (int64_t)bh * D * a.S_pad;
+
+  // K: rotate and copy; V: stage row-major in LDS
+#pragma unroll
+  for (int idx = tid; idx < PK * CH; idx += PT) {
+    const int r = idx / CH, c = idx % CH;
+    const int key = k0 + r;
+    u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
+    if (key < a.S) {
+      kw = *reinterpret_cast<const u32x4 *>(kb + (int64_t)key * a.k_ss + 8 * c);
+      if constexpr (ROPE) kw = rope_chunk_bf16(kw, a.rope + (int64_t)key * (D / 2) + 4 * c);
+      vw = *reinterpret_cast<const u32x4 *>(vb + (int64_t)key * a.v_ss + 8 * c);
+    }
+    *reinterpret_cast<u32x4 *>(krb + (int64_t)key * D + 8 * c) = kw;
+    *reinterpret_cast<u32x4 *>(vs + r * VSTR + 8 * c) = vw;
+  }
+  __syncthreads();
+
+  // V^T: row d, 8 keys per 16-byte chunk, in P-slot order within 16-key groups
+#pragma unroll
+  for (int idx = tid; idx < D * (PK / 8); idx += PT) {
+    const int d = idx / (PK / 8), j = idx % (PK / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int p0 = 8 * j + 2 * e, p1 = p0 + 1;
+      const int r0 = 16 * (p0 / 16) + vt_key_of_slot(p0 % 16);
+      const int r1 = 16 * (p1 / 16) + vt_key_of_slot(p1 % 16);
+      const uint32_t lo = bit_cast<uint16_t>(vs[r0 * VSTR + d]);
+      const uint32_t hi = bit_cast<uint16_t>(vs[r1 * VSTR + d]);
+      w[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4 *>(vtb + (int64_t)d * a.S_pad + k0 + 8 * j) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+}  // namespace
+
+int prep_pad(int S) { return (S + PK - 1) / PK * PK; }
+
+int64_t prep_kv_bytes(const AttnLayout &L) {
+  return 2 * (int64_t)L.B * L.H * prep_pad(L.S) * L.D * 2;
+}
+
+hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v,
+                               const float *rope, void *kv, hipStream_t st) {
+  PrepArgs a;
+  a.k = static_cast<const bf16 *>(k);
+  a.v = static_cast<const bf16 *>(v);
+  a.rope = reinterpret_cast<const float2 *>(rope);
+  a.kr = static_cast<bf16 *>(kv);
+  a.vt = a.kr + (int64_t)L.B * L.H * prep_pad(L.S) * L.D;
+  a.k_sb = L.k_sb; a.k_ss = L.k_ss; a.k_sh = L.k_sh;
+  a.v_sb = L.v_sb; a.v_ss = L.v_ss; a.v_sh = L.v_sh;
+  a.S = L.S;
+  a.S_pad = prep_pad(L.S);
+  a.H = L.H;
+  const dim3 grid((unsigned)((int64_t)(a.S_pad / PK) * L.B * L.H));
+  const bool r = rope != nullptr;
+  if (L.D == 64)
+    hipLaunchKernelGGL((r ? prep_kv_bf16_kernel<64, true> : prep_kv_bf16_kernel<64, false>),
+                       grid, dim3(PT), 0, st, a);
+  else
+    hipLaunchKernelGGL((r ? prep_kv_bf16_kernel<128, true> : prep_kv_bf16_kernel<128, false>),
+                       grid, dim3(PT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace ja

@@ -48,11 +48,14 @@ def _p(b=1, s=80, h=2, d=64):
     return p
 
 
-def _fwd(lib, p, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, rope=None, lse=None,
-         ws=None, ws_bytes=0):
+KV_BYTES = 1 << 30   # stand-in size of the prepared K/V buffer
+
+
+def _fwd(lib, p, q=FAKE, kv=FAKE + 0x1000, o=FAKE + 0x3000, rope=None, lse=None,
+         ws=None, ws_bytes=0, kv_bytes=KV_BYTES):
     vp = ctypes.c_void_p
-    return lib.joint_attn_fwd_bf16(ctypes.byref(p) if p is not None else None, vp(q), vp(k),
-                                   vp(v), vp(rope), vp(o), vp(lse), vp(ws), ws_bytes, None)
+    return lib.joint_attn_fwd_bf16(ctypes.byref(p) if p is not None else None, vp(q), vp(kv),
+                                   kv_bytes, vp(rope), vp(o), vp(lse), vp(ws), ws_bytes, None)
 
 
 @pytest.mark.parametrize("mutate,expect", [
@@ -78,7 +81,9 @@ def test_fwd_bf16_rejects_bad_pointers(lib):
     assert _fwd(lib, None) == ja.JA_ERR_INVALID_ARG
     assert _fwd(lib, _p(), q=0) == ja.JA_ERR_INVALID_ARG
     assert _fwd(lib, _p(), o=0) == ja.JA_ERR_INVALID_ARG
-    assert _fwd(lib, _p(), k=FAKE + 2) == ja.JA_ERR_INVALID_ARG         # misaligned
+    assert _fwd(lib, _p(), kv=FAKE + 2) == ja.JA_ERR_INVALID_ARG        # misaligned
+    assert _fwd(lib, _p(), kv=0) == ja.JA_ERR_INVALID_ARG
+    assert _fwd(lib, _p(), kv_bytes=1024) == ja.JA_ERR_INVALID_ARG      # too small
     assert _fwd(lib, _p(), rope=FAKE + 8) == ja.JA_ERR_INVALID_ARG      # misaligned table
     assert _fwd(lib, _p(), lse=FAKE + 2) == ja.JA_ERR_INVALID_ARG
     assert _fwd(lib, _p(), o=FAKE) == ja.JA_ERR_INVALID_ARG             # o aliases q
@@ -150,8 +155,8 @@ def test_block_sparse_validation(lib):
 
     def call(p, mask=FAKE + 0x5000, o=FAKE + 0x3000, q=FAKE):
         return lib.joint_attn_fwd_bf16_block_sparse(
-            ctypes.byref(p) if p is not None else None, vp(q), vp(FAKE + 0x1000),
-            vp(FAKE + 0x2000), None, vp(mask), vp(o), None, None, 0, None)
+            ctypes.byref(p) if p is not None else None, vp(q), vp(FAKE + 0x1000), KV_BYTES,
+            None, vp(mask), vp(o), None, None, 0, None)
 
     assert call(None) == ja.JA_ERR_INVALID_ARG
     assert call(_p(), mask=0) == ja.JA_ERR_INVALID_ARG                  # mask required
@@ -162,3 +167,24 @@ def test_block_sparse_validation(lib):
     assert call(bad) == ja.JA_ERR_UNSUPPORTED
     assert call(_p(s=(1 << 20) + 1)) == ja.JA_ERR_UNSUPPORTED           # longest sequence
     assert ja.block_mask_shape(2, 300, 3) == (2, 3, 3, 5)
+
+
+def test_prep_kv_validation(lib):
+    vp = ctypes.c_void_p
+    p = _p(s=300, h=2, d=64)
+    need = lib.joint_attn_prep_kv_bf16_bytes(ctypes.byref(p))
+    # rotated K and transposed V: 2 tensors x B*H*ceil(S/64)*64*D bf16
+    assert need == 2 * 1 * 2 * 320 * 64 * 2
+    assert lib.joint_attn_prep_kv_bf16_bytes(None) == 0
+    f = lib.joint_attn_prep_kv_bf16
+    assert f(None, vp(FAKE), vp(FAKE), None, vp(FAKE + 0x4000), need, None) == ja.JA_ERR_INVALID_ARG
+    assert f(ctypes.byref(p), vp(FAKE), vp(FAKE + 0x1000), None, vp(FAKE + 0x4000), need - 16,
+             None) == ja.JA_ERR_INVALID_ARG                                # too small
+    assert f(ctypes.byref(p), vp(FAKE + 2), vp(FAKE + 0x1000), None, vp(FAKE + 0x4000), need,
+             None) == ja.JA_ERR_INVALID_ARG                                # misaligned
+    assert f(ctypes.byref(p), vp(FAKE), vp(0), None, vp(FAKE + 0x4000), need,
+             None) == ja.JA_ERR_INVALID_ARG
+    bad = _p()
+    bad.head_dim = 96
+    assert f(ctypes.byref(bad), vp(FAKE), vp(FAKE + 0x1000), None, vp(FAKE + 0x4000), need,
+             None) == ja.JA_ERR_UNSUPPORTED

@@ -203,3 +203,37 @@ def test_split_last_round_parity():
     # about 2^-9 relative in the row sum, a few 1e-3 in the LSE.
     assert rel_l2(out.cpu(), out_ns.cpu()) <= 2e-3
     assert max_abs(lse, lse_ns) <= 1e-2
+
+
+def _slot_key(p):
+    # key of P-operand slot p in a 16-key group (the V^T order the header documents)
+    return 4 * (p // 8) + (p % 8 if p % 8 < 4 else p % 8 + 4)
+
+
+@pytest.mark.parametrize("s,d,strided", [(200, 64, False), (1037, 128, False), (130, 128, True)])
+def test_prep_kv_bit_exact(s, d, strided):
+    # rotated K equals the oracle's bf16-rounded rotation bit for bit; V^T is
+    # V transposed in the documented key order; padding is zero
+    w = synth.Workload("prep", 2, 3, d, n_text=s, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=21)
+    pos = np.random.default_rng(s).integers(0, 300, size=(s, 2)).astype(np.int32)
+    if strided:
+        kd, vd = (t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3) for t in (k, v))
+    else:
+        kd, vd = k.to(DEV), v.to(DEV)
+    rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), d)
+    _say(f"prep kv S={s} D={d} strided={strided}")
+    kv = ja.prep_kv_bf16(kd, vd, rope).cpu()
+    s_pad = (s + 63) // 64 * 64
+    n = 2 * 3 * s_pad * d
+    kr = kv[: 2 * n].view(torch.bfloat16).view(2, 3, s_pad, d)
+    vt = kv[2 * n:].view(torch.bfloat16).view(2, 3, d, s_pad)
+    table = oracle.rope_table_fp32(pos, d)
+    kref = torch.from_numpy(oracle.rotate_fp32(k.float().numpy(), table)).to(torch.bfloat16)
+    assert torch.equal(kr[:, :, :s].view(torch.int16), kref.permute(0, 2, 1, 3).contiguous().view(torch.int16))
+    assert not kr[:, :, s:].view(torch.int16).any()
+    order = torch.tensor([16 * (j // 16) + _slot_key(j % 16) for j in range(s_pad)])
+    vpad = torch.zeros((2, s_pad, 3, d), dtype=torch.bfloat16)
+    vpad[:, :s] = v
+    vref = vpad[:, order].permute(0, 2, 3, 1)            # [B, H, D, S_pad]
+    assert torch.equal(vt.view(torch.int16), vref.contiguous().view(torch.int16))
