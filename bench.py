@@ -180,9 +180,11 @@ def main() -> int:
                 "traffic": _traffic_for_current_kernel("attn_fwd_bf16_t2i_2048_traffic.txt",
                                                        "attn_bf16.hip"),
                 "kernel": "attn_fwd_bf16_kernel<128, true, false> (+ merge_split_kernel of the "
-                          "split last round)",
+                          "split last round); K/V preparation in prep_kv",
                 "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4),
                 "prep_kv": {"ms": round(p_avg, 4),
+                            "traffic": _traffic_for_current_kernel(
+                                "prep_kv_bf16_t2i_2048_traffic.txt", "prep_kv.hip"),
                             "gbs": round(prep_bytes / (p_avg * 1e-3) / 1e9, 1),
                             "frac_of_hbm": round(prep_bytes / (p_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                                  4)}}
