@@ -19,7 +19,9 @@ FLUX 3 Image Klein on NVIDIA Blackwell GPUs"):
   v_dtype fp8), and the repair of the tokens with the largest quantization
   error (same section, VC-Attention FP8 with vc_repair_budget);
 * block-sparse attention on a given block mask (same section: Sol-Attention
-  runs on a general block-sparse attention kernel).
+  runs on a general block-sparse attention kernel);
+* RMS normalization of Q and K before RoPE (section "GEMM kernel
+  optimization": query/key normalization in the QKV epilogue).
 
 The pages state none of the arithmetic; the readings taken where they are
 silent (2D-axial frequencies, pair convention, bf16 rounding point of the
@@ -32,6 +34,7 @@ here is pinned by tests in `tests/test_oracle_*.py` against closed forms,
 brute force, exact rational arithmetic and library routines.
 """
 from .rope import rope_angles, apply_rope, rope_table_fp32, rotate_fp32, fma32
+from .norm import (NORM_EPS, sum_squares_fp32, rms_norm_fp32, rms_norm, prologue_fp32)
 from .attention import (attention, joint_attention, brute_force_attention,
                         block_sparse_attention, QUERY_BLOCK, KEY_BLOCK)
 from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, quant_rope_fp8,
@@ -40,6 +43,7 @@ from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, quant_rope_fp8,
 
 __all__ = [
     "rope_angles", "apply_rope", "rope_table_fp32", "rotate_fp32", "fma32",
+    "NORM_EPS", "sum_squares_fp32", "rms_norm_fp32", "rms_norm", "prologue_fp32",
     "attention", "joint_attention", "brute_force_attention", "block_sparse_attention",
     "QUERY_BLOCK", "KEY_BLOCK",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "quant_rope_fp8",

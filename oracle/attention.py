@@ -23,6 +23,7 @@ import torch
 import numpy as _np
 
 from .rope import apply_rope, rope_table_fp32, rotate_fp32
+from .norm import prologue_fp32
 
 _CHUNK = 2048
 
@@ -63,7 +64,7 @@ def attention(q, k, v, scale: float | None = None, rows=None):
 
 def joint_attention(q, k, v, pos=None, theta: float = 10000.0,
                     scale: float | None = None, round_rotated: bool = True,
-                    rows=None):
+                    rows=None, norm=None):
     """The bf16 hot path's reference: RoPE on Q and K, then attention.
 
     Reading of where the rotated Q/K are rounded: the pages place RoPE in the
@@ -74,10 +75,16 @@ def joint_attention(q, k, v, pos=None, theta: float = 10000.0,
     bf16 code) and rounded once to bf16 (round to nearest even) before
     Q K^T; attention itself is fp64.  round_rotated=False rotates in fp64
     and keeps the result unrounded, for information.  pos=None: no RoPE.
+    norm=(g_q, g_k, eps): Q and K are first RMS-normalized (`oracle.norm`),
+    in fp32 and without a rounding of their own, then rotated and rounded.
     """
     q = torch.as_tensor(q)
     k = torch.as_tensor(k)
-    if pos is not None:
+    if norm is not None:
+        g_q, g_k, eps = norm
+        q = torch.from_numpy(prologue_fp32(q, pos, theta, g_q, eps)).to(torch.bfloat16)
+        k = torch.from_numpy(prologue_fp32(k, pos, theta, g_k, eps)).to(torch.bfloat16)
+    elif pos is not None:
         if round_rotated:
             table = rope_table_fp32(pos, q.shape[-1], theta)
             q = torch.from_numpy(rotate_fp32(q.to(torch.float32).numpy(), table)).to(torch.bfloat16)
@@ -125,7 +132,7 @@ KEY_BLOCK = 64
 
 def block_sparse_attention(q, k, v, mask, pos=None, theta: float = 10000.0,
                            scale: float | None = None, rows=None,
-                           q_block: int = QUERY_BLOCK, k_block: int = KEY_BLOCK):
+                           q_block: int = QUERY_BLOCK, k_block: int = KEY_BLOCK, norm=None):
     """Joint attention restricted by a block mask (the kernel half of the
     pages' block-sparse attention, section "Quantized and sparse attention":
     Sol-Attention runs on a general block-sparse attention kernel; how its
@@ -140,10 +147,10 @@ def block_sparse_attention(q, k, v, mask, pos=None, theta: float = 10000.0,
     """
     q = torch.as_tensor(q)
     k = torch.as_tensor(k)
-    if pos is not None:
-        table = rope_table_fp32(pos, q.shape[-1], theta)
-        q = torch.from_numpy(rotate_fp32(q.to(torch.float32).numpy(), table)).to(torch.bfloat16)
-        k = torch.from_numpy(rotate_fp32(k.to(torch.float32).numpy(), table)).to(torch.bfloat16)
+    if norm is not None or pos is not None:
+        g_q, g_k, eps = norm if norm is not None else (None, None, 0.0)
+        q = torch.from_numpy(prologue_fp32(q, pos, theta, g_q, eps)).to(torch.bfloat16)
+        k = torch.from_numpy(prologue_fp32(k, pos, theta, g_k, eps)).to(torch.bfloat16)
     q = q.to(torch.float64)
     k = k.to(torch.float64)
     v = torch.as_tensor(v).to(torch.float64)

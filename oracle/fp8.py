@@ -27,6 +27,7 @@ import torch
 
 from .attention import attention
 from .rope import rope_table_fp32, rotate_fp32
+from .norm import prologue_fp32
 
 E4M3_MAX = 448.0
 
@@ -91,17 +92,15 @@ def _quantize_rows(r: np.ndarray):
     return codes, np.ascontiguousarray(np.transpose(scale, (0, 2, 1)))
 
 
-def quant_rope_fp8(q, k, v, pos, theta: float = 10000.0):
+def quant_rope_fp8(q, k, v, pos, theta: float = 10000.0, norm=None):
     """RoPE on Q and K (fp32, `rotate_fp32` order), then per-token e4m3 quantization
     of Q, K and V.  Returns (q8, k8, v8, sq, sk, sv): uint8 codes
-    [B, S, H, D] and fp32 scales [B, H, S].  pos=None skips the rotation."""
-    q = torch.as_tensor(q).to(torch.float32).numpy()
-    k = torch.as_tensor(k).to(torch.float32).numpy()
+    [B, S, H, D] and fp32 scales [B, H, S].  pos=None skips the rotation;
+    norm=(g_q, g_k, eps) RMS-normalizes Q and K first (`oracle.norm`)."""
+    g_q, g_k, eps = norm if norm is not None else (None, None, 0.0)
+    q = prologue_fp32(q, pos, theta, g_q, eps)
+    k = prologue_fp32(k, pos, theta, g_k, eps)
     v = torch.as_tensor(v).to(torch.float32).numpy()
-    if pos is not None:
-        table = rope_table_fp32(pos, q.shape[-1], theta)
-        q = rotate_fp32(q, table)
-        k = rotate_fp32(k, table)
     q8, sq = _quantize_rows(q)
     k8, sk = _quantize_rows(k)
     v8, sv = _quantize_rows(v)
@@ -160,12 +159,12 @@ def quant_error(x32, codes, scales) -> np.ndarray:
     return np.ascontiguousarray(np.transpose(err.max(axis=-1), (0, 2, 1)))
 
 
-def repair_errors(k, v, pos, k8, v8, sk, sv, theta: float = 10000.0) -> np.ndarray:
-    """Per-(b, h, token) error e = err(K) + err(V) in fp32, float32 [B, H, S]."""
-    k32 = torch.as_tensor(k).to(torch.float32).numpy()
+def repair_errors(k, v, pos, k8, v8, sk, sv, theta: float = 10000.0, norm=None) -> np.ndarray:
+    """Per-(b, h, token) error e = err(K) + err(V) in fp32, float32 [B, H, S]
+    (K as the quantizer saw it: normalized with norm's g_k if given, rotated)."""
+    k32 = prologue_fp32(k, pos, theta, norm[1] if norm is not None else None,
+                        norm[2] if norm is not None else 0.0)
     v32 = torch.as_tensor(v).to(torch.float32).numpy()
-    if pos is not None:
-        k32 = rotate_fp32(k32, rope_table_fp32(pos, k32.shape[-1], theta))
     return (quant_error(k32, k8, sk) + quant_error(v32, v8, sv)).astype(np.float32)
 
 
@@ -183,12 +182,12 @@ def repair_select(err, n: int) -> np.ndarray:
     return out
 
 
-def repair_values(k, v, pos, idx, theta: float = 10000.0):
+def repair_values(k, v, pos, idx, theta: float = 10000.0, norm=None):
     """Exact key and value of the repaired tokens: the bf16-rounded rotated
-    key (as on the bf16 path) and the bf16 value, float64 [B, H, n, D]."""
-    k32 = torch.as_tensor(k).to(torch.float32).numpy()
-    if pos is not None:
-        k32 = rotate_fp32(k32, rope_table_fp32(pos, k32.shape[-1], theta))
+    (and, with norm, normalized) key as on the bf16 path, and the bf16 value,
+    float64 [B, H, n, D]."""
+    k32 = prologue_fp32(k, pos, theta, norm[1] if norm is not None else None,
+                        norm[2] if norm is not None else 0.0)
     kb = torch.from_numpy(np.ascontiguousarray(k32)).to(torch.bfloat16).to(torch.float64)
     vb = torch.as_tensor(v).to(torch.float64)
     idx = np.asarray(idx)
