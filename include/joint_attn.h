@@ -59,6 +59,21 @@ typedef enum {
  *   x_ss = H*D, x_sh = D, x_sb = S*H*D; [B, H, S, D] works too.  Strides must
  *   be multiples of 8 and base pointers 16-byte aligned (16-byte vector
  *   loads).  softmax_scale = 0 selects 1/sqrt(head_dim).
+ *
+ *   q_norm, k_norm, norm_eps: optional query/key RMS normalization (the
+ *   pages fuse "query/key normalization" with RoPE into the QKV epilogue,
+ *   section "GEMM kernel optimization").  q_norm / k_norm are device fp32
+ *   weights [head_dim] (16-byte aligned), shared by all heads; NULL = that
+ *   tensor is not normalized.  Each (batch, token, head) vector x becomes
+ *     y_d = fl(fl(x_d * r) * g_d),  r = 1 / sqrt(ss / head_dim + eps)
+ *   in fp32 (IEEE square root and division), before RoPE and with no rounding
+ *   of its own; ss, the sum of squares, is taken chunk by chunk (8 elements,
+ *   fma in element order) and then pairwise over chunk c and c ^ k for
+ *   k = 2, 4, ..., head_dim/16, then k = 1.  norm_eps = 0 selects 1e-6.  The
+ *   normalization happens wherever RoPE is applied: the Q load of the bf16
+ *   forwards, joint_attn_prep_kv_bf16 (K), joint_attn_quant_rope_fp8 (Q, K)
+ *   and joint_attn_fp8_repair_plan (K).  Zero-initialize the struct to get
+ *   no normalization.
  */
 typedef struct {
   int32_t batch, seq_len, heads, head_dim;
@@ -67,6 +82,8 @@ typedef struct {
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
   float softmax_scale;
+  const float *q_norm, *k_norm;
+  float norm_eps;
 } ja_params;
 
 /*

@@ -46,6 +46,8 @@ class Params(ctypes.Structure):
         ("v_sb", ctypes.c_int64), ("v_ss", ctypes.c_int64), ("v_sh", ctypes.c_int64),
         ("o_sb", ctypes.c_int64), ("o_ss", ctypes.c_int64), ("o_sh", ctypes.c_int64),
         ("softmax_scale", ctypes.c_float),
+        ("q_norm", ctypes.c_void_p), ("k_norm", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -139,6 +141,19 @@ def _params(q, k, v, o, softmax_scale):
     return p
 
 
+def _set_norm(p, q_norm=None, k_norm=None, norm_eps: float = 0.0):
+    """Optional query/key RMS-norm weights: fp32 contiguous [head_dim] device
+    tensors (None = that tensor is not normalized); norm_eps 0 = 1e-6."""
+    for t, n in ((q_norm, "q_norm"), (k_norm, "k_norm")):
+        if t is not None and (t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous()
+                              or t.numel() != p.head_dim or not t.is_cuda):
+            raise ValueError(f"{n} must be a contiguous fp32 [{p.head_dim}] device tensor")
+    p.q_norm = None if q_norm is None else q_norm.data_ptr()
+    p.k_norm = None if k_norm is None else k_norm.data_ptr()
+    p.norm_eps = float(norm_eps)
+    return p
+
+
 def rope_table_2d(pos: torch.Tensor, head_dim: int, theta: float = 10000.0) -> torch.Tensor:
     """(cos, sin) table [S, head_dim/2, 2] fp32 of 2D-axial RoPE for int32 pos [S, 2]."""
     if pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[1] != 2 or not pos.is_contiguous():
@@ -156,11 +171,12 @@ def _check_bf16(**tensors):
             raise ValueError(f"{n} must be bfloat16")
 
 
-def prep_kv_bf16(k, v, rope=None):
-    """Prepared K/V buffer of the bf16 forward (uint8 device tensor): K rotated
-    with `rope` (or not), V transposed."""
+def prep_kv_bf16(k, v, rope=None, k_norm=None, norm_eps: float = 0.0):
+    """Prepared K/V buffer of the bf16 forward (uint8 device tensor): K
+    RMS-normalized with weights `k_norm` (if given), rotated with `rope` (if
+    given), V transposed."""
     _check_bf16(k=k, v=v)
-    p = _params(k, k, v, k, 0.0)
+    p = _set_norm(_params(k, k, v, k, 0.0), None, k_norm, norm_eps)
     lib = load()
     n = int(lib.joint_attn_prep_kv_bf16_bytes(ctypes.byref(p)))
     if n == 0:
@@ -172,13 +188,14 @@ def prep_kv_bf16(k, v, rope=None):
     return kv
 
 
-def _fwd_prepared(fn, name, q, kv, rope, mask, softmax_scale, out, return_lse, split):
+def _fwd_prepared(fn, name, q, kv, rope, mask, softmax_scale, out, return_lse, split,
+                  q_norm=None, norm_eps=0.0):
     _check_bf16(q=q)
     if kv.dtype != torch.uint8 or kv.dim() != 1 or kv.device != q.device:
         raise ValueError("kv must be the uint8 buffer from prep_kv_bf16 on q's device")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    p = _params(q, q, q, out, softmax_scale)
+    p = _set_norm(_params(q, q, q, out, softmax_scale), q_norm, None, norm_eps)
     lse = None
     if return_lse:
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
@@ -194,23 +211,25 @@ def _fwd_prepared(fn, name, q, kv, rope, mask, softmax_scale, out, return_lse, s
 
 
 def fwd_bf16_prepared(q, kv, rope=None, softmax_scale: float = 0.0, out=None,
-                      return_lse: bool = False, split: bool = True):
+                      return_lse: bool = False, split: bool = True, q_norm=None,
+                      norm_eps: float = 0.0):
     """Joint attention of bf16 Q [B, S, H, D] on K/V prepared by prep_kv_bf16
-    (with the same `rope`).  `split` passes the workspace that lets a mostly
-    idle last round of workgroups be split over key ranges."""
+    (with the same `rope`); Q RMS-normalized with `q_norm` if given.  `split`
+    passes the workspace that lets a mostly idle last round of workgroups be
+    split over key ranges."""
     return _fwd_prepared(load().joint_attn_fwd_bf16, "joint_attn_fwd_bf16", q, kv, rope, None,
-                         softmax_scale, out, return_lse, split)
+                         softmax_scale, out, return_lse, split, q_norm, norm_eps)
 
 
 def fwd_bf16(q, k, v, rope=None, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
-             split: bool = True):
-    """Joint attention on bf16 [B, S, H, D] tensors; RoPE from `rope` (or none):
-    prep_kv_bf16 then fwd_bf16_prepared."""
+             split: bool = True, q_norm=None, k_norm=None, norm_eps: float = 0.0):
+    """Joint attention on bf16 [B, S, H, D] tensors; optional Q/K RMS norm,
+    RoPE from `rope` (or none): prep_kv_bf16 then fwd_bf16_prepared."""
     _check_bf16(q=q, k=k, v=v)
     if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
         raise ValueError("q, k, v must have the same [B, S, H, D] shape")
-    kv = prep_kv_bf16(k, v, rope)
-    return fwd_bf16_prepared(q, kv, rope, softmax_scale, out, return_lse, split)
+    kv = prep_kv_bf16(k, v, rope, k_norm, norm_eps)
+    return fwd_bf16_prepared(q, kv, rope, softmax_scale, out, return_lse, split, q_norm, norm_eps)
 
 
 def block_mask_shape(batch: int, seq_len: int, heads: int):
@@ -219,7 +238,8 @@ def block_mask_shape(batch: int, seq_len: int, heads: int):
 
 
 def fwd_bf16_block_sparse_prepared(q, kv, block_mask, rope=None, softmax_scale: float = 0.0,
-                                   out=None, return_lse: bool = False, split: bool = True):
+                                   out=None, return_lse: bool = False, split: bool = True,
+                                   q_norm=None, norm_eps: float = 0.0):
     """fwd_bf16_prepared restricted to the (128-query x 64-key) blocks where the
     uint8 `block_mask` [B, H, ceil(S/128), ceil(S/64)] is nonzero; query rows
     that keep no key get O = 0 and LSE = -inf."""
@@ -229,18 +249,19 @@ def fwd_bf16_block_sparse_prepared(q, kv, block_mask, rope=None, softmax_scale: 
         raise ValueError(f"block_mask must be a contiguous uint8 {want} tensor on {q.device}")
     return _fwd_prepared(load().joint_attn_fwd_bf16_block_sparse,
                          "joint_attn_fwd_bf16_block_sparse", q, kv, rope, block_mask,
-                         softmax_scale, out, return_lse, split)
+                         softmax_scale, out, return_lse, split, q_norm, norm_eps)
 
 
 def fwd_bf16_block_sparse(q, k, v, block_mask, rope=None, softmax_scale: float = 0.0, out=None,
-                          return_lse: bool = False, split: bool = True):
+                          return_lse: bool = False, split: bool = True, q_norm=None, k_norm=None,
+                          norm_eps: float = 0.0):
     """prep_kv_bf16 then fwd_bf16_block_sparse_prepared."""
     _check_bf16(q=q, k=k, v=v)
     if tuple(k.shape) != tuple(q.shape) or tuple(v.shape) != tuple(q.shape):
         raise ValueError("q, k, v must have the same [B, S, H, D] shape")
-    kv = prep_kv_bf16(k, v, rope)
+    kv = prep_kv_bf16(k, v, rope, k_norm, norm_eps)
     return fwd_bf16_block_sparse_prepared(q, kv, block_mask, rope, softmax_scale, out,
-                                          return_lse, split)
+                                          return_lse, split, q_norm, norm_eps)
 
 
 def _contiguous_params(batch, seq_len, heads, head_dim):
@@ -259,14 +280,14 @@ def fwd_bf16_workspace_bytes(batch: int, seq_len: int, heads: int, head_dim: int
     return int(load().joint_attn_fwd_bf16_workspace_bytes(ctypes.byref(p)))
 
 
-def quant_rope_fp8(q, k, v, rope=None):
-    """RoPE on Q/K + per-token e4m3 quantization.  Returns (q8, k8, v8, sq, sk, sv):
-    uint8 codes [B, S, H, D] and fp32 scales [B, H, S]."""
+def quant_rope_fp8(q, k, v, rope=None, q_norm=None, k_norm=None, norm_eps: float = 0.0):
+    """Optional Q/K RMS norm, RoPE on Q/K, per-token e4m3 quantization.  Returns
+    (q8, k8, v8, sq, sk, sv): uint8 codes [B, S, H, D] and fp32 scales [B, H, S]."""
     b, s, h, d = q.shape
     dev = q.device
     q8, k8, v8 = (torch.empty((b, s, h, d), dtype=torch.uint8, device=dev) for _ in range(3))
     sq, sk, sv = (torch.empty((b, h, s), dtype=torch.float32, device=dev) for _ in range(3))
-    p = _params(q, k, v, q, 0.0)
+    p = _set_norm(_params(q, k, v, q, 0.0), q_norm, k_norm, norm_eps)
     st = load().joint_attn_quant_rope_fp8(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(rope),
                                           _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk),
                                           _ptr(sv), _stream(dev))
@@ -287,7 +308,8 @@ def repair_count(budget: float, seq_len: int) -> int:
     return int(math.ceil(float(budget) * seq_len))
 
 
-def fp8_repair_plan(k, v, rope, k8, v8, sk, sv, n_rep: int) -> Fp8Repair:
+def fp8_repair_plan(k, v, rope, k8, v8, sk, sv, n_rep: int, k_norm=None,
+                    norm_eps: float = 0.0) -> Fp8Repair:
     """Select the n_rep tokens per (batch, head) with the largest FP8 quantization
     error of their key and value, and gather their exact rotated keys and values."""
     b, s, h, d = k.shape
@@ -297,7 +319,7 @@ def fp8_repair_plan(k, v, rope, k8, v8, sk, sv, n_rep: int) -> Fp8Repair:
     kr = torch.empty((b, h, n_pad, d), dtype=torch.bfloat16, device=dev)
     vr = torch.empty((b, h, n_pad, d), dtype=torch.bfloat16, device=dev)
     kbias = torch.empty((b, h, s), dtype=torch.float32, device=dev)
-    p = _params(k, k, v, k, 0.0)
+    p = _set_norm(_params(k, k, v, k, 0.0), None, k_norm, norm_eps)
     st = load().joint_attn_fp8_repair_plan(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(rope), _ptr(k8),
                                            _ptr(v8), _ptr(sk), _ptr(sv), int(n_rep),
                                            _ptr(idx) if n_rep else None, _ptr(kr), _ptr(vr),

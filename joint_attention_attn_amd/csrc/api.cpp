@@ -55,6 +55,9 @@ ja::AttnLayout layout(const ja_params *p) {
   const float scale = p->softmax_scale != 0.f ? p->softmax_scale
                                               : 1.f / std::sqrt((float)p->head_dim);
   L.scale_log2 = scale * 1.4426950408889634f;
+  L.q_norm = p->q_norm;
+  L.k_norm = p->k_norm;
+  L.norm_eps = p->norm_eps != 0.f ? p->norm_eps : 1e-6f;
   return L;
 }
 
@@ -65,6 +68,9 @@ ja_status check_params(const ja_params *p, bool qkv_strided, int block_rows) {
   if (!shape_ok(p)) return JA_ERR_INVALID_ARG;
   if (!dim_supported(p->head_dim)) return JA_ERR_UNSUPPORTED;
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale < 0.f) return JA_ERR_INVALID_ARG;
+  if (!std::isfinite(p->norm_eps) || p->norm_eps < 0.f) return JA_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(p->q_norm) & 15u) || (reinterpret_cast<uintptr_t>(p->k_norm) & 15u))
+    return JA_ERR_INVALID_ARG;
   if (qkv_strided &&
       (!strides_ok(p->q_sb, p->q_ss, p->q_sh) || !strides_ok(p->k_sb, p->k_ss, p->k_sh) ||
        !strides_ok(p->v_sb, p->v_ss, p->v_sh)))

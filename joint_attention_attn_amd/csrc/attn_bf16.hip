@@ -95,6 +95,8 @@ constexpr int kBufferFlags = 0x00020000;
 
 struct FwdArgs {
   const bf16 *q;
+  const float *qn;          // Q RMS-norm weights [D], NULL = none
+  float eps;
   const bf16 *kr, *vt;      // prepared K and V^T (prep_kv.hip), S_pad keys
   const float2 *rope;
   bf16 *o;
@@ -277,8 +279,8 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     }
   };
 
-  // ---- Q rows of this lane (one per 32-row block): rotate, round to bf16,
-  //      keep in registers ----
+  // ---- Q rows of this lane (one per 32-row block): normalize (optional),
+  //      rotate, round to bf16, keep in registers ----
   int qi[RW];
   bf16x8 qreg[RW][D / 16];
 #pragma unroll
@@ -286,13 +288,39 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     qi[r] = qblk * BM + (wave * RW + r) * 32 + l32;
     const int qs = qi[r] < S ? qi[r] : S - 1;
     const bf16 *qrow = a.q + b * a.q_sb + (int64_t)qs * a.q_ss + h * a.q_sh;
+    // lane half hf holds chunks c = 2 kk + hf of the row
+    constexpr int NK = D / 16;
+    u32x4 w[NK];
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
+    for (int kk = 0; kk < NK; ++kk) w[kk] = *reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * hf);
+    float rn = 0.f;
+    if (a.qn) {
+      // RMS norm: the butterfly levels c ^ 2, c ^ 4, ... are kk ^ 1, kk ^ 2,
+      // ... inside the lane; the last level, c ^ 1, is the other lane half
+      float ss[NK];
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) ss[kk] = chunk_sumsq(w[kk]);
+#pragma unroll
+      for (int lev = 1; lev < NK; lev <<= 1) {
+        float t[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) t[kk] = ss[kk] + ss[kk ^ lev];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) ss[kk] = t[kk];
+      }
+      rn = rms_scale<D>(half_sum(ss[0]), a.eps);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
       const int d0 = 16 * kk + 8 * hf;
-      u32x4 w = *reinterpret_cast<const u32x4 *>(qrow + d0);
-      if constexpr (ROPE) w = rope_chunk_bf16(w, a.rope + (int64_t)qs * (D / 2) + d0 / 2);
-      if (qi[r] >= S) w = u32x4{0, 0, 0, 0};
-      qreg[r][kk] = bit_cast<bf16x8>(w);
+      u32x4 x = w[kk];
+      const float2 *cs = ROPE ? a.rope + (int64_t)qs * (D / 2) + d0 / 2 : nullptr;
+      if (a.qn)
+        x = norm_rope_chunk_bf16(x, rn, a.qn + d0, cs);
+      else if constexpr (ROPE)
+        x = rope_chunk_bf16(x, cs);
+      if (qi[r] >= S) x = u32x4{0, 0, 0, 0};
+      qreg[r][kk] = bit_cast<bf16x8>(x);
     }
   }
 
@@ -612,6 +640,8 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   const bf16 *vt = kr + prep_elems;
   FwdArgs a;
   a.q = static_cast<const bf16 *>(q);
+  a.qn = L.q_norm;
+  a.eps = L.norm_eps;
   a.kr = kr;
   a.vt = vt;
   a.rope = reinterpret_cast<const float2 *>(rope);

@@ -69,6 +69,75 @@ __device__ __forceinline__ u32x4 rope_chunk_bf16(u32x4 w, const float2 *cs) {
   return r;
 }
 
+// ---- query/key RMS normalization ("Speed Up Image Generation with FLUX 3
+// Image Klein on NVIDIA Blackwell GPUs", section "GEMM kernel optimization":
+// query/key normalization next to RoPE in the QKV epilogue), applied in fp32
+// before the rotation:  y_d = fl(fl(x_d * r) * g_d),
+// r = 1 / sqrt(ss / D + eps) with IEEE fp32 square root and division.  The sum
+// of squares ss has one fixed order wherever it is computed: chunk c of 8
+// elements accumulates fma(x, x, s) over its elements from 0, then the chunk
+// sums combine pairwise with partner c ^ k for k = 2, 4, ..., D/16, then
+// k = 1 (a butterfly: every chunk ends with the same total).
+
+// Sum of squares of the 8 bf16 of a 16-byte chunk, in element order.
+__device__ __forceinline__ float chunk_sumsq(u32x4 w) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s = __builtin_fmaf(bf16_lo(ws[e]), bf16_lo(ws[e]), s);
+    s = __builtin_fmaf(bf16_hi(ws[e]), bf16_hi(ws[e]), s);
+  }
+  return s;
+}
+
+// Butterfly over the chunk sums when lane (i % CH) of each group of CH
+// consecutive lanes holds chunk i % CH.
+template <int CH>
+__device__ __forceinline__ float chunk_sum_lanes(float s) {
+#pragma unroll
+  for (int k = 2; k < CH; k <<= 1) s = s + __shfl_xor(s, k);
+  if constexpr (CH > 1) s = s + __shfl_xor(s, 1);
+  return s;
+}
+
+// r = 1 / sqrt(ss / D + eps); D is a power of two, so ss / D is exact.
+template <int D>
+__device__ __forceinline__ float rms_scale(float ss, float eps) {
+  return 1.f / __builtin_sqrtf(ss * (1.f / D) + eps);
+}
+
+// The 8 values of a chunk normalized: fl(fl(x * r) * g) with g the chunk's 8
+// weights.
+__device__ __forceinline__ void norm_chunk(u32x4 w, float r, const float *g, float (&y)[8]) {
+#pragma clang fp contract(off)
+  const float4 g0 = reinterpret_cast<const float4 *>(g)[0];
+  const float4 g1 = reinterpret_cast<const float4 *>(g)[1];
+  const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[2 * e] = (bf16_lo(ws[e]) * r) * gv[2 * e];
+    y[2 * e + 1] = (bf16_hi(ws[e]) * r) * gv[2 * e + 1];
+  }
+}
+
+// Normalize (if g) and rotate (if cs) a chunk, rounded to bf16.
+__device__ __forceinline__ u32x4 norm_rope_chunk_bf16(u32x4 w, float r, const float *g,
+                                                      const float2 *cs) {
+  float y[8];
+  norm_chunk(w, r, g, y);
+  u32x4 o;
+  uint32_t *op = reinterpret_cast<uint32_t *>(&o);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float rx = y[2 * e], ry = y[2 * e + 1];
+    if (cs) rope_pair_f32(y[2 * e], y[2 * e + 1], cs[e], rx, ry);
+    op[e] = pack_bf16x2(rx, ry);
+  }
+  return o;
+}
+
 // Key held by slot p (0..15) of a 16-key group in the P operand of the P.V
 // MFMA: the S^T accumulator gives lane half hf = p / 8 the keys
 // 4hf + {0..3} and 4hf + {8..11} of the group, in that order.  V^T rows store

@@ -13,6 +13,9 @@ struct AttnLayout {
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
   float scale_log2;  // softmax scale * log2(e): scores live in the exp2 domain
+  // query/key RMS normalization weights [D] (NULL = none) and its epsilon
+  const float *q_norm = nullptr, *k_norm = nullptr;
+  float norm_eps = 1e-6f;
 };
 
 hipError_t launch_rope_table_2d(const int32_t *pos, int S, int D, float theta,

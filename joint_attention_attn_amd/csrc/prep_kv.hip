@@ -30,6 +30,8 @@ constexpr int PK = 64;        // keys per workgroup
 struct PrepArgs {
   const bf16 *k, *v;
   const float2 *rope;
+  const float *kn;     // K RMS-norm weights [D], NULL = none
+  float eps;
   bf16 *kr, *vt;
   int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
   int S, S_pad, H;
@@ -50,7 +52,9 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
   bf16 *krb = a.kr + (int64_t)bh * a.S_pad * D;
   bf16 *vtb = a.vt + (int64_t)bh * D * a.S_pad;
 
-  // K: rotate and copy; V: stage row-major in LDS
+  // K: (normalize,) rotate and copy; V: stage row-major in LDS.  The CH
+  // chunks of a row are CH consecutive lanes, so the norm's butterfly runs
+  // inside each lane group (every lane takes part; rows past S are zeros).
 #pragma unroll
   for (int idx = tid; idx < PK * CH; idx += PT) {
     const int r = idx / CH, c = idx % CH;
@@ -58,8 +62,14 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
     u32x4 kw = {0, 0, 0, 0}, vw = {0, 0, 0, 0};
     if (key < a.S) {
       kw = *reinterpret_cast<const u32x4 *>(kb + (int64_t)key * a.k_ss + 8 * c);
-      if constexpr (ROPE) kw = rope_chunk_bf16(kw, a.rope + (int64_t)key * (D / 2) + 4 * c);
       vw = *reinterpret_cast<const u32x4 *>(vb + (int64_t)key * a.v_ss + 8 * c);
+    }
+    const float2 *cs = ROPE && key < a.S ? a.rope + (int64_t)key * (D / 2) + 4 * c : nullptr;
+    if (a.kn) {
+      const float ss = chunk_sum_lanes<CH>(chunk_sumsq(kw));
+      kw = norm_rope_chunk_bf16(kw, rms_scale<D>(ss, a.eps), a.kn + 8 * c, cs);
+    } else if (cs) {
+      kw = rope_chunk_bf16(kw, cs);
     }
     *reinterpret_cast<u32x4 *>(krb + (int64_t)key * D + 8 * c) = kw;
     *reinterpret_cast<u32x4 *>(vs + r * VSTR + 8 * c) = vw;
@@ -98,6 +108,8 @@ hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v
   a.k = static_cast<const bf16 *>(k);
   a.v = static_cast<const bf16 *>(v);
   a.rope = reinterpret_cast<const float2 *>(rope);
+  a.kn = L.k_norm;
+  a.eps = L.norm_eps;
   a.kr = static_cast<bf16 *>(kv);
   a.vt = a.kr + (int64_t)L.B * L.H * prep_pad(L.S) * L.D;
   a.k_sb = L.k_sb; a.k_ss = L.k_ss; a.k_sh = L.k_sh;

@@ -25,6 +25,8 @@ struct QuantArgs {
   uint8_t *x8[3];
   float *scale[3];
   const float2 *rope;
+  const float *norm[2];   // Q / K RMS-norm weights [D], NULL = none
+  float eps;
   int S, H;
   int64_t rows;  // B * S * H
 };
@@ -46,7 +48,20 @@ __global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
       a.x[t] + b * a.sb[t] + s * a.ss[t] + h * a.sh[t] + sub * 8);
   const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
   float r[8];
-  if (a.rope && t < 2) {
+  const float *g = t < 2 ? a.norm[t] : nullptr;
+  if (g) {
+    // RMS norm (the LPR lanes of a vector hold its chunks in order), then RoPE
+    const float rn = rms_scale<D>(chunk_sum_lanes<LPR>(chunk_sumsq(w)), a.eps);
+    norm_chunk(w, rn, g + sub * 8, r);
+    if (a.rope) {
+      const float2 *cs = a.rope + s * (D / 2) + sub * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = r[2 * e], x1 = r[2 * e + 1];
+        rope_pair_f32(x0, x1, cs[e], r[2 * e], r[2 * e + 1]);
+      }
+    }
+  } else if (a.rope && t < 2) {
     const float2 *cs = a.rope + s * (D / 2) + sub * 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -101,6 +116,9 @@ hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
   a.scale[1] = sk;
   a.scale[2] = sv;
   a.rope = reinterpret_cast<const float2 *>(rope);
+  a.norm[0] = L.q_norm;
+  a.norm[1] = L.k_norm;
+  a.eps = L.norm_eps;
   a.S = L.S;
   a.H = L.H;
   a.rows = (int64_t)L.B * L.S * L.H;

@@ -33,6 +33,8 @@ struct ErrArgs {
   const bf16 *k, *v;
   int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
   const float2 *rope;
+  const float *kn;              // K RMS-norm weights [D], NULL = none
+  float eps;
   const uint8_t *k8, *v8;
   const float *sk, *sv;
   float *err;                   // [B][H][S]
@@ -74,7 +76,19 @@ __global__ __launch_bounds__(256) void repair_err_kernel(ErrArgs a) {
   float x[8];
   const u32x4 kw = *reinterpret_cast<const u32x4 *>(a.k + b * a.k_sb + s * a.k_ss + h * a.k_sh + sub * 8);
   const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-  if (a.rope) {
+  if (a.kn) {
+    // the key as the quantizer saw it: normalized, then rotated
+    const float rn = rms_scale<D>(chunk_sum_lanes<LPR>(chunk_sumsq(kw)), a.eps);
+    norm_chunk(kw, rn, a.kn + sub * 8, x);
+    if (a.rope) {
+      const float2 *cs = a.rope + s * (D / 2) + sub * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = x[2 * e], x1 = x[2 * e + 1];
+        rope_pair_f32(x0, x1, cs[e], x[2 * e], x[2 * e + 1]);
+      }
+    }
+  } else if (a.rope) {
     const float2 *cs = a.rope + s * (D / 2) + sub * 4;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -111,6 +125,8 @@ struct SelArgs {
   const bf16 *k, *v;
   int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
   const float2 *rope;
+  const float *kn;              // K RMS-norm weights [D], NULL = none
+  float eps;
   bf16 *kr, *vr;                // [B][H][n_pad][D]
   int S, H, n, n_pad;
 };
@@ -201,8 +217,15 @@ __global__ __launch_bounds__(SEL_NT) void repair_select_kernel(SelArgs a) {
     if (i < n) {
       const int64_t s = a.idx[bh * n + i];
       kw = *reinterpret_cast<const u32x4 *>(a.k + b * a.k_sb + s * a.k_ss + h * a.k_sh + c * 8);
-      if (a.rope) kw = rope_chunk_bf16(kw, a.rope + s * (D / 2) + c * 4);
+      if (a.rope && !a.kn) kw = rope_chunk_bf16(kw, a.rope + s * (D / 2) + c * 4);
       vw = *reinterpret_cast<const u32x4 *>(a.v + b * a.v_sb + s * a.v_ss + h * a.v_sh + c * 8);
+    }
+    if (a.kn) {
+      // the CH chunks of a key are CH consecutive lanes (SEL_NT % CH == 0)
+      const int64_t s = i < n ? a.idx[bh * n + i] : 0;
+      const float rn = rms_scale<D>(chunk_sum_lanes<CH>(chunk_sumsq(kw)), a.eps);
+      kw = norm_rope_chunk_bf16(kw, rn, a.kn + c * 8,
+                                a.rope && i < n ? a.rope + s * (D / 2) + c * 4 : nullptr);
     }
     const int64_t o = (bh * a.n_pad + i) * D + c * 8;
     *reinterpret_cast<u32x4 *>(a.kr + o) = kw;
@@ -226,6 +249,8 @@ hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
   e.k_sb = L.k_sb; e.k_ss = L.k_ss; e.k_sh = L.k_sh;
   e.v_sb = L.v_sb; e.v_ss = L.v_ss; e.v_sh = L.v_sh;
   e.rope = reinterpret_cast<const float2 *>(rope);
+  e.kn = L.k_norm;
+  e.eps = L.norm_eps;
   e.k8 = static_cast<const uint8_t *>(k8);
   e.v8 = static_cast<const uint8_t *>(v8);
   e.sk = sk;
@@ -251,6 +276,8 @@ hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
   a.k_sb = L.k_sb; a.k_ss = L.k_ss; a.k_sh = L.k_sh;
   a.v_sb = L.v_sb; a.v_ss = L.v_ss; a.v_sh = L.v_sh;
   a.rope = e.rope;
+  a.kn = L.k_norm;
+  a.eps = L.norm_eps;
   a.kr = static_cast<bf16 *>(kr);
   a.vr = static_cast<bf16 *>(vr);
   a.S = L.S;

@@ -22,7 +22,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "positions", "make_qkv", "outlier_tokens",
-           "make_block_mask", "SPARSE_DENSITY"]
+           "make_block_mask", "SPARSE_DENSITY", "make_norm_weights"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -133,3 +133,13 @@ def make_block_mask(w: Workload, density: float = SPARSE_DENSITY, seed: int = 0,
     s = w.seq_len
     shape = (w.batch, w.heads, -(-s // q_block), -(-s // k_block))
     return (torch.rand(shape, generator=gen, dtype=torch.float64) < density).to(torch.uint8)
+
+
+def make_norm_weights(head_dim: int, seed: int = 0):
+    """Seeded stand-ins for the learned query/key RMS-norm weights (no trained
+    checkpoint here): fp32 [D] vectors g_q, g_k = 1 + 0.1 * N(0, 1), drawn in
+    that order from a CPU generator seeded with `seed`."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    gq = 1.0 + 0.1 * torch.randn(head_dim, generator=gen, dtype=torch.float32)
+    gk = 1.0 + 0.1 * torch.randn(head_dim, generator=gen, dtype=torch.float32)
+    return gq.numpy(), gk.numpy()

@@ -188,3 +188,20 @@ def test_prep_kv_validation(lib):
     bad.head_dim = 96
     assert f(ctypes.byref(bad), vp(FAKE), vp(FAKE + 0x1000), None, vp(FAKE + 0x4000), need,
              None) == ja.JA_ERR_UNSUPPORTED
+
+
+def test_norm_validation(lib):
+    p = _p()
+    p.norm_eps = -1.0
+    assert _fwd(lib, p) == ja.JA_ERR_INVALID_ARG
+    p = _p()
+    p.norm_eps = float("nan")
+    assert _fwd(lib, p) == ja.JA_ERR_INVALID_ARG
+    p = _p()
+    p.q_norm = FAKE + 4                                                 # misaligned weights
+    assert _fwd(lib, p) == ja.JA_ERR_INVALID_ARG
+    p = _p()
+    p.k_norm = FAKE + 8
+    vp = ctypes.c_void_p
+    assert lib.joint_attn_prep_kv_bf16(ctypes.byref(p), vp(FAKE), vp(FAKE + 0x1000), None,
+                                       vp(FAKE + 0x4000), 1 << 30, None) == ja.JA_ERR_INVALID_ARG
