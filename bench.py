@@ -16,6 +16,9 @@ Also reported on the same JSON line:
                 way, against the fp8 MFMA peak and HBM bandwidth, and with the
                 repair of the tokens with the largest quantization error
                 (budget 0.005);
+  qk_norm       the same passes with query/key RMS normalization fused
+                where RoPE is (seeded weights): K/V preparation, forward,
+                FP8 quantize;
   sparse        the block-sparse forward on a seeded mask over 128-query x
                 64-key blocks at the block density of the sparse steps
                 (half the blocks kept), against the flops of the kept blocks;
@@ -61,6 +64,7 @@ def _parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-sparse", action="store_true")
+    ap.add_argument("--no-norm", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
@@ -171,7 +175,7 @@ def main() -> int:
     kms = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope, out=out), max(args.steps, 5))
     k_avg = sum(kms) / len(kms)
     pms = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope), max(args.steps, 5))
-    p_avg = sum(pms) / len(pms)
+    prep_avg = sum(pms) / len(pms)
     # algorithmic bytes of the preparation: read K, V and the table, write both
     prep_bytes = 4 * B * S * H * D * 2 + S * (D // 2) * 8
     achieved = flops / (k_avg * 1e-3) / 1e12
@@ -182,14 +186,14 @@ def main() -> int:
                 "kernel": "attn_fwd_bf16_kernel<128, true, false> (+ merge_split_kernel of the "
                           "split last round); K/V preparation in prep_kv",
                 "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4),
-                "prep_kv": {"ms": round(p_avg, 4),
+                "prep_kv": {"ms": round(prep_avg, 4),
                             "traffic": _traffic_for_current_kernel(
                                 "prep_kv_bf16_t2i_2048_traffic.txt", "prep_kv.hip"),
-                            "gbs": round(prep_bytes / (p_avg * 1e-3) / 1e9, 1),
-                            "frac_of_hbm": round(prep_bytes / (p_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "gbs": round(prep_bytes / (prep_avg * 1e-3) / 1e9, 1),
+                            "frac_of_hbm": round(prep_bytes / (prep_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                                  4)}}
     _log(f"[bench] fwd kernel avg {k_avg:.3f} ms -> {achieved:.1f} TFLOP/s "
-         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); K/V prep {p_avg:.3f} ms")
+         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); K/V prep {prep_avg:.3f} ms")
 
     fp8 = None
     fp8_outs = None
@@ -237,6 +241,11 @@ def main() -> int:
         _log(f"[bench] fp8 + repair ({n_rep} tokens/head): plan {p_avg:.3f} ms, fwd {r_avg:.3f} ms")
         fp8_outs = (out8, out8r)
 
+    qk_norm = None
+    if not args.no_norm:
+        qk_norm = _norm_leg(ja, w, qd, kd, vd, rope, out, k_avg, prep_avg,
+                            fp8["quant_ms"] if fp8 else None, max(args.steps, 5), args.seed)
+
     sparse = None
     if not args.no_sparse:
         sparse = _sparse_leg(ja, w, qd, kv, rope, out, k_avg, max(args.steps, 5), args.seed)
@@ -256,9 +265,37 @@ def main() -> int:
                                   f"{100 * w.outlier_frac:g}% x{w.outlier_scale:g} outlier tokens",
                       "batch": B, "seq_len": S, "heads": H, "head_dim": D,
                       "flops_per_step": flops},
-           "roofline": roofline, "cpu_baseline": cpu, "fp8": fp8, "sparse": sparse}
+           "roofline": roofline, "cpu_baseline": cpu, "fp8": fp8, "qk_norm": qk_norm,
+           "sparse": sparse}
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def _norm_leg(ja, w, qd, kd, vd, rope, out, fwd_ms, prep_ms, quant_ms, n, seed):
+    """Query/key RMS normalization fused into the passes that apply RoPE:
+    their times with it, beside the times without (same run)."""
+    import torch
+    import synth
+    B, S, H, D = w.shape
+    gq, gk = (torch.from_numpy(g).to(qd.device) for g in synth.make_norm_weights(D, seed))
+    kv = ja.prep_kv_bf16(kd, vd, rope, k_norm=gk)
+    for _ in range(3):
+        ja.fwd_bf16_prepared(qd, kv, rope, out=out, q_norm=gq)
+    torch.cuda.synchronize()
+    pm = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope, k_norm=gk), n)
+    fm = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope, out=out, q_norm=gq), n)
+    p_avg, f_avg = sum(pm) / n, sum(fm) / n
+    rec = {"weights": "seeded g = 1 + 0.1 N(0,1), eps 1e-6",
+           "prep_kv_ms": round(p_avg, 4), "prep_kv_ms_without": round(prep_ms, 4),
+           "fwd_ms": round(f_avg, 4), "fwd_ms_without": round(fwd_ms, 4)}
+    if quant_ms is not None:
+        qm = _time_launches(lambda: ja.quant_rope_fp8(qd, kd, vd, rope, q_norm=gq, k_norm=gk), n)
+        rec["quant_ms"] = round(sum(qm) / n, 4)
+        rec["quant_ms_without"] = round(quant_ms, 4)
+    _log(f"[bench] qk norm: prep {p_avg:.3f} ms (without {prep_ms:.3f}), fwd {f_avg:.3f} ms "
+         f"(without {fwd_ms:.3f})" + (f", quant {rec['quant_ms']:.3f} ms (without {quant_ms:.3f})"
+                                     if quant_ms is not None else ""))
+    return rec
 
 
 def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
