@@ -42,6 +42,8 @@
 // stages only the tiles of that list.  A wave computes a staged tile only if
 // its own query block keeps it (a wave-uniform branch); staging and the
 // barrier are shared.  Query rows that keep no key get O = 0 and LSE = -inf.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -597,16 +599,24 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   }
 }
 
-// Dynamic LDS of one instantiation; kernels that need more than the default
-// limit get it raised once per process.
+// Dynamic LDS of one instantiation; its limit is raised once per device (the
+// attribute is set with the device current).
 template <int D, bool ROPE, bool SPARSE>
 hipError_t launch_instance(const FwdArgs &a, dim3 grid, hipStream_t st) {
   const int bytes = SPARSE ? Lds<D>::sparse_bytes(a.nkb) : Lds<D>::BYTES;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<D, ROPE, SPARSE>),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      SPARSE ? Lds<D>::sparse_bytes((kSparseMaxSeq + kKeyBlock - 1) / kKeyBlock) : Lds<D>::BYTES);
-  if (attr != hipSuccess) return attr;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> done[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices || !done[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<D, ROPE, SPARSE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        SPARSE ? Lds<D>::sparse_bytes((kSparseMaxSeq + kKeyBlock - 1) / kKeyBlock) : Lds<D>::BYTES);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
+  }
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, ROPE, SPARSE>), grid, dim3(NT), bytes, st, a);
   return hipGetLastError();
 }
