@@ -18,8 +18,8 @@
 //
 // Structure as in the bf16 kernel: one workgroup of eight wave64s (two per
 // SIMD) per (256-query block, head, batch row), XCD-aware placement, K/V tiles
-// of 64 keys double-buffered in LDS with the next tiles loaded one iteration
-// ahead, one barrier per tile.  K rows are copied as they are; V is
+// of 64 keys double-buffered in LDS through registers, one barrier per tile,
+// and Q K^T of the next tile issued ahead of the softmax of this one.  K rows are copied as they are; V is
 // staged transposed (one row per head-dimension column, keys in the order in
 // which the P' operand holds them) by a 4 x 4 byte transpose in registers, so
 // both MFMA operands are 16-byte LDS reads.
@@ -33,8 +33,8 @@ namespace ja {
 namespace {
 
 // Waves per workgroup, 32 query rows each, two per SIMD: a wave of this
-// kernel needs about 200 VGPRs (three waves per SIMD would allow 168, and the
-// spills that forces cost more than the third wave gains).
+// kernel needs about 245 VGPRs (two tiles of S accumulators in flight); three
+// waves per SIMD would allow only 168.
 constexpr int NW = 8;
 constexpr int BM = 32 * NW;         // query rows per workgroup
 constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
@@ -330,32 +330,53 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     return pb;
   };
 
-  // ---- loop over the key tiles t0 .. t1-1 (local index i): local tile i
-  //      lives in K buffer i%2 and V buffer i%2 (with its scales).  Iteration
-  //      i computes Q K^T, the softmax and P.V of tile i, then stores K and V
-  //      of tile i+1 (into the buffers read by iteration i-1) and issues the
-  //      loads of tile i+2; a barrier closes the iteration. ----
+  // ---- loop over the key tiles t0 .. t1-1 (local index i), software
+  //      pipelined: iteration i issues Q K^T of tile i+1 before the softmax
+  //      of tile i, so the matrix cores work on the next tile while the
+  //      vector units exponentiate this one.  K tile i lives in K buffer i%2,
+  //      V tile i (with its scales) in V buffer i%2; iteration i reads K(i+1)
+  //      and V(i), stores K(i+2) and V(i+1) (loaded one iteration earlier)
+  //      into the buffers that iteration i-1 finished with, issues the loads
+  //      of K(i+3) and V(i+2), and a barrier closes it. ----
   const int nt = t1 - t0;
   load(t0, true, true);
   store_k(0);
   store_v(0);
-  if (nt > 1) load(t0 + 1, true, true);
+  if (nt > 1) {
+    load(t0 + 1, true, false);
+    store_k(1);
+  }
+  if (nt > 2) load(t0 + 2, true, false);
+  if (nt > 1) load(t0 + 1, false, true);
   __syncthreads();
-  f32x16 sacc[2];
-  auto iteration = [&]<bool NEXT>(int i) JA_INLINE {
+  f32x16 sacc[2][2];
+  qk(0, sacc[0]);
+  auto iteration = [&]<int PAR, bool LAST>(int i) JA_INLINE {
     const int t = t0 + i;
-    qk(i & 1, sacc);
-    const i32x8 pb = softmax.template operator()<!NEXT>(sacc, t * BN, i & 1);
+    if constexpr (!LAST) qk((i + 1) & 1, sacc[PAR ^ 1]);
+    const i32x8 pb = softmax.template operator()<LAST>(sacc[PAR], t * BN, i & 1);
     pv(pb, i & 1);
-    if constexpr (NEXT) {
-      store_k((i + 1) & 1);
+    if constexpr (!LAST) {
+      if (i + 2 < nt) store_k(i & 1);
       store_v((i + 1) & 1);
-      if (i + 2 < nt) load(t + 2, true, true);
+      if (i + 3 < nt) load(t + 3, true, false);
+      if (i + 2 < nt) load(t + 2, false, true);
+      __syncthreads();
+    } else if constexpr (REPAIR) {
+      __syncthreads();        // the repair pass restages through these buffers
     }
-    __syncthreads();
   };
-  for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<true>(i);
-  iteration.template operator()<false>(nt - 1);
+  int i = 0;
+  for (; i + 2 < nt; i += 2) {
+    iteration.template operator()<0, false>(i);
+    iteration.template operator()<1, false>(i + 1);
+  }
+  if (i + 1 < nt) {
+    iteration.template operator()<0, false>(i);
+    iteration.template operator()<1, true>(i + 1);
+  } else {
+    iteration.template operator()<0, true>(i);
+  }
 
   // ---- repaired keys: one more pass over them with their exact values, on
   //      bf16 MFMA (an e4m3 code times its scale is exact in this product:
