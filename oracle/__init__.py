@@ -37,7 +37,7 @@ from .rope import rope_angles, apply_rope, rope_table_fp32, rotate_fp32, fma32
 from .norm import (NORM_EPS, sum_squares_fp32, rms_norm_fp32, rms_norm, prologue_fp32)
 from .attention import (attention, joint_attention, brute_force_attention,
                         block_sparse_attention, QUERY_BLOCK, KEY_BLOCK)
-from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, quant_rope_fp8,
+from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, pow2_scale, quant_rope_fp8,
                   dequantize, fp8_attention, repair_count, quant_error, repair_errors,
                   repair_select, repair_values, fp8_repaired_attention)
 
@@ -46,7 +46,7 @@ __all__ = [
     "NORM_EPS", "sum_squares_fp32", "rms_norm_fp32", "rms_norm", "prologue_fp32",
     "attention", "joint_attention", "brute_force_attention", "block_sparse_attention",
     "QUERY_BLOCK", "KEY_BLOCK",
-    "e4m3_round", "e4m3_encode", "e4m3_decode", "quant_rope_fp8",
+    "e4m3_round", "e4m3_encode", "e4m3_decode", "pow2_scale", "quant_rope_fp8",
     "dequantize", "fp8_attention", "repair_count", "quant_error", "repair_errors",
     "repair_select", "repair_values", "fp8_repaired_attention",
 ]

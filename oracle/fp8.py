@@ -9,8 +9,15 @@ Up Image Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", section
   finite magnitude 448, subnormal spacing 2^-9), round to nearest even,
   saturating to +-448;
 * granularity: one fp32 scale per (batch, token, head) over the D elements of
-  that head vector ("per token"), scale = amax / 448, and scale = 1 when the
-  vector is all zeros; Q and K are quantized after RoPE, V as given;
+  that head vector ("per token"), scale = 1 when the vector is all zeros;
+  Q and K are quantized after RoPE, V as given;
+* scale value: for V, amax / 448 (the largest element lands on 448); for Q
+  and K, the smallest power of two s with amax <= 448 s (at least 2^-126, the
+  smallest normal fp32 power of two).  A power of two is the OCP microscaling
+  convention for shared scales (an E8M0 exponent): the matrix cores apply it
+  exactly to the Q K^T product, and x / s is exact.  e4m3 is a floating-point
+  format, so its relative precision does not depend on where amax lands in
+  (224, 448];
 * precision of the decision: the quantizer rounds values that were computed
   in fp32 with a fixed operation order (`oracle.rope.rotate_fp32`, then
   fl(x / scale)), so the codes it produces are a deterministic function of
@@ -76,16 +83,31 @@ def e4m3_decode(code) -> np.ndarray:
     return s * val
 
 
-def _quantize_rows(r: np.ndarray):
+def pow2_scale(amax) -> np.ndarray:
+    """Smallest power of two s with amax <= 448 s, as fp32 (1 when amax = 0,
+    at least 2^-126).  With amax = f 2^x, f in [0.5, 1): 448 = 0.875 2^9, so
+    s = 2^(x - 9) when f <= 0.875 and 2^(x - 8) otherwise."""
+    amax = np.asarray(amax, np.float32)
+    f, x = np.frexp(amax.astype(np.float64))
+    k = np.maximum(x - 9 + (f > 0.875), -126)
+    s = np.ldexp(np.float64(1.0), k).astype(np.float32)
+    return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def _quantize_rows(r: np.ndarray, pow2: bool = False):
     """Per-(b, s, h) e4m3 quantization of fp32 r [B, S, H, D].
 
-    amax = max |r| over D; scale = fl32(amax / 448) (1 when amax = 0);
-    code = e4m3(clamp(fl32(r / scale), -448, 448)).  Returns (uint8 codes
-    [B, S, H, D], fp32 scales [B, H, S]).
+    amax = max |r| over D; scale = fl32(amax / 448), or pow2_scale(amax) when
+    pow2 (1 when amax = 0 either way); code = e4m3(clamp(fl32(r / scale),
+    -448, 448)) (the division is exact for a power of two).  Returns (uint8
+    codes [B, S, H, D], fp32 scales [B, H, S]).
     """
     amax = np.max(np.abs(r), axis=-1)                                   # fp32 exact
-    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+    if pow2:
+        scale = pow2_scale(amax)
+    else:
+        scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
     y = (r / scale[..., None]).astype(np.float32)
     y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     codes = e4m3_encode(e4m3_round(y))
@@ -94,15 +116,15 @@ def _quantize_rows(r: np.ndarray):
 
 def quant_rope_fp8(q, k, v, pos, theta: float = 10000.0, norm=None):
     """RoPE on Q and K (fp32, `rotate_fp32` order), then per-token e4m3 quantization
-    of Q, K and V.  Returns (q8, k8, v8, sq, sk, sv): uint8 codes
-    [B, S, H, D] and fp32 scales [B, H, S].  pos=None skips the rotation;
+    of Q, K (power-of-two scales) and V (amax / 448).  Returns (q8, k8, v8,
+    sq, sk, sv): uint8 codes [B, S, H, D] and fp32 scales [B, H, S].  pos=None skips the rotation;
     norm=(g_q, g_k, eps) RMS-normalizes Q and K first (`oracle.norm`)."""
     g_q, g_k, eps = norm if norm is not None else (None, None, 0.0)
     q = prologue_fp32(q, pos, theta, g_q, eps)
     k = prologue_fp32(k, pos, theta, g_k, eps)
     v = torch.as_tensor(v).to(torch.float32).numpy()
-    q8, sq = _quantize_rows(q)
-    k8, sk = _quantize_rows(k)
+    q8, sq = _quantize_rows(q, pow2=True)
+    k8, sk = _quantize_rows(k, pow2=True)
     v8, sv = _quantize_rows(v)
     return q8, k8, v8, sq, sk, sv
 

@@ -54,21 +54,64 @@ def test_saturation_reading():
     assert list(r) == [448.0, 448.0, 448.0, -448.0]
 
 
+def test_pow2_scale_closed_forms():
+    # 448 = 0.875 * 2^9 sits exactly on a boundary; one ulp above it needs
+    # the next power of two; all-zero vectors keep scale 1; the smallest
+    # normal fp32 power of two bounds the scale from below
+    amax = np.array([448.0, 449.0, np.nextafter(np.float32(448), np.float32(1e9)), 224.0,
+                     225.0, 896.0, 897.0, 3.0, 0.0, 1e-40, 2.0 ** -140, 1e30], np.float32)
+    want = [1.0, 2.0, 2.0, 0.5, 1.0, 2.0, 4.0, 2.0 ** -7, 1.0, 2.0 ** -126, 2.0 ** -126,
+            2.0 ** 91]
+    assert list(oracle.pow2_scale(amax).astype(np.float64)) == want
+
+
+def test_pow2_scale_is_the_smallest_power_of_two():
+    # brute force in exact float64 arithmetic (448 * 2^k is exact): the first
+    # k from -126 up with amax <= 448 * 2^k
+    rng = np.random.default_rng(5)
+    amax = np.exp2(rng.uniform(-60, 60, 3000)).astype(np.float32)
+    edges = np.array([448.0 * 2.0 ** j for j in range(-20, 21)], np.float32)
+    amax = np.concatenate([amax, edges, np.nextafter(edges, np.float32(0)),
+                           np.nextafter(edges, np.float32(np.inf))])
+    got = oracle.pow2_scale(amax)
+    for a, s in zip(amax.astype(np.float64), got.astype(np.float64)):
+        k = -126
+        while a > 448.0 * 2.0 ** k:
+            k += 1
+        assert s == 2.0 ** k, (a, s, k)
+
+
 def test_quantizer_properties():
     w = synth.WORKLOADS["tiny"].replace(outlier_frac=0.05)
     q, k, v, _ = synth.make_qkv(w, seed=1)
     v = v.clone()
     v[0, 3, 1] = 0.0                                        # an all-zero head vector
+    k = k.clone()
+    k[0, 5, 0] = 0.0
     pos = synth.positions(w)
     q8, k8, v8, sq, sk, sv = oracle.quant_rope_fp8(q, k, v, pos)
-    for x8, s in ((q8, sq), (k8, sk), (v8, sv)):
+    x32 = {"q": oracle.apply_rope(q, pos).numpy(), "k": oracle.apply_rope(k, pos).numpy()}
+    for x8, s, name in ((q8, sq, "q"), (k8, sk, "k"), (v8, sv, "v")):
         vals = oracle.e4m3_decode(x8)
         amax = np.abs(vals).max(-1)                         # [B, S, H]
-        nz = np.transpose(s, (0, 2, 1)) != 1.0
-        # the largest element of every non-zero vector lands exactly on 448
-        assert np.all(amax[nz] == 448.0)
+        sc = np.transpose(s, (0, 2, 1))
+        nz = amax > 0
         assert x8.dtype == np.uint8 and s.dtype == np.float32
+        if name in x32:
+            # a power of two, and the smallest one that keeps the codes in
+            # range: amax / scale lies in (224, 448] before rounding, so the
+            # largest code lies in [224, 448]
+            mant, _ = np.frexp(s.astype(np.float64))
+            assert np.all(mant == 0.5)
+            ratio = np.abs(x32[name]).max(-1) / sc
+            assert np.all(ratio[nz] <= 448.0) and np.all(ratio[nz] > 224.0)
+            assert np.all(amax[nz] <= 448.0) and np.all(amax[nz] >= 224.0)
+        else:
+            # the largest element of every non-zero vector lands exactly on 448
+            assert np.all(amax[nz] == 448.0)
+        assert np.all(sc[~nz] == 1.0)
     assert sv[0, 1, 3] == 1.0 and np.all(v8[0, 3, 1] == 0)
+    assert sk[0, 0, 5] == 1.0 and np.all(k8[0, 5, 0] == 0)
     # dequantization error is at most half an e4m3 spacing of x/scale
     qr = oracle.apply_rope(q, pos).numpy()
     deq = oracle.dequantize(q8, sq).numpy()
