@@ -203,7 +203,9 @@ ja_status joint_attn_fwd_bf16_block_sparse(const ja_params *p, const void *q, co
  *   sq, sk, sv  device float [batch][heads][seq_len]: one scale per (b, token,
  *               head).  For each head vector x (after RoPE, computed in fp32
  *               as (fma(x, c, -fl(y s)), fma(x, s, fl(y c)))): amax = max|x|;
- *               scale = amax/448 (1 if amax = 0);
+ *               Q and K: scale = the smallest power of two s with
+ *               amax <= 448 s, at least 2^-126 (an E8M0 exponent);
+ *               V: scale = amax/448; all three: 1 if amax = 0;
  *               code = e4m3_rne(clamp(fl(x/scale), -448, 448)).
  */
 ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q,
@@ -256,7 +258,13 @@ typedef struct {
  *   q8, k8, v8  device e4m3, contiguous [batch][seq_len][heads][head_dim]
  *               (the Q, K and V strides of p are ignored).
  *   sq, sk, sv  device float [batch][heads][seq_len] dequantization scales,
- *               16-byte aligned.
+ *               16-byte aligned.  sq and sk must be positive normal powers
+ *               of two (joint_attn_quant_rope_fp8 writes such scales): their
+ *               exponents are the E8M0 block scales of the Q K^T MFMA.  A
+ *               workgroup that meets any other value writes NaN into its O
+ *               rows and LSE entries (the head's rows for a K scale, the
+ *               256-row query block for a Q scale).  sv may be any positive
+ *               value.
  *   repair      nullable: repaired tokens from joint_attn_fp8_repair_plan.
  *               Their keys are removed from the FP8 tiles and attended from
  *               kr / vr (bf16 products) in the same softmax.
@@ -265,11 +273,13 @@ typedef struct {
  *   workspace, workspace_bytes
  *               optional scratch of joint_attn_fwd_fp8_workspace_bytes(p)
  *               bytes, as for joint_attn_fwd_bf16.
- * Q K^T and P.V run on FP8 MFMA.  The K scale multiplies the fp32 scores,
- * the Q scale joins the softmax scale; V's per-key scale is folded into the
- * probabilities before they are rounded to e4m3 for P.V
- * (P' = P * sv[key] * 64 / max(sv), undone in the epilogue).  Softmax
- * statistics and accumulation are fp32; the output is bf16.
+ * Q K^T and P.V run on FP8 MFMA, Q K^T with the Q and K scales as E8M0
+ * block scales.  V's per-key scale is folded into the probabilities before
+ * they are rounded to e4m3 for P.V: each score accumulator starts at
+ * log2(sv[key]) / c (c the softmax scale in the exp2 domain), so that
+ * P' = exp2(c acc - ref) = P * sv[key], with the reference ref kept 6 below
+ * the running row max (P' < 2^8).  Softmax statistics and accumulation are
+ * fp32; the output is bf16.
  */
 ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
                              const void *v8, const float *sq, const float *sk,

@@ -282,7 +282,8 @@ def fwd_bf16_workspace_bytes(batch: int, seq_len: int, heads: int, head_dim: int
 
 def quant_rope_fp8(q, k, v, rope=None, q_norm=None, k_norm=None, norm_eps: float = 0.0):
     """Optional Q/K RMS norm, RoPE on Q/K, per-token e4m3 quantization.  Returns
-    (q8, k8, v8, sq, sk, sv): uint8 codes [B, S, H, D] and fp32 scales [B, H, S]."""
+    (q8, k8, v8, sq, sk, sv): uint8 codes [B, S, H, D] and fp32 scales [B, H, S]
+    (powers of two for Q and K, amax/448 for V)."""
     b, s, h, d = q.shape
     dev = q.device
     q8, k8, v8 = (torch.empty((b, s, h, d), dtype=torch.uint8, device=dev) for _ in range(3))
@@ -331,7 +332,9 @@ def fp8_repair_plan(k, v, rope, k8, v8, sk, sv, n_rep: int, k_norm=None,
 def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
             split: bool = True, repair: "Fp8Repair | None" = None):
     """Joint attention on contiguous e4m3 codes [B, S, H, D] with fp32 scales [B, H, S].
-    `split` as for fwd_bf16; `repair` from fp8_repair_plan (None: no repair)."""
+    sq and sk must be powers of two, as quant_rope_fp8 writes them (rows that
+    meet another value come back NaN).  `split` as for fwd_bf16; `repair`
+    from fp8_repair_plan (None: no repair)."""
     b, s, h, d = q8.shape
     for t in (q8, k8, v8):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous() \

@@ -4,17 +4,21 @@
 // FP8 attention is the pages' qk_dtype / v_dtype fp8 setting ("Speed Up Image
 // Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", section
 // "Quantized and sparse attention").  Both products run on
-// v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands, no block scaling) in the
-// transposed orientation of the bf16 kernel, so a lane owns one query row:
-//   S^T[key][q] = K8 . Q8^T, then t = acc * sk[key]; scores = t * sq[q] * scale
+// v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 operands) in the transposed
+// orientation of the bf16 kernel, so a lane owns one query row:
+//   acc[key][q] = log2(sv[key]) / c + sk[key] sq[q] (K8 . Q8^T)[key][q]
 //   O^T[d][q]  += V8^T . P'^T
-// V's scale is per key, i.e. on the reduction index of P.V, so it is folded
-// into P before the e4m3 cast: P'[q][key] = P * sv[key] * 64 / sv_max, where
-// sv_max is the largest V scale of the (batch, head).  P stays below 2^2 (the
-// running max is refreshed whenever a row max grows by more than 2 in the
-// exp2 domain), so P' stays below 256, inside the e4m3 range; the epilogue
-// multiplies by sv_max / 64.  The softmax normaliser sums the unquantized
-// fp32 P.
+// Q's and K's scales are powers of two (the quantizer's choice): the MFMA
+// applies them exactly as E8M0 block scales.  V's scale is per key, i.e. on
+// the reduction index of P.V, where no block scale reaches; it enters the
+// exp2 argument through the accumulator's initial value instead, so that
+// P' = exp2(c acc - ref) = P sv[key] with c the softmax scale in the exp2
+// domain, and P'.V8 is P.V in true units.  The running max of c acc is
+// refreshed whenever a row max grows by more than 2, and the reference sits
+// 6 below it, so P' stays below 2^8, inside the e4m3 range.  The softmax
+// normaliser sums the unquantized fp32 P' / sv[key].  A key past the end or
+// a repaired key starts at -inf.  Per score this leaves a max, an FMA, an
+// exp2, the sum's FMA and half a conversion.
 //
 // Structure as in the bf16 kernel: one workgroup of eight wave64s (two per
 // SIMD) per (256-query block, head, batch row), XCD-aware placement, K/V tiles
@@ -41,10 +45,12 @@ constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
 constexpr int NT = 64 * NW;         // threads per workgroup
 constexpr int VTSTR = BN + 16;      // bytes per V^T row in LDS (16-byte pad)
 
-// P may exceed 1 by up to 2^kRescaleLog2 before the running max is refreshed;
-// kPScale = 256 / 2^kRescaleLog2 keeps P' = P * sv / sv_max * kPScale <= 256.
+// The running max m is refreshed when some row's max grows by more than
+// kRescaleLog2 (exp2 domain); until then P' = exp2(u - m + kPOffset) stays
+// below 2^(kRescaleLog2 + kPOffset) = 256, inside the e4m3 range, and the
+// largest P' of a row sits near the top of that range.
 constexpr float kRescaleLog2 = 2.f;
-constexpr float kPScale = 64.f;
+constexpr float kPOffset = 6.f;
 
 constexpr int kBufferFlags = 0x00020000;
 
@@ -66,9 +72,24 @@ struct Fp8Args {
   int n_rep, n_pad;
 };
 
+// Formats 0 = fp8 e4m3 for both operands; sa / sb are E8M0 exponents (127 =
+// x1): lane (l32, hf) gives the scale of A row l32 and of B column l32 for
+// the 32-element k-block hf (checked on hardware).
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+// Unscaled (constant zero scale operands select the plain instruction).
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
-  // format 0 = fp8 e4m3 for both operands, no block scaling
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// E8M0 exponent of a scale, which must be a positive normal power of two (its
+// fp32 exponent field); anything else sets `bad`.
+__device__ __forceinline__ int e8m0_of(float s, bool &bad) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t e = u >> 23;                 // includes the sign bit
+  bad = bad || (u & 0x7fffffu) != 0 || e == 0 || e >= 255;
+  return (int)e;
 }
 
 __device__ __forceinline__ float half_max(float x) {
@@ -105,10 +126,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   static_assert(K_THREADS <= NT && V_THREADS <= NT, "staging layout");
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2][Fp8Lds<D>::KTILE];
   __shared__ __attribute__((aligned(16))) uint8_t Vt[2][Fp8Lds<D>::VTILE];
-  __shared__ __attribute__((aligned(16))) float sk_t[2][BN];
-  __shared__ __attribute__((aligned(16))) float wv_t[2][BN];
-  __shared__ __attribute__((aligned(16))) float kb_t[REPAIR ? 2 : 1][REPAIR ? BN : 4];
-  __shared__ float red[NW];
+  // per key of a staged tile: with K, the initial value of its score
+  // accumulator (log2 of its V scale over the softmax scale; -inf past the
+  // end or for a repaired key) and the E8M0 exponent of its K scale; with V,
+  // the reciprocal of its V scale
+  __shared__ __attribute__((aligned(16))) float bias_t[2][BN];
+  __shared__ __attribute__((aligned(16))) int ke_t[2][BN];
+  __shared__ __attribute__((aligned(16))) float inv_t[2][BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -138,18 +162,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t row_stride = (int64_t)a.H * D;  // contiguous [B, S, H, D]
 
-  // ---- largest V scale of this (b, h) ----
-  float vmax = 0.f;
-  for (int s = tid; s < S; s += NT) vmax = fmaxf(vmax, a.sv[bh * S + s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-  if (lane == 0) red[wave] = vmax;
-  __syncthreads();
-  float sv_max = red[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) sv_max = fmaxf(sv_max, red[w]);
-  const float wv_mul = kPScale / sv_max;
-
   // ---- Q8 of this lane's query row ----
   const int qi = qblk * BM + wave * 32 + l32;
   const int qs = qi < S ? qi : S - 1;
@@ -162,7 +174,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     qreg[kk] = i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     if (qi >= S) qreg[kk] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
-  const float qmul = a.sq[bh * S + qs] * a.scale_log2;
+  // Q's scale enters Q K^T as an E8M0 block scale (the repair pass uses it
+  // in the exp2 argument instead)
+  bool bad = false;
+  const float sqv = a.sq[bh * S + qs];
+  const int qe = e8m0_of(sqv, bad);
+  const float c = a.scale_log2;
+  const float qmul = sqv * c;
 
   // ---- staging through buffer resources (rows past the end read as 0) ----
   const uint8_t *kbase = a.k + (int64_t)b * S * row_stride + (int64_t)h * D;
@@ -182,10 +200,22 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const int voff = (int)(4 * vm * row_stride) + 4 * vn;
   u32x4 kreg;
   uint32_t vreg[4];
-  float skreg = 0.f, svreg = 0.f, kbreg = 0.f;
+  // per-key values of the tile being staged: with K, its K scale, V scale
+  // and repair bias; with V, its V scale (keys past the end: K scale 1, V
+  // scale 0)
+  float skreg = 1.f, svkreg = 0.f, kbreg = 0.f, svvreg = 0.f;
+  const float inv_c = 1.f / c;
   auto load = [&](int t, bool with_k, bool with_v) JA_INLINE {
-    if (with_k && tid < K_THREADS)
-      kreg = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(krs, koff, t * tile_bytes, 0));
+    const int key = t * BN + tid;
+    if (with_k) {
+      if (tid < K_THREADS)
+        kreg = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(krs, koff, t * tile_bytes, 0));
+      if (tid < BN) {
+        skreg = key < S ? a.sk[bh * S + key] : 1.f;
+        svkreg = key < S ? a.sv[bh * S + key] : 0.f;
+        if constexpr (REPAIR) kbreg = key < S ? a.kbias[bh * S + key] : 0.f;
+      }
+    }
     if (with_v) {
       if (tid < V_THREADS) {
 #pragma unroll
@@ -193,16 +223,19 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
           vreg[k] = __builtin_amdgcn_raw_buffer_load_b32(vrs, voff + (int)(k * row_stride),
                                                          t * tile_bytes, 0);
       }
-      if (tid < BN) {
-        const int key = t * BN + tid;
-        skreg = key < S ? a.sk[bh * S + key] : 0.f;
-        if constexpr (REPAIR) kbreg = key < S ? a.kbias[bh * S + key] : 0.f;
-        svreg = key < S ? a.sv[bh * S + key] : 0.f;
-      }
+      if (tid < BN) svvreg = key < S ? a.sv[bh * S + key] : 0.f;
     }
   };
   auto store_k = [&](int buf) JA_INLINE {
     if (tid < K_THREADS) *reinterpret_cast<u32x4 *>(&Ks[buf][kr * KSTR + kc * 16]) = kreg;
+    if (tid < BN) {
+      // c * (acc + log2(sv)/c) = c * score + log2(sv): exp2 of it carries the
+      // factor sv that P.V needs (log2(0) = -inf removes a key past the end)
+      float bias = log2f(svkreg) * inv_c;
+      if constexpr (REPAIR) bias += kbreg;          // -inf for a repaired key
+      bias_t[buf][tid] = bias;
+      ke_t[buf][tid] = e8m0_of(skreg, bad);
+    }
   };
   auto store_v = [&](int buf) JA_INLINE {
     if (tid < V_THREADS) {
@@ -221,26 +254,32 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       for (int j = 0; j < 4; ++j)
         *reinterpret_cast<uint32_t *>(&Vt[buf][(4 * vn + j) * VTSTR + pos]) = u[j];
     }
-    if (tid < BN) {
-      sk_t[buf][tid] = skreg;
-      if constexpr (REPAIR) kb_t[buf][tid] = kbreg;
-      wv_t[buf][tid] = svreg * wv_mul;
-    }
+    if (tid < BN) inv_t[buf][tid] = svvreg > 0.f ? 1.f / svvreg : 0.f;
   };
 
-  // ---- S^T = K8 . Q8^T for the 64 keys of a tile (two 32-key blocks) ----
+  // ---- S^T = K8 . Q8^T for the 64 keys of a tile (two 32-key blocks), the
+  //      K and Q scales applied as E8M0 block scales, each accumulator
+  //      starting at its key's bias (element i of a lane is key
+  //      kb*32 + 8(i/4) + 4hf + i%4): acc = sk sq K8.Q8 + log2(sv)/c ----
   auto qk = [&](int buf, f32x16 (&sacc)[2]) JA_INLINE {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+      for (int g = 0; g < 4; ++g) {
+        const float4 bg = *reinterpret_cast<const float4 *>(&bias_t[buf][kb * 32 + g * 8 + hf * 4]);
+        sacc[kb][4 * g] = bg.x;
+        sacc[kb][4 * g + 1] = bg.y;
+        sacc[kb][4 * g + 2] = bg.z;
+        sacc[kb][4 * g + 3] = bg.w;
+      }
+      const int ke = ke_t[buf][kb * 32 + l32];    // A row l32 is key kb*32 + l32
       const uint8_t *krow = &Ks[buf][(kb * 32 + l32) * KSTR + 32 * hf];
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk) {
         const i32x4 lo = *reinterpret_cast<const i32x4 *>(krow + 64 * kk);
         const i32x4 hi = *reinterpret_cast<const i32x4 *>(krow + 64 * kk + 16);
         sacc[kb] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qreg[kk],
-                            sacc[kb]);
+                            sacc[kb], ke, qe);
       }
     }
   };
@@ -260,60 +299,51 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     }
   };
 
-  // ---- online softmax of one tile; m_run is in the exp2 domain.  As in the
-  //      bf16 kernel, P is first computed against the running max and only
-  //      recomputed (with O and l rescaled) when some row max grew by more
-  //      than the threshold. ----
-  float m_run = -INFINITY, l_run = 0.f;
+  // ---- online softmax of one tile.  u = c acc = c score + log2(sv) is a
+  //      key's score in the exp2 domain plus log2 of its V scale; m_run
+  //      tracks the row max of u, and P' = exp2(u - m_run + kPOffset) is P
+  //      times sv against the reference m_run - kPOffset, so P'.V8 is P.V in
+  //      true units and the row sum adds P' / sv.  As in the bf16 kernel, P'
+  //      is first computed against the running max and only recomputed (with
+  //      O and l rescaled) when some row max grew by more than the threshold.
+  //      m_run starts finite, so that a tile whose keys are all -inf leaves
+  //      it (and O, l) unchanged. ----
+  float m_run = -1e30f, l_run = 0.f;
   auto exp_tile = [&](const f32x16 (&t)[2], float mref, int buf, float &psum) JA_INLINE -> i32x8 {
+    const float nref = kPOffset - mref;
     uint32_t pw[8];
     psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 wg = *reinterpret_cast<const float4 *>(&wv_t[buf][kb * 32 + g * 8 + hf * 4]);
+        const float4 ig = *reinterpret_cast<const float4 *>(&inv_t[buf][kb * 32 + g * 8 + hf * 4]);
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][4 * g + i], qmul, -mref));
-          psum += p[i];
-        }
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0] * wg.x, p[1] * wg.y, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2] * wg.z, p[3] * wg.w, w, true);
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][4 * g + i], c, nref));
+        psum = __builtin_fmaf(p[0], ig.x, psum);
+        psum = __builtin_fmaf(p[1], ig.y, psum);
+        psum = __builtin_fmaf(p[2], ig.z, psum);
+        psum = __builtin_fmaf(p[3], ig.w, psum);
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pw[kb * 4 + g] = (uint32_t)w;
       }
     return bit_cast<i32x8>(pw);
   };
-  auto softmax = [&]<bool TAIL>(f32x16 (&sacc)[2], int j0, int buf) JA_INLINE -> i32x8 {
+  auto softmax = [&](f32x16 (&sacc)[2], int buf) JA_INLINE -> i32x8 {
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 skg = *reinterpret_cast<const float4 *>(&sk_t[buf][kb * 32 + g * 8 + hf * 4]);
-        const float skv[4] = {skg.x, skg.y, skg.z, skg.w};
-        float kbv[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (REPAIR) {
-          const float4 kbg = *reinterpret_cast<const float4 *>(&kb_t[buf][kb * 32 + g * 8 + hf * 4]);
-          kbv[0] = kbg.x; kbv[1] = kbg.y; kbv[2] = kbg.z; kbv[3] = kbg.w;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // a repaired key's bias is -inf: it leaves the FP8 tile and is
-          // attended from its exact values after the loop
-          float t = REPAIR ? __builtin_fmaf(sacc[kb][4 * g + i], skv[i], kbv[i])
-                           : sacc[kb][4 * g + i] * skv[i];
-          if (TAIL && j0 + kb * 32 + g * 8 + hf * 4 + i >= S) t = -INFINITY;
-          sacc[kb][4 * g + i] = t;
-          tmax = fmaxf(tmax, t);
-        }
-      }
-    // the row max of t * qmul is qmul * max(t) (qmul > 0)
-    const float mx = half_max(tmax) * qmul;
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
+    const float mx = half_max(tmax) * c;      // c > 0
     const bool grow = mx > m_run + kRescaleLog2;
     float psum;
     i32x8 pb = exp_tile(sacc, m_run, buf, psum);
+    // the fast path's sum stays before the branch (sunk past it, its
+    // reciprocal-scale reads would wait one by one)
+    asm volatile("" ::"v"(psum));
     if (__builtin_amdgcn_ballot_w64(grow)) {
       asm volatile("" ::"v"(pb));
       const float m_new = grow ? mx : m_run;
@@ -354,7 +384,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   auto iteration = [&]<int PAR, bool LAST>(int i) JA_INLINE {
     const int t = t0 + i;
     if constexpr (!LAST) qk((i + 1) & 1, sacc[PAR ^ 1]);
-    const i32x8 pb = softmax.template operator()<LAST>(sacc[PAR], t * BN, i & 1);
+    const i32x8 pb = softmax(sacc[PAR], i & 1);
     pv(pb, i & 1);
     if constexpr (!LAST) {
       if (i + 2 < nt) store_k(i & 1);
@@ -381,9 +411,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   // ---- repaired keys: one more pass over them with their exact values, on
   //      bf16 MFMA (an e4m3 code times its scale is exact in this product:
   //      the codes are bf16-representable and the scale stays in the exp2
-  //      argument), within the same online softmax.  P.V adds P * 64/sv_max
-  //      times the exact V, the units of the FP8 accumulator.  Only one part
-  //      of a split item runs it. ----
+  //      argument), within the same online softmax: P against the reference
+  //      m_run - kPOffset times the exact V, in the true units of the FP8
+  //      accumulator.  Only one part of a split item runs it. ----
   if constexpr (REPAIR) {
     if (a.n_rep > 0 && (unit < 0 || unit % a.parts == 0)) {
       constexpr int KBS = D + 8;          // bf16 per staged K row (16-byte pad)
@@ -409,15 +439,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         if (qi >= S) w = u32x4{0, 0, 0, 0};
         qb[kk] = bit_cast<bf16x8>(w);
       }
-      const float pmul = kPScale / sv_max;
       const bf16 *krb = a.kr + bh * a.n_pad * D;
       const bf16 *vrb = a.vr + bh * a.n_pad * D;
       for (int r0 = 0; r0 < a.n_pad; r0 += 32) {
         // stage 32 keys: K row-major, V transposed in the P operand's key order
         if (tid < 32 * (D / 8)) {
-          const int r = tid / (D / 8), c = tid % (D / 8);
-          *reinterpret_cast<u32x4 *>(kbuf + r * KBS + c * 8) =
-              *reinterpret_cast<const u32x4 *>(krb + (int64_t)(r0 + r) * D + c * 8);
+          const int r = tid / (D / 8), ch = tid % (D / 8);
+          *reinterpret_cast<u32x4 *>(kbuf + r * KBS + ch * 8) =
+              *reinterpret_cast<const u32x4 *>(krb + (int64_t)(r0 + r) * D + ch * 8);
         }
         if (tid < D * 4) {
           const int vd = tid % D, vc = tid / D;
@@ -455,10 +484,11 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
             uint32_t w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * g + 2 * e], qmul, -mref));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * g + 2 * e + 1], qmul, -mref));
+              const float nref = kPOffset - mref;
+              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * g + 2 * e], qmul, nref));
+              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * g + 2 * e + 1], qmul, nref));
               ps += p0 + p1;
-              w[e] = pack_bf16x2(p0 * pmul, p1 * pmul);
+              w[e] = pack_bf16x2(p0, p1);
             }
             pbr[g] = bit_cast<bf16x8>(u32x4{w[0], w[1], w[2], w[3]});
           }
@@ -491,10 +521,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     }
   }
 
+  // a Q or K scale that is not a positive normal power of two turns the rows
+  // of its workgroup into NaN
+  const bool bad_wg = __syncthreads_or(bad);
+  const float o_mul = bad_wg ? __builtin_nanf("") : 1.f;
   const float l_tot = half_sum(l_run);
-  const float o_mul = sv_max / kPScale;
+  const float ref = m_run - kPOffset;       // P was computed against ref
   if (unit >= 0) {
-    // split part: unnormalised O in true units, row max (exp2 domain), sum
+    // split part: unnormalised O in true units, reference (exp2 domain), sum
     const int row = wave * 32 + l32;
     float *orow = a.ws.o + ((int64_t)unit * BM + row) * D;
 #pragma unroll
@@ -506,7 +540,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
                         oacc[db][4 * grp + 2] * o_mul, oacc[db][4 * grp + 3] * o_mul);
     if (hf == 0)
       *reinterpret_cast<float2 *>(a.ws.ml + ((int64_t)unit * BM + row) * 2) =
-          make_float2(m_run, l_tot);
+          make_float2(ref * o_mul, l_tot);
     return;
   }
   if (qi < S) {
@@ -522,7 +556,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         w.y = pack_bf16x2(oacc[db][4 * grp + 2] * inv, oacc[db][4 * grp + 3] * inv);
         *reinterpret_cast<u32x2 *>(orow + d) = w;
       }
-    if (a.lse && hf == 0) a.lse[bh * S + qi] = (m_run + __log2f(l_tot)) * kLn2;
+    if (a.lse && hf == 0) a.lse[bh * S + qi] = (ref + __log2f(l_tot)) * kLn2 * o_mul;
   }
 }
 

@@ -3,15 +3,18 @@
 // The pages switch attention to FP8 Q/K and V (qk_dtype / v_dtype fp8,
 // "Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA Blackwell
 // GPUs", section "Quantized and sparse attention").  Granularity and format
-// here: one fp32 scale per (batch, token, head) head vector, amax/448, codes
-// in OCP e4m3 (v_cvt_pk_fp8_f32 produces OCP e4m3 on gfx950), round to
-// nearest even, saturated at +-448.
+// here: one fp32 scale per (batch, token, head) head vector, codes in OCP
+// e4m3 (v_cvt_pk_fp8_f32 produces OCP e4m3 on gfx950), round to nearest even,
+// saturated at +-448.  V's scale is amax/448.  Q's and K's is the smallest
+// power of two s with amax <= 448 s (an E8M0 exponent, which the fp8 matrix
+// core applies exactly in Q K^T).
 //
 // The pass is HBM-bound (read bf16, write 1-byte codes): each head vector of
 // D elements is handled by D/8 lanes with one 16-byte load each; its amax is
 // reduced with lane exchanges inside that lane group.  The rotation uses the
-// fixed fp32 operation order of rope_pair_f32 and the division x / scale is
-// IEEE-rounded, so the codes are a fixed function of the inputs.
+// fixed fp32 operation order of rope_pair_f32 and x / scale is IEEE-rounded
+// (for a power of two, the exact product x * 2^-k), so the codes are a fixed
+// function of the inputs.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -78,14 +81,27 @@ __global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
   for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(r[e]));
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  float scale = 1.f, inv = 1.f;
+  if (t < 2) {
+    // amax = m 2^E with m in [1, 2) and 448 = 1.75 2^8: s = 2^(E-8), or
+    // 2^(E-7) when m > 1.75; at least 2^-126 (subnormal amax included)
+    const uint32_t ab = __float_as_uint(amax);
+    const int k = max((int)(ab >> 23) - 135 + ((ab & 0x7fffffu) > 0x600000u ? 1 : 0), -126);
+    if (amax > 0.f) {
+      scale = __uint_as_float((uint32_t)(127 + k) << 23);
+      inv = __uint_as_float((uint32_t)(127 - k) << 23);
+    }
+  } else if (amax > 0.f) {
+    scale = amax / 448.f;
+  }
 
   uint32_t packed[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     float y[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(r[4 * e + j] / scale, -448.f), 448.f);
+    for (int j = 0; j < 4; ++j)
+      y[j] = fminf(fmaxf(t < 2 ? r[4 * e + j] * inv : r[4 * e + j] / scale, -448.f), 448.f);
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     packed[e] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
   }

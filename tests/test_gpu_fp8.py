@@ -83,6 +83,34 @@ def test_fp8_forward_ragged(s, d):
     assert rel_l2(out, ref) <= FP8_REL_L2
 
 
+@pytest.mark.parametrize("which", ["k", "q"])
+def test_fp8_forward_poisons_rows_of_non_power_of_two_scales(which):
+    # Q and K scales must be powers of two (the MFMA applies their exponent);
+    # a violation turns the affected rows into NaN: every row of the head for
+    # a K scale, the workgroup's 256-row query block for a Q scale.  Other
+    # heads are untouched.
+    w = synth.Workload("badscale", 1, 2, 64, n_text=300, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=3)
+    q8, k8, v8, sq, sk, sv = oracle.quant_rope_fp8(q, k, v, None)
+    _say(f"fp8 fwd with a non-power-of-two {which} scale")
+    ref = _fwd_fp8_from_oracle_codes(q8, k8, v8, sq, sk, sv, split=False).cpu()
+    sq, sk = sq.copy(), sk.copy()
+    if which == "k":
+        sk[0, 1, 200] *= 1.5
+    else:
+        sq[0, 1, 10] *= 1.5
+    out, lse = _fwd_fp8_from_oracle_codes(q8, k8, v8, sq, sk, sv, split=False, return_lse=True)
+    out, lse = out.cpu(), lse.cpu()
+    assert torch.equal(out[:, :, 0].view(torch.int16), ref[:, :, 0].view(torch.int16))
+    assert not torch.isnan(lse[:, 0]).any()
+    head1 = out[:, :, 1].float()
+    if which == "k":
+        assert torch.isnan(head1).all() and torch.isnan(lse[:, 1]).all()
+    else:
+        assert torch.isnan(head1[:, :256]).all() and torch.isnan(lse[:, 1, :256]).all()
+        assert not torch.isnan(head1[:, 256:]).any()
+
+
 def test_fp8_full_path_1024():
     # GPU quantizer -> GPU FP8 forward, against oracle quantizer -> fp64 attention.
     w = synth.WORKLOADS["t2i_1024"]
