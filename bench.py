@@ -12,8 +12,9 @@ Also reported on the same JSON line:
   roofline      the attention forward's own average duration (HIP events on
                 the launch stream, the K/V preparation excluded and reported
                 beside it) against the bf16 dense MFMA peak;
-  fp8           the FP8 path (RoPE+quantize pass, FP8 forward) timed the same
-                way, against the fp8 MFMA peak and HBM bandwidth, and with the
+  fp8           the FP8 path (RoPE+quantize pass, K/V preparation, FP8
+                forward) timed the same way, against the fp8 MFMA peak and
+                HBM bandwidth, and with the
                 repair of the tokens with the largest quantization error
                 (budget 0.005);
   qk_norm       the same passes with query/key RMS normalization fused
@@ -199,17 +200,23 @@ def main() -> int:
     fp8_outs = None
     if not args.no_fp8:
         q8, k8, v8, sq, sk, sv = ja.quant_rope_fp8(qd, kd, vd, rope)
+        kv8 = ja.prep_kv_fp8(k8, v8, sk, sv)
         out8 = torch.empty_like(out)
         for _ in range(2):
             ja.quant_rope_fp8(qd, kd, vd, rope)
-            ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8)
+            ja.prep_kv_fp8(k8, v8, sk, sv)
+            ja.fwd_fp8_prepared(q8, sq, kv8, out=out8)
         torch.cuda.synchronize()
         n = max(args.steps, 5)
         qms = _time_launches(lambda: ja.quant_rope_fp8(qd, kd, vd, rope), n)
-        fms = _time_launches(lambda: ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8), n)
-        q_avg, f_avg = sum(qms) / n, sum(fms) / n
+        pp8 = _time_launches(lambda: ja.prep_kv_fp8(k8, v8, sk, sv), n)
+        fms = _time_launches(lambda: ja.fwd_fp8_prepared(q8, sq, kv8, out=out8), n)
+        q_avg, pp_avg, f_avg = sum(qms) / n, sum(pp8) / n, sum(fms) / n
         elems = B * S * H * D
         q_bytes = 3 * elems * 2 + S * (D // 2) * 8 + 3 * elems + 3 * B * H * S * 4
+        # preparation: read K and V codes and two scales, write the prepared
+        # K, V^T and 16 bytes of per-key values per key (64-key padding aside)
+        pp_bytes = 2 * elems + 2 * B * H * S * 4 + 2 * elems + B * H * S * 16
         f_tf = flops / (f_avg * 1e-3) / 1e12
         fp8 = {"fwd_ms": round(f_avg, 4), "fwd_tflops": round(f_tf, 2),
                "fwd_frac_of_fp8_peak": round(f_tf / PEAK_FP8_TFLOPS, 4),
@@ -220,24 +227,28 @@ def main() -> int:
                "quant_frac_of_hbm": round(q_bytes / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                "quant_traffic": _traffic_for_current_kernel("quant_rope_fp8_t2i_2048_traffic.txt",
                                                             "quant_fp8.hip"),
-               "path_tflops": round(flops / ((f_avg + q_avg) * 1e-3) / 1e12, 2)}
+               "prep_ms": round(pp_avg, 4),
+               "prep_gbs": round(pp_bytes / (pp_avg * 1e-3) / 1e9, 1),
+               "path_tflops": round(flops / ((f_avg + q_avg + pp_avg) * 1e-3) / 1e12, 2)}
         _log(f"[bench] fp8: fwd {f_avg:.3f} ms ({f_tf:.1f} TFLOP/s), quant {q_avg:.3f} ms "
-             f"({fp8['quant_gbs']} GB/s)")
+             f"({fp8['quant_gbs']} GB/s), K/V prep {pp_avg:.3f} ms ({fp8['prep_gbs']} GB/s)")
         # repair of the tokens with the largest quantization error, at the
         # pages' budget 0.005
         n_rep = ja.repair_count(REPAIR_BUDGET, S)
         rp = ja.fp8_repair_plan(kd, vd, rope, k8, v8, sk, sv, n_rep)
+        kv8r = ja.prep_kv_fp8(k8, v8, sk, sv, repair=rp)
         out8r = torch.empty_like(out)
         for _ in range(2):
-            ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8r, repair=rp)
+            ja.fwd_fp8_prepared(q8, sq, kv8r, out=out8r, repair=rp)
         torch.cuda.synchronize()
         pms = _time_launches(lambda: ja.fp8_repair_plan(kd, vd, rope, k8, v8, sk, sv, n_rep), n)
-        rms = _time_launches(lambda: ja.fwd_fp8(q8, k8, v8, sq, sk, sv, out=out8r, repair=rp), n)
+        rms = _time_launches(lambda: ja.fwd_fp8_prepared(q8, sq, kv8r, out=out8r, repair=rp), n)
         p_avg, r_avg = sum(pms) / n, sum(rms) / n
         fp8["repair"] = {"budget": REPAIR_BUDGET, "tokens_per_head": n_rep,
                          "plan_ms": round(p_avg, 4), "fwd_ms": round(r_avg, 4),
                          "fwd_tflops": round(flops / (r_avg * 1e-3) / 1e12, 2),
-                         "path_tflops": round(flops / ((q_avg + p_avg + r_avg) * 1e-3) / 1e12, 2)}
+                         "path_tflops": round(flops / ((q_avg + p_avg + pp_avg + r_avg) * 1e-3)
+                                              / 1e12, 2)}
         _log(f"[bench] fp8 + repair ({n_rep} tokens/head): plan {p_avg:.3f} ms, fwd {r_avg:.3f} ms")
         fp8_outs = (out8, out8r)
 

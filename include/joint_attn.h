@@ -253,21 +253,58 @@ typedef struct {
 } ja_fp8_repair;
 
 /*
+ * joint_attn_prep_kv_fp8_bytes - bytes of the prepared K/V buffer of the FP8
+ * forward for this shape (0 if p is invalid).  Host-only.
+ */
+size_t joint_attn_prep_kv_fp8_bytes(const ja_params *p);
+
+/*
+ * joint_attn_prep_kv_fp8 - K/V preparation of the FP8 forward: the e4m3 keys
+ * and values of each (batch, head) laid out as the forward's LDS tiles, with
+ * the per-key values of its softmax.  One pass over K and V.
+ *   p           shape and softmax_scale (the forward must use the same); the
+ *               Q, K, V and O strides are unused.
+ *   k8, v8, sk, sv   joint_attn_quant_rope_fp8's outputs: e4m3 codes
+ *               contiguous [batch][seq_len][heads][head_dim], 16-byte aligned;
+ *               fp32 scales [batch][heads][seq_len].  sk must hold positive
+ *               normal powers of two (the quantizer's K scales), sv positive
+ *               finite values; a key that breaks this turns every row of its
+ *               (batch, head) into NaN in the forward.
+ *   repair      nullable; with n_rep > 0 its kbias (0, or -inf for a
+ *               repaired key, from joint_attn_fp8_repair_plan) removes the
+ *               repaired keys from the FP8 tiles.
+ *   kv8, kv8_bytes   device output of at least
+ *               joint_attn_prep_kv_fp8_bytes(p) bytes, 16-byte aligned:
+ *               K [B*H][S_pad][D], then V^T [B*H][D][S_pad] (keys of each
+ *               64-key tile in the order in which the forward's P' operand
+ *               holds them), then [B*H][S_pad/64] blocks of 256 words per
+ *               tile: log2(sv)/c (+ kbias; -inf past the end), 1/sv (0 past
+ *               the end), the E8M0 exponent of sk (127 past the end), c; with
+ *               S_pad = seq_len rounded up to 64, c the softmax scale times
+ *               log2(e), rows past the end zero.
+ * Same size limits as joint_attn_fwd_fp8.
+ */
+ja_status joint_attn_prep_kv_fp8(const ja_params *p, const void *k8, const void *v8,
+                                 const float *sk, const float *sv, const ja_fp8_repair *repair,
+                                 void *kv8, size_t kv8_bytes, void *stream);
+
+/*
  * joint_attn_fwd_fp8 - joint attention on FP8 inputs produced by
- * joint_attn_quant_rope_fp8 (RoPE already applied).
- *   q8, k8, v8  device e4m3, contiguous [batch][seq_len][heads][head_dim]
- *               (the Q, K and V strides of p are ignored).
- *   sq, sk, sv  device float [batch][heads][seq_len] dequantization scales,
- *               16-byte aligned.  sq and sk must be positive normal powers
- *               of two (joint_attn_quant_rope_fp8 writes such scales): their
- *               exponents are the E8M0 block scales of the Q K^T MFMA.  A
- *               workgroup that meets any other value writes NaN into its O
- *               rows and LSE entries (the head's rows for a K scale, the
- *               256-row query block for a Q scale).  sv may be any positive
- *               value.
- *   repair      nullable: repaired tokens from joint_attn_fp8_repair_plan.
- *               Their keys are removed from the FP8 tiles and attended from
- *               kr / vr (bf16 products) in the same softmax.
+ * joint_attn_quant_rope_fp8 (RoPE already applied), with K and V prepared
+ * by joint_attn_prep_kv_fp8.
+ *   q8          device e4m3, contiguous [batch][seq_len][heads][head_dim]
+ *               (the Q, K and V strides of p are ignored), 16-byte aligned.
+ *   sq          device float [batch][heads][seq_len]: Q's dequantization
+ *               scales, positive normal powers of two (the quantizer's);
+ *               their exponents are the E8M0 block scales of the Q K^T MFMA.
+ *               A workgroup that meets another value writes NaN into its O
+ *               rows and LSE entries (its 256-row query block).
+ *   kv8, kv8_bytes   the prepared K/V buffer.  If it was prepared for another
+ *               softmax scale, every row comes back NaN.
+ *   repair      nullable: with n_rep > 0, the repaired tokens from
+ *               joint_attn_fp8_repair_plan (kr, vr; kbias went to the
+ *               preparation), attended from their bf16 values in the same
+ *               softmax.
  *   o           device bf16, layout per ja_params (o_* strides).
  *   lse         device float [batch][heads][seq_len], nullable.
  *   workspace, workspace_bytes
@@ -277,14 +314,14 @@ typedef struct {
  * block scales.  V's per-key scale is folded into the probabilities before
  * they are rounded to e4m3 for P.V: each score accumulator starts at
  * log2(sv[key]) / c (c the softmax scale in the exp2 domain), so that
- * P' = exp2(c acc - ref) = P * sv[key], with the reference ref kept 6 below
+ * P' = exp2(c acc - ref) = P * sv[key], with the reference ref kept 5 below
  * the running row max (P' < 2^8).  Softmax statistics and accumulation are
- * fp32; the output is bf16.
+ * fp32; the output is bf16.  The size of one (batch, head)'s prepared K or V
+ * (S_pad * head_dim bytes) must stay below 2^31: JA_ERR_UNSUPPORTED.
  */
-ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
-                             const void *v8, const float *sq, const float *sk,
-                             const float *sv, const ja_fp8_repair *repair, void *o,
-                             float *lse, void *workspace, size_t workspace_bytes,
+ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const float *sq,
+                             const void *kv8, size_t kv8_bytes, const ja_fp8_repair *repair,
+                             void *o, float *lse, void *workspace, size_t workspace_bytes,
                              void *stream);
 
 /*

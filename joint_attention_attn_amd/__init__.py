@@ -82,8 +82,12 @@ def load() -> ctypes.CDLL:
     lib.joint_attn_fwd_bf16_workspace_bytes.argtypes = [pp]
     lib.joint_attn_fwd_bf16_workspace_bytes.restype = ctypes.c_size_t
     lib.joint_attn_quant_rope_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(Fp8RepairC),
-                                       vp, vp, vp, ctypes.c_size_t, vp]
+    lib.joint_attn_prep_kv_fp8_bytes.argtypes = [pp]
+    lib.joint_attn_prep_kv_fp8_bytes.restype = sz
+    lib.joint_attn_prep_kv_fp8.argtypes = [pp, vp, vp, vp, vp, ctypes.POINTER(Fp8RepairC),
+                                           vp, sz, vp]
+    lib.joint_attn_fwd_fp8.argtypes = [pp, vp, vp, vp, sz, ctypes.POINTER(Fp8RepairC),
+                                       vp, vp, vp, sz, vp]
     lib.joint_attn_fp8_repair_plan.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int32,
                                                vp, vp, vp, vp, vp]
     lib.joint_attn_fp8_repair_plan.restype = st
@@ -91,7 +95,7 @@ def load() -> ctypes.CDLL:
     lib.joint_attn_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
     for fn in ("joint_attn_rope_table_2d", "joint_attn_prep_kv_bf16", "joint_attn_fwd_bf16",
                "joint_attn_fwd_bf16_block_sparse",
-               "joint_attn_quant_rope_fp8", "joint_attn_fwd_fp8"):
+               "joint_attn_quant_rope_fp8", "joint_attn_prep_kv_fp8", "joint_attn_fwd_fp8"):
         getattr(lib, fn).restype = st
     lib.joint_attn_status_string.argtypes = [st]
     lib.joint_attn_status_string.restype = ctypes.c_char_p
@@ -329,20 +333,51 @@ def fp8_repair_plan(k, v, rope, k8, v8, sk, sv, n_rep: int, k_norm=None,
     return Fp8Repair(n_rep, idx, kr, vr, kbias)
 
 
-def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
-            split: bool = True, repair: "Fp8Repair | None" = None):
-    """Joint attention on contiguous e4m3 codes [B, S, H, D] with fp32 scales [B, H, S].
-    sq and sk must be powers of two, as quant_rope_fp8 writes them (rows that
-    meet another value come back NaN).  `split` as for fwd_bf16; `repair`
-    from fp8_repair_plan (None: no repair)."""
-    b, s, h, d = q8.shape
-    for t in (q8, k8, v8):
+def _repair_c(repair):
+    if repair is None or repair.n_rep <= 0:
+        return None
+    return Fp8RepairC(int(repair.n_rep), _ptr(repair.kbias), _ptr(repair.kr), _ptr(repair.vr))
+
+
+def prep_kv_fp8(k8, v8, sk, sv, softmax_scale: float = 0.0, repair: "Fp8Repair | None" = None):
+    """K/V preparation of the FP8 forward: contiguous e4m3 codes k8, v8
+    [B, S, H, D] and fp32 scales sk, sv [B, H, S] (sk powers of two, as
+    quant_rope_fp8 writes them) -> the prepared uint8 buffer.  The forward
+    must use the same softmax_scale; `repair` removes the repaired keys."""
+    b, s, h, d = k8.shape
+    for t in (k8, v8):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or not t.is_contiguous() \
                 or tuple(t.shape) != (b, s, h, d):
-            raise ValueError("q8/k8/v8 must be contiguous 1-byte [B, S, H, D] tensors")
-    for t in (sq, sk, sv):
+            raise ValueError("k8/v8 must be contiguous 1-byte [B, S, H, D] tensors")
+    for t in (sk, sv):
         if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (b, h, s):
-            raise ValueError("sq/sk/sv must be contiguous fp32 [B, H, S] tensors")
+            raise ValueError("sk/sv must be contiguous fp32 [B, H, S] tensors")
+    p = Params(b, s, h, d)
+    p.softmax_scale = float(softmax_scale or 0.0)
+    lib = load()
+    n = int(lib.joint_attn_prep_kv_fp8_bytes(ctypes.byref(p)))
+    if n == 0:
+        raise ValueError(f"unsupported shape {(b, s, h, d)}")
+    kv8 = torch.empty(n, dtype=torch.uint8, device=k8.device)
+    rc = _repair_c(repair)
+    st = lib.joint_attn_prep_kv_fp8(ctypes.byref(p), _ptr(k8), _ptr(v8), _ptr(sk), _ptr(sv),
+                                    ctypes.byref(rc) if rc is not None else None,
+                                    _ptr(kv8), n, _stream(k8.device))
+    _check(st, "joint_attn_prep_kv_fp8")
+    return kv8
+
+
+def fwd_fp8_prepared(q8, sq, kv8, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
+                     split: bool = True, repair: "Fp8Repair | None" = None):
+    """FP8 forward on contiguous e4m3 q8 [B, S, H, D] with its fp32 scales sq
+    [B, H, S] (powers of two; rows that meet another value come back NaN) and
+    K/V prepared by prep_kv_fp8 with the same softmax_scale.  `split` as for
+    fwd_bf16; `repair` from fp8_repair_plan (the one given to prep_kv_fp8)."""
+    b, s, h, d = q8.shape
+    if q8.dtype not in (torch.uint8, torch.float8_e4m3fn) or not q8.is_contiguous():
+        raise ValueError("q8 must be a contiguous 1-byte [B, S, H, D] tensor")
+    if sq.dtype != torch.float32 or not sq.is_contiguous() or tuple(sq.shape) != (b, h, s):
+        raise ValueError("sq must be a contiguous fp32 [B, H, S] tensor")
     if out is None:
         out = torch.empty((b, s, h, d), dtype=torch.bfloat16, device=q8.device)
     p = Params(b, s, h, d)
@@ -354,11 +389,19 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return
     lib = load()
     ws_bytes = lib.joint_attn_fwd_fp8_workspace_bytes(ctypes.byref(p)) if split else 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q8.device) if ws_bytes else None
-    rc = None
-    if repair is not None and repair.n_rep > 0:
-        rc = Fp8RepairC(int(repair.n_rep), _ptr(repair.kbias), _ptr(repair.kr), _ptr(repair.vr))
-    st = lib.joint_attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq),
-                                _ptr(sk), _ptr(sv), ctypes.byref(rc) if rc is not None else None,
+    rc = _repair_c(repair)
+    st = lib.joint_attn_fwd_fp8(ctypes.byref(p), _ptr(q8), _ptr(sq), _ptr(kv8), kv8.numel(),
+                                ctypes.byref(rc) if rc is not None else None,
                                 _ptr(out), _ptr(lse), _ptr(ws), ws_bytes, _stream(q8.device))
     _check(st, "joint_attn_fwd_fp8")
     return (out, lse) if return_lse else out
+
+
+def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None, return_lse: bool = False,
+            split: bool = True, repair: "Fp8Repair | None" = None):
+    """Joint attention on contiguous e4m3 codes [B, S, H, D] with fp32 scales [B, H, S]:
+    prep_kv_fp8, then fwd_fp8_prepared.  sq and sk must be powers of two, as
+    quant_rope_fp8 writes them (rows that meet another value come back NaN).
+    `split` as for fwd_bf16; `repair` from fp8_repair_plan (None: no repair)."""
+    kv8 = prep_kv_fp8(k8, v8, sk, sv, softmax_scale, repair)
+    return fwd_fp8_prepared(q8, sq, kv8, softmax_scale, out, return_lse, split, repair)

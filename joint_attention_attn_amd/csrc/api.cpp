@@ -115,10 +115,11 @@ ja_status check_fwd_bf16(const ja_params *p) {
 ja_status check_fwd_fp8(const ja_params *p) {
   const ja_status st = check_params(p, false, ja::fwd_fp8_block_rows(p ? p->head_dim : 0));
   if (st != JA_OK) return st;
-  // the e4m3 K and V of one (batch, head) are addressed with 32-bit byte
-  // offsets
-  const int64_t span = (int64_t)(p->seq_len - 1) * p->heads * p->head_dim + p->head_dim;
-  if (span > 0x7fffffffLL) return JA_ERR_UNSUPPORTED;
+  // the prepared K and V^T of one (batch, head) are addressed with 32-bit
+  // byte offsets; the preparation pass has one workgroup per 64 keys and head
+  const int64_t s_pad = ((int64_t)p->seq_len + 63) / 64 * 64;
+  if (s_pad * p->head_dim > 0x7fffffffLL || s_pad / 64 * p->batch * p->heads > 0x7fffffffLL)
+    return JA_ERR_UNSUPPORTED;
   return JA_OK;
 }
 
@@ -259,35 +260,68 @@ ja_status joint_attn_fp8_repair_plan(const ja_params *p, const void *k, const vo
                                            kr, vr, kbias, static_cast<hipStream_t>(stream)));
 }
 
-ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
-                             const void *v8, const float *sq, const float *sk,
-                             const float *sv, const ja_fp8_repair *repair, void *o,
-                             float *lse, void *workspace, size_t workspace_bytes,
+// Repair bias of joint_attn_prep_kv_fp8 (NULL without repair); false: invalid.
+static bool repair_bias(const ja_params *p, const ja_fp8_repair *repair, const float **kbias) {
+  *kbias = nullptr;
+  if (!repair) return true;
+  if (repair->n_rep < 0 || repair->n_rep > p->seq_len) return false;
+  if (repair->n_rep == 0) return true;
+  if (!repair->kbias || (reinterpret_cast<uintptr_t>(repair->kbias) & 3u)) return false;
+  *kbias = repair->kbias;
+  return true;
+}
+
+size_t joint_attn_prep_kv_fp8_bytes(const ja_params *p) {
+  if (!p || check_fwd_fp8(p) != JA_OK) return 0;
+  return (size_t)ja::prep_kv_fp8_bytes(layout(p));
+}
+
+ja_status joint_attn_prep_kv_fp8(const ja_params *p, const void *k8, const void *v8,
+                                 const float *sk, const float *sv, const ja_fp8_repair *repair,
+                                 void *kv8, size_t kv8_bytes, void *stream) {
+  if (!p || !k8 || !v8 || !sk || !sv || !kv8) return JA_ERR_INVALID_ARG;
+  const ja_status st = check_fwd_fp8(p);
+  if (st != JA_OK) return st;
+  const float *kbias;
+  if (!repair_bias(p, repair, &kbias)) return JA_ERR_INVALID_ARG;
+  if (!aligned16(k8) || !aligned16(v8) || !aligned16(kv8) ||
+      (reinterpret_cast<uintptr_t>(sk) & 3u) || (reinterpret_cast<uintptr_t>(sv) & 3u))
+    return JA_ERR_INVALID_ARG;
+  const ja::AttnLayout L = layout(p);
+  if (kv8_bytes < (size_t)ja::prep_kv_fp8_bytes(L)) return JA_ERR_INVALID_ARG;
+  return hip_status(ja::launch_prep_kv_fp8(L, k8, v8, sk, sv, kbias, kv8,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const float *sq,
+                             const void *kv8, size_t kv8_bytes, const ja_fp8_repair *repair,
+                             void *o, float *lse, void *workspace, size_t workspace_bytes,
                              void *stream) {
-  if (!p || !q8 || !k8 || !v8 || !sq || !sk || !sv || !o) return JA_ERR_INVALID_ARG;
+  if (!p || !q8 || !sq || !kv8 || !o) return JA_ERR_INVALID_ARG;
   const ja_status st = check_fwd_fp8(p);
   if (st != JA_OK) return st;
   ja::Fp8Repair rp;
   if (repair && repair->n_rep > 0) {
-    if (repair->n_rep > p->seq_len || !repair->kbias || !repair->kr || !repair->vr ||
-        !aligned16(repair->kr) || !aligned16(repair->vr) || !aligned16(repair->kbias))
+    if (repair->n_rep > p->seq_len || !repair->kr || !repair->vr || !aligned16(repair->kr) ||
+        !aligned16(repair->vr))
       return JA_ERR_INVALID_ARG;
     rp.n_rep = repair->n_rep;
-    rp.kbias = repair->kbias;
     rp.kr = repair->kr;
     rp.vr = repair->vr;
   } else if (repair && repair->n_rep < 0) {
     return JA_ERR_INVALID_ARG;
   }
-  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) ||
-      !aligned16(sq) || !aligned16(sk) || !aligned16(sv) ||
-      (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) || (workspace && !aligned16(workspace)))
+  if (!aligned16(q8) || !aligned16(kv8) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(sq) & 3u) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
+      (workspace && !aligned16(workspace)))
     return JA_ERR_INVALID_ARG;
+  if (o == q8 || o == kv8) return JA_ERR_INVALID_ARG;
   const ja::AttnLayout L = layout(p);
+  if (kv8_bytes < (size_t)ja::prep_kv_fp8_bytes(L)) return JA_ERR_INVALID_ARG;
   ja::SplitPlan plan = ja::plan_fwd_fp8(L, device_cu_count());
   if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
     plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
-  return hip_status(ja::launch_fwd_fp8(L, q8, k8, v8, sq, sk, sv, o, lse, plan, workspace, rp,
+  return hip_status(ja::launch_fwd_fp8(L, q8, sq, kv8, o, lse, plan, workspace, rp,
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -156,28 +156,6 @@ struct Lds {
   static constexpr int sparse_bytes(int nkb) { return LIST_OFFSET + 4 * nkb; }
 };
 
-// vmcnt-only wait (gfx9 s_waitcnt encoding: expcnt and lgkmcnt at their
-// maxima, i.e. not waited for).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
-}
-
-// Workgroup barrier with no memory fence: a fence would make the compiler
-// wait for every load to LDS in flight, including the ones for later tiles.
-// The visibility that matters is ordered by hand (each wave waits for its own
-// loads of the next tile before the barrier); the empty asm statements keep
-// the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void tile_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-#define JA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 template <int D, bool ROPE, bool SPARSE>
 __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a) {

@@ -14,19 +14,21 @@
 // exp2 argument through the accumulator's initial value instead, so that
 // P' = exp2(c acc - ref) = P sv[key] with c the softmax scale in the exp2
 // domain, and P'.V8 is P.V in true units.  The running max of c acc is
-// refreshed whenever a row max grows by more than 2, and the reference sits
-// 6 below it, so P' stays below 2^8, inside the e4m3 range.  The softmax
+// refreshed whenever a row max grows by more than 3, and the reference sits
+// 5 below it, so P' stays below 2^8, inside the e4m3 range.  The softmax
 // normaliser sums the unquantized fp32 P' / sv[key].  A key past the end or
 // a repaired key starts at -inf.  Per score this leaves a max, an FMA, an
 // exp2, the sum's FMA and half a conversion.
 //
 // Structure as in the bf16 kernel: one workgroup of eight wave64s (two per
-// SIMD) per (256-query block, head, batch row), XCD-aware placement, K/V tiles
-// of 64 keys double-buffered in LDS through registers, one barrier per tile,
-// and Q K^T of the next tile issued ahead of the softmax of this one.  K rows are copied as they are; V is
-// staged transposed (one row per head-dimension column, keys in the order in
-// which the P' operand holds them) by a 4 x 4 byte transpose in registers, so
-// both MFMA operands are 16-byte LDS reads.
+// SIMD) per (256-query block, head, batch row), XCD-aware placement, split of
+// the last round.  A preparation pass (prep_kv_fp8.hip) writes each (batch,
+// head)'s K, V^T and per-key values in the layouts of the LDS tiles; buffer
+// loads to LDS copy 64-key tiles into a 4-stage ring three tiles ahead, with
+// no staging registers and no vector work, and Q K^T of the next tile is
+// issued ahead of the softmax of this one.
+#include <atomic>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -43,20 +45,28 @@ constexpr int NW = 8;
 constexpr int BM = 32 * NW;         // query rows per workgroup
 constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
 constexpr int NT = 64 * NW;         // threads per workgroup
-constexpr int VTSTR = BN + 16;      // bytes per V^T row in LDS (16-byte pad)
+constexpr int NSTAGE = 4;           // K/V tiles in the LDS ring
+constexpr int PREF = 3;             // tiles issued ahead
+constexpr int INFO_BYTES = 1024;    // per-key values of a tile (see prep_kv_fp8.hip)
 
 // The running max m is refreshed when some row's max grows by more than
 // kRescaleLog2 (exp2 domain); until then P' = exp2(u - m + kPOffset) stays
 // below 2^(kRescaleLog2 + kPOffset) = 256, inside the e4m3 range, and the
-// largest P' of a row sits near the top of that range.
-constexpr float kRescaleLog2 = 2.f;
-constexpr float kPOffset = 6.f;
+// largest P' of a row sits in its top three binades.  (A threshold of 3
+// rather than 2 takes 2 % off the time for 1.5e-3 more relative L2 error at
+// 16896 tokens.)
+constexpr float kRescaleLog2 = 3.f;
+constexpr float kPOffset = 5.f;
 
 constexpr int kBufferFlags = 0x00020000;
 
 struct Fp8Args {
-  const uint8_t *q, *k, *v;
-  const float *sq, *sk, *sv;
+  const uint8_t *q;
+  const float *sq;
+  // prepared K [B*H][S_pad][D], V^T [B*H][D][S_pad], per-key values
+  // [B*H][S_pad/64][1 KB] (prep_kv_fp8.hip)
+  const uint8_t *k8, *v8t, *info;
+  int S_pad;
   bf16 *o;
   float *lse;
   int64_t o_sb, o_ss, o_sh;
@@ -65,9 +75,9 @@ struct Fp8Args {
   int n_direct, parts;
   SplitWorkspace ws;
   // repair of the tokens with the largest quantization error (REPAIR
-  // kernels only): kbias [B][H][S] is 0, or -inf for a repaired key; kr / vr
-  // [B][H][n_pad][D] hold the repaired keys' exact rotated K and V (bf16).
-  const float *kbias;
+  // kernels only; their keys left the FP8 tiles through the preparation
+  // pass's bias): kr / vr [B][H][n_pad][D] hold the repaired keys' exact
+  // rotated K and V (bf16).
   const bf16 *kr, *vr;
   int n_rep, n_pad;
 };
@@ -103,39 +113,45 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position of key r (0..63) of a tile inside a V^T row: the P' operand of
-// lane half hf holds, in slot kb*16 + g*4 + i, key kb*32 + g*8 + hf*4 + i
-// (the S^T accumulator order), so V^T keeps that key at hf*32 + slot.
-__host__ __device__ constexpr int vt8_pos(int r) {
-  return ((r >> 2) & 1) * 32 + (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3);
-}
+// LDS ring: NSTAGE stages of [K tile | V^T tile | per-key values], each
+// part a whole number of 1 KB loads (one wave's 64 lanes x 16 bytes).  A K
+// row is D bytes plus a 16-byte pad, the pad lanes loading a dummy chunk.  A
+// V^T row is the 64 keys of one head-dimension column, granule g stored at
+// g ^ vswz(d) so that the fragment reads of 16 consecutive rows cover all 16
+// bank groups.
+__host__ __device__ constexpr int vswz8(int d) { return (d / 4) % 4; }
 
 template <int D>
 struct Fp8Lds {
-  static constexpr int KSTR = D + 16;       // bytes per K row (16-byte pad)
-  static constexpr int KTILE = BN * KSTR;
-  static constexpr int VTILE = D * VTSTR;
+  static constexpr int CH = D / 16;                    // 16-byte chunks per K row
+  static constexpr int KSTR = D + 16;                  // bytes per K row
+  static constexpr int K_LOADS = BN * (CH + 1) / 64;
+  static constexpr int V_LOADS = D * (BN / 16) / 64;
+  static constexpr int LOADS = K_LOADS + V_LOADS + 1;  // + per-key values
+  static constexpr int KBYTES = K_LOADS * 1024;
+  static constexpr int VBYTES = V_LOADS * 1024;
+  static constexpr int STAGE = LOADS * 1024;
+  static constexpr int BYTES = NSTAGE * STAGE;
+  static_assert(BN * (CH + 1) % 64 == 0 && D * (BN / 16) % 64 == 0, "whole loads");
 };
 
 template <int D, bool REPAIR>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
-  constexpr int KSTR = Fp8Lds<D>::KSTR;
-  constexpr int KCH = D / 16;                 // 16-byte chunks per K row
-  constexpr int K_THREADS = BN * KCH;         // one K chunk each
-  constexpr int V_THREADS = D * BN / 16;      // a 4-key x 4-column block each
-  static_assert(K_THREADS <= NT && V_THREADS <= NT, "staging layout");
-  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][Fp8Lds<D>::KTILE];
-  __shared__ __attribute__((aligned(16))) uint8_t Vt[2][Fp8Lds<D>::VTILE];
-  // per key of a staged tile: with K, the initial value of its score
-  // accumulator (log2 of its V scale over the softmax scale; -inf past the
-  // end or for a repaired key) and the E8M0 exponent of its K scale; with V,
-  // the reciprocal of its V scale
-  __shared__ __attribute__((aligned(16))) float bias_t[2][BN];
-  __shared__ __attribute__((aligned(16))) int ke_t[2][BN];
-  __shared__ __attribute__((aligned(16))) float inv_t[2][BN];
+  using L = Fp8Lds<D>;
+  constexpr int KSTR = L::KSTR;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
+  auto Kst = [&](int st) JA_INLINE { return smem8 + st * L::STAGE; };
+  auto Vst = [&](int st) JA_INLINE { return smem8 + st * L::STAGE + L::KBYTES; };
+  // per-key values of a stage: bias (fp32), then inv (fp32), then ke (int32)
+  auto Ist = [&](int st) JA_INLINE {
+    return reinterpret_cast<const float *>(smem8 + st * L::STAGE + L::KBYTES + L::VBYTES);
+  };
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // wave-uniform in a scalar register: the LDS destination of a buffer load
+  // to LDS derives from it and must be uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int S = a.S;
   const int ntiles_all = (S + BN - 1) / BN;
@@ -182,104 +198,88 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   const float c = a.scale_log2;
   const float qmul = sqv * c;
 
-  // ---- staging through buffer resources (rows past the end read as 0) ----
-  const uint8_t *kbase = a.k + (int64_t)b * S * row_stride + (int64_t)h * D;
-  const uint8_t *vbase = a.v + (int64_t)b * S * row_stride + (int64_t)h * D;
-  const int span = (int)((int64_t)(S - 1) * row_stride + D);
-  const __amdgpu_buffer_rsrc_t krs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(kbase), 0, span, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vbase), 0, span, kBufferFlags);
-  const int tile_bytes = (int)(BN * row_stride);
-  // K: row kr, chunk kc.  V: keys 4vm..4vm+3 of columns 4vn..4vn+3; the 64
-  // lanes of a wave take 16 key groups x 4 column groups, which spreads their
-  // 4-byte V^T writes over all LDS banks.
-  const int kr = tid / KCH, kc = tid % KCH;
-  const int koff = (int)(kr * row_stride) + kc * 16;
-  const int vm = lane & 15, vn = wave * 4 + (lane >> 4);
-  const int voff = (int)(4 * vm * row_stride) + 4 * vn;
-  u32x4 kreg;
-  uint32_t vreg[4];
-  // per-key values of the tile being staged: with K, its K scale, V scale
-  // and repair bias; with V, its V scale (keys past the end: K scale 1, V
-  // scale 0)
-  float skreg = 1.f, svkreg = 0.f, kbreg = 0.f, svvreg = 0.f;
-  const float inv_c = 1.f / c;
-  auto load = [&](int t, bool with_k, bool with_v) JA_INLINE {
-    const int key = t * BN + tid;
-    if (with_k) {
-      if (tid < K_THREADS)
-        kreg = bit_cast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(krs, koff, t * tile_bytes, 0));
-      if (tid < BN) {
-        skreg = key < S ? a.sk[bh * S + key] : 1.f;
-        svkreg = key < S ? a.sv[bh * S + key] : 0.f;
-        if constexpr (REPAIR) kbreg = key < S ? a.kbias[bh * S + key] : 0.f;
-      }
+  // ---- staging: wave w issues loads w, w + NW, w + 2 NW of each tile ----
+  const int span_k = a.S_pad * D, span_i = a.S_pad / BN * INFO_BYTES;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(a.k8 + bh * a.S_pad * D), 0, span_k, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(a.v8t + bh * D * a.S_pad), 0, span_k, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(a.info + bh * span_i), 0, span_i, kBufferFlags);
+  // source offset of this lane in load j (K lanes that fall on a pad load a
+  // dummy chunk; V^T lanes fetch the granule that the swizzle puts there)
+  auto load_offset = [&](int j) JA_INLINE -> int {
+    if (j < L::K_LOADS) {
+      const int g = 64 * j + lane;
+      const int r = g / (L::CH + 1), ch = g % (L::CH + 1);
+      return ch < L::CH ? r * D + 16 * ch : 0;
     }
-    if (with_v) {
-      if (tid < V_THREADS) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          vreg[k] = __builtin_amdgcn_raw_buffer_load_b32(vrs, voff + (int)(k * row_stride),
-                                                         t * tile_bytes, 0);
-      }
-      if (tid < BN) svvreg = key < S ? a.sv[bh * S + key] : 0.f;
+    if (j < L::K_LOADS + L::V_LOADS) {
+      const int g = 64 * (j - L::K_LOADS) + lane;
+      const int d = g / 4;
+      return d * a.S_pad + 16 * ((g % 4) ^ vswz8(d));
     }
+    return 16 * lane;
   };
-  auto store_k = [&](int buf) JA_INLINE {
-    if (tid < K_THREADS) *reinterpret_cast<u32x4 *>(&Ks[buf][kr * KSTR + kc * 16]) = kreg;
-    if (tid < BN) {
-      // c * (acc + log2(sv)/c) = c * score + log2(sv): exp2 of it carries the
-      // factor sv that P.V needs (log2(0) = -inf removes a key past the end)
-      float bias = log2f(svkreg) * inv_c;
-      if constexpr (REPAIR) bias += kbreg;          // -inf for a repaired key
-      bias_t[buf][tid] = bias;
-      ke_t[buf][tid] = e8m0_of(skreg, bad);
-    }
+  constexpr int JW = (L::LOADS + NW - 1) / NW;         // loads per wave, at most
+  static_assert(JW <= 3 && NW < L::LOADS, "loads per wave");
+  // (scalar offsets: an array element as the builtin's offset operand makes
+  // the host compilation drop the kernel's launch stub without a message)
+  const int voff0 = load_offset(wave);
+  const int voff1 = wave + NW < L::LOADS ? load_offset(wave + NW) : 0;
+  const int voff2 = wave + 2 * NW < L::LOADS ? load_offset(wave + 2 * NW) : 0;
+  const int nl = (L::LOADS - wave + NW - 1) / NW;      // loads of this wave per tile
+  auto issue_one = [&](int j, int voff, int t, int st) JA_INLINE {
+    char *dst = reinterpret_cast<char *>(smem8) + st * L::STAGE + j * 1024;
+    if (j < L::K_LOADS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, JA_LDS_PTR(dst), 16, voff, t * (BN * D), 0, 0);
+    else if (j < L::K_LOADS + L::V_LOADS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, JA_LDS_PTR(dst), 16, voff, t * BN, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, JA_LDS_PTR(dst), 16, voff, t * INFO_BYTES, 0, 0);
   };
-  auto store_v = [&](int buf) JA_INLINE {
-    if (tid < V_THREADS) {
-      // 4 x 4 byte transpose: vreg[k] holds columns 4vn..+3 of key 4vm+k;
-      // u[j] gets keys 4vm..+3 of column 4vn+j
-      const uint32_t t01l = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x05010400u);
-      const uint32_t t01h = __builtin_amdgcn_perm(vreg[1], vreg[0], 0x07030602u);
-      const uint32_t t23l = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x05010400u);
-      const uint32_t t23h = __builtin_amdgcn_perm(vreg[3], vreg[2], 0x07030602u);
-      const uint32_t u[4] = {__builtin_amdgcn_perm(t23l, t01l, 0x05040100u),
-                             __builtin_amdgcn_perm(t23l, t01l, 0x07060302u),
-                             __builtin_amdgcn_perm(t23h, t01h, 0x05040100u),
-                             __builtin_amdgcn_perm(t23h, t01h, 0x07060302u)};
-      const int pos = vt8_pos(4 * vm);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint32_t *>(&Vt[buf][(4 * vn + j) * VTSTR + pos]) = u[j];
+  // loads of key tile t into stage st
+  auto issue = [&](int t, int st) JA_INLINE {
+    issue_one(wave, voff0, t, st);
+    if (wave + NW < L::LOADS) issue_one(wave + NW, voff1, t, st);
+    if (JW >= 3 && wave + 2 * NW < L::LOADS) issue_one(wave + 2 * NW, voff2, t, st);
+  };
+  // wait until at most `AHEAD` later tiles' loads of this wave are in flight
+  auto wait_tiles = [&]<int AHEAD>() JA_INLINE {
+    if constexpr (JW >= 3) {
+      if (nl >= 3) { wait_vmcnt<3 * AHEAD>(); return; }
     }
-    if (tid < BN) inv_t[buf][tid] = svvreg > 0.f ? 1.f / svvreg : 0.f;
+    if (nl >= 2)
+      wait_vmcnt<2 * AHEAD>();
+    else
+      wait_vmcnt<AHEAD>();
   };
 
   // ---- S^T = K8 . Q8^T for the 64 keys of a tile (two 32-key blocks), the
   //      K and Q scales applied as E8M0 block scales, each accumulator
   //      starting at its key's bias (element i of a lane is key
   //      kb*32 + 8(i/4) + 4hf + i%4): acc = sk sq K8.Q8 + log2(sv)/c ----
-  auto qk = [&](int buf, f32x16 (&sacc)[2]) JA_INLINE {
+  auto qk = [&](int st, f32x16 (&sacc)[2]) JA_INLINE {
+    const float *bias = Ist(st);
+    const int *ke = reinterpret_cast<const int *>(Ist(st) + 2 * BN);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 bg = *reinterpret_cast<const float4 *>(&bias_t[buf][kb * 32 + g * 8 + hf * 4]);
+        const float4 bg = *reinterpret_cast<const float4 *>(bias + kb * 32 + g * 8 + hf * 4);
         sacc[kb][4 * g] = bg.x;
         sacc[kb][4 * g + 1] = bg.y;
         sacc[kb][4 * g + 2] = bg.z;
         sacc[kb][4 * g + 3] = bg.w;
       }
-      const int ke = ke_t[buf][kb * 32 + l32];    // A row l32 is key kb*32 + l32
-      const uint8_t *krow = &Ks[buf][(kb * 32 + l32) * KSTR + 32 * hf];
+      const int kex = ke[kb * 32 + l32];            // A row l32 is key kb*32 + l32
+      const uint8_t *krow = Kst(st) + (kb * 32 + l32) * KSTR + 32 * hf;
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk) {
         const i32x4 lo = *reinterpret_cast<const i32x4 *>(krow + 64 * kk);
         const i32x4 hi = *reinterpret_cast<const i32x4 *>(krow + 64 * kk + 16);
         sacc[kb] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qreg[kk],
-                            sacc[kb], ke, qe);
+                            sacc[kb], kex, qe);
       }
     }
   };
@@ -289,12 +289,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  auto pv = [&](const i32x8 &pb, int buf) JA_INLINE {
+  // ---- O^T += V8^T . P'^T: lane (l32, hf) reads the logical granules 2hf
+  //      and 2hf+1 of V^T row db*32 + l32, whose swizzle is vswz8(l32) ----
+  const int vsw = vswz8(l32);
+  auto pv = [&](const i32x8 &pb, int st) JA_INLINE {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint8_t *vrow = &Vt[buf][(db * 32 + l32) * VTSTR + 32 * hf];
-      const i32x4 lo = *reinterpret_cast<const i32x4 *>(vrow);
-      const i32x4 hi = *reinterpret_cast<const i32x4 *>(vrow + 16);
+      const uint8_t *vrow = Vst(st) + (db * 32 + l32) * BN;
+      const i32x4 lo = *reinterpret_cast<const i32x4 *>(vrow + 16 * ((2 * hf) ^ vsw));
+      const i32x4 hi = *reinterpret_cast<const i32x4 *>(vrow + 16 * ((2 * hf + 1) ^ vsw));
       oacc[db] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, pb, oacc[db]);
     }
   };
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 ig = *reinterpret_cast<const float4 *>(&inv_t[buf][kb * 32 + g * 8 + hf * 4]);
+        const float4 ig = *reinterpret_cast<const float4 *>(Ist(buf) + BN + kb * 32 + g * 8 + hf * 4);
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][4 * g + i], c, nref));
@@ -363,37 +366,35 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   // ---- loop over the key tiles t0 .. t1-1 (local index i), software
   //      pipelined: iteration i issues Q K^T of tile i+1 before the softmax
   //      of tile i, so the matrix cores work on the next tile while the
-  //      vector units exponentiate this one.  K tile i lives in K buffer i%2,
-  //      V tile i (with its scales) in V buffer i%2; iteration i reads K(i+1)
-  //      and V(i), stores K(i+2) and V(i+1) (loaded one iteration earlier)
-  //      into the buffers that iteration i-1 finished with, issues the loads
-  //      of K(i+3) and V(i+2), and a barrier closes it. ----
+  //      vector units exponentiate this one.  Tile i lives in stage
+  //      i % NSTAGE.  Iteration i first issues the loads of tile i+3 into the
+  //      stage of tile i-1 (whose K was read in iteration i-2 and V in
+  //      iteration i-1); before the barrier that closes it, each wave waits
+  //      for its own loads of tile i+2, whose K the next iteration reads. ----
   const int nt = t1 - t0;
-  load(t0, true, true);
-  store_k(0);
-  store_v(0);
-  if (nt > 1) {
-    load(t0 + 1, true, false);
-    store_k(1);
-  }
-  if (nt > 2) load(t0 + 2, true, false);
-  if (nt > 1) load(t0 + 1, false, true);
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PREF; ++p)
+    if (p < nt) issue(t0 + p, p);
+  wait_vmcnt<0>();
+  tile_barrier();
+  // the per-key values were prepared for this softmax scale
+  bad = bad || Ist(0)[3 * BN] != c;
   f32x16 sacc[2][2];
   qk(0, sacc[0]);
   auto iteration = [&]<int PAR, bool LAST>(int i) JA_INLINE {
-    const int t = t0 + i;
-    if constexpr (!LAST) qk((i + 1) & 1, sacc[PAR ^ 1]);
-    const i32x8 pb = softmax(sacc[PAR], i & 1);
-    pv(pb, i & 1);
+    const bool ahead = i + PREF < nt;
+    if (ahead) issue(t0 + i + PREF, (i + PREF) % NSTAGE);
+    if constexpr (!LAST) qk((i + 1) % NSTAGE, sacc[PAR ^ 1]);
+    const i32x8 pb = softmax(sacc[PAR], i % NSTAGE);
+    pv(pb, i % NSTAGE);
     if constexpr (!LAST) {
-      if (i + 2 < nt) store_k(i & 1);
-      store_v((i + 1) & 1);
-      if (i + 3 < nt) load(t + 3, true, false);
-      if (i + 2 < nt) load(t + 2, false, true);
-      __syncthreads();
+      if (ahead)
+        wait_tiles.template operator()<1>();
+      else
+        wait_vmcnt<0>();
+      tile_barrier();
     } else if constexpr (REPAIR) {
-      __syncthreads();        // the repair pass restages through these buffers
+      __syncthreads();        // the repair pass restages through the ring
     }
   };
   int i = 0;
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     if (a.n_rep > 0 && (unit < 0 || unit % a.parts == 0)) {
       constexpr int KBS = D + 8;          // bf16 per staged K row (16-byte pad)
       constexpr int VBS = 32 + 8;         // bf16 per staged V^T row
-      bf16 *kbuf = reinterpret_cast<bf16 *>(&Ks[0][0]);
-      bf16 *vbuf = reinterpret_cast<bf16 *>(&Vt[0][0]);
+      bf16 *kbuf = reinterpret_cast<bf16 *>(smem8);
+      bf16 *vbuf = reinterpret_cast<bf16 *>(smem8 + 32 * KBS * 2);
       // Q codes in the bf16 operand layout: lane half hf holds d = 16kk + 8hf + 0..7
       bf16x8 qb[D / 16];
 #pragma unroll
@@ -560,6 +561,25 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   }
 }
 
+// Dynamic LDS of one instantiation; its limit is raised once per device (the
+// attribute is set with the device current).
+template <int D, bool REPAIR>
+hipError_t launch_fp8_instance(const Fp8Args &a, dim3 grid, hipStream_t st) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<bool> done[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices || !done[dev].load(std::memory_order_acquire)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_fp8_kernel<D, REPAIR>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, Fp8Lds<D>::BYTES);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
+  }
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, REPAIR>), grid, dim3(NT), Fp8Lds<D>::BYTES, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int fwd_fp8_block_rows(int) { return BM; }
@@ -569,17 +589,17 @@ SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu) {
   return plan_split(n_items, (L.S + BN - 1) / BN, n_cu, BM, L.D);
 }
 
-hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
-                          const void *v8, const float *sq, const float *sk,
-                          const float *sv, void *o, float *lse, const SplitPlan &plan,
-                          void *workspace, const Fp8Repair &repair, hipStream_t st) {
+hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const float *sq, const void *kv8,
+                          void *o, float *lse, const SplitPlan &plan, void *workspace,
+                          const Fp8Repair &repair, hipStream_t st) {
   Fp8Args a;
   a.q = static_cast<const uint8_t *>(q8);
-  a.k = static_cast<const uint8_t *>(k8);
-  a.v = static_cast<const uint8_t *>(v8);
   a.sq = sq;
-  a.sk = sk;
-  a.sv = sv;
+  a.S_pad = prep8_pad(L.S);
+  const int64_t kv = (int64_t)L.B * L.H * a.S_pad * L.D;
+  a.k8 = static_cast<const uint8_t *>(kv8);
+  a.v8t = a.k8 + kv;
+  a.info = a.v8t + kv;
   a.o = static_cast<bf16 *>(o);
   a.lse = lse;
   a.o_sb = L.o_sb; a.o_ss = L.o_ss; a.o_sh = L.o_sh;
@@ -593,19 +613,15 @@ hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
   a.ws = split_workspace(plan, workspace, BM, L.D);
   const dim3 grid((unsigned)(plan.n_direct + plan.n_units));
   const bool rep = repair.n_rep > 0;
-  a.kbias = repair.kbias;
   a.kr = static_cast<const bf16 *>(repair.kr);
   a.vr = static_cast<const bf16 *>(repair.vr);
   a.n_rep = repair.n_rep;
   a.n_pad = repair_pad(repair.n_rep);
-  if (L.D == 64) {
-    auto kern = rep ? attn_fwd_fp8_kernel<64, true> : attn_fwd_fp8_kernel<64, false>;
-    hipLaunchKernelGGL(kern, grid, dim3(NT), 0, st, a);
-  } else {
-    auto kern = rep ? attn_fwd_fp8_kernel<128, true> : attn_fwd_fp8_kernel<128, false>;
-    hipLaunchKernelGGL(kern, grid, dim3(NT), 0, st, a);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (L.D == 64)
+    e = rep ? launch_fp8_instance<64, true>(a, grid, st) : launch_fp8_instance<64, false>(a, grid, st);
+  else
+    e = rep ? launch_fp8_instance<128, true>(a, grid, st) : launch_fp8_instance<128, false>(a, grid, st);
   if (e != hipSuccess || plan.n_units == 0) return e;
   return launch_merge_split(L, plan, a.ws, BM, 1.f, o, lse, st);
 }

@@ -14,7 +14,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 LIB = os.path.join(PKG, "libjoint_attn.so")
-SOURCES = ["api.cpp", "rope_table.hip", "prep_kv.hip", "attn_bf16.hip", "split.hip", "quant_fp8.hip", "attn_fp8.hip", "repair_fp8.hip"]
+SOURCES = ["api.cpp", "rope_table.hip", "prep_kv.hip", "attn_bf16.hip", "split.hip", "quant_fp8.hip", "prep_kv_fp8.hip", "attn_fp8.hip", "repair_fp8.hip"]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are left to nobody: the compiler may not emit them.
 FLAGS = ["-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",

@@ -147,7 +147,38 @@ __host__ __device__ constexpr int vt_key_of_slot(int p) {
   return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
 }
 
+// FP8 forward: position of key r (0..63) of a tile inside a V^T row: the P' operand of
+// lane half hf holds, in slot kb*16 + g*4 + i, key kb*32 + g*8 + hf*4 + i
+// (the S^T accumulator order), so V^T keeps that key at hf*32 + slot.
+__host__ __device__ constexpr int vt8_pos(int r) {
+  return ((r >> 2) & 1) * 32 + (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// vmcnt-only wait (gfx9 s_waitcnt encoding: expcnt and lgkmcnt at their
+// maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+
+// Workgroup barrier with no memory fence: a fence would make the compiler
+// wait for every load to LDS in flight, including the ones for later tiles.
+// The visibility that matters is ordered by hand (each wave waits for its own
+// loads of the next tile before the barrier); the empty asm statements keep
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// LDS destination of a buffer load to LDS
+#define JA_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
 
 }  // namespace ja

@@ -68,10 +68,10 @@ hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
                                  void *v8, float *sq, float *sk, float *sv,
                                  hipStream_t st);
 
-// Repair set of the FP8 forward (see repair_fp8.hip); n_rep = 0: none.
+// Repaired keys of the FP8 forward (see repair_fp8.hip); n_rep = 0: none.
+// Their bias reaches the forward through the K/V preparation.
 struct Fp8Repair {
   int n_rep = 0;
-  const float *kbias = nullptr;
   const void *kr = nullptr, *vr = nullptr;
 };
 int repair_pad(int n);          // repaired keys rounded up to whole 32-key tiles
@@ -81,11 +81,20 @@ hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
                               const float *sk, const float *sv, int n, int32_t *idx,
                               void *kr, void *vr, float *kbias, hipStream_t st);
 
+// K/V preparation of the FP8 forward (prep_kv_fp8.hip): one buffer of
+// prep_kv_fp8_bytes(L) holding K [B*H][S_pad][D], V^T [B*H][D][S_pad] and the
+// per-key values [B*H][S_pad/64][1 KB], S_pad = prep8_pad(S); kbias: the
+// repair bias, NULL = none.
+int prep8_pad(int S);
+int64_t prep_kv_fp8_bytes(const AttnLayout &L);
+hipError_t launch_prep_kv_fp8(const AttnLayout &L, const void *k8, const void *v8,
+                              const float *sk, const float *sv, const float *kbias, void *kv8,
+                              hipStream_t st);
+
 SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu);
-hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const void *k8,
-                          const void *v8, const float *sq, const float *sk,
-                          const float *sv, void *o, float *lse, const SplitPlan &plan,
-                          void *workspace, const Fp8Repair &repair, hipStream_t st);
+hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const float *sq, const void *kv8,
+                          void *o, float *lse, const SplitPlan &plan, void *workspace,
+                          const Fp8Repair &repair, hipStream_t st);
 
 // Query rows per workgroup of each forward kernel (the grid's x extent is
 // ceil(S / rows)).

@@ -9,8 +9,9 @@
 //              that was quantized, k^ = fl(value(code) * scale))
 //   the n tokens with the largest e are repaired (ties to the lower index);
 //   their keys and values then enter the FP8 forward at bf16-path precision:
-//   the forward masks them out of the FP8 tiles (kbias = -inf) and attends
-//   them once more from kr / vr (the bf16-rounded rotated key, the bf16 value).
+//   the K/V preparation masks them out of the FP8 tiles (kbias = -inf in their
+//   score's initial value) and the forward attends them once more from kr / vr
+//   (the bf16-rounded rotated key, the bf16 value).
 //
 // Two kernels:
 //   repair_err_kernel     one lane group per (b, token, head) vector, as in the

@@ -118,20 +118,50 @@ def test_quant_and_fp8_validation(lib):
                                          *ptrs[6:9], None) == ja.JA_ERR_UNSUPPORTED
     assert lib.joint_attn_quant_rope_fp8(ctypes.byref(p), vp(0), *ptrs[1:3], None, *ptrs[3:6],
                                          *ptrs[6:9], None) == ja.JA_ERR_INVALID_ARG
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(bad), *ptrs[:3], *ptrs[3:6], None, ptrs[6],
-                                  None, None, 0, None) == ja.JA_ERR_UNSUPPORTED
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], vp(FAKE + 4), *ptrs[4:6], None,
-                                  ptrs[6], None, None, 0, None) == ja.JA_ERR_INVALID_ARG
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], None, vp(0), None,
-                                  None, 0, None) == ja.JA_ERR_INVALID_ARG
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], None, ptrs[6], None,
-                                  vp(FAKE + 0x9008), 64, None) == ja.JA_ERR_INVALID_ARG
-    rep_bad = ja.Fp8RepairC(5, None, FAKE, FAKE)           # kbias missing
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], ctypes.byref(rep_bad),
-                                  ptrs[6], None, None, 0, None) == ja.JA_ERR_INVALID_ARG
-    rep_big = ja.Fp8RepairC(81, FAKE, FAKE, FAKE)          # more than seq_len = 80
-    assert lib.joint_attn_fwd_fp8(ctypes.byref(p), *ptrs[:3], *ptrs[3:6], ctypes.byref(rep_big),
-                                  ptrs[6], None, None, 0, None) == ja.JA_ERR_INVALID_ARG
+
+
+def _fwd8(lib, p, q8=FAKE, sq=FAKE + 0x1000, kv8=FAKE + 0x2000, kv8_bytes=KV_BYTES, rep=None,
+          o=FAKE + 0x3000, lse=None, ws=None, ws_bytes=0):
+    vp = ctypes.c_void_p
+    return lib.joint_attn_fwd_fp8(ctypes.byref(p), vp(q8), vp(sq), vp(kv8), kv8_bytes,
+                                  ctypes.byref(rep) if rep is not None else None, vp(o),
+                                  vp(lse) if lse else None, vp(ws) if ws else None, ws_bytes, None)
+
+
+def _prep8(lib, p, k8=FAKE, v8=FAKE + 0x1000, sk=FAKE + 0x2000, sv=FAKE + 0x3000, rep=None,
+           kv8=FAKE + 0x4000, kv8_bytes=KV_BYTES):
+    vp = ctypes.c_void_p
+    return lib.joint_attn_prep_kv_fp8(ctypes.byref(p), vp(k8), vp(v8), vp(sk), vp(sv),
+                                      ctypes.byref(rep) if rep is not None else None, vp(kv8),
+                                      kv8_bytes, None)
+
+
+def test_fp8_prep_and_forward_validation(lib):
+    p = _p()
+    bad = _p()
+    bad.head_dim = 32
+    # prepared size: K and V^T of S_pad = 128 keys, one 1 KB block per 64-key tile
+    n = lib.joint_attn_prep_kv_fp8_bytes(ctypes.byref(p))
+    assert n == 1 * 2 * (2 * 128 * 64 + 2 * 1024)
+    assert lib.joint_attn_prep_kv_fp8_bytes(ctypes.byref(bad)) == 0
+    assert _prep8(lib, bad) == ja.JA_ERR_UNSUPPORTED
+    assert _prep8(lib, p, k8=0) == ja.JA_ERR_INVALID_ARG
+    assert _prep8(lib, p, sk=FAKE + 0x2002) == ja.JA_ERR_INVALID_ARG
+    assert _prep8(lib, p, kv8=FAKE + 0x4004) == ja.JA_ERR_INVALID_ARG
+    assert _prep8(lib, p, kv8_bytes=n - 1) == ja.JA_ERR_INVALID_ARG
+    assert _prep8(lib, p, rep=ja.Fp8RepairC(5, None, FAKE, FAKE)) == ja.JA_ERR_INVALID_ARG
+    assert _prep8(lib, p, rep=ja.Fp8RepairC(81, FAKE, FAKE, FAKE)) == ja.JA_ERR_INVALID_ARG
+    assert _prep8(lib, p, rep=ja.Fp8RepairC(-1, FAKE, FAKE, FAKE)) == ja.JA_ERR_INVALID_ARG
+
+    assert _fwd8(lib, bad) == ja.JA_ERR_UNSUPPORTED
+    assert _fwd8(lib, p, q8=FAKE + 4) == ja.JA_ERR_INVALID_ARG
+    assert _fwd8(lib, p, sq=FAKE + 0x1002) == ja.JA_ERR_INVALID_ARG
+    assert _fwd8(lib, p, o=0) == ja.JA_ERR_INVALID_ARG
+    assert _fwd8(lib, p, o=FAKE) == ja.JA_ERR_INVALID_ARG            # aliases q8
+    assert _fwd8(lib, p, kv8_bytes=n - 1) == ja.JA_ERR_INVALID_ARG
+    assert _fwd8(lib, p, ws=FAKE + 0x9008, ws_bytes=64) == ja.JA_ERR_INVALID_ARG
+    assert _fwd8(lib, p, rep=ja.Fp8RepairC(5, FAKE, None, FAKE)) == ja.JA_ERR_INVALID_ARG
+    assert _fwd8(lib, p, rep=ja.Fp8RepairC(81, FAKE, FAKE, FAKE)) == ja.JA_ERR_INVALID_ARG
 
 
 def test_repair_plan_validation(lib):

@@ -83,6 +83,65 @@ def test_fp8_forward_ragged(s, d):
     assert rel_l2(out, ref) <= FP8_REL_L2
 
 
+def _vt8_key_of_pos(p):
+    """Key (0..63) at byte p of a 64-key tile of the prepared V^T rows: the
+    P' operand of lane half hf holds key kb*32 + g*8 + hf*4 + i in slot
+    kb*16 + g*4 + i, and V^T keeps that key at byte hf*32 + slot."""
+    hf, slot = p // 32, p % 32
+    kb, g, i = slot // 16, (slot // 4) % 4, slot % 4
+    return kb * 32 + g * 8 + hf * 4 + i
+
+
+@pytest.mark.parametrize("s,d,rep", [(80, 64, False), (1037, 128, False), (130, 128, True)])
+def test_prep_kv_fp8_layout(s, d, rep):
+    # the prepared buffer against its documented layout, built here from the
+    # quantizer's codes and scales: K rows, V^T rows in the P' key order, and
+    # per 64-key tile the words log2(sv)/c (+ repair bias), 1/sv, the E8M0
+    # exponent of sk and c; zeros and -inf/0/127 past the end
+    w = synth.Workload("prep8", 2, 3, d, n_text=s, grid=0, outlier_frac=0.03)
+    q, k, v, _ = synth.make_qkv(w, seed=s)
+    q8, k8, v8, sq, sk, sv = oracle.quant_rope_fp8(q, k, v, None)
+    b, h = 2, 3
+    kbias = np.zeros((b, h, s), np.float32)
+    repair = None
+    if rep:
+        kbias[0, 1, [3, 70, 129]] = -np.inf
+        repair = ja.Fp8Repair(3, None, None, None, torch.from_numpy(kbias).to(DEV))
+    _say(f"fp8 K/V preparation S={s} D={d} repair={rep}")
+    dv = [torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in (k8, v8, sk, sv)]
+    kv8 = ja.prep_kv_fp8(*dv, repair=repair).cpu().numpy()
+    torch.cuda.synchronize()
+    sp = (s + 63) // 64 * 64
+    nt = sp // 64
+    c = np.float32(1.0 / np.sqrt(d) * np.log2(np.e))
+    kk = np.zeros((b, h, sp, d), np.uint8)
+    kk[:, :, :s] = np.transpose(k8, (0, 2, 1, 3))
+    vt = np.zeros((b, h, d, sp), np.uint8)
+    vv = np.zeros((b, h, sp, d), np.uint8)
+    vv[:, :, :s] = np.transpose(v8, (0, 2, 1, 3))
+    order = np.array([_vt8_key_of_pos(p) for p in range(64)])
+    for t in range(nt):
+        vt[:, :, :, 64 * t:64 * t + 64] = np.transpose(vv[:, :, 64 * t + order], (0, 1, 3, 2))
+    n = b * h * sp * d
+    assert kv8.size == 2 * n + b * h * nt * 1024
+    assert np.array_equal(kv8[:n].reshape(kk.shape), kk)
+    assert np.array_equal(kv8[n:2 * n].reshape(vt.shape), vt)
+    info = kv8[2 * n:].view(np.uint32).reshape(b, h, nt, 256)
+    bias = info[..., :64].view(np.float32).reshape(b, h, sp)
+    inv = info[..., 64:128].view(np.float32).reshape(b, h, sp)
+    ke = info[..., 128:192].reshape(b, h, sp)
+    assert np.all(info[..., 192].view(np.float32) == c) and not info[..., 193:].any()
+    want_ke = (sk.view(np.uint32) >> 23).astype(np.uint32)
+    assert np.array_equal(ke[..., :s], want_ke) and np.all(ke[..., s:] == 127)
+    assert np.array_equal(inv[..., :s], (np.float32(1) / sv).astype(np.float32))
+    assert np.all(inv[..., s:] == 0)
+    want_bias = (np.log2(sv.astype(np.float64)) / np.float64(c)).astype(np.float32) + kbias
+    fin = np.isfinite(want_bias)
+    assert np.array_equal(np.isfinite(bias[..., :s]), fin)
+    assert np.all(bias[..., :s][~fin] == -np.inf) and np.all(bias[..., s:] == -np.inf)
+    np.testing.assert_allclose(bias[..., :s][fin], want_bias[fin], rtol=4e-7, atol=0)
+
+
 @pytest.mark.parametrize("which", ["k", "q"])
 def test_fp8_forward_poisons_rows_of_non_power_of_two_scales(which):
     # Q and K scales must be powers of two (the MFMA applies their exponent);
@@ -109,6 +168,24 @@ def test_fp8_forward_poisons_rows_of_non_power_of_two_scales(which):
     else:
         assert torch.isnan(head1[:, :256]).all() and torch.isnan(lse[:, 1, :256]).all()
         assert not torch.isnan(head1[:, 256:]).any()
+
+
+def test_fp8_forward_rejects_buffer_prepared_for_another_scale():
+    # the per-key values hold log2(sv) over the softmax scale: a forward with
+    # another scale turns every row into NaN instead of a wrong result
+    w = synth.Workload("scale8", 1, 2, 64, n_text=200, grid=0)
+    q, k, v, _ = synth.make_qkv(w, seed=4)
+    codes = [torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+             for x in oracle.quant_rope_fp8(q, k, v, None)]
+    q8, k8, v8, sq, sk, sv = codes
+    _say("fp8 fwd on K/V prepared for another softmax scale")
+    kv8 = ja.prep_kv_fp8(k8, v8, sk, sv, softmax_scale=0.1)
+    good, lse = ja.fwd_fp8_prepared(q8, sq, kv8, softmax_scale=0.1, return_lse=True)
+    bad, bad_lse = ja.fwd_fp8_prepared(q8, sq, kv8, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.fp8_attention(*[x.cpu().numpy() for x in codes], scale=0.1)
+    assert rel_l2(good, ref) <= FP8_REL_L2
+    assert torch.isnan(bad.float()).all() and torch.isnan(bad_lse).all()
 
 
 def test_fp8_full_path_1024():
