@@ -3,6 +3,7 @@
 // call never touches the device.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -100,7 +101,8 @@ int device_cu_count() {
 
 // Checks of joint_attn_fwd_bf16 that do not involve device pointers.
 ja_status check_fwd_bf16(const ja_params *p) {
-  const ja_status st = check_params(p, true, ja::fwd_bf16_block_rows(p ? p->head_dim : 0));
+  // the block-sparse forward has the smaller workgroups, hence the larger grid
+  const ja_status st = check_params(p, true, ja::fwd_bf16_block_rows(true));
   if (st != JA_OK) return st;
   // the prepared K and V^T of one (batch, head) are addressed with 32-bit
   // byte offsets; the preparation pass has one workgroup per 64 keys and head
@@ -170,7 +172,10 @@ ja_status joint_attn_prep_kv_bf16(const ja_params *p, const void *k, const void 
 
 size_t joint_attn_fwd_bf16_workspace_bytes(const ja_params *p) {
   if (!p || check_fwd_bf16(p) != JA_OK) return 0;
-  return (size_t)ja::plan_fwd_bf16(layout(p), device_cu_count()).ws_bytes;
+  const ja::AttnLayout L = layout(p);
+  const int n_cu = device_cu_count();
+  return (size_t)std::max(ja::plan_fwd_bf16(L, n_cu, false).ws_bytes,
+                          ja::plan_fwd_bf16(L, n_cu, true).ws_bytes);
 }
 
 // Shared checks and launch of the dense and block-sparse BF16 forwards.
@@ -186,7 +191,7 @@ static ja_status fwd_bf16_call(const ja_params *p, const void *q, const void *kv
   if (o == q || o == kv) return JA_ERR_INVALID_ARG;
   const ja::AttnLayout L = layout(p);
   if (kv_bytes < (size_t)ja::prep_kv_bytes(L)) return JA_ERR_INVALID_ARG;
-  ja::SplitPlan plan = ja::plan_fwd_bf16(L, device_cu_count());
+  ja::SplitPlan plan = ja::plan_fwd_bf16(L, device_cu_count(), mask != nullptr);
   if (plan.n_units > 0 && (!workspace || workspace_bytes < (size_t)plan.ws_bytes))
     plan = ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
   return hip_status(ja::launch_fwd_bf16(L, q, kv, rope, mask, o, lse, plan, workspace,

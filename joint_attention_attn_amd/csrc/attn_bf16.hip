@@ -21,9 +21,10 @@
 // K and V arrive from the preparation pass (prep_kv.hip) as rotated K rows
 // and as V^T rows whose keys are in the order in which the P operand holds
 // them, so both MFMA operands are single 16-byte LDS reads.  Tiles of 32 keys
-// go from HBM straight into a four-stage LDS ring with buffer loads to LDS:
-// no registers, no VALU work, and the loads of a tile are issued three tiles
-// ahead of its use.  K rows are padded by one 16-byte granule (the lanes that
+// go from HBM straight into an LDS ring (four stages; three for the
+// block-sparse variant's smaller workgroups) with buffer loads to LDS: no
+// registers, no VALU work, and the loads of a tile are issued a ring's depth
+// minus one tiles ahead of its use.  K rows are padded by one 16-byte granule (the lanes that
 // would fill a pad load a dummy chunk) and V^T rows are XOR-swizzled, so that
 // the 16 lanes served together by a fragment read hit distinct banks.
 //
@@ -37,11 +38,12 @@
 // Block-sparse variant (the kernel half of the pages' sparse attention,
 // section "Quantized and sparse attention": attention restricted to the
 // blocks of a given block mask over 128-query x 64-key blocks).  A workgroup
-// covers three query blocks; it first compacts, in LDS, the list of key
-// blocks that any of the three keeps, with a 3-bit flag per entry, then
-// stages only the tiles of that list.  A wave computes a staged tile only if
-// its own query block keeps it (a wave-uniform branch); staging and the
-// barrier are shared.  Query rows that keep no key get O = 0 and LSE = -inf.
+// of four waves covers one query block, three such workgroups share a CU; it
+// first compacts, in LDS, the list of key blocks its query block keeps, then
+// stages only the tiles of that list.  (The code keeps a per-entry flag for
+// each query block of a workgroup and a wave-uniform skip of tiles its own
+// block does not keep, which a one-block workgroup never takes.)  Query rows
+// that keep no key get O = 0 and LSE = -inf.
 #include <atomic>
 
 #include "common.hpp"
@@ -51,30 +53,32 @@ namespace ja {
 
 namespace {
 
-#ifndef JA_BF16_WAVES
-#define JA_BF16_WAVES 12
-#endif
-#ifndef JA_BF16_RW
-#define JA_BF16_RW 1
-#endif
-constexpr int NW = JA_BF16_WAVES;   // waves per workgroup
-constexpr int RW = JA_BF16_RW;      // 32-row query blocks per wave
-constexpr int BM = 32 * RW * NW;    // query rows per workgroup
+constexpr int RW = 1;               // 32-row query blocks per wave
 constexpr int BN = 32;              // keys per K/V tile
-constexpr int NT = 64 * NW;         // threads per workgroup
-constexpr int NSTAGE = 4;           // K/V tiles in the LDS ring
-// One workgroup per CU: 12 waves, three per SIMD, at most 168 VGPRs each.
-// Latency is hidden by the three waves of a SIMD rather than by deeper
-// software pipelining inside a wave (which needs more registers).
-constexpr int WG_PER_CU = 1;
 
 // Block-mask granularity of the block-sparse variant.
 constexpr int kQueryBlock = 128;
 constexpr int kKeyBlock = 64;
 constexpr int KB_TILES = kKeyBlock / BN;              // key tiles per key block
-constexpr int QB_PER_WG = BM / kQueryBlock;           // query blocks per workgroup
-static_assert(BM % kQueryBlock == 0 && kKeyBlock % BN == 0, "mask blocks");
-static_assert(QB_PER_WG <= 16, "query-block flags");
+
+// Workgroup shape.  Dense: one workgroup of 12 waves per CU, three per SIMD
+// at most 168 VGPRs each, over a 4-stage ring; latency is hidden by the three
+// waves of a SIMD rather than by deeper software pipelining inside a wave
+// (which needs more registers).  Block-sparse: one 128-row query block per
+// workgroup of 4 waves, three workgroups per CU over 3-stage rings, so that a
+// workgroup stages only the key tiles its own query block keeps and no wave
+// waits on a tile it does not use.
+template <bool SPARSE>
+struct Cfg {
+  static constexpr int NW = SPARSE ? 4 : 12;          // waves per workgroup
+  static constexpr int NSTAGE = SPARSE ? 3 : 4;       // K/V tiles in the LDS ring
+  static constexpr int WG_PER_CU = SPARSE ? 3 : 1;
+  static constexpr int BM = 32 * RW * NW;             // query rows per workgroup
+  static constexpr int NT = 64 * NW;                  // threads per workgroup
+  static constexpr int QB_PER_WG = BM / kQueryBlock;  // query blocks per workgroup
+  static_assert(BM % kQueryBlock == 0 && kKeyBlock % BN == 0, "mask blocks");
+  static_assert(QB_PER_WG <= 16, "query-block flags");
+};
 // Longest sequence of the block-sparse variant (its key-block list lives in
 // LDS, 4 bytes per key block, and entries hold the key block in 16 bits).
 constexpr int kSparseMaxSeq = 1 << 20;
@@ -140,7 +144,7 @@ __device__ __forceinline__ float half_sum(float x) {
 // together by a fragment read then cover all 16 bank groups of 16 bytes.
 __host__ __device__ constexpr int vswz(int d) { return (d / 4) % 4; }
 
-template <int D>
+template <int D, int NSTAGE>
 struct Lds {
   static constexpr int CH = D / 8;                    // 16-byte chunks per K row
   static constexpr int KSTR = D + 8;                  // bf16 per K row
@@ -158,15 +162,20 @@ struct Lds {
 
 
 template <int D, bool ROPE, bool SPARSE>
-__global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int CH = Lds<D>::CH;
-  constexpr int KSTR = Lds<D>::KSTR;
-  constexpr int LOADS = Lds<D>::LOADS, K_LOADS = Lds<D>::K_LOADS;
-  static_assert(LOADS <= 2 * NW, "at most two tile loads per wave");
+__global__ __launch_bounds__(Cfg<SPARSE>::NT, Cfg<SPARSE>::WG_PER_CU)
+void attn_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NW = Cfg<SPARSE>::NW, NT = Cfg<SPARSE>::NT, BM = Cfg<SPARSE>::BM;
+  constexpr int NSTAGE = Cfg<SPARSE>::NSTAGE, QB_PER_WG = Cfg<SPARSE>::QB_PER_WG;
+  using L = Lds<D, NSTAGE>;
+  constexpr int CH = L::CH;
+  constexpr int KSTR = L::KSTR;
+  constexpr int LOADS = L::LOADS, K_LOADS = L::K_LOADS;
+  constexpr int JW = (LOADS + NW - 1) / NW;           // tile loads per wave, at most
+  static_assert(JW <= 5, "at most five tile loads per wave");
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-  auto Kst = [&](int st) JA_INLINE { return smem + st * (Lds<D>::STAGE / 2); };
+  auto Kst = [&](int st) JA_INLINE { return smem + st * (L::STAGE / 2); };
   auto Vst = [&](int st) JA_INLINE {
-    return smem + st * (Lds<D>::STAGE / 2) + Lds<D>::KBYTES / 2;
+    return smem + st * (L::STAGE / 2) + L::KBYTES / 2;
   };
 
   const int tid = threadIdx.x;
@@ -199,10 +208,10 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   //      key block | (flags of the query blocks that keep it) << 16.  The
   //      workgroup's key tiles are then the tiles of the listed blocks that
   //      lie inside the sequence; the dense kernel's tiles are 0..ntiles-1. ----
-  uint32_t *blist = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(smem) + Lds<D>::LIST_OFFSET);
+  uint32_t *blist = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(smem) + L::LIST_OFFSET);
   int ntiles = ntiles_all;
   if constexpr (SPARSE) {
-    int *wcnt = reinterpret_cast<int *>(reinterpret_cast<char *>(smem) + Lds<D>::BYTES);
+    int *wcnt = reinterpret_cast<int *>(reinterpret_cast<char *>(smem) + L::BYTES);
     const int qb0 = qblk * QB_PER_WG;
     const uint8_t *mrow = a.mask + ((int64_t)bh * a.nqb + qb0) * a.nkb;
     int nact = 0;
@@ -310,8 +319,10 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   //      G % (CH+1) of row G / (CH+1), and pad or slack granules take a dummy
   //      chunk.  The others carry V^T rows, 16 per load: row
   //      d = 16 (j - K_LOADS) + i / 4, position i % 4 holding granule
-  //      (i % 4) ^ vswz(d) of the row.  Wave w issues loads w and w + NW.
-  //      The lane offsets are fixed; the tile offset is scalar. ----
+  //      (i % 4) ^ vswz(d) of the row.  Wave w issues loads w, w + NW, ...
+  //      The lane offsets are fixed (scalars: an array element as the
+  //      builtin's offset operand makes the host compilation drop the
+  //      kernel's launch stub); the tile offset is scalar. ----
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16 *>(a.kr + (int64_t)bh * a.S_pad * D), 0, a.S_pad * D * 2, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -325,11 +336,14 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
     const int d = 16 * (j - K_LOADS) + lane / 4;
     return (d * a.S_pad + 8 * ((lane % 4) ^ vswz(d))) * 2;
   };
-  const int j0 = wave, j1 = wave + NW;
-  const int voff0 = j0 < LOADS ? load_offset(j0) : 0;
-  const int voff1 = j1 < LOADS ? load_offset(j1) : 0;
+  auto voff_of = [&](int m) JA_INLINE -> int {
+    return wave + m * NW < LOADS ? load_offset(wave + m * NW) : 0;
+  };
+  const int voff0 = voff_of(0), voff1 = voff_of(1), voff2 = voff_of(2), voff3 = voff_of(3),
+            voff4 = voff_of(4);
+  const int nl = (LOADS - wave + NW - 1) / NW;         // loads of this wave per tile
   auto issue_one = [&](int j, int voff, int t, int st) JA_INLINE {
-    char *dst = reinterpret_cast<char *>(smem) + st * Lds<D>::STAGE + j * 1024;
+    char *dst = reinterpret_cast<char *>(smem) + st * L::STAGE + j * 1024;
     if (j < K_LOADS)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, JA_LDS_PTR(dst), 16, voff, t * (BN * D * 2), 0, 0);
     else
@@ -337,12 +351,21 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
   };
   // loads of key tile t into stage st
   auto issue = [&](int t, int st) JA_INLINE {
-    if (j0 < LOADS) issue_one(j0, voff0, t, st);
-    if (j1 < LOADS) issue_one(j1, voff1, t, st);
+    if (0 < nl) issue_one(wave, voff0, t, st);
+    if (JW > 1 && 1 < nl) issue_one(wave + NW, voff1, t, st);
+    if (JW > 2 && 2 < nl) issue_one(wave + 2 * NW, voff2, t, st);
+    if (JW > 3 && 3 < nl) issue_one(wave + 3 * NW, voff3, t, st);
+    if (JW > 4 && 4 < nl) issue_one(wave + 4 * NW, voff4, t, st);
   };
   // wait until at most `ahead` later tiles' loads of this wave are in flight
   auto wait_tiles = [&]<int AHEAD>() JA_INLINE {
-    if (j1 < LOADS)
+    if (JW > 4 && nl == 5)
+      wait_vmcnt<5 * AHEAD>();
+    else if (JW > 3 && nl == 4)
+      wait_vmcnt<4 * AHEAD>();
+    else if (JW > 2 && nl == 3)
+      wait_vmcnt<3 * AHEAD>();
+    else if (JW > 1 && nl == 2)
       wait_vmcnt<2 * AHEAD>();
     else
       wait_vmcnt<AHEAD>();
@@ -581,7 +604,8 @@ __global__ __launch_bounds__(NT, WG_PER_CU) void attn_fwd_bf16_kernel(FwdArgs a)
 // attribute is set with the device current).
 template <int D, bool ROPE, bool SPARSE>
 hipError_t launch_instance(const FwdArgs &a, dim3 grid, hipStream_t st) {
-  const int bytes = SPARSE ? Lds<D>::sparse_bytes(a.nkb) : Lds<D>::BYTES;
+  using L = Lds<D, Cfg<SPARSE>::NSTAGE>;
+  const int bytes = SPARSE ? L::sparse_bytes(a.nkb) : L::BYTES;
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> done[kMaxDevices];
   int dev = 0;
@@ -591,11 +615,12 @@ hipError_t launch_instance(const FwdArgs &a, dim3 grid, hipStream_t st) {
     e = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<D, ROPE, SPARSE>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        SPARSE ? Lds<D>::sparse_bytes((kSparseMaxSeq + kKeyBlock - 1) / kKeyBlock) : Lds<D>::BYTES);
+        SPARSE ? L::sparse_bytes((kSparseMaxSeq + kKeyBlock - 1) / kKeyBlock) : L::BYTES);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, ROPE, SPARSE>), grid, dim3(NT), bytes, st, a);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, ROPE, SPARSE>), grid, dim3(Cfg<SPARSE>::NT), bytes,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -610,11 +635,13 @@ hipError_t launch_dim(const FwdArgs &a, dim3 grid, bool rope_on, hipStream_t st)
 
 }  // namespace
 
-int fwd_bf16_block_rows(int) { return BM; }
+int fwd_bf16_block_rows(bool sparse) { return sparse ? Cfg<true>::BM : Cfg<false>::BM; }
 
-SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu) {
-  const int n_items = ((L.S + BM - 1) / BM) * L.H * L.B;
-  return plan_split(n_items, (L.S + BN - 1) / BN, n_cu * WG_PER_CU, BM, L.D);
+SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse) {
+  const int bm = fwd_bf16_block_rows(sparse);
+  const int wg = sparse ? Cfg<true>::WG_PER_CU : Cfg<false>::WG_PER_CU;
+  const int n_items = ((L.S + bm - 1) / bm) * L.H * L.B;
+  return plan_split(n_items, (L.S + BN - 1) / BN, n_cu * wg, bm, L.D);
 }
 
 int fwd_bf16_sparse_max_seq() { return kSparseMaxSeq; }
@@ -641,11 +668,12 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   a.S_pad = prep_pad(L.S);
   a.H = L.H;
   a.B = L.B;
-  a.n_qblk = (L.S + BM - 1) / BM;
+  const int bm = fwd_bf16_block_rows(mask != nullptr);
+  a.n_qblk = (L.S + bm - 1) / bm;
   a.scale_log2 = L.scale_log2;
   a.n_direct = plan.n_direct;
   a.parts = plan.parts;
-  a.ws = split_workspace(plan, workspace, BM, L.D);
+  a.ws = split_workspace(plan, workspace, bm, L.D);
   a.mask = mask;
   a.nqb = (L.S + kQueryBlock - 1) / kQueryBlock;
   a.nkb = (L.S + kKeyBlock - 1) / kKeyBlock;
@@ -653,7 +681,7 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   const hipError_t e = L.D == 64 ? launch_dim<64>(a, grid, rope != nullptr, st)
                                  : launch_dim<128>(a, grid, rope != nullptr, st);
   if (e != hipSuccess || plan.n_units == 0) return e;
-  return launch_merge_split(L, plan, a.ws, BM, L.scale_log2, o, lse, st);
+  return launch_merge_split(L, plan, a.ws, bm, L.scale_log2, o, lse, st);
 }
 
 }  // namespace ja

@@ -53,7 +53,7 @@ int64_t prep_kv_bytes(const AttnLayout &L);
 hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v,
                                const float *rope, void *kv, hipStream_t st);
 
-SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu);
+SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse);
 // kv: the prepared K/V buffer; mask: NULL = dense, else the block mask of the
 // block-sparse variant, uint8 [B][H][ceil(S/128)][ceil(S/64)] (nonzero =
 // keep).  workspace: the split's partial results (plan.ws_bytes).
@@ -98,7 +98,7 @@ hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const float *sq, 
 
 // Query rows per workgroup of each forward kernel (the grid's x extent is
 // ceil(S / rows)).
-int fwd_bf16_block_rows(int D);
+int fwd_bf16_block_rows(bool sparse);
 int fwd_fp8_block_rows(int D);
 
 }  // namespace ja

@@ -71,16 +71,18 @@ def test_ragged_parity(s, d, density):
 
 
 def test_all_kept_equals_dense_bit_exact():
-    # an all-ones mask stages the same tiles in the same order with the same
-    # split as the dense kernel: identical arithmetic, identical bits
+    # an all-ones mask stages every tile in order, as the dense kernel does:
+    # each row goes through identical arithmetic, so without the split of the
+    # last round (whose plan depends on the workgroup shape) the bits agree
     w = synth.WORKLOADS["t2i_1024"]
     q, k, v, _ = synth.make_qkv(w, seed=4)
     pos = synth.positions(w)
     mask = torch.ones(ja.block_mask_shape(w.batch, w.seq_len, w.heads), dtype=torch.uint8)
     _say("sparse all-ones vs dense t2i_1024")
-    out, lse = _run(q, k, v, mask, pos)
+    out, lse = _run(q, k, v, mask, pos, split=False)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    dense, dense_lse = ja.fwd_bf16(qd, kd, vd, _rope(pos, w.head_dim), return_lse=True)
+    dense, dense_lse = ja.fwd_bf16(qd, kd, vd, _rope(pos, w.head_dim), return_lse=True,
+                                   split=False)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), dense.view(torch.int16))
     assert torch.equal(lse, dense_lse)
