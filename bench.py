@@ -317,8 +317,9 @@ def _norm_leg(ja, w, qd, kd, vd, rope, out, fwd_ms, prep_ms, quant_ms, n, seed):
 
 def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
     """Block-sparse forward on the seeded mask of the workload: its kernel
-    time, the flops of the kept blocks per second, and the blocks staged
-    (kept by any of the three query blocks one workgroup covers)."""
+    time, the flops of the kept blocks per second, and the fraction of the
+    key blocks staged (a workgroup covers one query block and stages the key
+    blocks it keeps)."""
     import numpy as np
     import torch
     import synth
@@ -330,10 +331,7 @@ def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
     kcols = np.minimum(S - kb * np.arange(m.shape[3]), kb)
     pairs = float((m * qrows[:, None] * kcols[None, :]).sum())
     kept_flops = 4.0 * D * pairs
-    nq3 = -(-m.shape[2] // 3)
-    m3 = np.zeros((B, H, nq3 * 3, m.shape[3]), bool)
-    m3[:, :, :m.shape[2]] = m
-    staged = m3.reshape(B, H, nq3, 3, m.shape[3]).any(axis=3).mean()
+    staged = m.mean()
     mask_d = mask.to(qd.device)
     outs = torch.empty_like(out)
     for _ in range(3):
