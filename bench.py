@@ -187,6 +187,7 @@ def main() -> int:
                 "kernel": "attn_fwd_bf16_kernel<128, true, false> (+ merge_split_kernel of the "
                           "split last round); K/V preparation in prep_kv",
                 "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4),
+                "kernel_ms_median": round(sorted(kms)[len(kms) // 2], 4),
                 "prep_kv": {"ms": round(prep_avg, 4),
                             "traffic": _traffic_for_current_kernel(
                                 "prep_kv_bf16_t2i_2048_traffic.txt", "prep_kv.hip"),
