@@ -76,21 +76,26 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
   }
   __syncthreads();
 
-  // V^T: row d, 8 keys per 16-byte chunk, in P-slot order within 16-key groups
+  // V^T: rows d and d+1, 8 keys per 16-byte chunk, in P-slot order within
+  // 16-key groups.  One 4-byte LDS read holds a key's values in both rows;
+  // v_perm_b32 pairs the low halves (row d) and the high halves (row d+1).
 #pragma unroll
-  for (int idx = tid; idx < D * (PK / 8); idx += PT) {
-    const int d = idx / (PK / 8), j = idx % (PK / 8);
-    uint32_t w[4];
+  for (int idx = tid; idx < (D / 2) * (PK / 8); idx += PT) {
+    const int d = 2 * (idx / (PK / 8)), j = idx % (PK / 8);
+    uint32_t w[4], x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int p0 = 8 * j + 2 * e, p1 = p0 + 1;
       const int r0 = 16 * (p0 / 16) + vt_key_of_slot(p0 % 16);
       const int r1 = 16 * (p1 / 16) + vt_key_of_slot(p1 % 16);
-      const uint32_t lo = bit_cast<uint16_t>(vs[r0 * VSTR + d]);
-      const uint32_t hi = bit_cast<uint16_t>(vs[r1 * VSTR + d]);
-      w[e] = lo | (hi << 16);
+      const uint32_t v0 = *reinterpret_cast<const uint32_t *>(vs + r0 * VSTR + d);
+      const uint32_t v1 = *reinterpret_cast<const uint32_t *>(vs + r1 * VSTR + d);
+      w[e] = __builtin_amdgcn_perm(v1, v0, 0x05040100u);    // row d:   key r0 | key r1
+      x[e] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);    // row d+1: key r0 | key r1
     }
     *reinterpret_cast<u32x4 *>(vtb + (int64_t)d * a.S_pad + k0 + 8 * j) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4 *>(vtb + (int64_t)(d + 1) * a.S_pad + k0 + 8 * j) =
+        u32x4{x[0], x[1], x[2], x[3]};
   }
 }
 
