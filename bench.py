@@ -23,6 +23,9 @@ Also reported on the same JSON line:
   sparse        the block-sparse forward on a seeded mask over 128-query x
                 64-key blocks at the block density of the sparse steps
                 (half the blocks kept), against the flops of the kept blocks;
+  gemm_context  a large bf16 GEMM through torch.matmul (the vendor BLAS) timed
+                in the same run: the dense MFMA rate this power-limited part
+                sustains in practice, next to which the forward's rate reads;
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
                 sample of query rows (scaled to TFLOP/s), plus the parity of
                 the GPU output on those rows.
@@ -67,6 +70,7 @@ def _parse():
     ap.add_argument("--no-sparse", action="store_true")
     ap.add_argument("--no-norm", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-context", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -197,6 +201,8 @@ def main() -> int:
     _log(f"[bench] fwd kernel avg {k_avg:.3f} ms -> {achieved:.1f} TFLOP/s "
          f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); K/V prep {prep_avg:.3f} ms")
 
+    gemm = None if args.no_gemm_context else _gemm_context(achieved, max(args.steps, 5))
+
     fp8 = None
     fp8_outs = None
     if not args.no_fp8:
@@ -280,10 +286,34 @@ def main() -> int:
                                   f"{100 * w.outlier_frac:g}% x{w.outlier_scale:g} outlier tokens",
                       "batch": B, "seq_len": S, "heads": H, "head_dim": D,
                       "flops_per_step": flops},
-           "roofline": roofline, "cpu_baseline": cpu, "fp8": fp8, "qk_norm": qk_norm,
+           "roofline": roofline, "gemm_context": gemm, "cpu_baseline": cpu, "fp8": fp8,
+           "qk_norm": qk_norm,
            "sparse": sparse}
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def _gemm_context(fwd_tflops, n):
+    """A 16384 x 16384 x 8192 bf16 GEMM through torch.matmul, timed per
+    launch like the forward: the practical dense bf16 MFMA rate of this GPU
+    under its power limit, for context (not part of the hot path)."""
+    import torch
+    m, nn, kk = 16384, 16384, 8192
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    a = torch.randn(m, kk, generator=g).to(device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(kk, nn, generator=g).to(device="cuda:0", dtype=torch.bfloat16)
+    c = torch.empty(m, nn, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    ms = _time_launches(lambda: torch.matmul(a, b, out=c), n)
+    avg = sum(ms) / len(ms)
+    tf = 2.0 * m * nn * kk / (avg * 1e-3) / 1e12
+    _log(f"[bench] torch.matmul bf16 {m}x{nn}x{kk}: {avg:.3f} ms, {tf:.1f} TFLOP/s")
+    del a, b, c
+    return {"op": f"torch.matmul bf16 {m}x{nn}x{kk}", "ms": round(avg, 4),
+            "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "fwd_over_gemm": round(fwd_tflops / tf, 4)}
 
 
 def _norm_leg(ja, w, qd, kd, vd, rope, out, fwd_ms, prep_ms, quant_ms, n, seed):

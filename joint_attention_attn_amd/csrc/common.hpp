@@ -157,12 +157,12 @@ __host__ __device__ constexpr int vt8_pos(int r) {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// vmcnt-only wait (gfx9 s_waitcnt encoding: expcnt and lgkmcnt at their
-// maxima, i.e. not waited for).
+// vmcnt-only wait (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
+// expcnt and lgkmcnt at their maxima, i.e. not waited for).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Workgroup barrier with no memory fence: a fence would make the compiler

@@ -11,7 +11,9 @@
 //
 // The pass is HBM-bound (read bf16, write 1-byte codes): each head vector of
 // D elements is handled by D/8 lanes with one 16-byte load each; its amax is
-// reduced with lane exchanges inside that lane group.  The rotation uses the
+// reduced with lane exchanges inside that lane group.  A lane handles RPT
+// head vectors and issues all their loads first, so that enough bytes are in
+// flight to cover the HBM latency.  The rotation uses the
 // fixed fp32 operation order of rope_pair_f32 and x / scale is IEEE-rounded
 // (for a power of two, the exact product x * 2^-k), so the codes are a fixed
 // function of the inputs.
@@ -34,21 +36,17 @@ struct QuantArgs {
   int64_t rows;  // B * S * H
 };
 
+constexpr int RPT = 2;        // head vectors per lane
+
 template <int D>
-__global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
+__device__ __forceinline__ void quant_row(const QuantArgs &a, int t, int64_t row, int sub,
+                                          u32x4 w) {
   constexpr int LPR = D / 8;  // lanes per head vector
-  const int t = blockIdx.y;   // 0 = Q, 1 = K, 2 = V
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / LPR;
-  const int sub = (int)(gid % LPR);
   const bool live = row < a.rows;
   const int64_t rr = live ? row : 0;
   const int h = (int)(rr % a.H);
   const int64_t s = (rr / a.H) % a.S;
   const int64_t b = rr / ((int64_t)a.H * a.S);
-
-  const u32x4 w = *reinterpret_cast<const u32x4 *>(
-      a.x[t] + b * a.sb[t] + s * a.ss[t] + h * a.sh[t] + sub * 8);
   const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
   float r[8];
   const float *g = t < 2 ? a.norm[t] : nullptr;
@@ -111,6 +109,29 @@ __global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
   }
 }
 
+// Workgroup of 256 lanes: RPT blocks of 256 / LPR consecutive head vectors.
+template <int D>
+__global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
+  constexpr int LPR = D / 8;
+  constexpr int ROWS = 256 / LPR;
+  const int t = blockIdx.y;   // 0 = Q, 1 = K, 2 = V
+  const int sub = threadIdx.x % LPR;
+  const int64_t row0 = (int64_t)blockIdx.x * ROWS * RPT + threadIdx.x / LPR;
+  u32x4 w[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int64_t row = row0 + j * ROWS;
+    const int64_t rr = row < a.rows ? row : 0;
+    const int h = (int)(rr % a.H);
+    const int64_t s = (rr / a.H) % a.S;
+    const int64_t b = rr / ((int64_t)a.H * a.S);
+    w[j] = *reinterpret_cast<const u32x4 *>(a.x[t] + b * a.sb[t] + s * a.ss[t] + h * a.sh[t] +
+                                            sub * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) quant_row<D>(a, t, row0 + j * ROWS, sub, w[j]);
+}
+
 }  // namespace
 
 hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
@@ -138,8 +159,8 @@ hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
   a.S = L.S;
   a.H = L.H;
   a.rows = (int64_t)L.B * L.S * L.H;
-  const int64_t threads = a.rows * (L.D / 8);
-  const dim3 grid((unsigned)((threads + 255) / 256), 3);
+  const int64_t rows_per_wg = (256 / (L.D / 8)) * RPT;
+  const dim3 grid((unsigned)((a.rows + rows_per_wg - 1) / rows_per_wg), 3);
   if (L.D == 64)
     hipLaunchKernelGGL(quant_rope_fp8_kernel<64>, grid, dim3(256), 0, st, a);
   else

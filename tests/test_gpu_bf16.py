@@ -210,11 +210,14 @@ def _slot_key(p):
     return 4 * (p // 8) + (p % 8 if p % 8 < 4 else p % 8 + 4)
 
 
-@pytest.mark.parametrize("s,d,strided", [(200, 64, False), (1037, 128, False), (130, 128, True)])
-def test_prep_kv_bit_exact(s, d, strided):
+# head counts 3, 6 and 4: workgroups of one, two and four heads
+@pytest.mark.parametrize("s,d,strided,h", [(200, 64, False, 3), (1037, 128, False, 3),
+                                           (130, 128, True, 3), (300, 128, False, 4),
+                                           (130, 64, True, 6)])
+def test_prep_kv_bit_exact(s, d, strided, h):
     # rotated K equals the oracle's bf16-rounded rotation bit for bit; V^T is
     # V transposed in the documented key order; padding is zero
-    w = synth.Workload("prep", 2, 3, d, n_text=s, grid=0)
+    w = synth.Workload("prep", 2, h, d, n_text=s, grid=0)
     q, k, v, _ = synth.make_qkv(w, seed=21)
     pos = np.random.default_rng(s).integers(0, 300, size=(s, 2)).astype(np.int32)
     if strided:
@@ -222,18 +225,18 @@ def test_prep_kv_bit_exact(s, d, strided):
     else:
         kd, vd = k.to(DEV), v.to(DEV)
     rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), d)
-    _say(f"prep kv S={s} D={d} strided={strided}")
+    _say(f"prep kv S={s} D={d} H={h} strided={strided}")
     kv = ja.prep_kv_bf16(kd, vd, rope).cpu()
     s_pad = (s + 63) // 64 * 64
-    n = 2 * 3 * s_pad * d
-    kr = kv[: 2 * n].view(torch.bfloat16).view(2, 3, s_pad, d)
-    vt = kv[2 * n:].view(torch.bfloat16).view(2, 3, d, s_pad)
+    n = 2 * h * s_pad * d
+    kr = kv[: 2 * n].view(torch.bfloat16).view(2, h, s_pad, d)
+    vt = kv[2 * n:].view(torch.bfloat16).view(2, h, d, s_pad)
     table = oracle.rope_table_fp32(pos, d)
     kref = torch.from_numpy(oracle.rotate_fp32(k.float().numpy(), table)).to(torch.bfloat16)
     assert torch.equal(kr[:, :, :s].view(torch.int16), kref.permute(0, 2, 1, 3).contiguous().view(torch.int16))
     assert not kr[:, :, s:].view(torch.int16).any()
     order = torch.tensor([16 * (j // 16) + _slot_key(j % 16) for j in range(s_pad)])
-    vpad = torch.zeros((2, s_pad, 3, d), dtype=torch.bfloat16)
+    vpad = torch.zeros((2, s_pad, h, d), dtype=torch.bfloat16)
     vpad[:, :s] = v
     vref = vpad[:, order].permute(0, 2, 3, 1)            # [B, H, D, S_pad]
     assert torch.equal(vt.view(torch.int16), vref.contiguous().view(torch.int16))
