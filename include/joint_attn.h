@@ -298,7 +298,7 @@ ja_status joint_attn_prep_kv_fp8(const ja_params *p, const void *k8, const void 
  *               scales, positive normal powers of two (the quantizer's);
  *               their exponents are the E8M0 block scales of the Q K^T MFMA.
  *               A workgroup that meets another value writes NaN into its O
- *               rows and LSE entries (its 256-row query block).
+ *               rows and LSE entries (its 384-row query block).
  *   kv8, kv8_bytes   the prepared K/V buffer.  If it was prepared for another
  *               softmax scale, every row comes back NaN.
  *   repair      nullable: with n_rep > 0, the repaired tokens from

@@ -20,13 +20,14 @@
 // a repaired key starts at -inf.  Per score this leaves a max, an FMA, an
 // exp2, the sum's FMA and half a conversion.
 //
-// Structure as in the bf16 kernel: one workgroup of eight wave64s (two per
-// SIMD) per (256-query block, head, batch row), XCD-aware placement, split of
-// the last round.  A preparation pass (prep_kv_fp8.hip) writes each (batch,
-// head)'s K, V^T and per-key values in the layouts of the LDS tiles; buffer
-// loads to LDS copy 64-key tiles into a 4-stage ring three tiles ahead, with
-// no staging registers and no vector work, and Q K^T of the next tile is
-// issued ahead of the softmax of this one.
+// Structure as in the bf16 kernel: one workgroup of twelve wave64s (three
+// per SIMD) per (384-query block, head, batch row), XCD-aware placement,
+// split of the last round.  A preparation pass (prep_kv_fp8.hip) writes each
+// (batch, head)'s K, V^T and per-key values in the layouts of the LDS tiles;
+// buffer loads to LDS copy 64-key tiles into a 4-stage ring three tiles
+// ahead, with no staging registers and no vector work.  Each wave runs
+// Q K^T, softmax and P.V of a tile in turn, and the three waves of a SIMD
+// overlap one another's matrix and vector work.
 #include <atomic>
 
 #include "common.hpp"
@@ -38,10 +39,11 @@ namespace ja {
 
 namespace {
 
-// Waves per workgroup, 32 query rows each, two per SIMD: a wave of this
-// kernel needs about 245 VGPRs (two tiles of S accumulators in flight); three
-// waves per SIMD would allow only 168.
-constexpr int NW = 8;
+// Waves per workgroup, 32 query rows each, three per SIMD (at most 168 VGPRs
+// each).  Software pipelining inside a wave (Q K^T of the next tile issued
+// ahead of this tile's softmax) would keep two tiles of accumulators live,
+// about 245 VGPRs, and allow only two waves per SIMD, which is slower.
+constexpr int NW = 12;
 constexpr int BM = 32 * NW;         // query rows per workgroup
 constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
 constexpr int NT = 64 * NW;         // threads per workgroup
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     return 16 * lane;
   };
   constexpr int JW = (L::LOADS + NW - 1) / NW;         // loads per wave, at most
-  static_assert(JW <= 3 && NW < L::LOADS, "loads per wave");
+  static_assert(JW <= 3, "loads per wave");
   // (scalar offsets: an array element as the builtin's offset operand makes
   // the host compilation drop the kernel's launch stub without a message)
   const int voff0 = load_offset(wave);
@@ -238,9 +240,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, JA_LDS_PTR(dst), 16, voff, t * INFO_BYTES, 0, 0);
   };
-  // loads of key tile t into stage st
+  // loads of key tile t into stage st (at D = 64 a tile has fewer loads than
+  // the workgroup has waves; the last waves issue none)
   auto issue = [&](int t, int st) JA_INLINE {
-    issue_one(wave, voff0, t, st);
+    if (wave < L::LOADS) issue_one(wave, voff0, t, st);
     if (wave + NW < L::LOADS) issue_one(wave + NW, voff1, t, st);
     if (JW >= 3 && wave + 2 * NW < L::LOADS) issue_one(wave + 2 * NW, voff2, t, st);
   };
@@ -363,14 +366,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     return pb;
   };
 
-  // ---- loop over the key tiles t0 .. t1-1 (local index i), software
-  //      pipelined: iteration i issues Q K^T of tile i+1 before the softmax
-  //      of tile i, so the matrix cores work on the next tile while the
-  //      vector units exponentiate this one.  Tile i lives in stage
-  //      i % NSTAGE.  Iteration i first issues the loads of tile i+3 into the
-  //      stage of tile i-1 (whose K was read in iteration i-2 and V in
-  //      iteration i-1); before the barrier that closes it, each wave waits
-  //      for its own loads of tile i+2, whose K the next iteration reads. ----
+  // ---- loop over the key tiles t0 .. t1-1 (local index i).  Tile i lives
+  //      in stage i % NSTAGE.  Iteration i first issues the loads of tile
+  //      i+3 into the stage of tile i-1, which every wave finished before the
+  //      barrier that closed iteration i-1; then Q K^T, the softmax and P.V
+  //      of tile i; before the barrier that closes it, each wave waits for
+  //      its own loads of tile i+1 only. ----
   const int nt = t1 - t0;
 #pragma unroll
   for (int p = 0; p < PREF; ++p)
@@ -379,17 +380,16 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   tile_barrier();
   // the per-key values were prepared for this softmax scale
   bad = bad || Ist(0)[3 * BN] != c;
-  f32x16 sacc[2][2];
-  qk(0, sacc[0]);
-  auto iteration = [&]<int PAR, bool LAST>(int i) JA_INLINE {
+  f32x16 sacc[2];
+  auto iteration = [&]<bool LAST>(int i) JA_INLINE {
     const bool ahead = i + PREF < nt;
     if (ahead) issue(t0 + i + PREF, (i + PREF) % NSTAGE);
-    if constexpr (!LAST) qk((i + 1) % NSTAGE, sacc[PAR ^ 1]);
-    const i32x8 pb = softmax(sacc[PAR], i % NSTAGE);
+    qk(i % NSTAGE, sacc);
+    const i32x8 pb = softmax(sacc, i % NSTAGE);
     pv(pb, i % NSTAGE);
     if constexpr (!LAST) {
       if (ahead)
-        wait_tiles.template operator()<1>();
+        wait_tiles.template operator()<PREF - 1>();
       else
         wait_vmcnt<0>();
       tile_barrier();
@@ -397,17 +397,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       __syncthreads();        // the repair pass restages through the ring
     }
   };
-  int i = 0;
-  for (; i + 2 < nt; i += 2) {
-    iteration.template operator()<0, false>(i);
-    iteration.template operator()<1, false>(i + 1);
-  }
-  if (i + 1 < nt) {
-    iteration.template operator()<0, false>(i);
-    iteration.template operator()<1, true>(i + 1);
-  } else {
-    iteration.template operator()<0, true>(i);
-  }
+  for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<false>(i);
+  iteration.template operator()<true>(nt - 1);
 
   // ---- repaired keys: one more pass over them with their exact values, on
   //      bf16 MFMA (an e4m3 code times its scale is exact in this product:

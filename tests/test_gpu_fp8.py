@@ -146,9 +146,9 @@ def test_prep_kv_fp8_layout(s, d, rep):
 def test_fp8_forward_poisons_rows_of_non_power_of_two_scales(which):
     # Q and K scales must be powers of two (the MFMA applies their exponent);
     # a violation turns the affected rows into NaN: every row of the head for
-    # a K scale, the workgroup's 256-row query block for a Q scale.  Other
+    # a K scale, the workgroup's 384-row query block for a Q scale.  Other
     # heads are untouched.
-    w = synth.Workload("badscale", 1, 2, 64, n_text=300, grid=0)
+    w = synth.Workload("badscale", 1, 2, 64, n_text=500, grid=0)
     q, k, v, _ = synth.make_qkv(w, seed=3)
     q8, k8, v8, sq, sk, sv = oracle.quant_rope_fp8(q, k, v, None)
     _say(f"fp8 fwd with a non-power-of-two {which} scale")
@@ -166,8 +166,8 @@ def test_fp8_forward_poisons_rows_of_non_power_of_two_scales(which):
     if which == "k":
         assert torch.isnan(head1).all() and torch.isnan(lse[:, 1]).all()
     else:
-        assert torch.isnan(head1[:, :256]).all() and torch.isnan(lse[:, 1, :256]).all()
-        assert not torch.isnan(head1[:, 256:]).any()
+        assert torch.isnan(head1[:, :384]).all() and torch.isnan(lse[:, 1, :384]).all()
+        assert not torch.isnan(head1[:, 384:]).any()
 
 
 def test_fp8_forward_rejects_buffer_prepared_for_another_scale():
