@@ -146,3 +146,29 @@ def test_full_size_sampled_rows(name):
     ref, ref_lse = oracle.block_sparse_attention(q, k, v, mask, pos, rows=rows)
     got = out.cpu()[:, torch.as_tensor(rows)]
     _check(got, lse.cpu()[:, :, torch.as_tensor(rows)], ref, ref_lse, scaled=True)
+
+
+def test_longest_sequence_sampled_rows():
+    # the longest sequence the block-sparse forward takes (2^20 tokens, a key
+    # block list of 16384 entries in LDS): each query block keeps its diagonal
+    # key block, the last key block and one seeded other; the oracle attends
+    # sampled rows over all 2^20 keys under the same mask
+    s = 1 << 20
+    w = synth.Workload("sparse_max", 1, 1, 64, n_text=s, grid=0, outlier_frac=0.0)
+    q, k, v, _ = synth.make_qkv(w, seed=5)
+    nqb, nkb = ja.block_mask_shape(1, s, 1)[2:]
+    mask = torch.zeros((1, 1, nqb, nkb), dtype=torch.uint8)
+    qb = torch.arange(nqb)
+    other = torch.from_numpy(np.random.default_rng(6).integers(0, nkb, size=nqb))
+    mask[0, 0, qb, 2 * qb] = 1
+    mask[0, 0, qb, nkb - 1] = 1
+    mask[0, 0, qb, other] = 1
+    _say(f"sparse S={s} (longest), {int(mask.sum())} kept blocks")
+    out, lse = _run(q, k, v, mask, None)
+    rows = np.unique(np.concatenate([np.random.default_rng(7).choice(s, 14, replace=False),
+                                     [0, s - 1]]))
+    ref, ref_lse = oracle.block_sparse_attention(q, k, v, mask, None, rows=rows)
+    got = out.cpu()[:, rows]
+    _say(f"  rel_l2={rel_l2(got, ref):.3e}")
+    assert rel_l2(got, ref) <= BF16_REL_L2 and max_abs(got, ref) <= BF16_MAX_ABS
+    _lse_close(lse.cpu()[:, :, rows], ref_lse)
