@@ -240,3 +240,29 @@ def test_prep_kv_bit_exact(s, d, strided, h):
     vpad[:, :s] = v
     vref = vpad[:, order].permute(0, 2, 3, 1)            # [B, H, D, S_pad]
     assert torch.equal(vt.view(torch.int16), vref.contiguous().view(torch.int16))
+
+
+def test_tensors_past_32_bit_element_offsets():
+    # Q, K, V and O of 2.18e9 elements each (4.4 GB), beyond 2^31: element
+    # offsets of the last heads need 64-bit arithmetic in every pass (table,
+    # preparation, forward, epilogue).  Inputs are drawn on the GPU from a
+    # seeded generator; the oracle checks sampled rows of the first and last
+    # heads.
+    s, h, d = 32768 + 5, 520, 128
+    assert s * h * d > 2 ** 31
+    g = torch.Generator(device=DEV).manual_seed(11)
+    q, k, v = (torch.randn((1, s, h, d), device=DEV, generator=g, dtype=torch.bfloat16)
+               for _ in range(3))
+    pos = np.random.default_rng(12).integers(0, 200, size=(s, 2)).astype(np.int32)
+    rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), d)
+    _say(f"bf16 S={s} H={h} D={d}: {s * h * d / 2 ** 31:.3f} x 2^31 elements per tensor")
+    out = ja.fwd_bf16(q, k, v, rope)
+    torch.cuda.synchronize()
+    heads = [0, h - 1]
+    rows = np.unique(np.concatenate([np.random.default_rng(13).choice(s, 14, replace=False),
+                                     [0, s - 1]]))
+    qs, ks, vs = (t[:, :, heads].cpu() for t in (q, k, v))
+    ref, _ = oracle.joint_attention(qs, ks, vs, pos, rows=rows)
+    got = out[:, :, heads].cpu()[:, rows]
+    _say(f"  rel_l2={rel_l2(got, ref):.3e} max_abs={max_abs(got, ref):.3e}")
+    assert rel_l2(got, ref) <= BF16_REL_L2 and max_abs(got, ref) <= BF16_MAX_ABS
