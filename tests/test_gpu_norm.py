@@ -8,7 +8,8 @@ import torch
 import joint_attention_attn_amd as ja
 import oracle
 import synth
-from parity_util import BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, max_abs, rel_l2, row_scaled_max_abs
+from parity_util import (BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, max_abs, rel_l2,
+                         row_scaled_max_abs, sample_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -120,3 +121,25 @@ def test_repair_plan_with_norm_bit_exact():
     kr, vr = oracle.repair_values(k, v, pos, idx, norm=(gq, gk, EPS))
     assert torch.equal(rp.kr.cpu()[:, :, :n].to(torch.float64), kr)
     assert torch.equal(rp.vr.cpu()[:, :, :n].to(torch.float64), vr)
+
+
+def test_forward_with_norm_2048_sampled():
+    # the bench's norm leg: t2i_2048 with seeded norm weights, sampled rows
+    # (random, 16 outlier rows, first/last text and last rows) by the oracle
+    w = synth.WORKLOADS["t2i_2048"]
+    q, k, v, idx = synth.make_qkv(w, 0)
+    pos = synth.positions(w)
+    gq, gk = synth.make_norm_weights(w.head_dim, 0)
+    rope = ja.rope_table_2d(_dev(pos), w.head_dim)
+    _say("bf16 forward with norm, t2i_2048")
+    out, lse = ja.fwd_bf16(q.to(DEV), k.to(DEV), v.to(DEV), rope, return_lse=True,
+                           q_norm=_dev(gq), k_norm=_dev(gk), norm_eps=EPS)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.seq_len, w.n_text, idx[:16], 64, seed=3)
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos, norm=(gq, gk, EPS), rows=rows)
+    got = out.cpu()[:, torch.as_tensor(rows)]
+    got_lse = lse.cpu()[:, :, torch.as_tensor(rows)]
+    _say(f"  rel_l2={rel_l2(got, ref):.3e}")
+    assert rel_l2(got, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(got, ref) <= BF16_MAX_ABS
+    assert max_abs(got_lse, ref_lse) <= 1e-2
