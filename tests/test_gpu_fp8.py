@@ -226,6 +226,12 @@ def test_fp8_2048_sampled(name, n_rows):
 
 # ---- repair of the tokens with the largest quantization error ----
 
+def _oracle_repair_idx(k, v, pos, ref_codes, n):
+    # the oracle's own selection of the repaired tokens, from its own codes
+    err = oracle.repair_errors(k, v, pos, ref_codes[1], ref_codes[2], ref_codes[4], ref_codes[5])
+    return oracle.repair_select(err, n)
+
+
 def _repair_gpu(q, k, v, pos, n_rep):
     d = q.shape[-1]
     rope = ja.rope_table_2d(torch.from_numpy(pos).to(DEV), d) if pos is not None else None
@@ -279,7 +285,8 @@ def test_repaired_forward_ragged(s, d, budget):
     out = ja.fwd_fp8(*codes, repair=rep)
     torch.cuda.synchronize()
     ref_codes = oracle.quant_rope_fp8(q, k, v, pos)
-    idx = rep.idx.cpu().numpy()
+    idx = _oracle_repair_idx(k, v, pos, ref_codes, n)
+    assert np.array_equal(rep.idx.cpu().numpy(), idx)
     kr, vr = oracle.repair_values(k, v, pos, idx)
     ref, _ = oracle.fp8_repaired_attention(*ref_codes, idx, kr, vr)
     assert not torch.isnan(out).any()
@@ -302,7 +309,8 @@ def test_repaired_forward_1024_closer_to_bf16_path():
     out_0 = ja.fwd_fp8(*codes)
     torch.cuda.synchronize()
     ref_codes = oracle.quant_rope_fp8(q, k, v, pos)
-    idx = rep.idx.cpu().numpy()
+    idx = _oracle_repair_idx(k, v, pos, ref_codes, n)
+    assert np.array_equal(rep.idx.cpu().numpy(), idx)
     kr, vr = oracle.repair_values(k, v, pos, idx)
     rows = sample_rows(w.seq_len, w.n_text, oidx, 192, seed=3)
     ref_r, ref_lse = oracle.fp8_repaired_attention(*ref_codes, idx, kr, vr, rows=rows)

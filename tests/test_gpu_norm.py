@@ -114,7 +114,7 @@ def test_repair_plan_with_norm_bit_exact():
     rp = ja.fp8_repair_plan(kd, vd, rope, codes[1], codes[2], codes[4], codes[5], n,
                             k_norm=_dev(gk), norm_eps=EPS)
     torch.cuda.synchronize()
-    q8, k8, v8, sq, sk, sv = (c.cpu().numpy() for c in codes)
+    _, k8, v8, _, sk, sv = oracle.quant_rope_fp8(q, k, v, pos, norm=(gq, gk, EPS))
     err = oracle.repair_errors(k, v, pos, k8, v8, sk, sv, norm=(gq, gk, EPS))
     idx = oracle.repair_select(err, n)
     assert np.array_equal(rp.idx.cpu().numpy(), idx)
