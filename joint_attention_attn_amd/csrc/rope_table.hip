@@ -13,19 +13,26 @@
 
 namespace ja {
 
+// The D/4 frequencies are computed once per workgroup (fp64 pow is the most
+// expensive step); every entry then takes one fp64 product and one sincos
+// (a shared argument reduction for the cosine and the sine).
 __global__ __launch_bounds__(256) void rope_table_2d_kernel(
     const int32_t *__restrict__ pos, int S, int D, double theta,
     float2 *__restrict__ table) {
+  __shared__ double freq[32];                 // D/4 <= 32
   const int half = D / 2, quarter = D / 4;
+  if ((int)threadIdx.x < quarter) freq[threadIdx.x] = pow(theta, (double)(-4 * (int)threadIdx.x) / (double)D);
+  __syncthreads();
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)S * half) return;
   const int p = (int)(idx % half);
   const int64_t s = idx / half;
   const int axis = p / quarter;
   const int k = p - axis * quarter;
-  const double w = pow(theta, (double)(-4 * k) / (double)D);
-  const double ang = (double)pos[2 * s + axis] * w;
-  table[idx] = make_float2((float)cos(ang), (float)sin(ang));
+  const double ang = (double)pos[2 * s + axis] * freq[k];
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  table[idx] = make_float2((float)cs, (float)sn);
 }
 
 hipError_t launch_rope_table_2d(const int32_t *pos, int S, int D, float theta,
