@@ -150,14 +150,11 @@ def main() -> int:
     out = torch.empty_like(qd)
     torch.cuda.synchronize()
 
-    rope_holder = {}
-
     def step():
-        rope = ja.rope_table_2d(pos_d, D, w.theta)
-        kv = ja.prep_kv_bf16(kd, vd, rope)
-        ja.fwd_bf16_prepared(qd, kv, rope, out=out)
-        rope_holder["rope"] = rope
-        rope_holder["kv"] = kv
+        # the whole path in one call: RoPE table from the positions, K/V
+        # preparation (K rotated, V transposed), forward (RoPE fused into the
+        # Q load)
+        ja.fwd_bf16(qd, kd, vd, pos_d, w.theta, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -175,12 +172,18 @@ def main() -> int:
     _log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
     # dominant kernel: the attention forward (RoPE fused into the Q load),
-    # timed per launch; the K/V preparation beside it
-    rope, kv = rope_holder["rope"], rope_holder["kv"]
-    kms = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope, out=out), max(args.steps, 5))
+    # timed per launch on K/V prepared once; the preparation beside it
+    rope = ja.rope_table_2d(pos_d, D, w.theta)
+    kv = ja.prep_kv_bf16(kd, vd, rope=rope)
+    n_t = max(args.steps, 5)
+    kms = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope=rope, out=out), n_t)
     k_avg = sum(kms) / len(kms)
-    pms = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope), max(args.steps, 5))
+    pms = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope=rope), n_t)
     prep_avg = sum(pms) / len(pms)
+    tms = _time_launches(lambda: ja.rope_table_2d(pos_d, D, w.theta), n_t)
+    table_avg = sum(tms) / len(tms)
+    # the benchmarked output comes from the one-call path
+    ja.fwd_bf16(qd, kd, vd, pos_d, w.theta, out=out)
     # algorithmic bytes of the preparation: read K, V and the table, write both
     prep_bytes = 4 * B * S * H * D * 2 + S * (D // 2) * 8
     achieved = flops / (k_avg * 1e-3) / 1e12
@@ -192,6 +195,7 @@ def main() -> int:
                           "split last round); K/V preparation in prep_kv",
                 "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4),
                 "kernel_ms_median": round(sorted(kms)[len(kms) // 2], 4),
+                "rope_table_ms": round(table_avg, 4),
                 "prep_kv": {"ms": round(prep_avg, 4),
                             "traffic": _traffic_for_current_kernel(
                                 "prep_kv_bf16_t2i_2048_traffic.txt", "prep_kv.hip"),
@@ -199,23 +203,24 @@ def main() -> int:
                             "frac_of_hbm": round(prep_bytes / (prep_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                                  4)}}
     _log(f"[bench] fwd kernel avg {k_avg:.3f} ms -> {achieved:.1f} TFLOP/s "
-         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); K/V prep {prep_avg:.3f} ms")
+         f"({100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 peak); K/V prep {prep_avg:.3f} ms, "
+         f"table {table_avg:.3f} ms")
 
     gemm = None if args.no_gemm_context else _gemm_context(achieved, max(args.steps, 5))
 
     fp8 = None
     fp8_outs = None
     if not args.no_fp8:
-        q8, k8, v8, sq, sk, sv = ja.quant_rope_fp8(qd, kd, vd, rope)
+        q8, k8, v8, sq, sk, sv = ja.quant_rope_fp8(qd, kd, vd, rope=rope)
         kv8 = ja.prep_kv_fp8(k8, v8, sk, sv)
         out8 = torch.empty_like(out)
         for _ in range(2):
-            ja.quant_rope_fp8(qd, kd, vd, rope)
+            ja.quant_rope_fp8(qd, kd, vd, rope=rope)
             ja.prep_kv_fp8(k8, v8, sk, sv)
             ja.fwd_fp8_prepared(q8, sq, kv8, out=out8)
         torch.cuda.synchronize()
         n = max(args.steps, 5)
-        qms = _time_launches(lambda: ja.quant_rope_fp8(qd, kd, vd, rope), n)
+        qms = _time_launches(lambda: ja.quant_rope_fp8(qd, kd, vd, rope=rope), n)
         pp8 = _time_launches(lambda: ja.prep_kv_fp8(k8, v8, sk, sv), n)
         fms = _time_launches(lambda: ja.fwd_fp8_prepared(q8, sq, kv8, out=out8), n)
         q_avg, pp_avg, f_avg = sum(qms) / n, sum(pp8) / n, sum(fms) / n
@@ -245,13 +250,14 @@ def main() -> int:
         # repair of the tokens with the largest quantization error, at the
         # pages' budget 0.005
         n_rep = ja.repair_count(REPAIR_BUDGET, S)
-        rp = ja.fp8_repair_plan(kd, vd, rope, k8, v8, sk, sv, n_rep)
+        rp = ja.fp8_repair_plan(kd, vd, k8, v8, sk, sv, n_rep, rope=rope)
         kv8r = ja.prep_kv_fp8(k8, v8, sk, sv, repair=rp)
         out8r = torch.empty_like(out)
         for _ in range(2):
             ja.fwd_fp8_prepared(q8, sq, kv8r, out=out8r, repair=rp)
         torch.cuda.synchronize()
-        pms = _time_launches(lambda: ja.fp8_repair_plan(kd, vd, rope, k8, v8, sk, sv, n_rep), n)
+        pms = _time_launches(lambda: ja.fp8_repair_plan(kd, vd, k8, v8, sk, sv, n_rep, rope=rope),
+                             n)
         rms = _time_launches(lambda: ja.fwd_fp8_prepared(q8, sq, kv8r, out=out8r, repair=rp), n)
         p_avg, r_avg = sum(pms) / n, sum(rms) / n
         fp8["repair"] = {"budget": REPAIR_BUDGET, "tokens_per_head": n_rep,
@@ -323,21 +329,22 @@ def _norm_leg(ja, w, qd, kd, vd, rope, out, fwd_ms, prep_ms, quant_ms, n, seed):
     import synth
     B, S, H, D = w.shape
     gq, gk = (torch.from_numpy(g).to(qd.device) for g in synth.make_norm_weights(D, seed))
-    kv = ja.prep_kv_bf16(kd, vd, rope, k_norm=gk)
+    kv = ja.prep_kv_bf16(kd, vd, rope=rope, k_norm=gk)
     # its own output buffer: `out` keeps the plain forward's result, which
     # the CPU baseline checks
     outn = torch.empty_like(out)
     for _ in range(3):
-        ja.fwd_bf16_prepared(qd, kv, rope, out=outn, q_norm=gq)
+        ja.fwd_bf16_prepared(qd, kv, rope=rope, out=outn, q_norm=gq)
     torch.cuda.synchronize()
-    pm = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope, k_norm=gk), n)
-    fm = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope, out=outn, q_norm=gq), n)
+    pm = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope=rope, k_norm=gk), n)
+    fm = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope=rope, out=outn, q_norm=gq), n)
     p_avg, f_avg = sum(pm) / n, sum(fm) / n
     rec = {"weights": "seeded g = 1 + 0.1 N(0,1), eps 1e-6",
            "prep_kv_ms": round(p_avg, 4), "prep_kv_ms_without": round(prep_ms, 4),
            "fwd_ms": round(f_avg, 4), "fwd_ms_without": round(fwd_ms, 4)}
     if quant_ms is not None:
-        qm = _time_launches(lambda: ja.quant_rope_fp8(qd, kd, vd, rope, q_norm=gq, k_norm=gk), n)
+        qm = _time_launches(lambda: ja.quant_rope_fp8(qd, kd, vd, rope=rope, q_norm=gq, k_norm=gk),
+                            n)
         rec["quant_ms"] = round(sum(qm) / n, 4)
         rec["quant_ms_without"] = round(quant_ms, 4)
     _log(f"[bench] qk norm: prep {p_avg:.3f} ms (without {prep_ms:.3f}), fwd {f_avg:.3f} ms "
@@ -366,9 +373,10 @@ def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
     mask_d = mask.to(qd.device)
     outs = torch.empty_like(out)
     for _ in range(3):
-        ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope, out=outs)
+        ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope=rope, out=outs)
     torch.cuda.synchronize()
-    ms = _time_launches(lambda: ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope, out=outs), n)
+    ms = _time_launches(lambda: ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope=rope,
+                                                                  out=outs), n)
     avg = sum(ms) / n
     tf = kept_flops / (avg * 1e-3) / 1e12
     _log(f"[bench] sparse (density {synth.SPARSE_DENSITY}): {avg:.3f} ms, {tf:.1f} TFLOP/s of "
@@ -382,14 +390,17 @@ def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
 
 def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s, fp8_outs=None):
     """The fp64 oracle on this host's cores over a bounded sample of query
-    rows (all keys, all heads), scaled to TFLOP/s; plus parity on those rows
-    (and, on the same rows, the distance of the FP8 and repaired FP8 outputs
-    from the oracle)."""
+    rows (all keys, all heads), scaled to TFLOP/s; plus the parity of the GPU
+    output on those rows, the distance of the FP8 and repaired FP8 outputs
+    from the bf16 path's oracle on them, and the FP8 output's parity with the
+    oracle's own FP8 path (its quantizer, then fp64 attention on the
+    dequantized codes) on the first rows of the sample."""
     import numpy as np
     import torch
     import oracle
 
     threads = torch.get_num_threads()
+    cores = len(os.sched_getaffinity(0))
     B, S, H, D = w.shape
     rng = np.random.default_rng(7)
     order = rng.permutation(S)
@@ -414,15 +425,27 @@ def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s, fp8_outs=None):
     sample_flops = 4.0 * B * H * n * S * D
     tflops = sample_flops / spent / 1e12
     _log(f"[bench] cpu oracle: {n} query rows x {H} heads in {spent:.1f} s on {threads} "
-         f"threads -> {tflops * 1e3:.2f} GFLOP/s")
-    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} random query rows x {B * H} (batch, head) pairs x all {S} keys "
-                      f"({sample_flops / 1e9:.1f} GFLOP) of {w.name}, fp64 torch-CPU",
-            "seconds": round(spent, 2),
-            "gpu_rel_l2_on_sample": round(math.sqrt(errs_num / errs_den), 6),
-            **({"fp8_rel_l2_on_sample": round(math.sqrt(f8_num[0] / errs_den), 6),
-                "fp8_repair_rel_l2_on_sample": round(math.sqrt(f8_num[1] / errs_den), 6)}
-               if f8_all else {})}
+         f"threads ({cores} cores in the affinity mask) -> {tflops * 1e3:.2f} GFLOP/s")
+    rec = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": cores, "torch_threads": threads,
+           "kind": "oracle",
+           "sample": f"{n} random query rows x {B * H} (batch, head) pairs x all {S} keys "
+                     f"({sample_flops / 1e9:.1f} GFLOP) of {w.name}, fp64 torch-CPU",
+           "seconds": round(spent, 2),
+           "gpu_rel_l2_on_sample": round(math.sqrt(errs_num / errs_den), 6)}
+    if f8_all:
+        rec["fp8_vs_bf16_oracle_rel_l2_on_sample"] = round(math.sqrt(f8_num[0] / errs_den), 6)
+        rec["fp8_repair_vs_bf16_oracle_rel_l2_on_sample"] = round(math.sqrt(f8_num[1] / errs_den), 6)
+        # the FP8 criterion: the oracle run on its own dequantized codes
+        rows = np.sort(order[:256])
+        t0 = time.perf_counter()
+        codes = oracle.quant_rope_fp8(q, k, v, pos, w.theta)
+        ref8, _ = oracle.fp8_attention(*codes, rows=rows)
+        got8 = f8_all[0][:, rows].double()
+        rec["fp8_rel_l2_vs_fp8_oracle"] = round(float((got8 - ref8).norm() / ref8.norm()), 6)
+        rec["fp8_oracle_rows"] = len(rows)
+        _log(f"[bench] fp8 vs the oracle's FP8 path on {len(rows)} rows: "
+             f"rel-L2 {rec['fp8_rel_l2_vs_fp8_oracle']:.3e} ({time.perf_counter() - t0:.1f} s)")
+    return rec
 
 
 if __name__ == "__main__":

@@ -4,8 +4,9 @@
 // NVIDIA Blackwell GPUs", section "FLUX 3 inference with TensorRT LLM
 // VisualGen"): one dense softmax over the concatenated text / target / reference
 // tokens.  RoPE is applied to Q and K before the product (same page, section
-// "GEMM kernel optimization"); here it is applied in fp32 while Q and K are
-// loaded and the rotated values are rounded to bf16 for the MFMA.
+// "GEMM kernel optimization"); here it is applied in fp64 while Q is loaded
+// (K in the preparation pass) and the rotated values are rounded once to
+// bf16 for the MFMA.
 //
 // Work decomposition: one workgroup per (384-query block, head, batch row),
 // twelve wave64s of 32 query rows each, three per SIMD.  Both products are
@@ -104,7 +105,7 @@ struct FwdArgs {
   const float *qn;          // Q RMS-norm weights [D], NULL = none
   float eps;
   const bf16 *kr, *vt;      // prepared K and V^T (prep_kv.hip), S_pad keys
-  const float2 *rope;
+  const double2 *rope;      // RoPE table [S][D/2] (cos, sin) in fp64
   bf16 *o;
   float *lse;
   int64_t q_sb, q_ss, q_sh, o_sb, o_ss, o_sh;
@@ -282,32 +283,21 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
     u32x4 w[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) w[kk] = *reinterpret_cast<const u32x4 *>(qrow + 16 * kk + 8 * hf);
-    float rn = 0.f;
+    // RMS norm scale (fp64: the lane half holds half the row's chunks)
+    double rn = 0.0;
     if (a.qn) {
-      // RMS norm: the butterfly levels c ^ 2, c ^ 4, ... are kk ^ 1, kk ^ 2,
-      // ... inside the lane; the last level, c ^ 1, is the other lane half
-      float ss[NK];
+      double ss = 0.0;
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) ss[kk] = chunk_sumsq(w[kk]);
-#pragma unroll
-      for (int lev = 1; lev < NK; lev <<= 1) {
-        float t[NK];
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) t[kk] = ss[kk] + ss[kk ^ lev];
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) ss[kk] = t[kk];
-      }
-      rn = rms_scale<D>(half_sum(ss[0]), a.eps);
+      for (int kk = 0; kk < NK; ++kk) ss += chunk_sumsq_f64(w[kk]);
+      rn = rms_scale_f64<D>(ss + __shfl_xor(ss, 32), a.eps);
     }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int d0 = 16 * kk + 8 * hf;
       u32x4 x = w[kk];
-      const float2 *cs = ROPE ? a.rope + (int64_t)qs * (D / 2) + d0 / 2 : nullptr;
-      if (a.qn)
-        x = norm_rope_chunk_bf16(x, rn, a.qn + d0, cs);
-      else if constexpr (ROPE)
-        x = rope_chunk_bf16(x, cs);
+      if (ROPE || a.qn)
+        x = prologue_chunk_bf16(x, rn, a.qn ? a.qn + d0 : nullptr,
+                                ROPE ? a.rope + (int64_t)qs * (D / 2) + d0 / 2 : nullptr);
       if (qi[r] >= S) x = u32x4{0, 0, 0, 0};
       qreg[r][kk] = bit_cast<bf16x8>(x);
     }
@@ -647,7 +637,7 @@ SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse) {
 int fwd_bf16_sparse_max_seq() { return kSparseMaxSeq; }
 
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
-                           const float *rope, const uint8_t *mask, void *o, float *lse,
+                           const double *rope, const uint8_t *mask, void *o, float *lse,
                            const SplitPlan &plan, void *workspace, hipStream_t st) {
   // kv: prepared K | prepared V^T (prep_kv.hip)
   const int64_t prep_elems = (int64_t)L.B * L.H * prep_pad(L.S) * L.D;
@@ -659,7 +649,7 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   a.eps = L.norm_eps;
   a.kr = kr;
   a.vt = vt;
-  a.rope = reinterpret_cast<const float2 *>(rope);
+  a.rope = reinterpret_cast<const double2 *>(rope);
   a.o = static_cast<bf16 *>(o);
   a.lse = lse;
   a.q_sb = L.q_sb; a.q_ss = L.q_ss; a.q_sh = L.q_sh;

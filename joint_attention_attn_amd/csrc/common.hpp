@@ -1,5 +1,6 @@
-// Device-side vocabulary shared by the gfx950 kernels: vector types,
-// bf16 packing and the RoPE pair rotation.
+// Device-side vocabulary shared by the gfx950 kernels: vector types, bf16
+// packing, and the Q/K prologue (RMS normalization and RoPE in fp64, one
+// rounding to the operand format).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -34,108 +35,110 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// RoPE of one adjacent pair (x, y) by the angle whose (cos, sin) is cs:
-// (x c - y s, x s + y c) in fp32 with a fixed operation order, the y term
-// rounded on its own and the x term fused onto it:
-//   rx = fma(x, c, -fl(y s)),  ry = fma(x, s, fl(y c)).
-// The result is later rounded to bf16 or e4m3, so the order is pinned down
-// (no compiler contraction) to make those rounding decisions reproducible.
-__device__ __forceinline__ void rope_pair_f32(float x, float y, float2 cs, float &rx,
-                                              float &ry) {
+// ---- The Q/K prologue: the query/key RMS normalization and the RoPE
+// rotation that the pages put in the epilogue of the QKV projection ("Speed
+// Up Image Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs",
+// section "GEMM kernel optimization"), evaluated in fp64 and rounded ONCE to
+// the operand format (bf16, or e4m3 after the scale):
+//   y_d = x_d * r * g_d,  r = 1 / sqrt(sum(x^2) / D + eps)   (optional)
+//   (y_2p, y_2p+1) -> (y_2p cos - y_2p+1 sin, y_2p sin + y_2p+1 cos)
+// fp64 carries the exact products and, for bf16 inputs, the exact sum of
+// squares, so the rounded result is the rounding of the exact value except
+// in cases of probability ~2^-40.  The single rounding goes through fp32
+// with round-to-odd, which keeps the second rounding (fp32 -> bf16 or e4m3,
+// 24 against 8 or 4 significant bits) correct.
+
+// fp64 -> fp32, rounded to odd: truncation toward zero, with the last bit
+// set when the result is inexact.
+__device__ __forceinline__ float f32_round_odd(double x) {
+  const float f = (float)x;                       // to nearest even
+  uint32_t u = __float_as_uint(f);
+  if ((double)f != x && (u & 1u) == 0) {
+    // the odd neighbour on x's side of f
+    u += __builtin_fabs(x) > __builtin_fabs((double)f) ? 1 : -1;
+  }
+  return __uint_as_float(u);
+}
+
+// Two fp64 values -> packed bf16x2, each rounded once to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2_f64(double a, double b) {
+  return pack_bf16x2(f32_round_odd(a), f32_round_odd(b));
+}
+
+// Rotation of one adjacent pair (x, y) by the angle whose (cos, sin) is cs,
+// in fp64 (products and difference each rounded, as the formula reads).
+__device__ __forceinline__ void rope_pair_f64(double x, double y, double2 cs, double &rx,
+                                              double &ry) {
 #pragma clang fp contract(off)
-  const float ys = y * cs.y;
-  const float yc = y * cs.x;
-  rx = __builtin_fmaf(x, cs.x, -ys);
-  ry = __builtin_fmaf(x, cs.y, yc);
+  rx = x * cs.x - y * cs.y;
+  ry = x * cs.y + y * cs.x;
 }
 
-// The same rotation of a packed bf16 pair, rounded back to packed bf16.
-__device__ __forceinline__ uint32_t rope_pair_bf16(uint32_t w, float2 cs) {
-  float rx, ry;
-  rope_pair_f32(bf16_lo(w), bf16_hi(w), cs, rx, ry);
-  return pack_bf16x2(rx, ry);
-}
-
-// Rotate the 8 bf16 (4 pairs) of a 16-byte chunk with 4 consecutive table
-// entries.
-__device__ __forceinline__ u32x4 rope_chunk_bf16(u32x4 w, const float2 *cs) {
-  const float4 t01 = reinterpret_cast<const float4 *>(cs)[0];
-  const float4 t23 = reinterpret_cast<const float4 *>(cs)[1];
-  u32x4 r;
-  r.x = rope_pair_bf16(w.x, make_float2(t01.x, t01.y));
-  r.y = rope_pair_bf16(w.y, make_float2(t01.z, t01.w));
-  r.z = rope_pair_bf16(w.z, make_float2(t23.x, t23.y));
-  r.w = rope_pair_bf16(w.w, make_float2(t23.z, t23.w));
-  return r;
-}
-
-// ---- query/key RMS normalization ("Speed Up Image Generation with FLUX 3
-// Image Klein on NVIDIA Blackwell GPUs", section "GEMM kernel optimization":
-// query/key normalization next to RoPE in the QKV epilogue), applied in fp32
-// before the rotation:  y_d = fl(fl(x_d * r) * g_d),
-// r = 1 / sqrt(ss / D + eps) with IEEE fp32 square root and division.  The sum
-// of squares ss has one fixed order wherever it is computed: chunk c of 8
-// elements accumulates fma(x, x, s) over its elements from 0, then the chunk
-// sums combine pairwise with partner c ^ k for k = 2, 4, ..., D/16, then
-// k = 1 (a butterfly: every chunk ends with the same total).
-
-// Sum of squares of the 8 bf16 of a 16-byte chunk, in element order.
-__device__ __forceinline__ float chunk_sumsq(u32x4 w) {
+// Sum of squares of the 8 bf16 of a 16-byte chunk, in fp64 (exact: every
+// square has 16 significant bits).
+__device__ __forceinline__ double chunk_sumsq_f64(u32x4 w) {
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-  float s = 0.f;
+  double s = 0.0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    s = __builtin_fmaf(bf16_lo(ws[e]), bf16_lo(ws[e]), s);
-    s = __builtin_fmaf(bf16_hi(ws[e]), bf16_hi(ws[e]), s);
+    const double lo = bf16_lo(ws[e]), hi = bf16_hi(ws[e]);
+    s = __builtin_fma(lo, lo, s);
+    s = __builtin_fma(hi, hi, s);
   }
   return s;
 }
 
-// Butterfly over the chunk sums when lane (i % CH) of each group of CH
-// consecutive lanes holds chunk i % CH.
+// Sum over the chunks of a row when lane (i % CH) of each group of CH
+// consecutive lanes holds chunk i % CH (every lane gets the total).
 template <int CH>
-__device__ __forceinline__ float chunk_sum_lanes(float s) {
+__device__ __forceinline__ double chunk_sum_lanes_f64(double s) {
 #pragma unroll
-  for (int k = 2; k < CH; k <<= 1) s = s + __shfl_xor(s, k);
-  if constexpr (CH > 1) s = s + __shfl_xor(s, 1);
+  for (int k = 1; k < CH; k <<= 1) s += __shfl_xor(s, k);
   return s;
 }
 
-// r = 1 / sqrt(ss / D + eps); D is a power of two, so ss / D is exact.
+// r = 1 / sqrt(ss / D + eps) in fp64.
 template <int D>
-__device__ __forceinline__ float rms_scale(float ss, float eps) {
-  return 1.f / __builtin_sqrtf(ss * (1.f / D) + eps);
+__device__ __forceinline__ double rms_scale_f64(double ss, float eps) {
+  return 1.0 / __builtin_sqrt(ss * (1.0 / D) + (double)eps);
 }
 
-// The 8 values of a chunk normalized: fl(fl(x * r) * g) with g the chunk's 8
-// weights.
-__device__ __forceinline__ void norm_chunk(u32x4 w, float r, const float *g, float (&y)[8]) {
+// The prologue of one 16-byte chunk (elements d0 .. d0+7 of a head vector)
+// in fp64: normalized with r and the chunk's 8 weights g (if g), rotated
+// with the chunk's 4 table entries cs (if cs).
+__device__ __forceinline__ void prologue_chunk_f64(u32x4 w, double r, const float *g,
+                                                   const double2 *cs, double (&y)[8]) {
 #pragma clang fp contract(off)
-  const float4 g0 = reinterpret_cast<const float4 *>(g)[0];
-  const float4 g1 = reinterpret_cast<const float4 *>(g)[1];
-  const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    y[2 * e] = (bf16_lo(ws[e]) * r) * gv[2 * e];
-    y[2 * e + 1] = (bf16_hi(ws[e]) * r) * gv[2 * e + 1];
+    y[2 * e] = bf16_lo(ws[e]);
+    y[2 * e + 1] = bf16_hi(ws[e]);
+  }
+  if (g) {
+    const float4 g0 = reinterpret_cast<const float4 *>(g)[0];
+    const float4 g1 = reinterpret_cast<const float4 *>(g)[1];
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * r * (double)gv[e];
+  }
+  if (cs) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double2 t = cs[e];
+      const double x0 = y[2 * e], x1 = y[2 * e + 1];
+      rope_pair_f64(x0, x1, t, y[2 * e], y[2 * e + 1]);
+    }
   }
 }
 
-// Normalize (if g) and rotate (if cs) a chunk, rounded to bf16.
-__device__ __forceinline__ u32x4 norm_rope_chunk_bf16(u32x4 w, float r, const float *g,
-                                                      const float2 *cs) {
-  float y[8];
-  norm_chunk(w, r, g, y);
-  u32x4 o;
-  uint32_t *op = reinterpret_cast<uint32_t *>(&o);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float rx = y[2 * e], ry = y[2 * e + 1];
-    if (cs) rope_pair_f32(y[2 * e], y[2 * e + 1], cs[e], rx, ry);
-    op[e] = pack_bf16x2(rx, ry);
-  }
-  return o;
+// The prologue of a chunk rounded to bf16 (the MFMA operand).
+__device__ __forceinline__ u32x4 prologue_chunk_bf16(u32x4 w, double r, const float *g,
+                                                     const double2 *cs) {
+  double y[8];
+  prologue_chunk_f64(w, r, g, cs, y);
+  return u32x4{pack_bf16x2_f64(y[0], y[1]), pack_bf16x2_f64(y[2], y[3]),
+               pack_bf16x2_f64(y[4], y[5]), pack_bf16x2_f64(y[6], y[7])};
 }
 
 // Key held by slot p (0..15) of a 16-key group in the P operand of the P.V

@@ -18,8 +18,9 @@ struct AttnLayout {
   float norm_eps = 1e-6f;
 };
 
+// RoPE table: (cos, sin) in fp64 per (token, pair), [S][D/2][2] doubles.
 hipError_t launch_rope_table_2d(const int32_t *pos, int S, int D, float theta,
-                                float *table, hipStream_t st);
+                                double *table, hipStream_t st);
 
 // Split of the last partial round of workgroups over key ranges.  A forward
 // launch has n_items (query block, head, batch row) work items for `slots`
@@ -51,20 +52,20 @@ hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
 int prep_pad(int S);
 int64_t prep_kv_bytes(const AttnLayout &L);
 hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v,
-                               const float *rope, void *kv, hipStream_t st);
+                               const double *rope, void *kv, hipStream_t st);
 
 SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse);
 // kv: the prepared K/V buffer; mask: NULL = dense, else the block mask of the
 // block-sparse variant, uint8 [B][H][ceil(S/128)][ceil(S/64)] (nonzero =
 // keep).  workspace: the split's partial results (plan.ws_bytes).
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
-                           const float *rope, const uint8_t *mask, void *o, float *lse,
+                           const double *rope, const uint8_t *mask, void *o, float *lse,
                            const SplitPlan &plan, void *workspace, hipStream_t st);
 int fwd_bf16_sparse_max_seq();   // longest sequence of the block-sparse variant
 
 hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
                                  const void *k, const void *v,
-                                 const float *rope, void *q8, void *k8,
+                                 const double *rope, void *q8, void *k8,
                                  void *v8, float *sq, float *sk, float *sv,
                                  hipStream_t st);
 
@@ -77,7 +78,7 @@ struct Fp8Repair {
 int repair_pad(int n);          // repaired keys rounded up to whole 32-key tiles
 int repair_max_seq();           // longest sequence the selection handles
 hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
-                              const float *rope, const void *k8, const void *v8,
+                              const double *rope, const void *k8, const void *v8,
                               const float *sk, const float *sv, int n, int32_t *idx,
                               void *kr, void *vr, float *kbias, hipStream_t st);
 

@@ -5,8 +5,8 @@
 // RoPE on K ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
 // Blackwell GPUs", section "GEMM kernel optimization", where it is fused into
 // the epilogue that produces Q and K): here it is fused into this pass's
-// single load of K, with the same fp32 pair rotation and bf16 rounding as the
-// Q load of the attention kernel.  Every workgroup of the attention kernel
+// single load of K, with the same fp64 rotation and single bf16 rounding as
+// the Q load of the attention kernel.  Every workgroup of the attention kernel
 // reads each K tile once, so rotating there would redo the rotation (and its
 // table reads) once per query block.
 //
@@ -33,7 +33,7 @@ constexpr int PK = 64;        // keys per workgroup
 
 struct PrepArgs {
   const bf16 *k, *v;
-  const float2 *rope;
+  const double2 *rope;  // RoPE table [S][D/2] (cos, sin) in fp64
   const float *kn;     // K RMS-norm weights [D], NULL = none
   float eps;
   bf16 *kr, *vt;
@@ -74,25 +74,21 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
                                                  (int64_t)key * a.v_ss + 8 * c);
       }
     }
-    float2 cs[4];
+    double2 cs[4];
     const bool rot = ROPE && key < a.S;
     if (rot) {
-      const float4 *t = reinterpret_cast<const float4 *>(a.rope + (int64_t)key * (D / 2) + 4 * c);
-      const float4 t01 = t[0], t23 = t[1];
-      cs[0] = make_float2(t01.x, t01.y);
-      cs[1] = make_float2(t01.z, t01.w);
-      cs[2] = make_float2(t23.x, t23.y);
-      cs[3] = make_float2(t23.z, t23.w);
+      const double2 *t = a.rope + (int64_t)key * (D / 2) + 4 * c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cs[e] = t[e];
     }
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
       u32x4 x = kw[g];
       if (a.kn) {
-        const float ss = chunk_sum_lanes<CH>(chunk_sumsq(x));
-        x = norm_rope_chunk_bf16(x, rms_scale<D>(ss, a.eps), a.kn + 8 * c, rot ? cs : nullptr);
+        const double ss = chunk_sum_lanes_f64<CH>(chunk_sumsq_f64(x));
+        x = prologue_chunk_bf16(x, rms_scale_f64<D>(ss, a.eps), a.kn + 8 * c, rot ? cs : nullptr);
       } else if (rot) {
-        x = u32x4{rope_pair_bf16(x.x, cs[0]), rope_pair_bf16(x.y, cs[1]),
-                  rope_pair_bf16(x.z, cs[2]), rope_pair_bf16(x.w, cs[3])};
+        x = prologue_chunk_bf16(x, 0.0, nullptr, cs);
       }
       *reinterpret_cast<u32x4 *>(a.kr + ((bh0 + g) * a.S_pad + key) * D + 8 * c) = x;
       *reinterpret_cast<u32x4 *>(vs + (g * PK + r) * VSTR + 8 * c) = vw[g];
@@ -153,11 +149,11 @@ int64_t prep_kv_bytes(const AttnLayout &L) {
 }
 
 hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v,
-                               const float *rope, void *kv, hipStream_t st) {
+                               const double *rope, void *kv, hipStream_t st) {
   PrepArgs a;
   a.k = static_cast<const bf16 *>(k);
   a.v = static_cast<const bf16 *>(v);
-  a.rope = reinterpret_cast<const float2 *>(rope);
+  a.rope = reinterpret_cast<const double2 *>(rope);
   a.kn = L.k_norm;
   a.eps = L.norm_eps;
   a.kr = static_cast<bf16 *>(kv);

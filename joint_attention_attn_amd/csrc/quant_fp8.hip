@@ -13,10 +13,16 @@
 // D elements is handled by D/8 lanes with one 16-byte load each; its amax is
 // reduced with lane exchanges inside that lane group.  A lane handles RPT
 // head vectors and issues all their loads first, so that enough bytes are in
-// flight to cover the HBM latency.  The rotation uses the
-// fixed fp32 operation order of rope_pair_f32 and x / scale is IEEE-rounded
-// (for a power of two, the exact product x * 2^-k), so the codes are a fixed
-// function of the inputs.
+// flight to cover the HBM latency.
+//
+// Precision: Q and K go through the fp64 prologue (RMS norm, RoPE) of
+// common.hpp; amax and the power-of-two scale come from those fp64 values,
+// and the code is the e4m3 rounding of x * 2^-k taken once (round to odd to
+// fp32, then to nearest even).  V's scale is the IEEE fp32 quotient
+// amax / 448, and its code the e4m3 rounding of the exact quotient x / scale:
+// the fp32 division is correctly rounded, an fma gives its exact remainder,
+// and that decides the round-to-odd fp32 value that the e4m3 conversion
+// rounds once more (correctly, with 24 against 4 significant bits).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -29,7 +35,7 @@ struct QuantArgs {
   int64_t sb[3], ss[3], sh[3];
   uint8_t *x8[3];
   float *scale[3];
-  const float2 *rope;
+  const double2 *rope;    // RoPE table [S][D/2] (cos, sin) in fp64
   const float *norm[2];   // Q / K RMS-norm weights [D], NULL = none
   float eps;
   int S, H;
@@ -37,6 +43,31 @@ struct QuantArgs {
 };
 
 constexpr int RPT = 2;        // head vectors per lane
+
+// Four fp32 values (each already the single rounding of the value to code,
+// to odd) -> packed e4m3, saturated at +-448.
+__device__ __forceinline__ uint32_t pack_e4m3x4(const float (&y)[4]) {
+  float c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c[j] = fminf(fmaxf(y[j], -448.f), 448.f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+}
+
+// x / scale rounded to odd in fp32, from the correctly rounded quotient and
+// its exact remainder (x, scale > 0 finite fp32).
+__device__ __forceinline__ float div_round_odd(float x, float scale) {
+  const float q = x / scale;
+  const float t = __builtin_fmaf(q, scale, -x);        // q scale - x, exact
+  uint32_t u = __float_as_uint(q);
+  if (t != 0.f && (u & 1u) == 0) {
+    // the exact quotient lies beyond q (larger magnitude) when q scale falls
+    // short of x in magnitude
+    const bool up = x > 0.f ? t < 0.f : t > 0.f;
+    u += up ? 1 : -1;
+  }
+  return __uint_as_float(u);
+}
 
 template <int D>
 __device__ __forceinline__ void quant_row(const QuantArgs &a, int t, int64_t row, int sub,
@@ -47,61 +78,59 @@ __device__ __forceinline__ void quant_row(const QuantArgs &a, int t, int64_t row
   const int h = (int)(rr % a.H);
   const int64_t s = (rr / a.H) % a.S;
   const int64_t b = rr / ((int64_t)a.H * a.S);
-  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-  float r[8];
-  const float *g = t < 2 ? a.norm[t] : nullptr;
-  if (g) {
-    // RMS norm (the LPR lanes of a vector hold its chunks in order), then RoPE
-    const float rn = rms_scale<D>(chunk_sum_lanes<LPR>(chunk_sumsq(w)), a.eps);
-    norm_chunk(w, rn, g + sub * 8, r);
-    if (a.rope) {
-      const float2 *cs = a.rope + s * (D / 2) + sub * 4;
+  float scale = 1.f;
+  uint32_t packed[2];
+  if (t < 2) {
+    // Q, K: the fp64 prologue, amax and a power-of-two scale
+    const float *g = a.norm[t];
+    double rn = 0.0;
+    if (g) rn = rms_scale_f64<D>(chunk_sum_lanes_f64<LPR>(chunk_sumsq_f64(w)), a.eps);
+    double y[8];
+    prologue_chunk_f64(w, rn, g ? g + sub * 8 : nullptr,
+                       a.rope ? a.rope + s * (D / 2) + sub * 4 : nullptr, y);
+    double amax = 0.0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = r[2 * e], x1 = r[2 * e + 1];
-        rope_pair_f32(x0, x1, cs[e], r[2 * e], r[2 * e + 1]);
-      }
+    for (int e = 0; e < 8; ++e) amax = __builtin_fmax(amax, __builtin_fabs(y[e]));
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) amax = __builtin_fmax(amax, __shfl_xor(amax, off));
+    // amax = m 2^E with m in [1, 2) and 448 = 1.75 2^8: s = 2^(E-8), or
+    // 2^(E-7) when m > 1.75; at least 2^-126
+    int k = 0;
+    if (amax > 0.0) {
+      const uint64_t ab = __double_as_longlong(amax);
+      const int e2 = (int)(ab >> 52) - 1023;
+      k = max(e2 - 8 + ((ab & 0xfffffffffffffull) > 0xc000000000000ull ? 1 : 0), -126);
+      scale = __uint_as_float((uint32_t)(127 + k) << 23);
     }
-  } else if (a.rope && t < 2) {
-    const float2 *cs = a.rope + s * (D / 2) + sub * 4;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      rope_pair_f32(bf16_lo(ww[e]), bf16_hi(ww[e]), cs[e], r[2 * e], r[2 * e + 1]);
+    for (int e = 0; e < 2; ++e) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = f32_round_odd(__builtin_ldexp(y[4 * e + j], -k));
+      packed[e] = pack_e4m3x4(v);
+    }
   } else {
+    // V: exact in fp32; scale = amax / 448
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    float x[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      r[2 * e] = bf16_lo(ww[e]);
-      r[2 * e + 1] = bf16_hi(ww[e]);
+      x[2 * e] = bf16_lo(ww[e]);
+      x[2 * e + 1] = bf16_hi(ww[e]);
     }
-  }
-  float amax = 0.f;
+    float amax = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(r[e]));
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
-  for (int off = 1; off < LPR; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  float scale = 1.f, inv = 1.f;
-  if (t < 2) {
-    // amax = m 2^E with m in [1, 2) and 448 = 1.75 2^8: s = 2^(E-8), or
-    // 2^(E-7) when m > 1.75; at least 2^-126 (subnormal amax included)
-    const uint32_t ab = __float_as_uint(amax);
-    const int k = max((int)(ab >> 23) - 135 + ((ab & 0x7fffffu) > 0x600000u ? 1 : 0), -126);
-    if (amax > 0.f) {
-      scale = __uint_as_float((uint32_t)(127 + k) << 23);
-      inv = __uint_as_float((uint32_t)(127 - k) << 23);
+    for (int off = 1; off < LPR; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (amax > 0.f) scale = amax / 448.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = div_round_odd(x[4 * e + j], scale);
+      packed[e] = pack_e4m3x4(v);
     }
-  } else if (amax > 0.f) {
-    scale = amax / 448.f;
-  }
-
-  uint32_t packed[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    float y[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      y[j] = fminf(fmaxf(t < 2 ? r[4 * e + j] * inv : r[4 * e + j] / scale, -448.f), 448.f);
-    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    packed[e] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
   }
   if (live) {
     *reinterpret_cast<u32x2 *>(a.x8[t] + row * D + sub * 8) = u32x2{packed[0], packed[1]};
@@ -136,7 +165,7 @@ __global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
 
 hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
                                  const void *k, const void *v,
-                                 const float *rope, void *q8, void *k8,
+                                 const double *rope, void *q8, void *k8,
                                  void *v8, float *sq, float *sk, float *sv,
                                  hipStream_t st) {
   QuantArgs a;
@@ -152,7 +181,7 @@ hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
   a.scale[0] = sq;
   a.scale[1] = sk;
   a.scale[2] = sv;
-  a.rope = reinterpret_cast<const float2 *>(rope);
+  a.rope = reinterpret_cast<const double2 *>(rope);
   a.norm[0] = L.q_norm;
   a.norm[1] = L.k_norm;
   a.eps = L.norm_eps;

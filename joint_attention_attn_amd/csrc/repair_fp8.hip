@@ -5,13 +5,16 @@
 // correction ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
 // Blackwell GPUs", section "Quantized and sparse attention",
 // vc_repair_budget).  Here, per (batch, head):
-//   e[token] = max_d |k - k^| + max_d |v - v^|   (fp32; k the rotated key
-//              that was quantized, k^ = fl(value(code) * scale))
+//   e[token] = max_d |k - k^| + max_d |v - v^|   (k the rotated key that was
+//              quantized, from the fp64 prologue; k^ = value(code) * scale,
+//              exact in fp64; the differences, maxima and sum in fp64, the
+//              sum then rounded to fp32, the precision in which tokens are
+//              ranked)
 //   the n tokens with the largest e are repaired (ties to the lower index);
 //   their keys and values then enter the FP8 forward at bf16-path precision:
 //   the K/V preparation masks them out of the FP8 tiles (kbias = -inf in their
 //   score's initial value) and the forward attends them once more from kr / vr
-//   (the bf16-rounded rotated key, the bf16 value).
+//   (the rotated key rounded once to bf16, the bf16 value).
 //
 // Two kernels:
 //   repair_err_kernel     one lane group per (b, token, head) vector, as in the
@@ -33,7 +36,7 @@ constexpr int SEL_NT = 1024;   // threads of the selection workgroup
 struct ErrArgs {
   const bf16 *k, *v;
   int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
-  const float2 *rope;
+  const double2 *rope;          // RoPE table [S][D/2] (cos, sin) in fp64
   const float *kn;              // K RMS-norm weights [D], NULL = none
   float eps;
   const uint8_t *k8, *v8;
@@ -43,9 +46,10 @@ struct ErrArgs {
   int64_t rows;                 // B * S * H
 };
 
-// Max over the 8 elements of a chunk of |x - value(code) * scale|.
-__device__ __forceinline__ float chunk_error(const float (&x)[8], u32x2 codes, float scale) {
-  float e = 0.f;
+// Max over the 8 elements of a chunk of |x - value(code) * scale| in fp64
+// (value(code) * scale is exact there).
+__device__ __forceinline__ double chunk_error(const double (&x)[8], u32x2 codes, float scale) {
+  double e = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t w = i < 4 ? codes.x : codes.y;
@@ -56,7 +60,7 @@ __device__ __forceinline__ float chunk_error(const float (&x)[8], u32x2 codes, f
       case 2: dq = __builtin_amdgcn_cvt_f32_fp8((int)w, 2); break;
       default: dq = __builtin_amdgcn_cvt_f32_fp8((int)w, 3); break;
     }
-    e = fmaxf(e, fabsf(x[i] - dq * scale));
+    e = __builtin_fmax(e, __builtin_fabs(x[i] - (double)dq * (double)scale));
   }
   return e;
 }
@@ -74,50 +78,25 @@ __global__ __launch_bounds__(256) void repair_err_kernel(ErrArgs a) {
   const int64_t b = rr / ((int64_t)a.H * a.S);
   const int64_t sidx = (b * a.H + h) * a.S + s;
 
-  float x[8];
+  // the key as the quantizer saw it: normalized, then rotated (fp64)
+  double x[8];
   const u32x4 kw = *reinterpret_cast<const u32x4 *>(a.k + b * a.k_sb + s * a.k_ss + h * a.k_sh + sub * 8);
-  const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-  if (a.kn) {
-    // the key as the quantizer saw it: normalized, then rotated
-    const float rn = rms_scale<D>(chunk_sum_lanes<LPR>(chunk_sumsq(kw)), a.eps);
-    norm_chunk(kw, rn, a.kn + sub * 8, x);
-    if (a.rope) {
-      const float2 *cs = a.rope + s * (D / 2) + sub * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = x[2 * e], x1 = x[2 * e + 1];
-        rope_pair_f32(x0, x1, cs[e], x[2 * e], x[2 * e + 1]);
-      }
-    }
-  } else if (a.rope) {
-    const float2 *cs = a.rope + s * (D / 2) + sub * 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      rope_pair_f32(bf16_lo(kk[e]), bf16_hi(kk[e]), cs[e], x[2 * e], x[2 * e + 1]);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_lo(kk[e]);
-      x[2 * e + 1] = bf16_hi(kk[e]);
-    }
-  }
+  double rn = 0.0;
+  if (a.kn) rn = rms_scale_f64<D>(chunk_sum_lanes_f64<LPR>(chunk_sumsq_f64(kw)), a.eps);
+  prologue_chunk_f64(kw, rn, a.kn ? a.kn + sub * 8 : nullptr,
+                     a.rope ? a.rope + s * (D / 2) + sub * 4 : nullptr, x);
   const int64_t c8 = row * D + sub * 8;   // contiguous [B, S, H, D] codes
-  float ek = chunk_error(x, *reinterpret_cast<const u32x2 *>(a.k8 + (live ? c8 : 0)), a.sk[sidx]);
+  double ek = chunk_error(x, *reinterpret_cast<const u32x2 *>(a.k8 + (live ? c8 : 0)), a.sk[sidx]);
 
   const u32x4 vw = *reinterpret_cast<const u32x4 *>(a.v + b * a.v_sb + s * a.v_ss + h * a.v_sh + sub * 8);
-  const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = bf16_lo(vv[e]);
-    x[2 * e + 1] = bf16_hi(vv[e]);
-  }
-  float ev = chunk_error(x, *reinterpret_cast<const u32x2 *>(a.v8 + (live ? c8 : 0)), a.sv[sidx]);
+  prologue_chunk_f64(vw, 0.0, nullptr, nullptr, x);
+  double ev = chunk_error(x, *reinterpret_cast<const u32x2 *>(a.v8 + (live ? c8 : 0)), a.sv[sidx]);
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) {
-    ek = fmaxf(ek, __shfl_xor(ek, off));
-    ev = fmaxf(ev, __shfl_xor(ev, off));
+    ek = __builtin_fmax(ek, __shfl_xor(ek, off));
+    ev = __builtin_fmax(ev, __shfl_xor(ev, off));
   }
-  if (live && sub == 0) a.err[sidx] = ek + ev;
+  if (live && sub == 0) a.err[sidx] = (float)(ek + ev);
 }
 
 struct SelArgs {
@@ -125,7 +104,7 @@ struct SelArgs {
   int32_t *idx;                 // [B][H][n]
   const bf16 *k, *v;
   int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
-  const float2 *rope;
+  const double2 *rope;          // RoPE table [S][D/2] (cos, sin) in fp64
   const float *kn;              // K RMS-norm weights [D], NULL = none
   float eps;
   bf16 *kr, *vr;                // [B][H][n_pad][D]
@@ -218,16 +197,15 @@ __global__ __launch_bounds__(SEL_NT) void repair_select_kernel(SelArgs a) {
     if (i < n) {
       const int64_t s = a.idx[bh * n + i];
       kw = *reinterpret_cast<const u32x4 *>(a.k + b * a.k_sb + s * a.k_ss + h * a.k_sh + c * 8);
-      if (a.rope && !a.kn) kw = rope_chunk_bf16(kw, a.rope + s * (D / 2) + c * 4);
       vw = *reinterpret_cast<const u32x4 *>(a.v + b * a.v_sb + s * a.v_ss + h * a.v_sh + c * 8);
     }
-    if (a.kn) {
-      // the CH chunks of a key are CH consecutive lanes (SEL_NT % CH == 0)
-      const int64_t s = i < n ? a.idx[bh * n + i] : 0;
-      const float rn = rms_scale<D>(chunk_sum_lanes<CH>(chunk_sumsq(kw)), a.eps);
-      kw = norm_rope_chunk_bf16(kw, rn, a.kn + c * 8,
-                                a.rope && i < n ? a.rope + s * (D / 2) + c * 4 : nullptr);
-    }
+    // the CH chunks of a key are CH consecutive lanes (SEL_NT % CH == 0)
+    const int64_t s = i < n ? a.idx[bh * n + i] : 0;
+    double rn = 0.0;
+    if (a.kn) rn = rms_scale_f64<D>(chunk_sum_lanes_f64<CH>(chunk_sumsq_f64(kw)), a.eps);
+    if (i < n && (a.kn || a.rope))
+      kw = prologue_chunk_bf16(kw, rn, a.kn ? a.kn + c * 8 : nullptr,
+                               a.rope ? a.rope + s * (D / 2) + c * 4 : nullptr);
     const int64_t o = (bh * a.n_pad + i) * D + c * 8;
     *reinterpret_cast<u32x4 *>(a.kr + o) = kw;
     *reinterpret_cast<u32x4 *>(a.vr + o) = vw;
@@ -241,7 +219,7 @@ int repair_pad(int n) { return (n + 31) / 32 * 32; }
 int repair_max_seq() { return 160 * 1024 / 4 - 1024; }
 
 hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
-                              const float *rope, const void *k8, const void *v8,
+                              const double *rope, const void *k8, const void *v8,
                               const float *sk, const float *sv, int n, int32_t *idx,
                               void *kr, void *vr, float *kbias, hipStream_t st) {
   ErrArgs e;
@@ -249,7 +227,7 @@ hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
   e.v = static_cast<const bf16 *>(v);
   e.k_sb = L.k_sb; e.k_ss = L.k_ss; e.k_sh = L.k_sh;
   e.v_sb = L.v_sb; e.v_ss = L.v_ss; e.v_sh = L.v_sh;
-  e.rope = reinterpret_cast<const float2 *>(rope);
+  e.rope = reinterpret_cast<const double2 *>(rope);
   e.kn = L.k_norm;
   e.eps = L.norm_eps;
   e.k8 = static_cast<const uint8_t *>(k8);

@@ -46,9 +46,23 @@ __global__ __launch_bounds__(256) void merge_split_kernel(MergeArgs m) {
   if (qi >= m.S) return;
   const float c = m.scale_log2;
   const int64_t unit0 = (int64_t)sidx * m.parts;
+  bf16 *orow = m.o + b * m.o_sb + (int64_t)qi * m.o_ss + h * m.o_sh + ch * 8;
+  float *lse = m.lse ? m.lse + ((int64_t)b * m.H + h) * m.S + qi : nullptr;
   float mx = -INFINITY;
-  for (int j = 0; j < m.parts; ++j)
-    mx = fmaxf(mx, m.ws.ml[((unit0 + j) * m.block_rows + row) * 2]);
+  bool poisoned = false;
+  for (int j = 0; j < m.parts; ++j) {
+    const float mj = m.ws.ml[((unit0 + j) * m.block_rows + row) * 2];
+    poisoned = poisoned || mj != mj;
+    mx = fmaxf(mx, mj);
+  }
+  if (poisoned) {
+    // a part that met an invalid input (the FP8 forward's NaN poisoning)
+    // writes a NaN row maximum: the merged row is NaN too, not empty
+    const uint32_t qnan = 0x7fc07fc0u;   // two bf16 quiet NaNs
+    *reinterpret_cast<u32x4 *>(orow) = u32x4{qnan, qnan, qnan, qnan};
+    if (lse && ch == 0) *lse = __builtin_nanf("");
+    return;
+  }
   float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // a row that no part saw a key for (block-sparse rows that keep no key
   // block) has every part at max -inf and sum 0: O = 0, LSE = -inf
@@ -69,9 +83,8 @@ __global__ __launch_bounds__(256) void merge_split_kernel(MergeArgs m) {
   out.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
   out.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
   out.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  *reinterpret_cast<u32x4 *>(m.o + b * m.o_sb + (int64_t)qi * m.o_ss + h * m.o_sh + ch * 8) = out;
-  if (m.lse && ch == 0)
-    m.lse[((int64_t)b * m.H + h) * m.S + qi] = empty ? -INFINITY : (mx * c + __log2f(l)) * kLn2;
+  *reinterpret_cast<u32x4 *>(orow) = out;
+  if (lse && ch == 0) *lse = empty ? -INFINITY : (mx * c + __log2f(l)) * kLn2;
 }
 
 }  // namespace

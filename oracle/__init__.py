@@ -24,28 +24,27 @@ FLUX 3 Image Klein on NVIDIA Blackwell GPUs"):
   optimization": query/key normalization in the QKV epilogue).
 
 The pages state none of the arithmetic; the readings taken where they are
-silent (2D-axial frequencies, pair convention, bf16 rounding point of the
+silent (2D-axial frequencies, pair convention, the bf16 rounding point of the
 rotated Q/K, FP8 scale granularity, e4m3 format) are documented at each
-function.  The arithmetic is fp64 throughout, except where a floating-point
-value decides a rounded code (the bf16 of a rotated Q/K element, an e4m3
-code): there the value is computed in fp32 with the kernels' fixed operation
-order (`rotate_fp32`), so both sides take the same decision.  Every function
-here is pinned by tests in `tests/test_oracle_*.py` against closed forms,
-brute force, exact rational arithmetic and library routines.
+function.  The arithmetic is the plain definition in fp64 throughout; where
+the method stores a value in a narrower format (the rotated Q/K in bf16, the
+e4m3 codes, the fp32 V scales) the fp64 value is rounded once to that format.
+Every function here is pinned by tests in `tests/test_oracle_*.py` against
+closed forms, brute force, exact rational arithmetic and library routines.
 """
-from .rope import rope_angles, apply_rope, rope_table_fp32, rotate_fp32, fma32
-from .norm import (NORM_EPS, sum_squares_fp32, rms_norm_fp32, rms_norm, prologue_fp32)
-from .attention import (attention, joint_attention, brute_force_attention,
+from .rope import rope_angles, apply_rope
+from .bf16 import bf16_round
+from .norm import NORM_EPS, rms_norm, prologue
+from .attention import (attention, rotated_qk, joint_attention, brute_force_attention,
                         block_sparse_attention, QUERY_BLOCK, KEY_BLOCK)
 from .fp8 import (e4m3_round, e4m3_encode, e4m3_decode, pow2_scale, quant_rope_fp8,
                   dequantize, fp8_attention, repair_count, quant_error, repair_errors,
                   repair_select, repair_values, fp8_repaired_attention)
 
 __all__ = [
-    "rope_angles", "apply_rope", "rope_table_fp32", "rotate_fp32", "fma32",
-    "NORM_EPS", "sum_squares_fp32", "rms_norm_fp32", "rms_norm", "prologue_fp32",
-    "attention", "joint_attention", "brute_force_attention", "block_sparse_attention",
-    "QUERY_BLOCK", "KEY_BLOCK",
+    "rope_angles", "apply_rope", "bf16_round", "NORM_EPS", "rms_norm", "prologue",
+    "attention", "rotated_qk", "joint_attention", "brute_force_attention",
+    "block_sparse_attention", "QUERY_BLOCK", "KEY_BLOCK",
     "e4m3_round", "e4m3_encode", "e4m3_decode", "pow2_scale", "quant_rope_fp8",
     "dequantize", "fp8_attention", "repair_count", "quant_error", "repair_errors",
     "repair_select", "repair_values", "fp8_repaired_attention",

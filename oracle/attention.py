@@ -20,10 +20,8 @@ import math
 import numpy as np
 import torch
 
-import numpy as _np
-
-from .rope import apply_rope, rope_table_fp32, rotate_fp32
-from .norm import prologue_fp32
+from .bf16 import bf16_round
+from .norm import prologue
 
 _CHUNK = 2048
 
@@ -62,36 +60,34 @@ def attention(q, k, v, scale: float | None = None, rows=None):
     return o, lse
 
 
+def rotated_qk(x, pos=None, theta: float = 10000.0, norm_g=None, eps: float = 1e-6,
+               round_bf16: bool = True) -> torch.Tensor:
+    """Q or K as attention consumes it: the epilogue's RMSNorm (weight norm_g,
+    if given) and RoPE (if pos is given) in fp64, then, with round_bf16,
+    ONE rounding to bf16 (round to nearest even), because the pages place
+    both in the QKV projection's epilogue, whose output is stored in the
+    model's working precision before attention reads it.  With neither norm
+    nor RoPE the bf16 input is returned unchanged.  Returns fp64."""
+    x = torch.as_tensor(x)
+    if norm_g is None and pos is None:
+        return x.to(torch.float64)
+    y = prologue(x, pos, theta, norm_g, eps)
+    return bf16_round(y) if round_bf16 else y
+
+
 def joint_attention(q, k, v, pos=None, theta: float = 10000.0,
                     scale: float | None = None, round_rotated: bool = True,
                     rows=None, norm=None):
     """The bf16 hot path's reference: RoPE on Q and K, then attention.
 
-    Reading of where the rotated Q/K are rounded: the pages place RoPE in the
-    epilogue of the QKV projection, so attention consumes Q and K that were
-    rotated and then stored in the model's working precision.  With
-    round_rotated=True (the default) Q and K are rotated in fp32
-    (`rotate_fp32`, the kernels' operation order, since the result decides a
-    bf16 code) and rounded once to bf16 (round to nearest even) before
-    Q K^T; attention itself is fp64.  round_rotated=False rotates in fp64
-    and keeps the result unrounded, for information.  pos=None: no RoPE.
-    norm=(g_q, g_k, eps): Q and K are first RMS-normalized (`oracle.norm`),
-    in fp32 and without a rounding of their own, then rotated and rounded.
+    Q and K are normalized (norm=(g_q, g_k, eps), optional) and rotated
+    (pos, optional) in fp64 and rounded once to bf16 (`rotated_qk`); with
+    round_rotated=False they stay unrounded fp64, for information.
+    Attention itself is fp64.  pos=None: no RoPE.
     """
-    q = torch.as_tensor(q)
-    k = torch.as_tensor(k)
-    if norm is not None:
-        g_q, g_k, eps = norm
-        q = torch.from_numpy(prologue_fp32(q, pos, theta, g_q, eps)).to(torch.bfloat16)
-        k = torch.from_numpy(prologue_fp32(k, pos, theta, g_k, eps)).to(torch.bfloat16)
-    elif pos is not None:
-        if round_rotated:
-            table = rope_table_fp32(pos, q.shape[-1], theta)
-            q = torch.from_numpy(rotate_fp32(q.to(torch.float32).numpy(), table)).to(torch.bfloat16)
-            k = torch.from_numpy(rotate_fp32(k.to(torch.float32).numpy(), table)).to(torch.bfloat16)
-        else:
-            q = apply_rope(q, pos, theta)
-            k = apply_rope(k, pos, theta)
+    g_q, g_k, eps = norm if norm is not None else (None, None, 1e-6)
+    q = rotated_qk(q, pos, theta, g_q, eps, round_rotated)
+    k = rotated_qk(k, pos, theta, g_k, eps, round_rotated)
     return attention(q, k, v, scale=scale, rows=rows)
 
 
@@ -141,18 +137,13 @@ def block_sparse_attention(q, k, v, mask, pos=None, theta: float = 10000.0,
     mask: [B, H, ceil(S / q_block), ceil(S / k_block)], nonzero = computed.
     Query i attends key j iff mask[b, h, i // q_block, j // k_block] != 0;
     the softmax runs over the attended keys only.  A query row with no
-    attended key gets O = 0 and LSE = -inf.  RoPE and the bf16 rounding of the
-    rotated Q/K are those of `joint_attention`; attention itself is fp64.
+    attended key gets O = 0 and LSE = -inf.  The Q/K prologue and its bf16
+    rounding are those of `joint_attention`; attention itself is fp64.
     Returns (O [B, R, H, D] fp64, LSE [B, H, R] fp64).
     """
-    q = torch.as_tensor(q)
-    k = torch.as_tensor(k)
-    if norm is not None or pos is not None:
-        g_q, g_k, eps = norm if norm is not None else (None, None, 0.0)
-        q = torch.from_numpy(prologue_fp32(q, pos, theta, g_q, eps)).to(torch.bfloat16)
-        k = torch.from_numpy(prologue_fp32(k, pos, theta, g_k, eps)).to(torch.bfloat16)
-    q = q.to(torch.float64)
-    k = k.to(torch.float64)
+    g_q, g_k, eps = norm if norm is not None else (None, None, 1e-6)
+    q = rotated_qk(q, pos, theta, g_q, eps)
+    k = rotated_qk(k, pos, theta, g_k, eps)
     v = torch.as_tensor(v).to(torch.float64)
     mask = torch.as_tensor(np.asarray(mask)) != 0
     b, s, h, d = q.shape

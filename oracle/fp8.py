@@ -18,11 +18,10 @@ Up Image Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", section
   exactly to the Q K^T product, and x / s is exact.  e4m3 is a floating-point
   format, so its relative precision does not depend on where amax lands in
   (224, 448];
-* precision of the decision: the quantizer rounds values that were computed
-  in fp32 with a fixed operation order (`oracle.rope.rotate_fp32`, then
-  fl(x / scale)), so the codes it produces are a deterministic function of
-  the inputs that any fp32 implementation with the same order reproduces bit
-  for bit.
+* precision: the rotated (and normalized) Q/K come from the fp64 prologue
+  of `oracle.norm.prologue` with no intermediate rounding; amax is taken in
+  fp64; the V scale is stored as fp32 (fl32(amax / 448)); the code is the
+  e4m3 rounding of x / scale evaluated in fp64.
 
 The attention reference for this path is plain fp64 attention on the
 dequantized tensors (code value x scale), with no further RoPE.
@@ -33,8 +32,8 @@ import numpy as np
 import torch
 
 from .attention import attention
-from .rope import rope_table_fp32, rotate_fp32
-from .norm import prologue_fp32
+from .bf16 import bf16_round
+from .norm import prologue
 
 E4M3_MAX = 448.0
 
@@ -86,46 +85,51 @@ def e4m3_decode(code) -> np.ndarray:
 def pow2_scale(amax) -> np.ndarray:
     """Smallest power of two s with amax <= 448 s, as fp32 (1 when amax = 0,
     at least 2^-126).  With amax = f 2^x, f in [0.5, 1): 448 = 0.875 2^9, so
-    s = 2^(x - 9) when f <= 0.875 and 2^(x - 8) otherwise."""
-    amax = np.asarray(amax, np.float32)
+    s = 2^(x - 9) when f <= 0.875 and 2^(x - 8) otherwise.  amax may be fp32
+    or fp64."""
+    amax = np.asarray(amax)
     f, x = np.frexp(amax.astype(np.float64))
     k = np.maximum(x - 9 + (f > 0.875), -126)
     s = np.ldexp(np.float64(1.0), k).astype(np.float32)
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 
-def _quantize_rows(r: np.ndarray, pow2: bool = False):
-    """Per-(b, s, h) e4m3 quantization of fp32 r [B, S, H, D].
+def _quantize_rows(r, pow2: bool = False):
+    """Per-(b, s, h) e4m3 quantization of r [B, S, H, D] (fp64 values).
 
-    amax = max |r| over D; scale = fl32(amax / 448), or pow2_scale(amax) when
-    pow2 (1 when amax = 0 either way); code = e4m3(clamp(fl32(r / scale),
-    -448, 448)) (the division is exact for a power of two).  Returns (uint8
-    codes [B, S, H, D], fp32 scales [B, H, S]).
+    amax = max |r| over D; scale = pow2_scale(amax) when pow2, else
+    fl32(amax / 448) (the fp32 number that is stored); 1 when amax = 0 either
+    way.  code = e4m3(clamp(r / scale, -448, 448)) with r / scale in fp64.
+    Returns (uint8 codes [B, S, H, D], fp32 scales [B, H, S]).
     """
-    amax = np.max(np.abs(r), axis=-1)                                   # fp32 exact
+    r = np.asarray(r, np.float64)
+    amax = np.max(np.abs(r), axis=-1)
     if pow2:
         scale = pow2_scale(amax)
     else:
-        scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        # V is bf16: amax / 448 = (m / 7) 2^k has a period-3 binary expansion,
+        # so its fp64 value never lands on an fp32 midpoint and the cast is
+        # the correctly rounded fp32 quotient
+        scale = (amax / E4M3_MAX).astype(np.float32)
         scale = np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
-    y = (r / scale[..., None]).astype(np.float32)
-    y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    y = np.clip(r / scale.astype(np.float64)[..., None], -E4M3_MAX, E4M3_MAX)
     codes = e4m3_encode(e4m3_round(y))
     return codes, np.ascontiguousarray(np.transpose(scale, (0, 2, 1)))
 
 
 def quant_rope_fp8(q, k, v, pos, theta: float = 10000.0, norm=None):
-    """RoPE on Q and K (fp32, `rotate_fp32` order), then per-token e4m3 quantization
-    of Q, K (power-of-two scales) and V (amax / 448).  Returns (q8, k8, v8,
-    sq, sk, sv): uint8 codes [B, S, H, D] and fp32 scales [B, H, S].  pos=None skips the rotation;
-    norm=(g_q, g_k, eps) RMS-normalizes Q and K first (`oracle.norm`)."""
-    g_q, g_k, eps = norm if norm is not None else (None, None, 0.0)
-    q = prologue_fp32(q, pos, theta, g_q, eps)
-    k = prologue_fp32(k, pos, theta, g_k, eps)
-    v = torch.as_tensor(v).to(torch.float32).numpy()
-    q8, sq = _quantize_rows(q, pow2=True)
-    k8, sk = _quantize_rows(k, pow2=True)
-    v8, sv = _quantize_rows(v)
+    """RoPE on Q and K (after the optional RMS norm, all in fp64: the
+    epilogue's `prologue`), then per-token e4m3 quantization of Q, K
+    (power-of-two scales) and V (amax / 448).  Returns (q8, k8, v8, sq, sk,
+    sv): uint8 codes [B, S, H, D] and fp32 scales [B, H, S].  pos=None skips
+    the rotation; norm=(g_q, g_k, eps) RMS-normalizes Q and K first."""
+    g_q, g_k, eps = norm if norm is not None else (None, None, 1e-6)
+    q64 = prologue(q, pos, theta, g_q, eps).numpy()
+    k64 = prologue(k, pos, theta, g_k, eps).numpy()
+    v64 = torch.as_tensor(v).to(torch.float64).numpy()
+    q8, sq = _quantize_rows(q64, pow2=True)
+    k8, sk = _quantize_rows(k64, pow2=True)
+    v8, sv = _quantize_rows(v64)
     return q8, k8, v8, sq, sk, sv
 
 
@@ -153,14 +157,13 @@ def fp8_attention(q8, k8, v8, sq, sk, sv, scale=None, rows=None):
 #
 # * a token's error, per (batch, head), is the max-abs quantization error of
 #   its key plus that of its value: e = max_d |k - k^| + max_d |v - v^|, with
-#   k the fp32 rotated key that was quantized, k^ = fl32(code value * scale),
-#   and both maxima and their sum in fp32 (max is order-free, so any fp32
-#   implementation takes the same selection);
+#   k the rotated key that was quantized and k^ = code value * scale (all in
+#   fp64); tokens are ranked by e rounded to fp32;
 # * the ceil(rho * S) tokens with the largest e are repaired, ties to the
 #   lower token index;
 # * repairing a token adds its residual (k - k^, v - v^) back, i.e. the key
 #   and value of that token enter attention at the precision of the bf16 path
-#   (the bf16-rounded rotated key, the bf16 value).  Queries stay FP8: a
+#   (the rotated key rounded once to bf16, the bf16 value).  Queries stay FP8: a
 #   query's error only affects its own row, a key's error every row.
 # ---------------------------------------------------------------------------
 
@@ -170,47 +173,48 @@ def repair_count(budget: float, seq_len: int) -> int:
 
 
 def _bshd_scales(scales) -> np.ndarray:
-    return np.transpose(np.asarray(scales, dtype=np.float32), (0, 2, 1))[..., None]
+    return np.transpose(np.asarray(scales, dtype=np.float64), (0, 2, 1))[..., None]
 
 
-def quant_error(x32, codes, scales) -> np.ndarray:
-    """max over D of |x - fl32(value(code) * scale)|, all in fp32: float32
-    [B, H, S].  x32: the fp32 values that were quantized, [B, S, H, D]."""
-    deq = e4m3_decode(codes).astype(np.float32) * _bshd_scales(scales)   # one fp32 rounding
-    err = np.abs(np.asarray(x32, np.float32) - deq.astype(np.float32)).astype(np.float32)
+def quant_error(x, codes, scales) -> np.ndarray:
+    """max over D of |x - value(code) * scale| in fp64: float64 [B, H, S].
+    x: the values that were quantized, [B, S, H, D]."""
+    deq = e4m3_decode(codes) * _bshd_scales(scales)
+    err = np.abs(np.asarray(x, np.float64) - deq)
     return np.ascontiguousarray(np.transpose(err.max(axis=-1), (0, 2, 1)))
 
 
 def repair_errors(k, v, pos, k8, v8, sk, sv, theta: float = 10000.0, norm=None) -> np.ndarray:
-    """Per-(b, h, token) error e = err(K) + err(V) in fp32, float32 [B, H, S]
-    (K as the quantizer saw it: normalized with norm's g_k if given, rotated)."""
-    k32 = prologue_fp32(k, pos, theta, norm[1] if norm is not None else None,
-                        norm[2] if norm is not None else 0.0)
-    v32 = torch.as_tensor(v).to(torch.float32).numpy()
-    return (quant_error(k32, k8, sk) + quant_error(v32, v8, sv)).astype(np.float32)
+    """Per-(b, h, token) error e = err(K) + err(V) in fp64, rounded to fp32 for
+    the ranking: float32 [B, H, S] (K as the quantizer saw it: normalized
+    with norm's g_k if given, rotated)."""
+    k64 = prologue(k, pos, theta, norm[1] if norm is not None else None,
+                   norm[2] if norm is not None else 1e-6).numpy()
+    v64 = torch.as_tensor(v).to(torch.float64).numpy()
+    return (quant_error(k64, k8, sk) + quant_error(v64, v8, sv)).astype(np.float32)
 
 
 def repair_select(err, n: int) -> np.ndarray:
     """Token indices [B, H, n] (ascending) of the n largest errors of each
     (b, h) row; equal errors are taken in ascending token order."""
-    err = np.asarray(err, np.float32)
+    err = np.asarray(err, np.float64)
     b, h, s = err.shape
     out = np.empty((b, h, n), dtype=np.int32)
     idx = np.arange(s)
     for bi in range(b):
         for hi in range(h):
-            order = np.lexsort((idx, -err[bi, hi].astype(np.float64)))
+            order = np.lexsort((idx, -err[bi, hi]))
             out[bi, hi] = np.sort(order[:n])
     return out
 
 
 def repair_values(k, v, pos, idx, theta: float = 10000.0, norm=None):
-    """Exact key and value of the repaired tokens: the bf16-rounded rotated
-    (and, with norm, normalized) key as on the bf16 path, and the bf16 value,
-    float64 [B, H, n, D]."""
-    k32 = prologue_fp32(k, pos, theta, norm[1] if norm is not None else None,
-                        norm[2] if norm is not None else 0.0)
-    kb = torch.from_numpy(np.ascontiguousarray(k32)).to(torch.bfloat16).to(torch.float64)
+    """Exact key and value of the repaired tokens: the rotated (and, with
+    norm, normalized) key rounded once to bf16 as on the bf16 path, and the
+    bf16 value, float64 [B, H, n, D]."""
+    k64 = prologue(k, pos, theta, norm[1] if norm is not None else None,
+                   norm[2] if norm is not None else 1e-6)
+    kb = bf16_round(k64) if (pos is not None or norm is not None) else k64
     vb = torch.as_tensor(v).to(torch.float64)
     idx = np.asarray(idx)
     b, h, n = idx.shape

@@ -26,8 +26,7 @@ def _rope(pos, d):
 
 def _run(q, k, v, mask, pos, **kw):
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    out = ja.fwd_bf16_block_sparse(qd, kd, vd, mask.to(DEV), _rope(pos, q.shape[-1]),
-                                   return_lse=True, **kw)
+    out = ja.fwd_bf16_block_sparse(qd, kd, vd, mask.to(DEV), pos, return_lse=True, **kw)
     torch.cuda.synchronize()
     return out
 
@@ -81,7 +80,7 @@ def test_all_kept_equals_dense_bit_exact():
     _say("sparse all-ones vs dense t2i_1024")
     out, lse = _run(q, k, v, mask, pos, split=False)
     qd, kd, vd = (t.to(DEV) for t in (q, k, v))
-    dense, dense_lse = ja.fwd_bf16(qd, kd, vd, _rope(pos, w.head_dim), return_lse=True,
+    dense, dense_lse = ja.fwd_bf16(qd, kd, vd, rope=_rope(pos, w.head_dim), return_lse=True,
                                    split=False)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), dense.view(torch.int16))
@@ -123,7 +122,8 @@ def test_split_matches_unsplit():
     pos = synth.positions(w)
     mask = synth.make_block_mask(w, 0.5, seed=9)
     mask[0, 5, 3] = 0
-    if ja.fwd_bf16_workspace_bytes(w.batch, w.seq_len, w.heads, w.head_dim) == 0:
+    if ja.fwd_bf16_workspace_bytes(w.batch, w.seq_len, w.heads, w.head_dim) == \
+            ja.fwd_bf16_workspace_bytes(w.batch, w.seq_len, w.heads, w.head_dim, split=False):
         pytest.skip("no split planned for this shape on this device")
     _say("sparse split vs unsplit t2i_1024")
     a, la = _run(q, k, v, mask, pos, split=True)

@@ -177,9 +177,8 @@ def test_block_sparse_equals_attention_on_the_kept_keys():
     mask[..., 0] = 1                                  # no empty row
     o, l = oracle.block_sparse_attention(q, k, v, mask, pos)
     s = q.shape[1]
-    table = oracle.rope_table_fp32(pos, q.shape[-1])
-    qr = torch.from_numpy(oracle.rotate_fp32(q.float().numpy(), table)).to(torch.bfloat16)
-    kr = torch.from_numpy(oracle.rotate_fp32(k.float().numpy(), table)).to(torch.bfloat16)
+    qr = oracle.bf16_round(oracle.apply_rope(q, pos))
+    kr = oracle.bf16_round(oracle.apply_rope(k, pos))
     for h in range(2):
         for qb in range(nq):
             r0, r1 = qb * oracle.QUERY_BLOCK, min(s, (qb + 1) * oracle.QUERY_BLOCK)

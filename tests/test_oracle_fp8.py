@@ -189,9 +189,8 @@ def test_repaired_attention_limits():
     every = np.broadcast_to(np.arange(s, dtype=np.int32), (b, h, s))
     kr, vr = oracle.repair_values(k, v, pos, every)
     oa, la = oracle.fp8_repaired_attention(*codes, every, kr, vr)
-    # reference keys: the rotated keys of the bf16 path (fp32 rotation, bf16)
-    kx = torch.from_numpy(oracle.rotate_fp32(k.float().numpy(),
-                                             oracle.rope_table_fp32(pos, d))).to(torch.bfloat16)
+    # reference keys: the rotated keys of the bf16 path (rotated, rounded once)
+    kx = oracle.bf16_round(oracle.apply_rope(k, pos))
     ob, lb = oracle.attention(oracle.dequantize(q8, sq), kx, v)
     assert torch.allclose(oa, ob, rtol=0, atol=1e-12) and torch.allclose(la, lb, rtol=0, atol=1e-12)
 

@@ -112,67 +112,3 @@ def test_matches_gptj_rotary_on_each_axis(head_dim):
         expect[..., axis * half:(axis + 1) * half] = gptj.apply_rotary_pos_emb(part, sin, cos)
     got = oracle.apply_rope(x, pos)
     assert torch.allclose(got, expect.to(torch.float64), rtol=0, atol=2e-4)
-
-
-def test_fp32_table_is_rounded_fp64_cos_sin():
-    pos = _pos(11, 9, hi=256)
-    tab = oracle.rope_table_fp32(pos, 128)
-    assert tab.dtype == np.float32 and tab.shape == (11, 64, 2)
-    for i in range(11):
-        for p in (0, 5, 31, 32, 40, 63):
-            axis, k = divmod(p, 32)
-            ang = pos[i, axis] * 10000.0 ** (-4.0 * k / 128)
-            assert tab[i, p, 0] == np.float32(math.cos(ang))
-            assert tab[i, p, 1] == np.float32(math.sin(ang))
-
-
-def _exact_fma32(a, b, c):
-    """fp32 fma by exact rational arithmetic, rounded to nearest even."""
-    from fractions import Fraction
-    import struct
-    exact = Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c))
-    lo = np.float32(float(exact))            # within one fp32 step of exact
-    cands = [np.nextafter(lo, np.float32(-np.inf)), lo, np.nextafter(lo, np.float32(np.inf))]
-    best = min(cands, key=lambda r: (abs(Fraction(float(r)) - exact),
-                                     struct.unpack("<I", struct.pack("<f", r))[0] & 1))
-    return np.float32(best)
-
-
-def test_fma32_random_matches_exact_rounding():
-    rng = np.random.default_rng(0)
-    a = rng.standard_normal(3000).astype(np.float32)
-    b = rng.standard_normal(3000).astype(np.float32)
-    c = (rng.standard_normal(3000) * rng.choice([1e-6, 1.0, 1e6], 3000)).astype(np.float32)
-    got = oracle.fma32(a, b, c)
-    for i in range(0, 3000, 7):
-        assert got[i] == _exact_fma32(a[i], b[i], c[i])
-
-
-def test_fma32_double_rounding_ties():
-    # a*b = 2^-24 * (1 - i^2 2^-46) sits just below half an ulp of c in [1, 2):
-    # the fp64 sum rounds onto the fp32 midpoint, and the exact result must
-    # round down to c even when c's last bit is odd (plain fp64->fp32 rounding
-    # of the sum would go up to the even neighbour).
-    cs, as_, bs = [], [], []
-    for i in range(1, 40):
-        for odd in (0, 1):
-            c = np.float32(1.0 + (2 * i + odd) * 2.0 ** -23)
-            as_.append(np.float32(2.0 ** -24 * (1 + i * 2.0 ** -23)))
-            bs.append(np.float32(1 - i * 2.0 ** -23))
-            cs.append(c)
-    a, b, c = (np.array(x, np.float32) for x in (as_, bs, cs))
-    got = oracle.fma32(a, b, c)
-    naive = (a.astype(np.float64) * b.astype(np.float64) + c.astype(np.float64)).astype(np.float32)
-    for i in range(len(a)):
-        assert got[i] == _exact_fma32(a[i], b[i], c[i]) == c[i]
-    assert np.count_nonzero(naive != got) > 0      # the case the emulation must handle
-
-
-def test_fp32_rotation_close_to_fp64():
-    w_pos = _pos(40, 2, hi=256)
-    x = _rand((1, 40, 3, 128), 21).to(torch.bfloat16).to(torch.float32)
-    tab = oracle.rope_table_fp32(w_pos, 128)
-    r32 = oracle.rotate_fp32(x.numpy(), tab)
-    r64 = oracle.apply_rope(x, w_pos).numpy()
-    assert r32.dtype == np.float32
-    assert np.allclose(r32, r64, rtol=0, atol=4e-6 * np.abs(r64).max())
