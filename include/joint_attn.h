@@ -247,6 +247,23 @@ ja_status joint_attn_fwd_bf16_block_sparse_prepared(const ja_params *p, const vo
                                                     float *lse, void *workspace,
                                                     size_t workspace_bytes, void *stream);
 
+/*
+ * joint_attn_fwd_bf16_prepared_noalloc - joint_attn_fwd_bf16_prepared for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments and
+ * result, without the workspace.  Its scratch (the partial results of the
+ * split of the last round) is a static device array of
+ * JA_NOALLOC_SCRATCH_BYTES that every device the library runs on holds
+ * until the process ends; a shape whose split needs more gets
+ * JA_ERR_UNSUPPORTED (JA_FLAG_NO_SPLIT needs none).  All calls on one device
+ * share that array, so two calls that overlap on one device race.  The call
+ * allocates nothing.
+ */
+#define JA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ja_status joint_attn_fwd_bf16_prepared_noalloc(const ja_params *p, const void *q,
+                                               const void *kv, size_t kv_bytes, void *o,
+                                               float *lse, void *stream);
+
 /* ======================================================================
  * FP8 path
  * ====================================================================== */

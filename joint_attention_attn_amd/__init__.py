@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "JointAttnError", "library_path", "load", "Params", "rope_table_2d",
     "fwd_bf16", "fwd_bf16_block_sparse", "prep_kv_bf16", "fwd_bf16_prepared",
-    "fwd_bf16_block_sparse_prepared", "fwd_bf16_workspace_bytes",
+    "fwd_bf16_block_sparse_prepared", "fwd_bf16_workspace_bytes", "fwd_bf16_prepared_noalloc",
     "quant_rope_fp8", "fwd_fp8", "prep_kv_fp8", "fwd_fp8_prepared",
     "Fp8Repair", "repair_count", "fp8_repair_plan",
     "SPARSE_QUERY_BLOCK", "SPARSE_KEY_BLOCK", "block_mask_shape",
@@ -77,6 +77,7 @@ _SIGNATURES = {
     "joint_attn_fwd_bf16_prepared": [_pp, _vp, _vp, _sz, _vp, _vp, _vp, _sz, _vp],
     "joint_attn_fwd_bf16_block_sparse_prepared": [_pp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _sz,
                                                   _vp],
+    "joint_attn_fwd_bf16_prepared_noalloc": [_pp, _vp, _vp, _sz, _vp, _vp, _vp],
     "joint_attn_quant_rope_fp8_workspace_bytes": [_pp],
     "joint_attn_quant_rope_fp8": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                   _vp],
@@ -364,6 +365,24 @@ def fwd_bf16_prepared(q, kv, pos=None, theta: float = 10000.0, rope=None,
     pos / rope): joint_attn_fwd_bf16_prepared."""
     return _prepared_bf16("joint_attn_fwd_bf16_prepared", q, kv, None, pos, theta, rope,
                           softmax_scale, out, return_lse, split, q_norm, norm_eps)
+
+
+def fwd_bf16_prepared_noalloc(q, kv, pos=None, theta: float = 10000.0, rope=None,
+                              softmax_scale: float = 0.0, out=None, return_lse: bool = False,
+                              split: bool = True, q_norm=None, norm_eps: float = 0.0):
+    """fwd_bf16_prepared with the library's static scratch instead of a
+    workspace (joint_attn_fwd_bf16_prepared_noalloc): the call allocates
+    nothing (pass `out`, and `pos`/`rope` already on the device, to allocate
+    nothing here either)."""
+    c = _Call(q.shape, q.device, softmax_scale, split)
+    c.strides("q", q, "q")
+    c.rope(pos, theta, rope).norm(q_norm, None, norm_eps)
+    if kv.dtype != torch.uint8 or kv.dim() != 1 or kv.device != c.device:
+        raise ValueError("kv must be the uint8 buffer from prep_kv_bf16 on q's device")
+    out, lse = _out_lse(c, out, return_lse)
+    _call("joint_attn_fwd_bf16_prepared_noalloc", c.ref(), _ptr(q), _ptr(kv), kv.numel(),
+          _ptr(out), _ptr(lse), c.stream())
+    return (out, lse) if return_lse else out
 
 
 def fwd_bf16_block_sparse_prepared(q, kv, block_mask, pos=None, theta: float = 10000.0,

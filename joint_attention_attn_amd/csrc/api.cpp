@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/joint_attn.h"
 #include "internal.hpp"
@@ -303,6 +304,34 @@ ja_status fwd_fp8_launch(const ja_params *p, const void *q8, const float *sq, co
   return hip_status(ja::launch_fwd_fp8(layout(p), q8, sq, kv8, o, lse, plan, ws, rp, st));
 }
 
+// ---- scratch of joint_attn_fwd_bf16_prepared_noalloc ----
+// A static device array (each device the library runs on holds its own copy
+// until the process ends).  In host code `scratch` only names the symbol:
+// its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current.
+__device__ __align__(256) unsigned char scratch[JA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+void *g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch array.
+ja_status scratch_address(void **out) {
+  int dev = 0;
+  JA_TRY(hip_status(hipGetDevice(&dev)));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(JA_ERR_UNSUPPORTED, "device %d is past the %d devices the scratch table holds",
+                dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    JA_TRY(hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return JA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +413,21 @@ ja_status joint_attn_fwd_bf16_prepared(const ja_params *p, const void *q, const 
                                        size_t workspace_bytes, void *stream) {
   return fwd_bf16_prepared_call(p, q, kv, kv_bytes, nullptr, o, lse, workspace, workspace_bytes,
                                 stream);
+}
+
+ja_status joint_attn_fwd_bf16_prepared_noalloc(const ja_params *p, const void *q,
+                                               const void *kv, size_t kv_bytes, void *o,
+                                               float *lse, void *stream) {
+  JA_TRY(check_bf16(p, true, false));
+  const ja::SplitPlan plan = plan_bf16(p, false);
+  if ((size_t)plan.ws_bytes > JA_NOALLOC_SCRATCH_BYTES)
+    return fail(JA_ERR_UNSUPPORTED,
+                "the split needs %lld bytes of scratch, more than the %zu of the static array",
+                (long long)plan.ws_bytes, (size_t)JA_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (plan.n_units > 0) JA_TRY(scratch_address(&ws));
+  return fwd_bf16_prepared_call(p, q, kv, kv_bytes, nullptr, o, lse, ws,
+                                ws ? JA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 ja_status joint_attn_fwd_bf16_block_sparse_prepared(const ja_params *p, const void *q,
