@@ -20,9 +20,10 @@ Also reported on the same JSON line:
   qk_norm       the same passes with query/key RMS normalization fused
                 where RoPE is (seeded weights): K/V preparation, forward,
                 FP8 quantize;
-  sparse        the block-sparse forward on a seeded mask over 128-query x
-                64-key blocks at the block density of the sparse steps
-                (half the blocks kept), against the flops of the kept blocks;
+  sparse        the block-sparse forwards (bf16, and FP8 on the FP8 leg's
+                codes) on a seeded mask over 128-query x 64-key blocks at the
+                block density of the sparse steps (half the blocks kept),
+                against the flops of the kept blocks;
   gemm_context  a large bf16 GEMM through torch.matmul (the vendor BLAS) timed
                 in the same run: the dense MFMA rate this power-limited part
                 sustains in practice, next to which the forward's rate reads;
@@ -275,7 +276,9 @@ def main() -> int:
 
     sparse = None
     if not args.no_sparse:
-        sparse = _sparse_leg(ja, w, qd, kv, rope, out, k_avg, max(args.steps, 5), args.seed)
+        fp8_in = (q8, sq, kv8, fp8["fwd_ms"]) if fp8 else None
+        sparse = _sparse_leg(ja, w, qd, kv, rope, out, k_avg, max(args.steps, 5), args.seed,
+                             fp8_in)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -353,11 +356,11 @@ def _norm_leg(ja, w, qd, kd, vd, rope, out, fwd_ms, prep_ms, quant_ms, n, seed):
     return rec
 
 
-def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
-    """Block-sparse forward on the seeded mask of the workload: its kernel
-    time, the flops of the kept blocks per second, and the fraction of the
-    key blocks staged (a workgroup covers one query block and stages the key
-    blocks it keeps)."""
+def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed, fp8_in=None):
+    """Block-sparse forwards on the seeded mask of the workload: kernel time,
+    the flops of the kept blocks per second, and the fraction of the key
+    blocks staged (a workgroup covers one query block and stages the key
+    blocks it keeps); bf16, and FP8 on the FP8 leg's prepared K/V."""
     import numpy as np
     import torch
     import synth
@@ -381,11 +384,26 @@ def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed):
     tf = kept_flops / (avg * 1e-3) / 1e12
     _log(f"[bench] sparse (density {synth.SPARSE_DENSITY}): {avg:.3f} ms, {tf:.1f} TFLOP/s of "
          f"kept blocks, {dense_ms / avg:.2f}x the dense kernel")
-    return {"mask": f"seeded iid blocks of {qb}x{kb}, kept with p={synth.SPARSE_DENSITY}",
-            "kept_frac": round(float(m.mean()), 4), "staged_frac": round(float(staged), 4),
-            "kept_flops": kept_flops, "fwd_ms": round(avg, 4), "fwd_tflops": round(tf, 2),
-            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "speedup_vs_dense_kernel": round(dense_ms / avg, 3)}
+    rec = {"mask": f"seeded iid blocks of {qb}x{kb}, kept with p={synth.SPARSE_DENSITY}",
+           "kept_frac": round(float(m.mean()), 4), "staged_frac": round(float(staged), 4),
+           "kept_flops": kept_flops, "fwd_ms": round(avg, 4), "fwd_tflops": round(tf, 2),
+           "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "speedup_vs_dense_kernel": round(dense_ms / avg, 3)}
+    if fp8_in is not None:
+        q8, sq, kv8, fp8_dense_ms = fp8_in
+        for _ in range(3):
+            ja.fwd_fp8_block_sparse_prepared(q8, sq, kv8, mask_d, out=outs)
+        torch.cuda.synchronize()
+        ms8 = _time_launches(lambda: ja.fwd_fp8_block_sparse_prepared(q8, sq, kv8, mask_d,
+                                                                      out=outs), n)
+        avg8 = sum(ms8) / n
+        tf8 = kept_flops / (avg8 * 1e-3) / 1e12
+        _log(f"[bench] fp8 sparse: {avg8:.3f} ms, {tf8:.1f} TFLOP/s of kept blocks, "
+             f"{fp8_dense_ms / avg8:.2f}x the dense fp8 kernel")
+        rec["fp8"] = {"fwd_ms": round(avg8, 4), "fwd_tflops": round(tf8, 2),
+                      "frac_of_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+                      "speedup_vs_dense_fp8_kernel": round(fp8_dense_ms / avg8, 3)}
+    return rec
 
 
 def _cpu_baseline(w, q, k, v, pos, outl, out_gpu, target_s, fp8_outs=None):

@@ -23,6 +23,7 @@
  *   joint_attn_fwd_bf16_block_sparse  the same on the blocks of a block mask
  *   joint_attn_quant_rope_fp8         Q, K, V (bf16) -> e4m3 codes + fp32 scales
  *   joint_attn_fwd_fp8                e4m3 Q, K, V with their scales -> O
+ *   joint_attn_fwd_fp8_block_sparse   the same on the blocks of a block mask
  *   joint_attn_fp8_repair_count / _repair_plan   repair of the FP8 path
  *   joint_attn_rope_table_2d, joint_attn_prep_kv_bf16, joint_attn_prep_kv_fp8,
  *   joint_attn_fwd_*_prepared         the two phases of the forwards, for
@@ -326,6 +327,24 @@ ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8,
                              float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * joint_attn_fwd_fp8_block_sparse - joint_attn_fwd_fp8 restricted to the
+ * blocks of a given block mask (the pages' block-sparse attention on a
+ * general block-sparse kernel, section "Quantized and sparse attention", here
+ * on FP8 inputs).  block_mask as for joint_attn_fwd_bf16_block_sparse (128
+ * queries x 64 keys, one mask column per 64-key FP8 tile); a query row that
+ * keeps no key gets O = 0 and LSE = -inf.  Every other argument, the
+ * arithmetic and the workspace size (joint_attn_fwd_fp8_workspace_bytes) are
+ * those of joint_attn_fwd_fp8; an all-nonzero mask gives the same result as
+ * joint_attn_fwd_fp8 with JA_FLAG_NO_SPLIT.  seq_len up to 1048576
+ * (JA_ERR_UNSUPPORTED above).
+ */
+ja_status joint_attn_fwd_fp8_block_sparse(const ja_params *p, const void *q8, const void *k8,
+                                          const void *v8, const float *sq, const float *sk,
+                                          const float *sv, const uint8_t *block_mask, void *o,
+                                          float *lse, void *workspace, size_t workspace_bytes,
+                                          void *stream);
+
+/*
  * Repair of the FP8 path (the pages' VC-Attention FP8 with vc_repair_budget,
  * section "Quantized and sparse attention": a small budget of the tokens
  * whose quantization error is largest get their residual added back).
@@ -422,6 +441,14 @@ ja_status joint_attn_fwd_fp8_prepared(const ja_params *p, const void *q8, const 
                                       const void *kv8, size_t kv8_bytes,
                                       const ja_fp8_repair *repair, void *o, float *lse,
                                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* joint_attn_fwd_fp8_block_sparse on K/V prepared by joint_attn_prep_kv_fp8
+ * (without repair; workspace: joint_attn_fwd_fp8_prepared_workspace_bytes). */
+ja_status joint_attn_fwd_fp8_block_sparse_prepared(const ja_params *p, const void *q8,
+                                                   const float *sq, const void *kv8,
+                                                   size_t kv8_bytes, const uint8_t *block_mask,
+                                                   void *o, float *lse, void *workspace,
+                                                   size_t workspace_bytes, void *stream);
 
 /* ======================================================================
  * Status

@@ -18,7 +18,8 @@ __all__ = [
     "JointAttnError", "library_path", "load", "Params", "rope_table_2d",
     "fwd_bf16", "fwd_bf16_block_sparse", "prep_kv_bf16", "fwd_bf16_prepared",
     "fwd_bf16_block_sparse_prepared", "fwd_bf16_workspace_bytes", "fwd_bf16_prepared_noalloc",
-    "quant_rope_fp8", "fwd_fp8", "prep_kv_fp8", "fwd_fp8_prepared",
+    "quant_rope_fp8", "fwd_fp8", "prep_kv_fp8", "fwd_fp8_prepared", "fwd_fp8_block_sparse",
+    "fwd_fp8_block_sparse_prepared",
     "Fp8Repair", "repair_count", "fp8_repair_plan",
     "SPARSE_QUERY_BLOCK", "SPARSE_KEY_BLOCK", "block_mask_shape",
 ]
@@ -83,6 +84,10 @@ _SIGNATURES = {
                                   _vp],
     "joint_attn_fwd_fp8_workspace_bytes": [_pp],
     "joint_attn_fwd_fp8": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "joint_attn_fwd_fp8_block_sparse": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _sz, _vp],
+    "joint_attn_fwd_fp8_block_sparse_prepared": [_pp, _vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp,
+                                                 _sz, _vp],
     "joint_attn_fp8_repair_count": [ctypes.c_double, ctypes.c_int32],
     "joint_attn_fp8_repair_plan_workspace_bytes": [_pp],
     "joint_attn_fp8_repair_plan": [_pp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp, _vp,
@@ -437,6 +442,38 @@ def fwd_fp8(q8, k8, v8, sq, sk, sv, softmax_scale: float = 0.0, out=None,
     ws = _scratch(n, c.device)
     _call("joint_attn_fwd_fp8", c.ref(), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq), _ptr(sk),
           _ptr(sv), _ptr(out), _ptr(lse), _ptr(ws), n, c.stream())
+    return (out, lse) if return_lse else out
+
+
+def fwd_fp8_block_sparse(q8, k8, v8, sq, sk, sv, block_mask, softmax_scale: float = 0.0,
+                         out=None, return_lse: bool = False, split: bool = True):
+    """fwd_fp8 restricted to the (128-query x 64-key) blocks where the uint8
+    `block_mask` [B, H, ceil(S/128), ceil(S/64)] is nonzero; query rows that
+    keep no key get O = 0 and LSE = -inf (joint_attn_fwd_fp8_block_sparse)."""
+    c = _fp8_call(q8.shape, q8.device, softmax_scale, split,
+                  ((q8, "q8"), (k8, "k8"), (v8, "v8")), ((sq, "sq"), (sk, "sk"), (sv, "sv")))
+    _check_mask(c, block_mask)
+    out, lse = _out_lse(c, out, return_lse)
+    n = c.query("joint_attn_fwd_fp8_workspace_bytes")
+    ws = _scratch(n, c.device)
+    _call("joint_attn_fwd_fp8_block_sparse", c.ref(), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(sq),
+          _ptr(sk), _ptr(sv), _ptr(block_mask), _ptr(out), _ptr(lse), _ptr(ws), n, c.stream())
+    return (out, lse) if return_lse else out
+
+
+def fwd_fp8_block_sparse_prepared(q8, sq, kv8, block_mask, softmax_scale: float = 0.0, out=None,
+                                  return_lse: bool = False, split: bool = True):
+    """fwd_fp8_block_sparse on K/V from prep_kv_fp8 (prepared with the same
+    softmax_scale): joint_attn_fwd_fp8_block_sparse_prepared."""
+    c = _fp8_call(q8.shape, q8.device, softmax_scale, split, ((q8, "q8"),), ((sq, "sq"),))
+    _check_mask(c, block_mask)
+    if kv8.dtype != torch.uint8 or kv8.dim() != 1 or kv8.device != c.device:
+        raise ValueError("kv8 must be the uint8 buffer from prep_kv_fp8 on q8's device")
+    out, lse = _out_lse(c, out, return_lse)
+    n = c.query("joint_attn_fwd_fp8_prepared_workspace_bytes")
+    ws = _scratch(n, c.device)
+    _call("joint_attn_fwd_fp8_block_sparse_prepared", c.ref(), _ptr(q8), _ptr(sq), _ptr(kv8),
+          kv8.numel(), _ptr(block_mask), _ptr(out), _ptr(lse), _ptr(ws), n, c.stream())
     return (out, lse) if return_lse else out
 
 

@@ -157,9 +157,13 @@ ja::SplitPlan plan_bf16(const ja_params *p, bool sparse) {
   const ja::SplitPlan plan = ja::plan_fwd_bf16(layout(p), device_cu_count(), sparse);
   return (p->flags & JA_FLAG_NO_SPLIT) ? no_split(plan) : plan;
 }
-ja::SplitPlan plan_fp8(const ja_params *p) {
-  const ja::SplitPlan plan = ja::plan_fwd_fp8(layout(p), device_cu_count());
+ja::SplitPlan plan_fp8(const ja_params *p, bool sparse) {
+  const ja::SplitPlan plan = ja::plan_fwd_fp8(layout(p), device_cu_count(), sparse);
   return (p->flags & JA_FLAG_NO_SPLIT) ? no_split(plan) : plan;
+}
+// Workspace of the split for either FP8 forward (dense or block-sparse).
+int64_t fp8_split_bytes(const ja_params *p) {
+  return std::max(plan_fp8(p, false).ws_bytes, plan_fp8(p, true).ws_bytes);
 }
 
 // ---- BF16 path ----
@@ -268,7 +272,8 @@ ja_status fwd_bf16_prepared_call(const ja_params *p, const void *q, const void *
 ja_status check_fp8(const ja_params *p) {
   JA_TRY(check_common(p));
   JA_TRY(check_bf16_strides(p, false, false, true));
-  JA_TRY(check_grid(p, ja::fwd_fp8_block_rows(p->head_dim)));
+  // the block-sparse forward has the smaller workgroups, hence the larger grid
+  JA_TRY(check_grid(p, ja::fwd_fp8_block_rows(true)));
   // the prepared K and V^T of one (batch, head) are addressed with 32-bit
   // byte offsets; the preparation pass has one workgroup per 64 keys and head
   const int64_t s_pad = ((int64_t)p->seq_len + 63) / 64 * 64;
@@ -295,13 +300,65 @@ ja_status prep_fp8(const ja_params *p, const void *k8, const void *v8, const flo
 }
 
 ja_status fwd_fp8_launch(const ja_params *p, const void *q8, const float *sq, const void *kv8,
-                         const ja::Fp8Repair &rp, void *o, float *lse, void *ws,
-                         size_t ws_bytes, hipStream_t st) {
-  const ja::SplitPlan plan = plan_fp8(p);
+                         const uint8_t *mask, const ja::Fp8Repair &rp, void *o, float *lse,
+                         void *ws, size_t ws_bytes, hipStream_t st) {
+  const ja::SplitPlan plan = plan_fp8(p, mask != nullptr);
   if (plan.n_units > 0 && (size_t)plan.ws_bytes > ws_bytes)
     return fail(JA_ERR_INVALID_ARG, "workspace of %zu bytes is less than the %lld needed",
                 ws_bytes, (long long)plan.ws_bytes);
-  return hip_status(ja::launch_fwd_fp8(layout(p), q8, sq, kv8, o, lse, plan, ws, rp, st));
+  return hip_status(ja::launch_fwd_fp8(layout(p), q8, sq, kv8, mask, o, lse, plan, ws, rp, st));
+}
+
+// Checks and launch of the one-call FP8 forwards (dense, or block-sparse
+// with a mask).
+ja_status fwd_fp8_call(const ja_params *p, const void *q8, const void *k8, const void *v8,
+                       const float *sq, const float *sk, const float *sv, const uint8_t *mask,
+                       void *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+  JA_TRY(check_fp8(p));
+  if (!q8 || !k8 || !v8 || !sq || !sk || !sv || !o)
+    return fail(JA_ERR_INVALID_ARG, "every tensor pointer must be non-NULL");
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned4(sq) ||
+      !aligned4(sk) || !aligned4(sv) || !aligned4(lse) || !aligned16(ws))
+    return fail(JA_ERR_INVALID_ARG, "misaligned pointer (16 bytes; scales, lse 4 bytes)");
+  if (o == q8 || o == k8 || o == v8 || o == ws)
+    return fail(JA_ERR_INVALID_ARG, "o aliases an input");
+  const int64_t kv_bytes = align256(ja::prep_kv_fp8_bytes(layout(p)));
+  const int64_t need = kv_bytes + plan_fp8(p, mask != nullptr).ws_bytes;
+  if (!ws || ws_bytes < (size_t)need)
+    return fail(JA_ERR_INVALID_ARG, "workspace of %zu bytes is less than the %lld needed",
+                ws_bytes, (long long)need);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  JA_TRY(prep_fp8(p, k8, v8, sk, sv, nullptr, ws, st));
+  return fwd_fp8_launch(p, q8, sq, ws, mask, ja::Fp8Repair{}, o, lse, byte_ptr(ws, kv_bytes),
+                        ws_bytes - kv_bytes, st);
+}
+
+// Checks and launch of the FP8 forwards on prepared K/V.
+ja_status fwd_fp8_prepared_call(const ja_params *p, const void *q8, const float *sq,
+                                const void *kv8, size_t kv8_bytes, const ja_fp8_repair *repair,
+                                const uint8_t *mask, void *o, float *lse, void *ws,
+                                size_t ws_bytes, void *stream) {
+  JA_TRY(check_fp8(p));
+  if (!q8 || !sq || !kv8 || !o) return fail(JA_ERR_INVALID_ARG, "q8, sq, kv8 and o must be non-NULL");
+  ja::Fp8Repair rp;
+  if (repair && repair->n_rep != 0) {
+    if (repair->n_rep < 0 || repair->n_rep > p->seq_len)
+      return fail(JA_ERR_INVALID_ARG, "repair->n_rep must be in [0, seq_len]");
+    if (!repair->kr || !repair->vr || !aligned16(repair->kr) || !aligned16(repair->vr))
+      return fail(JA_ERR_INVALID_ARG, "repair->kr and repair->vr must be 16-byte aligned pointers");
+    rp.n_rep = repair->n_rep;
+    rp.kr = repair->kr;
+    rp.vr = repair->vr;
+  }
+  if (!aligned16(q8) || !aligned16(kv8) || !aligned16(o) || !aligned4(sq) || !aligned4(lse) ||
+      !aligned16(ws))
+    return fail(JA_ERR_INVALID_ARG, "misaligned pointer (16 bytes; sq, lse 4 bytes)");
+  if (o == q8 || o == kv8) return fail(JA_ERR_INVALID_ARG, "o aliases an input");
+  if (kv8_bytes < (size_t)ja::prep_kv_fp8_bytes(layout(p)))
+    return fail(JA_ERR_INVALID_ARG, "kv8_bytes %zu is less than joint_attn_prep_kv_fp8_bytes",
+                kv8_bytes);
+  return fwd_fp8_launch(p, q8, sq, kv8, mask, rp, o, lse, ws, ws ? ws_bytes : 0,
+                        static_cast<hipStream_t>(stream));
 }
 
 // ---- scratch of joint_attn_fwd_bf16_prepared_noalloc ----
@@ -539,61 +596,47 @@ ja_status joint_attn_prep_kv_fp8(const ja_params *p, const void *k8, const void 
 
 size_t joint_attn_fwd_fp8_prepared_workspace_bytes(const ja_params *p) {
   if (check_fp8(p) != JA_OK) return 0;
-  return (size_t)plan_fp8(p).ws_bytes;
+  return (size_t)fp8_split_bytes(p);
 }
 
 ja_status joint_attn_fwd_fp8_prepared(const ja_params *p, const void *q8, const float *sq,
                                       const void *kv8, size_t kv8_bytes,
                                       const ja_fp8_repair *repair, void *o, float *lse,
                                       void *workspace, size_t workspace_bytes, void *stream) {
-  JA_TRY(check_fp8(p));
-  if (!q8 || !sq || !kv8 || !o) return fail(JA_ERR_INVALID_ARG, "q8, sq, kv8 and o must be non-NULL");
-  ja::Fp8Repair rp;
-  if (repair && repair->n_rep != 0) {
-    if (repair->n_rep < 0 || repair->n_rep > p->seq_len)
-      return fail(JA_ERR_INVALID_ARG, "repair->n_rep must be in [0, seq_len]");
-    if (!repair->kr || !repair->vr || !aligned16(repair->kr) || !aligned16(repair->vr))
-      return fail(JA_ERR_INVALID_ARG, "repair->kr and repair->vr must be 16-byte aligned pointers");
-    rp.n_rep = repair->n_rep;
-    rp.kr = repair->kr;
-    rp.vr = repair->vr;
-  }
-  if (!aligned16(q8) || !aligned16(kv8) || !aligned16(o) || !aligned4(sq) || !aligned4(lse) ||
-      !aligned16(workspace))
-    return fail(JA_ERR_INVALID_ARG, "misaligned pointer (16 bytes; sq, lse 4 bytes)");
-  if (o == q8 || o == kv8) return fail(JA_ERR_INVALID_ARG, "o aliases an input");
-  if (kv8_bytes < (size_t)ja::prep_kv_fp8_bytes(layout(p)))
-    return fail(JA_ERR_INVALID_ARG, "kv8_bytes %zu is less than joint_attn_prep_kv_fp8_bytes",
-                kv8_bytes);
-  return fwd_fp8_launch(p, q8, sq, kv8, rp, o, lse, workspace, workspace ? workspace_bytes : 0,
-                        static_cast<hipStream_t>(stream));
+  return fwd_fp8_prepared_call(p, q8, sq, kv8, kv8_bytes, repair, nullptr, o, lse, workspace,
+                               workspace_bytes, stream);
+}
+
+ja_status joint_attn_fwd_fp8_block_sparse_prepared(const ja_params *p, const void *q8,
+                                                   const float *sq, const void *kv8,
+                                                   size_t kv8_bytes, const uint8_t *block_mask,
+                                                   void *o, float *lse, void *workspace,
+                                                   size_t workspace_bytes, void *stream) {
+  JA_TRY(check_sparse(p, block_mask, ja::fwd_fp8_sparse_max_seq()));
+  return fwd_fp8_prepared_call(p, q8, sq, kv8, kv8_bytes, nullptr, block_mask, o, lse, workspace,
+                               workspace_bytes, stream);
 }
 
 size_t joint_attn_fwd_fp8_workspace_bytes(const ja_params *p) {
   if (check_fp8(p) != JA_OK) return 0;
-  return (size_t)align256(ja::prep_kv_fp8_bytes(layout(p))) + (size_t)plan_fp8(p).ws_bytes;
+  return (size_t)align256(ja::prep_kv_fp8_bytes(layout(p))) + (size_t)fp8_split_bytes(p);
 }
 
 ja_status joint_attn_fwd_fp8(const ja_params *p, const void *q8, const void *k8, const void *v8,
                              const float *sq, const float *sk, const float *sv, void *o,
                              float *lse, void *workspace, size_t workspace_bytes, void *stream) {
-  JA_TRY(check_fp8(p));
-  if (!q8 || !k8 || !v8 || !sq || !sk || !sv || !o)
-    return fail(JA_ERR_INVALID_ARG, "every tensor pointer must be non-NULL");
-  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned4(sq) ||
-      !aligned4(sk) || !aligned4(sv) || !aligned4(lse) || !aligned16(workspace))
-    return fail(JA_ERR_INVALID_ARG, "misaligned pointer (16 bytes; scales, lse 4 bytes)");
-  if (o == q8 || o == k8 || o == v8 || o == workspace)
-    return fail(JA_ERR_INVALID_ARG, "o aliases an input");
-  const int64_t kv_bytes = align256(ja::prep_kv_fp8_bytes(layout(p)));
-  const int64_t need = kv_bytes + plan_fp8(p).ws_bytes;
-  if (!workspace || workspace_bytes < (size_t)need)
-    return fail(JA_ERR_INVALID_ARG, "workspace of %zu bytes is less than the %lld needed",
-                workspace_bytes, (long long)need);
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  JA_TRY(prep_fp8(p, k8, v8, sk, sv, nullptr, workspace, st));
-  return fwd_fp8_launch(p, q8, sq, workspace, ja::Fp8Repair{}, o, lse,
-                        byte_ptr(workspace, kv_bytes), workspace_bytes - kv_bytes, st);
+  return fwd_fp8_call(p, q8, k8, v8, sq, sk, sv, nullptr, o, lse, workspace, workspace_bytes,
+                      stream);
+}
+
+ja_status joint_attn_fwd_fp8_block_sparse(const ja_params *p, const void *q8, const void *k8,
+                                          const void *v8, const float *sq, const float *sk,
+                                          const float *sv, const uint8_t *block_mask, void *o,
+                                          float *lse, void *workspace, size_t workspace_bytes,
+                                          void *stream) {
+  JA_TRY(check_sparse(p, block_mask, ja::fwd_fp8_sparse_max_seq()));
+  return fwd_fp8_call(p, q8, k8, v8, sq, sk, sv, block_mask, o, lse, workspace, workspace_bytes,
+                      stream);
 }
 
 }  // extern "C"

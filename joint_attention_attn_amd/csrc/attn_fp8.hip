@@ -28,6 +28,14 @@
 // ahead, with no staging registers and no vector work.  Each wave runs
 // Q K^T, softmax and P.V of a tile in turn, and the three waves of a SIMD
 // overlap one another's matrix and vector work.
+//
+// Block-sparse variant (the pages' general block-sparse attention kernel,
+// section "Quantized and sparse attention", on a given mask of 128-query x
+// 64-key blocks): a workgroup of four waves covers one 128-row query block,
+// three workgroups share a CU over 3-stage rings; the workgroup compacts the
+// list of key blocks its query block keeps into LDS and stages only those
+// tiles (one 64-key tile is one key block).  Rows that keep no key get O = 0
+// and LSE = -inf.
 #include <atomic>
 
 #include "common.hpp"
@@ -39,16 +47,30 @@ namespace ja {
 
 namespace {
 
-// Waves per workgroup, 32 query rows each, three per SIMD (at most 168 VGPRs
-// each).  Software pipelining inside a wave (Q K^T of the next tile issued
-// ahead of this tile's softmax) would keep two tiles of accumulators live,
-// about 245 VGPRs, and allow only two waves per SIMD, which is slower.
-constexpr int NW = 12;
-constexpr int BM = 32 * NW;         // query rows per workgroup
 constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
-constexpr int NT = 64 * NW;         // threads per workgroup
-constexpr int NSTAGE = 4;           // K/V tiles in the LDS ring
-constexpr int PREF = 3;             // tiles issued ahead
+
+// Workgroup shape.  Dense: twelve waves of 32 query rows, three per SIMD (at
+// most 168 VGPRs each), over a 4-stage ring three tiles ahead.  Software
+// pipelining inside a wave (Q K^T of the next tile issued ahead of this
+// tile's softmax) would keep two tiles of accumulators live, about 245
+// VGPRs, and allow only two waves per SIMD, which is slower.  Block-sparse:
+// one 128-row query block per workgroup of four waves, three workgroups per
+// CU over 3-stage rings two tiles ahead.
+template <bool SPARSE>
+struct Cfg {
+  static constexpr int NW = SPARSE ? 4 : 12;      // waves per workgroup
+  static constexpr int NSTAGE = SPARSE ? 3 : 4;   // K/V tiles in the LDS ring
+  static constexpr int PREF = NSTAGE - 1;         // tiles issued ahead
+  static constexpr int WG_PER_CU = SPARSE ? 3 : 1;
+  static constexpr int BM = 32 * NW;              // query rows per workgroup
+  static constexpr int NT = 64 * NW;              // threads per workgroup
+};
+// Block-mask granularity of the block-sparse variant (a key block is a tile).
+constexpr int kQueryBlock = 128;
+static_assert(Cfg<true>::BM == kQueryBlock, "one query block per sparse workgroup");
+// Longest sequence of the block-sparse variant (its key-block list lives in
+// LDS, 4 bytes per key block).
+constexpr int kSparseMaxSeq = 1 << 20;
 constexpr int INFO_BYTES = 1024;    // per-key values of a tile (see prep_kv_fp8.hip)
 
 // The running max m is refreshed when some row's max grows by more than
@@ -82,6 +104,9 @@ struct Fp8Args {
   // rotated K and V (bf16).
   const bf16 *kr, *vr;
   int n_rep, n_pad;
+  // block-sparse variant: mask [B][H][nqb][nkb] (nonzero = keep)
+  const uint8_t *mask;
+  int nqb, nkb;
 };
 
 // Formats 0 = fp8 e4m3 for both operands; sa / sb are E8M0 exponents (127 =
@@ -117,30 +142,40 @@ __device__ __forceinline__ float half_sum(float x) {
 
 // LDS ring: NSTAGE stages of [K tile | V^T tile | per-key values], each
 // part a whole number of 1 KB loads (one wave's 64 lanes x 16 bytes).  A K
-// row is D bytes plus a 16-byte pad, the pad lanes loading a dummy chunk.  A
-// V^T row is the 64 keys of one head-dimension column, granule g stored at
-// g ^ vswz(d) so that the fragment reads of 16 consecutive rows cover all 16
-// bank groups.
+// row is D bytes whose 16-byte granules are XOR-swizzled (granule g of row r
+// at g ^ ksw(r)), a V^T row the 64 keys of one head-dimension column with
+// granule g at g ^ vswz8(d): the fragment reads of every 8 and every 16
+// consecutive lanes then cover distinct banks (checked on the CPU against
+// both the 32-bank and the 64-bank view of the LDS).
 __host__ __device__ constexpr int vswz8(int d) { return (d / 4) % 4; }
-
 template <int D>
+__host__ __device__ constexpr int ksw(int r) {
+  return D == 128 ? (r ^ (r >> 3)) & 7 : ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+template <int D, int NSTAGE>
 struct Fp8Lds {
-  static constexpr int CH = D / 16;                    // 16-byte chunks per K row
-  static constexpr int KSTR = D + 16;                  // bytes per K row
-  static constexpr int K_LOADS = BN * (CH + 1) / 64;
+  static constexpr int CH = D / 16;                    // 16-byte granules per K row
+  static constexpr int K_LOADS = BN * CH / 64;
   static constexpr int V_LOADS = D * (BN / 16) / 64;
   static constexpr int LOADS = K_LOADS + V_LOADS + 1;  // + per-key values
   static constexpr int KBYTES = K_LOADS * 1024;
   static constexpr int VBYTES = V_LOADS * 1024;
   static constexpr int STAGE = LOADS * 1024;
   static constexpr int BYTES = NSTAGE * STAGE;
-  static_assert(BN * (CH + 1) % 64 == 0 && D * (BN / 16) % 64 == 0, "whole loads");
+  // block-sparse variant: per-wave counts, then the key-block list
+  static constexpr int LIST_OFFSET = BYTES + 64;
+  static constexpr int sparse_bytes(int nkb) { return LIST_OFFSET + 4 * nkb; }
+  static_assert(BN * CH % 64 == 0 && D * (BN / 16) % 64 == 0, "whole loads");
 };
 
-template <int D, bool REPAIR>
-__global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
-  using L = Fp8Lds<D>;
-  constexpr int KSTR = L::KSTR;
+template <int D, bool REPAIR, bool SPARSE>
+__global__ __launch_bounds__(Cfg<SPARSE>::NT, Cfg<SPARSE>::WG_PER_CU)
+void attn_fwd_fp8_kernel(Fp8Args a) {
+  static_assert(!(REPAIR && SPARSE), "the repair pass is dense only");
+  constexpr int NW = Cfg<SPARSE>::NW, NT = Cfg<SPARSE>::NT, BM = Cfg<SPARSE>::BM;
+  constexpr int NSTAGE = Cfg<SPARSE>::NSTAGE, PREF = Cfg<SPARSE>::PREF;
+  using L = Fp8Lds<D, NSTAGE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
   auto Kst = [&](int st) JA_INLINE { return smem8 + st * L::STAGE; };
   auto Vst = [&](int st) JA_INLINE { return smem8 + st * L::STAGE + L::KBYTES; };
@@ -160,25 +195,62 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
   // ---- work item: XCD-aware placement of whole items, then the key-range
   //      parts of split items (see split.hip) ----
-  int item, t0, t1, unit = -1;
+  int item, part = 0, unit = -1;
   if ((int)blockIdx.x < a.n_direct) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per = a.n_direct >> 3, rem = a.n_direct & 7;
     item = xcd * per + min(xcd, rem) + slot;
-    t0 = 0;
-    t1 = ntiles_all;
   } else {
     unit = blockIdx.x - a.n_direct;
-    const int part = unit % a.parts;
+    part = unit % a.parts;
     item = a.n_direct + unit / a.parts;
-    t0 = (int)((int64_t)part * ntiles_all / a.parts);
-    t1 = (int)((int64_t)(part + 1) * ntiles_all / a.parts);
   }
   const int qblk = item % a.n_qblk;
   const int bh32 = item / a.n_qblk;
   const int h = bh32 % a.H, b = bh32 / a.H;
   const int64_t bh = (int64_t)b * a.H + h;
   const int64_t row_stride = (int64_t)a.H * D;  // contiguous [B, S, H, D]
+
+  // ---- block-sparse variant: the key blocks (= tiles) this query block
+  //      keeps, compacted in ascending order into an LDS list; the dense
+  //      kernel's tiles are 0 .. ntiles-1 ----
+  uint32_t *blist = reinterpret_cast<uint32_t *>(smem8 + L::LIST_OFFSET);
+  int ntiles = ntiles_all;
+  if constexpr (SPARSE) {
+    int *wcnt = reinterpret_cast<int *>(smem8 + L::BYTES);
+    const uint8_t *mrow = a.mask + ((int64_t)bh * a.nqb + qblk) * a.nkb;
+    int nact = 0;
+    for (int base = 0; base < a.nkb; base += NT) {
+      const int j = base + tid;
+      const bool keep = j < a.nkb && mrow[j] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+      if (lane == 0) wcnt[wave] = (int)__builtin_popcountll(bal);
+      __syncthreads();
+      int off = nact, tot = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int cw = wcnt[w];
+        off += w < wave ? cw : 0;
+        tot += cw;
+      }
+      if (keep) blist[off + __builtin_popcountll(bal & ((1ull << lane) - 1))] = (uint32_t)j;
+      nact += tot;
+      __syncthreads();
+    }
+    ntiles = nact;
+  }
+  int t0 = 0, t1 = ntiles;
+  if (unit >= 0) {
+    t0 = (int)((int64_t)part * ntiles / a.parts);
+    t1 = (int)((int64_t)(part + 1) * ntiles / a.parts);
+  }
+  // key tile of list position x
+  auto tile_of = [&](int x) JA_INLINE -> int {
+    if constexpr (SPARSE)
+      return (int)__builtin_amdgcn_readfirstlane(blist[x]);
+    else
+      return x;
+  };
 
   // ---- Q8 of this lane's query row ----
   const int qi = qblk * BM + wave * 32 + l32;
@@ -208,13 +280,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
       const_cast<uint8_t *>(a.v8t + bh * D * a.S_pad), 0, span_k, kBufferFlags);
   const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(a.info + bh * span_i), 0, span_i, kBufferFlags);
-  // source offset of this lane in load j (K lanes that fall on a pad load a
-  // dummy chunk; V^T lanes fetch the granule that the swizzle puts there)
+  // source offset of this lane in load j: K lanes fetch the granule that
+  // the row's swizzle puts at their LDS position, V^T lanes likewise
   auto load_offset = [&](int j) JA_INLINE -> int {
     if (j < L::K_LOADS) {
       const int g = 64 * j + lane;
-      const int r = g / (L::CH + 1), ch = g % (L::CH + 1);
-      return ch < L::CH ? r * D + 16 * ch : 0;
+      const int r = g / L::CH;
+      return r * D + 16 * ((g % L::CH) ^ ksw<D>(r));
     }
     if (j < L::K_LOADS + L::V_LOADS) {
       const int g = 64 * (j - L::K_LOADS) + lane;
@@ -224,12 +296,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     return 16 * lane;
   };
   constexpr int JW = (L::LOADS + NW - 1) / NW;         // loads per wave, at most
-  static_assert(JW <= 3, "loads per wave");
+  static_assert(JW <= 5, "loads per wave");
   // (scalar offsets: an array element as the builtin's offset operand makes
   // the host compilation drop the kernel's launch stub without a message)
-  const int voff0 = load_offset(wave);
-  const int voff1 = wave + NW < L::LOADS ? load_offset(wave + NW) : 0;
-  const int voff2 = wave + 2 * NW < L::LOADS ? load_offset(wave + 2 * NW) : 0;
+  auto voff_of = [&](int m) JA_INLINE -> int {
+    return wave + m * NW < L::LOADS ? load_offset(wave + m * NW) : 0;
+  };
+  const int voff0 = voff_of(0), voff1 = voff_of(1), voff2 = voff_of(2), voff3 = voff_of(3),
+            voff4 = voff_of(4);
   const int nl = (L::LOADS - wave + NW - 1) / NW;      // loads of this wave per tile
   auto issue_one = [&](int j, int voff, int t, int st) JA_INLINE {
     char *dst = reinterpret_cast<char *>(smem8) + st * L::STAGE + j * 1024;
@@ -240,19 +314,24 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, JA_LDS_PTR(dst), 16, voff, t * INFO_BYTES, 0, 0);
   };
-  // loads of key tile t into stage st (at D = 64 a tile has fewer loads than
-  // the workgroup has waves; the last waves issue none)
+  // loads of key tile t into stage st (a wave past the tile's load count
+  // issues none)
   auto issue = [&](int t, int st) JA_INLINE {
-    if (wave < L::LOADS) issue_one(wave, voff0, t, st);
-    if (wave + NW < L::LOADS) issue_one(wave + NW, voff1, t, st);
-    if (JW >= 3 && wave + 2 * NW < L::LOADS) issue_one(wave + 2 * NW, voff2, t, st);
+    if (0 < nl) issue_one(wave, voff0, t, st);
+    if (JW > 1 && 1 < nl) issue_one(wave + NW, voff1, t, st);
+    if (JW > 2 && 2 < nl) issue_one(wave + 2 * NW, voff2, t, st);
+    if (JW > 3 && 3 < nl) issue_one(wave + 3 * NW, voff3, t, st);
+    if (JW > 4 && 4 < nl) issue_one(wave + 4 * NW, voff4, t, st);
   };
   // wait until at most `AHEAD` later tiles' loads of this wave are in flight
   auto wait_tiles = [&]<int AHEAD>() JA_INLINE {
-    if constexpr (JW >= 3) {
-      if (nl >= 3) { wait_vmcnt<3 * AHEAD>(); return; }
-    }
-    if (nl >= 2)
+    if (JW > 4 && nl == 5)
+      wait_vmcnt<5 * AHEAD>();
+    else if (JW > 3 && nl == 4)
+      wait_vmcnt<4 * AHEAD>();
+    else if (JW > 2 && nl == 3)
+      wait_vmcnt<3 * AHEAD>();
+    else if (JW > 1 && nl == 2)
       wait_vmcnt<2 * AHEAD>();
     else
       wait_vmcnt<AHEAD>();
@@ -276,11 +355,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         sacc[kb][4 * g + 3] = bg.w;
       }
       const int kex = ke[kb * 32 + l32];            // A row l32 is key kb*32 + l32
-      const uint8_t *krow = Kst(st) + (kb * 32 + l32) * KSTR + 32 * hf;
+      const int krw = kb * 32 + l32;
+      const uint8_t *krow = Kst(st) + krw * D;
+      const int ks = ksw<D>(krw);
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk) {
-        const i32x4 lo = *reinterpret_cast<const i32x4 *>(krow + 64 * kk);
-        const i32x4 hi = *reinterpret_cast<const i32x4 *>(krow + 64 * kk + 16);
+        const int g0 = 4 * kk + 2 * hf;
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(krow + 16 * (g0 ^ ks));
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(krow + 16 * ((g0 + 1) ^ ks));
         sacc[kb] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qreg[kk],
                             sacc[kb], kex, qe);
       }
@@ -373,17 +455,21 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
   //      of tile i; before the barrier that closes it, each wave waits for
   //      its own loads of tile i+1 only. ----
   const int nt = t1 - t0;
+  // a dense workgroup always has at least one tile; a sparse one may have none
+  const bool any_tile = !SPARSE || nt > 0;
+  if (any_tile) {
 #pragma unroll
-  for (int p = 0; p < PREF; ++p)
-    if (p < nt) issue(t0 + p, p);
-  wait_vmcnt<0>();
-  tile_barrier();
-  // the per-key values were prepared for this softmax scale
-  bad = bad || Ist(0)[3 * BN] != c;
+    for (int p = 0; p < PREF; ++p)
+      if (p < nt) issue(tile_of(t0 + p), p);
+    wait_vmcnt<0>();
+    tile_barrier();
+    // the per-key values were prepared for this softmax scale
+    bad = bad || Ist(0)[3 * BN] != c;
+  }
   f32x16 sacc[2];
   auto iteration = [&]<bool LAST>(int i) JA_INLINE {
     const bool ahead = i + PREF < nt;
-    if (ahead) issue(t0 + i + PREF, (i + PREF) % NSTAGE);
+    if (ahead) issue(tile_of(t0 + i + PREF), (i + PREF) % NSTAGE);
     qk(i % NSTAGE, sacc);
     const i32x8 pb = softmax(sacc, i % NSTAGE);
     pv(pb, i % NSTAGE);
@@ -398,7 +484,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
     }
   };
   for (int i = 0; i + 1 < nt; ++i) iteration.template operator()<false>(i);
-  iteration.template operator()<true>(nt - 1);
+  if (any_tile) iteration.template operator()<true>(nt - 1);
 
   // ---- repaired keys: one more pass over them with their exact values, on
   //      bf16 MFMA (an e4m3 code times its scale is exact in this product:
@@ -530,13 +616,18 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
         *reinterpret_cast<float4 *>(orow + db * 32 + 8 * grp + 4 * hf) =
             make_float4(oacc[db][4 * grp] * o_mul, oacc[db][4 * grp + 1] * o_mul,
                         oacc[db][4 * grp + 2] * o_mul, oacc[db][4 * grp + 3] * o_mul);
+    // a block-sparse row that saw no key in this part: row max -inf, so
+    // that the merge treats it as empty
+    const float mref = SPARSE && l_tot == 0.f ? -INFINITY : ref;
     if (hf == 0)
       *reinterpret_cast<float2 *>(a.ws.ml + ((int64_t)unit * BM + row) * 2) =
-          make_float2(ref * o_mul, l_tot);
+          make_float2(mref * o_mul, l_tot);
     return;
   }
   if (qi < S) {
-    const float inv = o_mul / l_tot;
+    // a block-sparse row that keeps no key has l = 0 and O accumulators 0:
+    // O = 0, LSE = -inf (NaN if poisoned)
+    const float inv = SPARSE && l_tot == 0.f ? 0.f * o_mul : o_mul / l_tot;
     bf16 *orow = a.o + b * a.o_sb + (int64_t)qi * a.o_ss + h * a.o_sh;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -554,35 +645,51 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_fp8_kernel(Fp8Args a) {
 
 // Dynamic LDS of one instantiation; its limit is raised once per device (the
 // attribute is set with the device current).
-template <int D, bool REPAIR>
+template <int D, bool REPAIR, bool SPARSE>
 hipError_t launch_fp8_instance(const Fp8Args &a, dim3 grid, hipStream_t st) {
+  using L = Fp8Lds<D, Cfg<SPARSE>::NSTAGE>;
+  const int bytes = SPARSE ? L::sparse_bytes(a.nkb) : L::BYTES;
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> done[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !done[dev].load(std::memory_order_acquire)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_fp8_kernel<D, REPAIR>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, Fp8Lds<D>::BYTES);
+    e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&attn_fwd_fp8_kernel<D, REPAIR, SPARSE>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        SPARSE ? L::sparse_bytes((kSparseMaxSeq + BN - 1) / BN) : L::BYTES);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, REPAIR>), grid, dim3(NT), Fp8Lds<D>::BYTES, st, a);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, REPAIR, SPARSE>), grid, dim3(Cfg<SPARSE>::NT),
+                     bytes, st, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fp8_dim(const Fp8Args &a, dim3 grid, bool repair, hipStream_t st) {
+  if (a.mask) return launch_fp8_instance<D, false, true>(a, grid, st);
+  return repair ? launch_fp8_instance<D, true, false>(a, grid, st)
+                : launch_fp8_instance<D, false, false>(a, grid, st);
 }
 
 }  // namespace
 
-int fwd_fp8_block_rows(int) { return BM; }
+int fwd_fp8_block_rows(bool sparse) { return sparse ? Cfg<true>::BM : Cfg<false>::BM; }
 
-SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu) {
-  const int n_items = ((L.S + BM - 1) / BM) * L.H * L.B;
-  return plan_split(n_items, (L.S + BN - 1) / BN, n_cu, BM, L.D);
+int fwd_fp8_sparse_max_seq() { return kSparseMaxSeq; }
+
+SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu, bool sparse) {
+  const int bm = fwd_fp8_block_rows(sparse);
+  const int wg = sparse ? Cfg<true>::WG_PER_CU : Cfg<false>::WG_PER_CU;
+  const int n_items = ((L.S + bm - 1) / bm) * L.H * L.B;
+  return plan_split(n_items, (L.S + BN - 1) / BN, n_cu * wg, bm, L.D);
 }
 
 hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const float *sq, const void *kv8,
-                          void *o, float *lse, const SplitPlan &plan, void *workspace,
-                          const Fp8Repair &repair, hipStream_t st) {
+                          const uint8_t *mask, void *o, float *lse, const SplitPlan &plan,
+                          void *workspace, const Fp8Repair &repair, hipStream_t st) {
   Fp8Args a;
   a.q = static_cast<const uint8_t *>(q8);
   a.sq = sq;
@@ -597,24 +704,25 @@ hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const float *sq, 
   a.S = L.S;
   a.H = L.H;
   a.B = L.B;
-  a.n_qblk = (L.S + BM - 1) / BM;
+  const int bm = fwd_fp8_block_rows(mask != nullptr);
+  a.n_qblk = (L.S + bm - 1) / bm;
   a.scale_log2 = L.scale_log2;
   a.n_direct = plan.n_direct;
   a.parts = plan.parts;
-  a.ws = split_workspace(plan, workspace, BM, L.D);
+  a.ws = split_workspace(plan, workspace, bm, L.D);
+  a.mask = mask;
+  a.nqb = (L.S + kQueryBlock - 1) / kQueryBlock;
+  a.nkb = (L.S + BN - 1) / BN;
   const dim3 grid((unsigned)(plan.n_direct + plan.n_units));
-  const bool rep = repair.n_rep > 0;
+  const bool rep = repair.n_rep > 0 && mask == nullptr;
   a.kr = static_cast<const bf16 *>(repair.kr);
   a.vr = static_cast<const bf16 *>(repair.vr);
-  a.n_rep = repair.n_rep;
-  a.n_pad = repair_pad(repair.n_rep);
-  hipError_t e;
-  if (L.D == 64)
-    e = rep ? launch_fp8_instance<64, true>(a, grid, st) : launch_fp8_instance<64, false>(a, grid, st);
-  else
-    e = rep ? launch_fp8_instance<128, true>(a, grid, st) : launch_fp8_instance<128, false>(a, grid, st);
+  a.n_rep = rep ? repair.n_rep : 0;
+  a.n_pad = repair_pad(a.n_rep);
+  const hipError_t e = L.D == 64 ? launch_fp8_dim<64>(a, grid, rep, st)
+                                 : launch_fp8_dim<128>(a, grid, rep, st);
   if (e != hipSuccess || plan.n_units == 0) return e;
-  return launch_merge_split(L, plan, a.ws, BM, 1.f, o, lse, st);
+  return launch_merge_split(L, plan, a.ws, bm, 1.f, o, lse, st);
 }
 
 }  // namespace ja

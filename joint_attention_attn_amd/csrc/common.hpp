@@ -132,13 +132,32 @@ __device__ __forceinline__ void prologue_chunk_f64(u32x4 w, double r, const floa
   }
 }
 
+// Eight fp64 values rounded once to bf16 (nearest even), packed.  The
+// nearest fp32 value rounds to the same bf16 unless it lands exactly on a
+// bf16 midpoint (low 16 bits 0x8000) without being the fp64 value itself;
+// only then (about one element in 2^16) the round-to-odd path runs.
+__device__ __forceinline__ u32x4 pack8_bf16_f64(const double (&y)[8]) {
+  float f[8];
+  bool tie = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f[e] = (float)y[e];
+    tie = tie || (__float_as_uint(f[e]) & 0xffffu) == 0x8000u;
+  }
+  if (tie) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = f32_round_odd(y[e]);
+  }
+  return u32x4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+               pack_bf16x2(f[6], f[7])};
+}
+
 // The prologue of a chunk rounded to bf16 (the MFMA operand).
 __device__ __forceinline__ u32x4 prologue_chunk_bf16(u32x4 w, double r, const float *g,
                                                      const double2 *cs) {
   double y[8];
   prologue_chunk_f64(w, r, g, cs, y);
-  return u32x4{pack_bf16x2_f64(y[0], y[1]), pack_bf16x2_f64(y[2], y[3]),
-               pack_bf16x2_f64(y[4], y[5]), pack_bf16x2_f64(y[6], y[7])};
+  return pack8_bf16_f64(y);
 }
 
 // Key held by slot p (0..15) of a 16-key group in the P operand of the P.V
@@ -155,6 +174,44 @@ __host__ __device__ constexpr int vt_key_of_slot(int p) {
 // (the S^T accumulator order), so V^T keeps that key at hf*32 + slot.
 __host__ __device__ constexpr int vt8_pos(int r) {
   return ((r >> 2) & 1) * 32 + (r >> 5) * 16 + ((r >> 3) & 3) * 4 + (r & 3);
+}
+
+// Quotient of a 32-bit numerator by a runtime divisor d >= 1 through a
+// precomputed multiplier (round-up method): q = (umulhi(n, m) + n) >> s with
+// 2^(s-1) < d <= 2^s and m = 2^32 (2^s - d) / d + 1; the add is 64-bit, so
+// every n < 2^32 divides exactly.
+struct FastDiv {
+  uint32_t d = 1, m = 1, s = 0;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  while ((1ull << f.s) < d) ++f.s;
+  f.m = (uint32_t)(((1ull << 32) * ((1ull << f.s) - d)) / d + 1);
+  return f;
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.s);
+}
+
+// Batch row b, token s and head h of head vector `row` of a [B, S, H]
+// sequence of vectors (row = (b S + s) H + h).
+template <bool WIDE>
+__device__ __forceinline__ void split_row(int64_t row, const FastDiv &fh, const FastDiv &fs,
+                                          int64_t &b, int64_t &s, int &h) {
+  if constexpr (WIDE) {
+    h = (int)(row % fh.d);
+    const int64_t t = row / fh.d;
+    s = t % fs.d;
+    b = t / fs.d;
+  } else {
+    const uint32_t r = (uint32_t)row;
+    const uint32_t t = fast_div(r, fh);
+    h = (int)(r - t * fh.d);
+    const uint32_t bb = fast_div(t, fs);
+    s = (int64_t)(t - bb * fs.d);
+    b = bb;
+  }
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

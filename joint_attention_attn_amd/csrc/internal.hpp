@@ -92,14 +92,17 @@ hipError_t launch_prep_kv_fp8(const AttnLayout &L, const void *k8, const void *v
                               const float *sk, const float *sv, const float *kbias, void *kv8,
                               hipStream_t st);
 
-SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu);
+SplitPlan plan_fwd_fp8(const AttnLayout &L, int n_cu, bool sparse);
+// mask: NULL = dense, else the block mask of the block-sparse variant (no
+// repair then), uint8 [B][H][ceil(S/128)][ceil(S/64)].
 hipError_t launch_fwd_fp8(const AttnLayout &L, const void *q8, const float *sq, const void *kv8,
-                          void *o, float *lse, const SplitPlan &plan, void *workspace,
-                          const Fp8Repair &repair, hipStream_t st);
+                          const uint8_t *mask, void *o, float *lse, const SplitPlan &plan,
+                          void *workspace, const Fp8Repair &repair, hipStream_t st);
+int fwd_fp8_sparse_max_seq();    // longest sequence of the block-sparse variant
 
 // Query rows per workgroup of each forward kernel (the grid's x extent is
 // ceil(S / rows)).
 int fwd_bf16_block_rows(bool sparse);
-int fwd_fp8_block_rows(int D);
+int fwd_fp8_block_rows(bool sparse);
 
 }  // namespace ja

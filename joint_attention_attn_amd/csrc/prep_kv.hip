@@ -74,20 +74,16 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
                                                  (int64_t)key * a.v_ss + 8 * c);
       }
     }
-    double2 cs[4];
-    const bool rot = ROPE && key < a.S;
-    if (rot) {
-      const double2 *t = a.rope + (int64_t)key * (D / 2) + 4 * c;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cs[e] = t[e];
-    }
+    // the key's 4 table entries (a global pointer: the loads stay in
+    // registers across the HG heads)
+    const double2 *cs = ROPE && key < a.S ? a.rope + (int64_t)key * (D / 2) + 4 * c : nullptr;
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
       u32x4 x = kw[g];
       if (a.kn) {
         const double ss = chunk_sum_lanes_f64<CH>(chunk_sumsq_f64(x));
-        x = prologue_chunk_bf16(x, rms_scale_f64<D>(ss, a.eps), a.kn + 8 * c, rot ? cs : nullptr);
-      } else if (rot) {
+        x = prologue_chunk_bf16(x, rms_scale_f64<D>(ss, a.eps), a.kn + 8 * c, cs);
+      } else if (cs) {
         x = prologue_chunk_bf16(x, 0.0, nullptr, cs);
       }
       *reinterpret_cast<u32x4 *>(a.kr + ((bh0 + g) * a.S_pad + key) * D + 8 * c) = x;

@@ -40,18 +40,29 @@ struct QuantArgs {
   float eps;
   int S, H;
   int64_t rows;  // B * S * H
+  FastDiv fh, fs;  // division by H and by S
 };
 
 constexpr int RPT = 2;        // head vectors per lane
 
-// Four fp32 values (each already the single rounding of the value to code,
-// to odd) -> packed e4m3, saturated at +-448.
+// Four fp32 values -> packed e4m3 (nearest even), saturated at +-448.
 __device__ __forceinline__ uint32_t pack_e4m3x4(const float (&y)[4]) {
   float c[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) c[j] = fminf(fmaxf(y[j], -448.f), 448.f);
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+}
+
+// Whether an fp32 value lies within `ulps` of an e4m3 rounding midpoint (or
+// in e4m3's subnormal range, where the midpoints are spaced differently):
+// there the e4m3 rounding of the value and of a value `ulps` away may differ.
+// In the normal range a midpoint has a 1 in mantissa bit 19 and zeros below.
+__device__ __forceinline__ bool near_e4m3_midpoint(float f, uint32_t ulps) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t low = u & 0xfffffu;
+  const bool tiny = (u & 0x7fffffffu) < 0x3c800000u && (u & 0x7fffffffu) != 0u;  // 0 < |f| < 2^-6
+  return tiny || (low + ulps - 0x80000u) <= 2u * ulps;
 }
 
 // x / scale rounded to odd in fp32, from the correctly rounded quotient and
@@ -69,15 +80,14 @@ __device__ __forceinline__ float div_round_odd(float x, float scale) {
   return __uint_as_float(u);
 }
 
-template <int D>
+template <int D, bool WIDE>
 __device__ __forceinline__ void quant_row(const QuantArgs &a, int t, int64_t row, int sub,
                                           u32x4 w) {
   constexpr int LPR = D / 8;  // lanes per head vector
   const bool live = row < a.rows;
-  const int64_t rr = live ? row : 0;
-  const int h = (int)(rr % a.H);
-  const int64_t s = (rr / a.H) % a.S;
-  const int64_t b = rr / ((int64_t)a.H * a.S);
+  int64_t b, s;
+  int h;
+  split_row<WIDE>(live ? row : 0, a.fh, a.fs, b, s, h);
   float scale = 1.f;
   uint32_t packed[2];
   if (t < 2) {
@@ -102,13 +112,21 @@ __device__ __forceinline__ void quant_row(const QuantArgs &a, int t, int64_t row
       k = max(e2 - 8 + ((ab & 0xfffffffffffffull) > 0xc000000000000ull ? 1 : 0), -126);
       scale = __uint_as_float((uint32_t)(127 + k) << 23);
     }
+    // codes of y 2^-k: the nearest fp32 value rounds to the same e4m3 unless
+    // it is itself a midpoint (then round to odd from the fp64 value)
+    float v[8];
+    bool tie = false;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = f32_round_odd(__builtin_ldexp(y[4 * e + j], -k));
-      packed[e] = pack_e4m3x4(v);
+    for (int e = 0; e < 8; ++e) {
+      v[e] = (float)__builtin_ldexp(y[e], -k);
+      tie = tie || near_e4m3_midpoint(v[e], 0);
     }
+    if (tie) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = f32_round_odd(__builtin_ldexp(y[e], -k));
+    }
+    packed[0] = pack_e4m3x4({v[0], v[1], v[2], v[3]});
+    packed[1] = pack_e4m3x4({v[4], v[5], v[6], v[7]});
   } else {
     // V: exact in fp32; scale = amax / 448
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
@@ -124,13 +142,24 @@ __device__ __forceinline__ void quant_row(const QuantArgs &a, int t, int64_t row
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if (amax > 0.f) scale = amax / 448.f;
+    // x / scale through the reciprocal: within two fp32 ulps of the exact
+    // quotient (two roundings of 2^-24), so its e4m3 rounding is the exact
+    // one unless it sits within three ulps of a midpoint; only then the
+    // correctly rounded division
+    const float inv = 1.f / scale;
+    float v[8];
+    bool near = false;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = div_round_odd(x[4 * e + j], scale);
-      packed[e] = pack_e4m3x4(v);
+    for (int e = 0; e < 8; ++e) {
+      v[e] = x[e] * inv;
+      near = near || near_e4m3_midpoint(v[e], 3);
     }
+    if (near) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = div_round_odd(x[e], scale);
+    }
+    packed[0] = pack_e4m3x4({v[0], v[1], v[2], v[3]});
+    packed[1] = pack_e4m3x4({v[4], v[5], v[6], v[7]});
   }
   if (live) {
     *reinterpret_cast<u32x2 *>(a.x8[t] + row * D + sub * 8) = u32x2{packed[0], packed[1]};
@@ -139,7 +168,8 @@ __device__ __forceinline__ void quant_row(const QuantArgs &a, int t, int64_t row
 }
 
 // Workgroup of 256 lanes: RPT blocks of 256 / LPR consecutive head vectors.
-template <int D>
+// WIDE: more than 2^32 head vectors (64-bit index arithmetic).
+template <int D, bool WIDE>
 __global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
   constexpr int LPR = D / 8;
   constexpr int ROWS = 256 / LPR;
@@ -150,15 +180,22 @@ __global__ __launch_bounds__(256) void quant_rope_fp8_kernel(QuantArgs a) {
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
     const int64_t row = row0 + j * ROWS;
-    const int64_t rr = row < a.rows ? row : 0;
-    const int h = (int)(rr % a.H);
-    const int64_t s = (rr / a.H) % a.S;
-    const int64_t b = rr / ((int64_t)a.H * a.S);
+    int64_t b, s;
+    int h;
+    split_row<WIDE>(row < a.rows ? row : 0, a.fh, a.fs, b, s, h);
     w[j] = *reinterpret_cast<const u32x4 *>(a.x[t] + b * a.sb[t] + s * a.ss[t] + h * a.sh[t] +
                                             sub * 8);
   }
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) quant_row<D>(a, t, row0 + j * ROWS, sub, w[j]);
+  for (int j = 0; j < RPT; ++j) quant_row<D, WIDE>(a, t, row0 + j * ROWS, sub, w[j]);
+}
+
+template <int D>
+void launch_quant(const QuantArgs &a, dim3 grid, hipStream_t st) {
+  if (a.rows >= (1ll << 32))
+    hipLaunchKernelGGL((quant_rope_fp8_kernel<D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((quant_rope_fp8_kernel<D, false>), grid, dim3(256), 0, st, a);
 }
 
 }  // namespace
@@ -188,12 +225,14 @@ hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,
   a.S = L.S;
   a.H = L.H;
   a.rows = (int64_t)L.B * L.S * L.H;
+  a.fh = make_fastdiv((uint32_t)L.H);
+  a.fs = make_fastdiv((uint32_t)L.S);
   const int64_t rows_per_wg = (256 / (L.D / 8)) * RPT;
   const dim3 grid((unsigned)((a.rows + rows_per_wg - 1) / rows_per_wg), 3);
   if (L.D == 64)
-    hipLaunchKernelGGL(quant_rope_fp8_kernel<64>, grid, dim3(256), 0, st, a);
+    launch_quant<64>(a, grid, st);
   else
-    hipLaunchKernelGGL(quant_rope_fp8_kernel<128>, grid, dim3(256), 0, st, a);
+    launch_quant<128>(a, grid, st);
   return hipGetLastError();
 }
 

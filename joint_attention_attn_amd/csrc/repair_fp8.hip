@@ -44,6 +44,7 @@ struct ErrArgs {
   float *err;                   // [B][H][S]
   int S, H;
   int64_t rows;                 // B * S * H
+  FastDiv fh, fs;               // division by H and by S
 };
 
 // Max over the 8 elements of a chunk of |x - value(code) * scale| in fp64
@@ -65,17 +66,16 @@ __device__ __forceinline__ double chunk_error(const double (&x)[8], u32x2 codes,
   return e;
 }
 
-template <int D>
+template <int D, bool WIDE>
 __global__ __launch_bounds__(256) void repair_err_kernel(ErrArgs a) {
   constexpr int LPR = D / 8;  // lanes per head vector
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = gid / LPR;
   const int sub = (int)(gid % LPR);
   const bool live = row < a.rows;
-  const int64_t rr = live ? row : 0;
-  const int h = (int)(rr % a.H);
-  const int64_t s = (rr / a.H) % a.S;
-  const int64_t b = rr / ((int64_t)a.H * a.S);
+  int64_t b, s;
+  int h;
+  split_row<WIDE>(live ? row : 0, a.fh, a.fs, b, s, h);
   const int64_t sidx = (b * a.H + h) * a.S + s;
 
   // the key as the quantizer saw it: normalized, then rotated (fp64)
@@ -238,12 +238,14 @@ hipError_t launch_repair_plan(const AttnLayout &L, const void *k, const void *v,
   e.S = L.S;
   e.H = L.H;
   e.rows = (int64_t)L.B * L.S * L.H;
+  e.fh = make_fastdiv((uint32_t)L.H);
+  e.fs = make_fastdiv((uint32_t)L.S);
   const int64_t threads = e.rows * (L.D / 8);
   const dim3 grid((unsigned)((threads + 255) / 256));
-  if (L.D == 64)
-    hipLaunchKernelGGL(repair_err_kernel<64>, grid, dim3(256), 0, st, e);
-  else
-    hipLaunchKernelGGL(repair_err_kernel<128>, grid, dim3(256), 0, st, e);
+  const bool wide = e.rows >= (1ll << 32);
+  void (*err_kernel)(ErrArgs) = L.D == 64 ? (wide ? repair_err_kernel<64, true> : repair_err_kernel<64, false>)
+                                          : (wide ? repair_err_kernel<128, true> : repair_err_kernel<128, false>);
+  hipLaunchKernelGGL(err_kernel, grid, dim3(256), 0, st, e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

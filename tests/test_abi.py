@@ -363,6 +363,28 @@ def test_block_sparse_validation(lib):
     assert ja.block_mask_shape(2, 300, 3) == (2, 3, 3, 5)
 
 
+def test_fp8_block_sparse_validation(lib):
+    def call(p, mask=FAKE + 0x7000, o=FAKE + 0x6000):
+        return lib.joint_attn_fwd_fp8_block_sparse(
+            ctypes.byref(p), vp(FAKE), vp(FAKE + 0x1000), vp(FAKE + 0x2000), vp(FAKE + 0x3000),
+            vp(FAKE + 0x4000), vp(FAKE + 0x5000), vp(mask), vp(o), None, vp(FAKE + 0x8000), BIG,
+            None)
+
+    def call_prepared(p, mask=FAKE + 0x7000):
+        return lib.joint_attn_fwd_fp8_block_sparse_prepared(
+            ctypes.byref(p), vp(FAKE), vp(FAKE + 0x1000), vp(FAKE + 0x2000), BIG, vp(mask),
+            vp(FAKE + 0x6000), None, None, 0, None)
+
+    assert call(_p(), mask=0) == INV
+    assert call_prepared(_p(), mask=0) == INV
+    assert call(_p(), o=FAKE) == INV                                    # o aliases q8
+    assert call(_p(s=(1 << 20) + 1)) == UNS
+    assert call_prepared(_p(s=(1 << 20) + 1)) == UNS
+    bad = _p()
+    bad.head_dim = 96
+    assert call(bad) == UNS
+
+
 def test_norm_validation(lib):
     p = _p()
     p.norm_eps = -1.0
