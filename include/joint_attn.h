@@ -304,7 +304,7 @@ ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q, const voi
  *               quantizer's): their exponents are the E8M0 block scales of
  *               the Q K^T MFMA.  sv must be positive and finite.  Rows that
  *               meet another value come back NaN (O and LSE): a bad sq value
- *               poisons the rows of its 384-query block, a bad sk or sv value
+ *               poisons the rows of its 128-query block, a bad sk or sv value
  *               every row of its (batch, head).
  *   o           device bf16, layout per ja_params (o_* strides).
  *   lse         device float [batch][heads][seq_len], nullable.

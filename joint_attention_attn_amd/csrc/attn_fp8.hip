@@ -20,22 +20,21 @@
 // a repaired key starts at -inf.  Per score this leaves a max, an FMA, an
 // exp2, the sum's FMA and half a conversion.
 //
-// Structure as in the bf16 kernel: one workgroup of twelve wave64s (three
-// per SIMD) per (384-query block, head, batch row), XCD-aware placement,
-// split of the last round.  A preparation pass (prep_kv_fp8.hip) writes each
-// (batch, head)'s K, V^T and per-key values in the layouts of the LDS tiles;
-// buffer loads to LDS copy 64-key tiles into a 4-stage ring three tiles
-// ahead, with no staging registers and no vector work.  Each wave runs
-// Q K^T, softmax and P.V of a tile in turn, and the three waves of a SIMD
-// overlap one another's matrix and vector work.
+// Structure: one workgroup of four wave64s per (128-query block, head,
+// batch row), three workgroups per CU (three waves per SIMD), XCD-aware
+// placement, split of the last round.  A preparation pass (prep_kv_fp8.hip)
+// writes each (batch, head)'s K, V^T and per-key values in the layouts of
+// the LDS tiles; buffer loads to LDS copy 64-key tiles into a 3-stage ring
+// two tiles ahead, with no staging registers and no vector work.  Each wave
+// runs Q K^T, softmax and P.V of a tile in turn, and the three waves of a
+// SIMD (from three workgroups) overlap one another's matrix and vector work.
 //
 // Block-sparse variant (the pages' general block-sparse attention kernel,
 // section "Quantized and sparse attention", on a given mask of 128-query x
-// 64-key blocks): a workgroup of four waves covers one 128-row query block,
-// three workgroups share a CU over 3-stage rings; the workgroup compacts the
-// list of key blocks its query block keeps into LDS and stages only those
-// tiles (one 64-key tile is one key block).  Rows that keep no key get O = 0
-// and LSE = -inf.
+// 64-key blocks): the workgroup (one query block) compacts the list of key
+// blocks its query block keeps into LDS and stages only those tiles (one
+// 64-key tile is one key block).  Rows that keep no key get O = 0 and
+// LSE = -inf.
 #include <atomic>
 
 #include "common.hpp"
@@ -49,19 +48,23 @@ namespace {
 
 constexpr int BN = 64;              // keys per K/V tile (the MFMA's K extent)
 
-// Workgroup shape.  Dense: twelve waves of 32 query rows, three per SIMD (at
-// most 168 VGPRs each), over a 4-stage ring three tiles ahead.  Software
+// Workgroup shape: four waves of 32 query rows (one 128-row query block),
+// three workgroups per CU, so three waves per SIMD (at most 168 VGPRs each),
+// each workgroup over its own 3-stage ring two tiles ahead.  The three
+// workgroups of a CU keep their own barriers, so the waves of a SIMD drift
+// apart and one's matrix work overlaps another's vector work; one twelve-wave
+// workgroup sharing a 4-stage ring (each tile staged once per CU) keeps them
+// in step and is 7 % slower at 16896 tokens, 12 % at 4608.  Software
 // pipelining inside a wave (Q K^T of the next tile issued ahead of this
 // tile's softmax) would keep two tiles of accumulators live, about 245
-// VGPRs, and allow only two waves per SIMD, which is slower.  Block-sparse:
-// one 128-row query block per workgroup of four waves, three workgroups per
-// CU over 3-stage rings two tiles ahead.
+// VGPRs, and allow only two waves per SIMD.  The block-sparse variant has
+// the same shape; its workgroup stages the key blocks its query block keeps.
 template <bool SPARSE>
 struct Cfg {
-  static constexpr int NW = SPARSE ? 4 : 12;      // waves per workgroup
-  static constexpr int NSTAGE = SPARSE ? 3 : 4;   // K/V tiles in the LDS ring
+  static constexpr int NW = 4;                    // waves per workgroup
+  static constexpr int NSTAGE = 3;                // K/V tiles in the LDS ring
   static constexpr int PREF = NSTAGE - 1;         // tiles issued ahead
-  static constexpr int WG_PER_CU = SPARSE ? 3 : 1;
+  static constexpr int WG_PER_CU = 3;
   static constexpr int BM = 32 * NW;              // query rows per workgroup
   static constexpr int NT = 64 * NW;              // threads per workgroup
 };
@@ -153,6 +156,20 @@ __host__ __device__ constexpr int ksw(int r) {
   return D == 128 ? (r ^ (r >> 3)) & 7 : ((r >> 1) ^ (r >> 3)) & 3;
 }
 
+// The rows of the second 32-key block of a tile (r + 32) carry the swizzle
+// of row r XOR a constant that flips only the granule bit of the 64-byte
+// step kk, so a lane's reads of that block use the addresses of its reads of
+// the first block with kk swapped, plus 32 rows.
+template <int D>
+__host__ __device__ constexpr int ksw_flip() { return ksw<D>(32) ^ ksw<D>(0); }
+template <int D>
+constexpr bool ksw_flip_uniform() {
+  for (int r = 0; r < 32; ++r)
+    if ((ksw<D>(r + 32) ^ ksw<D>(r)) != ksw_flip<D>()) return false;
+  return ksw_flip<D>() % 4 == 0 && (ksw_flip<D>() >> 2) < D / 64 + (D == 64);
+}
+static_assert(ksw_flip_uniform<64>() && ksw_flip_uniform<128>(), "second key block swizzle");
+
 template <int D, int NSTAGE>
 struct Fp8Lds {
   static constexpr int CH = D / 16;                    // 16-byte granules per K row
@@ -177,12 +194,9 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   constexpr int NSTAGE = Cfg<SPARSE>::NSTAGE, PREF = Cfg<SPARSE>::PREF;
   using L = Fp8Lds<D, NSTAGE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem8[];
-  auto Kst = [&](int st) JA_INLINE { return smem8 + st * L::STAGE; };
-  auto Vst = [&](int st) JA_INLINE { return smem8 + st * L::STAGE + L::KBYTES; };
-  // per-key values of a stage: bias (fp32), then inv (fp32), then ke (int32)
-  auto Ist = [&](int st) JA_INLINE {
-    return reinterpret_cast<const float *>(smem8 + st * L::STAGE + L::KBYTES + L::VBYTES);
-  };
+  // per-key values of stage 0: bias (fp32), then inv (fp32), then ke (int32)
+  // and the softmax scale they were prepared for
+  const float *info0 = reinterpret_cast<const float *>(smem8 + L::KBYTES + L::VBYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -272,7 +286,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   const float c = a.scale_log2;
   const float qmul = sqv * c;
 
-  // ---- staging: wave w issues loads w, w + NW, w + 2 NW of each tile ----
+  // ---- staging of a tile: K, V^T, per-key values (loads of 1 KB) ----
   const int span_k = a.S_pad * D, span_i = a.S_pad / BN * INFO_BYTES;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t *>(a.k8 + bh * a.S_pad * D), 0, span_k, kBufferFlags);
@@ -295,74 +309,98 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
     }
     return 16 * lane;
   };
-  constexpr int JW = (L::LOADS + NW - 1) / NW;         // loads per wave, at most
-  static_assert(JW <= 5, "loads per wave");
-  // (scalar offsets: an array element as the builtin's offset operand makes
-  // the host compilation drop the kernel's launch stub without a message)
-  auto voff_of = [&](int m) JA_INLINE -> int {
-    return wave + m * NW < L::LOADS ? load_offset(wave + m * NW) : 0;
-  };
-  const int voff0 = voff_of(0), voff1 = voff_of(1), voff2 = voff_of(2), voff3 = voff_of(3),
-            voff4 = voff_of(4);
-  const int nl = (L::LOADS - wave + NW - 1) / NW;      // loads of this wave per tile
-  auto issue_one = [&](int j, int voff, int t, int st) JA_INLINE {
-    char *dst = reinterpret_cast<char *>(smem8) + st * L::STAGE + j * 1024;
-    if (j < L::K_LOADS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, JA_LDS_PTR(dst), 16, voff, t * (BN * D), 0, 0);
-    else if (j < L::K_LOADS + L::V_LOADS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, JA_LDS_PTR(dst), 16, voff, t * BN, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, JA_LDS_PTR(dst), 16, voff, t * INFO_BYTES, 0, 0);
-  };
-  // loads of key tile t into stage st (a wave past the tile's load count
-  // issues none)
+  // Wave w issues K loads w + NW m (m < MK), then V loads K_LOADS + w + NW m
+  // (m < MV); wave 0 also issues the per-key values.  Successive V loads of a
+  // wave are 16 NW head-dimension rows apart with the same swizzle, so they
+  // share one offset register and differ by a scalar offset.  (Scalar
+  // variables: an array element as the builtin's offset operand makes the
+  // host compilation drop the kernel's launch stub without a message.)
+  constexpr int MK = L::K_LOADS / NW, MV = L::V_LOADS / NW;
+  static_assert(L::K_LOADS % NW == 0 && L::V_LOADS % NW == 0 && MK <= 2, "load split");
+  static_assert(vswz8(16 * NW) == 0, "V loads of a wave share the swizzle");
+  const int koff0 = load_offset(wave);
+  const int koff1 = MK > 1 ? load_offset(wave + NW) : 0;
+  const int voff = load_offset(L::K_LOADS + wave);
   auto issue = [&](int t, int st) JA_INLINE {
-    if (0 < nl) issue_one(wave, voff0, t, st);
-    if (JW > 1 && 1 < nl) issue_one(wave + NW, voff1, t, st);
-    if (JW > 2 && 2 < nl) issue_one(wave + 2 * NW, voff2, t, st);
-    if (JW > 3 && 3 < nl) issue_one(wave + 3 * NW, voff3, t, st);
-    if (JW > 4 && 4 < nl) issue_one(wave + 4 * NW, voff4, t, st);
+    char *base = reinterpret_cast<char *>(smem8) + st * L::STAGE;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, JA_LDS_PTR(base + wave * 1024), 16, koff0,
+                                             t * (BN * D), 0, 0);
+    if constexpr (MK > 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, JA_LDS_PTR(base + (wave + NW) * 1024), 16,
+                                               koff1, t * (BN * D), 0, 0);
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          vrs, JA_LDS_PTR(base + (L::K_LOADS + wave + NW * m) * 1024), 16, voff,
+          t * BN + m * (16 * NW) * a.S_pad, 0, 0);
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(irs, JA_LDS_PTR(base + (L::LOADS - 1) * 1024), 16,
+                                               lane * 16, t * INFO_BYTES, 0, 0);
   };
   // wait until at most `AHEAD` later tiles' loads of this wave are in flight
   auto wait_tiles = [&]<int AHEAD>() JA_INLINE {
-    if (JW > 4 && nl == 5)
-      wait_vmcnt<5 * AHEAD>();
-    else if (JW > 3 && nl == 4)
-      wait_vmcnt<4 * AHEAD>();
-    else if (JW > 2 && nl == 3)
-      wait_vmcnt<3 * AHEAD>();
-    else if (JW > 1 && nl == 2)
-      wait_vmcnt<2 * AHEAD>();
+    if (wave == 0)
+      wait_vmcnt<(MK + MV + 1) * AHEAD>();
     else
-      wait_vmcnt<AHEAD>();
+      wait_vmcnt<(MK + MV) * AHEAD>();
   };
 
   // ---- S^T = K8 . Q8^T for the 64 keys of a tile (two 32-key blocks), the
   //      K and Q scales applied as E8M0 block scales, each accumulator
   //      starting at its key's bias (element i of a lane is key
   //      kb*32 + 8(i/4) + 4hf + i%4): acc = sk sq K8.Q8 + log2(sv)/c ----
+  // per-lane byte offsets of the fragment reads inside a stage, opaque to
+  // the compiler: each read address is one add of the stage base, the rest
+  // sits in the read's immediate offset.  kro[2j + half]: K granule
+  // 4j + 2hf + half of row l32; vro[half]: V^T granule 2hf + half of row
+  // l32; iro: this lane half's per-key values; ero: key l32's K exponent.
+  int kro[D / 32], vro[2];
+  {
+    const int ks = ksw<D>(l32), vsw = vswz8(l32);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        kro[2 * j + half] = l32 * D + 16 * ((4 * j + 2 * hf + half) ^ ks);
+        asm volatile("" : "+v"(kro[2 * j + half]));
+      }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      vro[half] = L::KBYTES + l32 * BN + 16 * ((2 * hf + half) ^ vsw);
+      asm volatile("" : "+v"(vro[half]));
+    }
+  }
+  int iro = L::KBYTES + L::VBYTES + 16 * hf;
+  int ero = L::KBYTES + L::VBYTES + 2 * BN * 4 + 4 * l32;
+  asm volatile("" : "+v"(iro), "+v"(ero));
+  constexpr int KFLIP = ksw_flip<D>() >> 2;
+  auto lds_at = [&](int st, int off) JA_INLINE { return smem8 + st * L::STAGE + off; };
+
+  // ---- S^T = K8 . Q8^T for the 64 keys of a tile (two 32-key blocks), the
+  //      K and Q scales applied as E8M0 block scales, each accumulator
+  //      starting at its key's bias (element i of a lane is key
+  //      kb*32 + 8(i/4) + 4hf + i%4): acc = sk sq K8.Q8 + log2(sv)/c ----
   auto qk = [&](int st, f32x16 (&sacc)[2]) JA_INLINE {
-    const float *bias = Ist(st);
-    const int *ke = reinterpret_cast<const int *>(Ist(st) + 2 * BN);
+    const uint8_t *ib = lds_at(st, iro);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 bg = *reinterpret_cast<const float4 *>(bias + kb * 32 + g * 8 + hf * 4);
+        const float4 bg = *reinterpret_cast<const float4 *>(ib + 4 * (kb * 32 + g * 8));
         sacc[kb][4 * g] = bg.x;
         sacc[kb][4 * g + 1] = bg.y;
         sacc[kb][4 * g + 2] = bg.z;
         sacc[kb][4 * g + 3] = bg.w;
       }
-      const int kex = ke[kb * 32 + l32];            // A row l32 is key kb*32 + l32
-      const int krw = kb * 32 + l32;
-      const uint8_t *krow = Kst(st) + krw * D;
-      const int ks = ksw<D>(krw);
+      // A row l32 is key kb*32 + l32
+      const int kex = *reinterpret_cast<const int *>(lds_at(st, ero) + 4 * 32 * kb);
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk) {
-        const int g0 = 4 * kk + 2 * hf;
-        const i32x4 lo = *reinterpret_cast<const i32x4 *>(krow + 16 * (g0 ^ ks));
-        const i32x4 hi = *reinterpret_cast<const i32x4 *>(krow + 16 * ((g0 + 1) ^ ks));
+        const int j = kb ? kk ^ KFLIP : kk;
+        const i32x4 lo =
+            *reinterpret_cast<const i32x4 *>(lds_at(st, kro[2 * j]) + kb * 32 * D);
+        const i32x4 hi =
+            *reinterpret_cast<const i32x4 *>(lds_at(st, kro[2 * j + 1]) + kb * 32 * D);
         sacc[kb] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qreg[kk],
                             sacc[kb], kex, qe);
       }
@@ -376,13 +414,12 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
     for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
   // ---- O^T += V8^T . P'^T: lane (l32, hf) reads the logical granules 2hf
   //      and 2hf+1 of V^T row db*32 + l32, whose swizzle is vswz8(l32) ----
-  const int vsw = vswz8(l32);
+  static_assert(vswz8(32) == 0, "V^T row blocks share the swizzle");
   auto pv = [&](const i32x8 &pb, int st) JA_INLINE {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint8_t *vrow = Vst(st) + (db * 32 + l32) * BN;
-      const i32x4 lo = *reinterpret_cast<const i32x4 *>(vrow + 16 * ((2 * hf) ^ vsw));
-      const i32x4 hi = *reinterpret_cast<const i32x4 *>(vrow + 16 * ((2 * hf + 1) ^ vsw));
+      const i32x4 lo = *reinterpret_cast<const i32x4 *>(lds_at(st, vro[0]) + db * 32 * BN);
+      const i32x4 hi = *reinterpret_cast<const i32x4 *>(lds_at(st, vro[1]) + db * 32 * BN);
       oacc[db] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, pb, oacc[db]);
     }
   };
@@ -405,7 +442,8 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 ig = *reinterpret_cast<const float4 *>(Ist(buf) + BN + kb * 32 + g * 8 + hf * 4);
+        const float4 ig =
+            *reinterpret_cast<const float4 *>(lds_at(buf, iro) + 4 * (BN + kb * 32 + g * 8));
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][4 * g + i], c, nref));
@@ -464,7 +502,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
     wait_vmcnt<0>();
     tile_barrier();
     // the per-key values were prepared for this softmax scale
-    bad = bad || Ist(0)[3 * BN] != c;
+    bad = bad || info0[3 * BN] != c;
   }
   f32x16 sacc[2];
   auto iteration = [&]<bool LAST>(int i) JA_INLINE {
@@ -498,11 +536,16 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
       constexpr int VBS = 32 + 8;         // bf16 per staged V^T row
       bf16 *kbuf = reinterpret_cast<bf16 *>(smem8);
       bf16 *vbuf = reinterpret_cast<bf16 *>(smem8 + 32 * KBS * 2);
-      // Q codes in the bf16 operand layout: lane half hf holds d = 16kk + 8hf + 0..7
-      bf16x8 qb[D / 16];
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        const u32x2 cw = *reinterpret_cast<const u32x2 *>(qrow + 16 * kk + 8 * hf);
+      // Q codes in the bf16 operand layout: lane half hf holds d = 16kk + 8hf
+      // + 0..7 (decoded for each 32-key block rather than held: the registers
+      // are the O accumulators')
+      // the row address is formed again from qi (kept opaque so that the
+      // compiler does not hold the 64-bit address through the tile loop)
+      int qr = qi < S ? qi : S - 1;
+      asm volatile("" : "+v"(qr));
+      const uint8_t *qrow_r = a.q + ((int64_t)b * S + qr) * row_stride + (int64_t)h * D;
+      auto q_operand = [&](int kk) JA_INLINE -> bf16x8 {
+        const u32x2 cw = *reinterpret_cast<const u32x2 *>(qrow_r + 16 * kk + 8 * hf);
         float f[8];
         f[0] = __builtin_amdgcn_cvt_f32_fp8((int)cw.x, 0);
         f[1] = __builtin_amdgcn_cvt_f32_fp8((int)cw.x, 1);
@@ -515,19 +558,19 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
         u32x4 w = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                    pack_bf16x2(f[6], f[7])};
         if (qi >= S) w = u32x4{0, 0, 0, 0};
-        qb[kk] = bit_cast<bf16x8>(w);
-      }
+        return bit_cast<bf16x8>(w);
+      };
       const bf16 *krb = a.kr + bh * a.n_pad * D;
       const bf16 *vrb = a.vr + bh * a.n_pad * D;
       for (int r0 = 0; r0 < a.n_pad; r0 += 32) {
         // stage 32 keys: K row-major, V transposed in the P operand's key order
-        if (tid < 32 * (D / 8)) {
-          const int r = tid / (D / 8), ch = tid % (D / 8);
+        for (int task = tid; task < 32 * (D / 8); task += NT) {
+          const int r = task / (D / 8), ch = task % (D / 8);
           *reinterpret_cast<u32x4 *>(kbuf + r * KBS + ch * 8) =
               *reinterpret_cast<const u32x4 *>(krb + (int64_t)(r0 + r) * D + ch * 8);
         }
-        if (tid < D * 4) {
-          const int vd = tid % D, vc = tid / D;
+        for (int task = tid; task < D * 4; task += NT) {
+          const int vd = task % D, vc = task / D;
           uint32_t hv[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j)
@@ -544,7 +587,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           const bf16x8 kv = *reinterpret_cast<const bf16x8 *>(kbuf + l32 * KBS + 16 * kk + 8 * hf);
-          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[kk], st, 0, 0, 0);
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, q_operand(kk), st, 0, 0, 0);
         }
         // accumulator row i is key r0 + 8(i/4) + 4hf + i%4; rows past n are padding
         float tmax = -INFINITY;

@@ -148,7 +148,7 @@ def test_prep_kv_fp8_layout(s, d, rep):
 def test_fp8_forward_poisons_rows_of_non_power_of_two_scales(which):
     # Q and K scales must be powers of two (the MFMA applies their exponent);
     # a violation turns the affected rows into NaN: every row of the head for
-    # a K scale, the workgroup's 384-row query block for a Q scale.  Other
+    # a K scale, the workgroup's 128-row query block for a Q scale.  Other
     # heads are untouched.
     w = synth.Workload("badscale", 1, 2, 64, n_text=500, grid=0)
     q, k, v, _ = synth.make_qkv(w, seed=3)
@@ -168,8 +168,8 @@ def test_fp8_forward_poisons_rows_of_non_power_of_two_scales(which):
     if which == "k":
         assert torch.isnan(head1).all() and torch.isnan(lse[:, 1]).all()
     else:
-        assert torch.isnan(head1[:, :384]).all() and torch.isnan(lse[:, 1, :384]).all()
-        assert not torch.isnan(head1[:, 384:]).any()
+        assert torch.isnan(head1[:, :128]).all() and torch.isnan(lse[:, 1, :128]).all()
+        assert not torch.isnan(head1[:, 128:]).any()
 
 
 @pytest.mark.parametrize("which", ["k", "q"])
@@ -196,7 +196,7 @@ def test_fp8_forward_poisons_rows_in_split_items(which):
     if which == "k":
         assert torch.isnan(last).all() and torch.isnan(lse[:, h_last]).all()
     else:
-        r0 = (s - 1) // 384 * 384
+        r0 = (s - 1) // 128 * 128
         assert torch.isnan(last[:, r0:]).all() and torch.isnan(lse[:, h_last, r0:]).all()
         assert not torch.isnan(last[:, :r0]).any()
 
