@@ -16,7 +16,9 @@
 // domain, and P'.V8 is P.V in true units.  The running max of c acc is
 // refreshed whenever a row max grows by more than 3, and the reference sits
 // 5 below it, so P' stays below 2^8, inside the e4m3 range.  The softmax
-// normaliser sums the unquantized fp32 P' / sv[key].  A key past the end or
+// normaliser sums the unquantized fp32 P' / sv[key] (a key with a small V
+// scale has a small P', which can vanish in e4m3 while its probability is
+// large, so the sum must not use the rounded P').  A key past the end or
 // a repaired key starts at -inf.  Per score this leaves a max, an FMA, an
 // exp2, the sum's FMA and half a conversion.
 //
@@ -114,7 +116,8 @@ struct Fp8Args {
 
 // Formats 0 = fp8 e4m3 for both operands; sa / sb are E8M0 exponents (127 =
 // x1): lane (l32, hf) gives the scale of A row l32 and of B column l32 for
-// the 32-element k-block hf (checked on hardware).
+// the 32-element k-block hf, and k-block s is operand dwords 4s..4s+3 of
+// every lane, of both lane halves (both checked on hardware).
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
@@ -135,7 +138,10 @@ __device__ __forceinline__ int e8m0_of(float s, bool &bad) {
 __device__ __forceinline__ float half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                                   false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  // a plain v_max_f32 (fmaxf would first canonicalize both swapped values)
+  float m;
+  asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  return m;
 }
 __device__ __forceinline__ float half_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
@@ -374,14 +380,15 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   int ero = L::KBYTES + L::VBYTES + 2 * BN * 4 + 4 * l32;
   asm volatile("" : "+v"(iro), "+v"(ero));
   constexpr int KFLIP = ksw_flip<D>() >> 2;
-  auto lds_at = [&](int st, int off) JA_INLINE { return smem8 + st * L::STAGE + off; };
+  // address of byte `off` of the stage that starts at byte sb (uniform)
+  auto lds_at = [&](int sb, int off) JA_INLINE { return smem8 + sb + off; };
 
   // ---- S^T = K8 . Q8^T for the 64 keys of a tile (two 32-key blocks), the
   //      K and Q scales applied as E8M0 block scales, each accumulator
   //      starting at its key's bias (element i of a lane is key
   //      kb*32 + 8(i/4) + 4hf + i%4): acc = sk sq K8.Q8 + log2(sv)/c ----
-  auto qk = [&](int st, f32x16 (&sacc)[2]) JA_INLINE {
-    const uint8_t *ib = lds_at(st, iro);
+  auto qk = [&](int sb, f32x16 (&sacc)[2]) JA_INLINE {
+    const uint8_t *ib = lds_at(sb, iro);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -393,14 +400,14 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
         sacc[kb][4 * g + 3] = bg.w;
       }
       // A row l32 is key kb*32 + l32
-      const int kex = *reinterpret_cast<const int *>(lds_at(st, ero) + 4 * 32 * kb);
+      const int kex = *reinterpret_cast<const int *>(lds_at(sb, ero) + 4 * 32 * kb);
 #pragma unroll
       for (int kk = 0; kk < D / 64; ++kk) {
         const int j = kb ? kk ^ KFLIP : kk;
         const i32x4 lo =
-            *reinterpret_cast<const i32x4 *>(lds_at(st, kro[2 * j]) + kb * 32 * D);
+            *reinterpret_cast<const i32x4 *>(lds_at(sb, kro[2 * j]) + kb * 32 * D);
         const i32x4 hi =
-            *reinterpret_cast<const i32x4 *>(lds_at(st, kro[2 * j + 1]) + kb * 32 * D);
+            *reinterpret_cast<const i32x4 *>(lds_at(sb, kro[2 * j + 1]) + kb * 32 * D);
         sacc[kb] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, qreg[kk],
                             sacc[kb], kex, qe);
       }
@@ -415,11 +422,11 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   // ---- O^T += V8^T . P'^T: lane (l32, hf) reads the logical granules 2hf
   //      and 2hf+1 of V^T row db*32 + l32, whose swizzle is vswz8(l32) ----
   static_assert(vswz8(32) == 0, "V^T row blocks share the swizzle");
-  auto pv = [&](const i32x8 &pb, int st) JA_INLINE {
+  auto pv = [&](const i32x8 &pb, int sb) JA_INLINE {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const i32x4 lo = *reinterpret_cast<const i32x4 *>(lds_at(st, vro[0]) + db * 32 * BN);
-      const i32x4 hi = *reinterpret_cast<const i32x4 *>(lds_at(st, vro[1]) + db * 32 * BN);
+      const i32x4 lo = *reinterpret_cast<const i32x4 *>(lds_at(sb, vro[0]) + db * 32 * BN);
+      const i32x4 hi = *reinterpret_cast<const i32x4 *>(lds_at(sb, vro[1]) + db * 32 * BN);
       oacc[db] = mfma_fp8(i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, pb, oacc[db]);
     }
   };
@@ -434,7 +441,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   //      m_run starts finite, so that a tile whose keys are all -inf leaves
   //      it (and O, l) unchanged. ----
   float m_run = -1e30f, l_run = 0.f;
-  auto exp_tile = [&](const f32x16 (&t)[2], float mref, int buf, float &psum) JA_INLINE -> i32x8 {
+  auto exp_tile = [&](const f32x16 (&t)[2], float mref, int sb, float &psum) JA_INLINE -> i32x8 {
     const float nref = kPOffset - mref;
     uint32_t pw[8];
     psum = 0.f;
@@ -443,7 +450,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 ig =
-            *reinterpret_cast<const float4 *>(lds_at(buf, iro) + 4 * (BN + kb * 32 + g * 8));
+            *reinterpret_cast<const float4 *>(lds_at(sb, iro) + 4 * (BN + kb * 32 + g * 8));
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][4 * g + i], c, nref));
@@ -451,13 +458,17 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
         psum = __builtin_fmaf(p[1], ig.y, psum);
         psum = __builtin_fmaf(p[2], ig.z, psum);
         psum = __builtin_fmaf(p[3], ig.w, psum);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        // the first conversion's upper half is overwritten by the second, so
+        // it starts from any register value (no zeroing move)
+        int any;
+        asm volatile("" : "=v"(any));
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], any, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pw[kb * 4 + g] = (uint32_t)w;
       }
     return bit_cast<i32x8>(pw);
   };
-  auto softmax = [&](f32x16 (&sacc)[2], int buf) JA_INLINE -> i32x8 {
+  auto softmax = [&](f32x16 (&sacc)[2], int sb) JA_INLINE -> i32x8 {
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -466,7 +477,7 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
     const float mx = half_max(tmax) * c;      // c > 0
     const bool grow = mx > m_run + kRescaleLog2;
     float psum;
-    i32x8 pb = exp_tile(sacc, m_run, buf, psum);
+    i32x8 pb = exp_tile(sacc, m_run, sb, psum);
     // the fast path's sum stays before the branch (sunk past it, its
     // reciprocal-scale reads would wait one by one)
     asm volatile("" ::"v"(psum));
@@ -480,12 +491,11 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      pb = exp_tile(sacc, m_new, buf, psum);
+      pb = exp_tile(sacc, m_new, sb, psum);
     }
     l_run += psum;
     return pb;
   };
-
   // ---- loop over the key tiles t0 .. t1-1 (local index i).  Tile i lives
   //      in stage i % NSTAGE.  Iteration i first issues the loads of tile
   //      i+3 into the stage of tile i-1, which every wave finished before the
@@ -508,9 +518,11 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   auto iteration = [&]<bool LAST>(int i) JA_INLINE {
     const bool ahead = i + PREF < nt;
     if (ahead) issue(tile_of(t0 + i + PREF), (i + PREF) % NSTAGE);
-    qk(i % NSTAGE, sacc);
-    const i32x8 pb = softmax(sacc, i % NSTAGE);
-    pv(pb, i % NSTAGE);
+    // stage byte offset as one scalar (each address is then a single add)
+    const int sb = __builtin_amdgcn_readfirstlane((i % NSTAGE) * L::STAGE);
+    qk(sb, sacc);
+    const i32x8 pb = softmax(sacc, sb);
+    pv(pb, sb);
     if constexpr (!LAST) {
       if (ahead)
         wait_tiles.template operator()<PREF - 1>();

@@ -10,7 +10,7 @@ import torch
 import joint_attention_attn_amd as ja
 import oracle
 import synth
-from parity_util import FP8_REL_L2, rel_l2, sample_rows
+from parity_util import FP8_REL_L2, max_abs, rel_l2, sample_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -83,6 +83,24 @@ def test_fp8_forward_ragged(s, d):
     ref, _ = oracle.fp8_attention(*codes)
     assert not torch.isnan(out).any()
     assert rel_l2(out, ref) <= FP8_REL_L2
+
+
+@pytest.mark.parametrize("s,d", [(300, 64), (517, 128)])
+def test_fp8_forward_widely_varying_v_scales(s, d):
+    # V rows whose magnitudes spread over 2^-8..2^8 (log-uniform): a key with
+    # a small V scale has a P' far below the others', which can vanish in
+    # e4m3 while its probability is not small, so the row sum must count its
+    # probability itself (the unrounded P' / sv), not the rounded P'
+    w = synth.Workload("vspread", 1, 2, d, n_text=s, grid=0, outlier_frac=0.0)
+    q, k, v, _ = synth.make_qkv(w, seed=s + 5)
+    mag = np.exp2(np.random.default_rng(s).uniform(-8, 8, size=(1, s, 1, 1)))
+    v = (v.double() * torch.from_numpy(mag)).to(torch.bfloat16)
+    codes = oracle.quant_rope_fp8(q, k, v, None)
+    _say(f"fp8 fwd, widely varying V scales S={s} D={d}")
+    out, lse = _fwd_fp8_from_oracle_codes(*codes, return_lse=True)
+    ref, ref_lse = oracle.fp8_attention(*codes)
+    assert rel_l2(out, ref) <= FP8_REL_L2
+    assert max_abs(lse.cpu(), ref_lse) <= 1e-2
 
 
 def _vt8_key_of_pos(p):
