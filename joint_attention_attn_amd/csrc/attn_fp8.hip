@@ -435,13 +435,20 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
   //      key's score in the exp2 domain plus log2 of its V scale; m_run
   //      tracks the row max of u, and P' = exp2(u - m_run + kPOffset) is P
   //      times sv against the reference m_run - kPOffset, so P'.V8 is P.V in
-  //      true units and the row sum adds P' / sv.  As in the bf16 kernel, P'
-  //      is first computed against the running max and only recomputed (with
-  //      O and l rescaled) when some row max grew by more than the threshold.
-  //      m_run starts finite, so that a tile whose keys are all -inf leaves
-  //      it (and O, l) unchanged. ----
+  //      true units and the row sum adds P' / sv.  The tile's row max is
+  //      taken first; when some row's max grew by more than the threshold,
+  //      the wave moves the references of the rows that grew (rescaling
+  //      their O and l), then computes P' once.  (Computing P' first against
+  //      the old reference and again after a move costs a second exp2 pass
+  //      in about a fifth of the tiles at 16896 tokens with outlier keys:
+  //      one growing row of 32 is enough.)  m_run starts finite, so that a
+  //      tile whose keys are all -inf leaves it (and O, l) unchanged. ----
   float m_run = -1e30f, l_run = 0.f;
-  auto exp_tile = [&](const f32x16 (&t)[2], float mref, int sb, float &psum) JA_INLINE -> i32x8 {
+  // P' of the tile against reference mref, and psum = sum of P' / sv over
+  // the lane's keys (ig: 1/sv of those keys, element kb*4 + g of group g of
+  // key block kb)
+  auto exp_tile = [&](const f32x16 (&t)[2], float mref, const f32x4 (&ig)[8],
+                      float &psum) JA_INLINE -> i32x8 {
     const float nref = kPOffset - mref;
     uint32_t pw[8];
     psum = 0.f;
@@ -449,15 +456,14 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 ig =
-            *reinterpret_cast<const float4 *>(lds_at(sb, iro) + 4 * (BN + kb * 32 + g * 8));
+        const f32x4 iv = ig[kb * 4 + g];
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][4 * g + i], c, nref));
-        psum = __builtin_fmaf(p[0], ig.x, psum);
-        psum = __builtin_fmaf(p[1], ig.y, psum);
-        psum = __builtin_fmaf(p[2], ig.z, psum);
-        psum = __builtin_fmaf(p[3], ig.w, psum);
+        psum = __builtin_fmaf(p[0], iv.x, psum);
+        psum = __builtin_fmaf(p[1], iv.y, psum);
+        psum = __builtin_fmaf(p[2], iv.z, psum);
+        psum = __builtin_fmaf(p[3], iv.w, psum);
         // the first conversion's upper half is overwritten by the second, so
         // it starts from any register value (no zeroing move)
         int any;
@@ -465,10 +471,20 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], any, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
         pw[kb * 4 + g] = (uint32_t)w;
+        // one group of four scores at a time, its sum included (left to the
+        // scheduler, the 32 exp2 results wait for the sums past the P.V
+        // products and overflow the register budget)
+        asm volatile("" : "+v"(psum));
+        __builtin_amdgcn_sched_barrier(0);
       }
     return bit_cast<i32x8>(pw);
   };
   auto softmax = [&](f32x16 (&sacc)[2], int sb) JA_INLINE -> i32x8 {
+    // 1/sv of the lane's 32 keys, read while the max is taken
+    f32x4 ig[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ig[j] = *reinterpret_cast<const f32x4 *>(lds_at(sb, iro) + 4 * (BN + 8 * j));
     float tmax = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -476,13 +492,10 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
       for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kb][i]);
     const float mx = half_max(tmax) * c;      // c > 0
     const bool grow = mx > m_run + kRescaleLog2;
-    float psum;
-    i32x8 pb = exp_tile(sacc, m_run, sb, psum);
-    // the fast path's sum stays before the branch (sunk past it, its
-    // reciprocal-scale reads would wait one by one)
-    asm volatile("" ::"v"(psum));
+    // the reads complete here, above the branch
+    asm volatile("" ::"v"(ig[0]), "v"(ig[1]), "v"(ig[2]), "v"(ig[3]), "v"(ig[4]), "v"(ig[5]),
+                 "v"(ig[6]), "v"(ig[7]));
     if (__builtin_amdgcn_ballot_w64(grow)) {
-      asm volatile("" ::"v"(pb));
       const float m_new = grow ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -491,11 +504,13 @@ void attn_fwd_fp8_kernel(Fp8Args a) {
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      pb = exp_tile(sacc, m_new, sb, psum);
     }
+    float psum;
+    const i32x8 pb = exp_tile(sacc, m_run, ig, psum);
     l_run += psum;
     return pb;
   };
+
   // ---- loop over the key tiles t0 .. t1-1 (local index i).  Tile i lives
   //      in stage i % NSTAGE.  Iteration i first issues the loads of tile
   //      i+3 into the stage of tile i-1, which every wave finished before the
