@@ -88,13 +88,67 @@ __device__ __forceinline__ double chunk_sumsq_f64(u32x4 w) {
   return s;
 }
 
-// Sum over the chunks of a row when lane (i % CH) of each group of CH
-// consecutive lanes holds chunk i % CH (every lane gets the total).
+// ---- Reductions over aligned groups of G = 2, 4, 8 or 16 consecutive lanes
+//      with DPP row operations (no LDS traffic, no lane arithmetic).  Step 0
+//      pairs lanes l and l^1, step 1 lanes l and l^2 (quad permutations),
+//      step 2 mirrors each half row (l <-> 7-l within 8 lanes), step 3
+//      mirrors each 16-lane row (l <-> 15-l); after steps 0..s every lane of
+//      an aligned group of 2^(s+1) lanes holds the combination of the whole
+//      group. ----
+template <int STEP>
+__device__ __forceinline__ uint32_t dpp_row_xchg(uint32_t v) {
+  static_assert(STEP >= 0 && STEP < 4, "16-lane rows");
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xf, 0xf, false);
+}
+template <int STEP>
+__device__ __forceinline__ double dpp_row_xchg_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_row_xchg<STEP>((uint32_t)u);
+  const uint64_t hi = dpp_row_xchg<STEP>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+template <int G>
+__device__ __forceinline__ double group_sum_f64(double s) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+  if constexpr (G > 1) s += dpp_row_xchg_f64<0>(s);
+  if constexpr (G > 2) s += dpp_row_xchg_f64<1>(s);
+  if constexpr (G > 4) s += dpp_row_xchg_f64<2>(s);
+  if constexpr (G > 8) s += dpp_row_xchg_f64<3>(s);
+  return s;
+}
+template <int G>
+__device__ __forceinline__ int group_max_i32(int v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+  if constexpr (G > 1) v = max(v, (int)dpp_row_xchg<0>((uint32_t)v));
+  if constexpr (G > 2) v = max(v, (int)dpp_row_xchg<1>((uint32_t)v));
+  if constexpr (G > 4) v = max(v, (int)dpp_row_xchg<2>((uint32_t)v));
+  if constexpr (G > 8) v = max(v, (int)dpp_row_xchg<3>((uint32_t)v));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+  if constexpr (G > 1) v = max(v, dpp_row_xchg<0>(v));
+  if constexpr (G > 2) v = max(v, dpp_row_xchg<1>(v));
+  if constexpr (G > 4) v = max(v, dpp_row_xchg<2>(v));
+  if constexpr (G > 8) v = max(v, dpp_row_xchg<3>(v));
+  return v;
+}
+
+// Sum over the chunks of a row when lane (i % CH) of each aligned group of
+// CH consecutive lanes holds chunk i % CH (every lane gets the total).
 template <int CH>
 __device__ __forceinline__ double chunk_sum_lanes_f64(double s) {
-#pragma unroll
-  for (int k = 1; k < CH; k <<= 1) s += __shfl_xor(s, k);
-  return s;
+  return group_sum_f64<CH>(s);
+}
+
+// max(m, |y|) for m >= 0 as one v_max_f64 with the abs modifier (fmax would
+// first canonicalize both operands); a NaN y leaves m (IEEE maxNum).
+__device__ __forceinline__ double max_abs_f64(double m, double y) {
+  double r;
+  asm("v_max_f64 %0, %1, |%2|" : "=v"(r) : "v"(m), "v"(y));
+  return r;
 }
 
 // r = 1 / sqrt(ss / D + eps) in fp64.
@@ -105,7 +159,34 @@ __device__ __forceinline__ double rms_scale_f64(double ss, float eps) {
 
 // The prologue of one 16-byte chunk (elements d0 .. d0+7 of a head vector)
 // in fp64: normalized with r and the chunk's 8 weights g (if g), rotated
-// with the chunk's 4 table entries cs (if cs).
+// with the chunk's 4 table entries cs (if rope; held in registers).
+__device__ __forceinline__ void prologue_chunk_f64_regs(u32x4 w, double r, const float *g,
+                                                        bool rope, const double2 (&cs)[4],
+                                                        double (&y)[8]) {
+#pragma clang fp contract(off)
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[2 * e] = bf16_lo(ws[e]);
+    y[2 * e + 1] = bf16_hi(ws[e]);
+  }
+  if (g) {
+    const float4 g0 = reinterpret_cast<const float4 *>(g)[0];
+    const float4 g1 = reinterpret_cast<const float4 *>(g)[1];
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * r * (double)gv[e];
+  }
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double x0 = y[2 * e], x1 = y[2 * e + 1];
+      rope_pair_f64(x0, x1, cs[e], y[2 * e], y[2 * e + 1]);
+    }
+  }
+}
+
+// The same with the chunk's 4 table entries read from cs (if cs).
 __device__ __forceinline__ void prologue_chunk_f64(u32x4 w, double r, const float *g,
                                                    const double2 *cs, double (&y)[8]) {
 #pragma clang fp contract(off)

@@ -10,9 +10,11 @@
 // reads each K tile once, so rotating there would redo the rotation (and its
 // table reads) once per query block.
 //
-// A workgroup covers 64 keys of HG heads of one batch row (HG = 4, 2 or 1,
-// whichever divides the head count): the rotation table entries of a key are
-// read once and applied to the key's rows in all HG heads.
+// A workgroup covers 64 keys of HG heads of one batch row (HG = 2, or 1 for
+// an odd head count): the rotation table entries of a key are read once and
+// applied to the key's rows in both heads.  (Four heads share the table
+// reads better but need 64 KB of LDS per workgroup, which leaves two
+// workgroups per CU: too few loads in flight for this HBM-bound pass.)
 //
 // Layout of the prepared buffer, Kr then Vt (S_pad = S rounded up to 64
 // keys; rows and columns past S are 0):
@@ -38,19 +40,34 @@ struct PrepArgs {
   float eps;
   bf16 *kr, *vt;
   int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
-  int S, S_pad, H;
+  int S, S_pad, H, B;
 };
+
+// Staged V row r keeps its 16-byte chunk c at c ^ vchunk_swz(r): the eight
+// rows that a transpose read touches at once (keys 0, 4, 16, 20, 32, 36, 48,
+// 52 plus a multiple of 2 or 8, see below) then sit in distinct bank groups.
+template <int CH>
+__device__ __forceinline__ int vchunk_swz(int r) {
+  return (2 * (((r >> 2) & 1) | (((r >> 4) & 3) << 1))) & (CH - 1);
+}
 
 template <int D, bool ROPE, int HG>
 __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
-  constexpr int VSTR = D + 8;        // bf16 per staged V row (16-byte pad)
-  __shared__ __attribute__((aligned(16))) bf16 vs[HG * PK * VSTR];
+  __shared__ __attribute__((aligned(16))) bf16 vs[HG * PK * D];
   const int tid = threadIdx.x;
   const int nkb = a.S_pad / PK;
-  const int k0 = (blockIdx.x % nkb) * PK;
-  const int bg = blockIdx.x / nkb;               // (batch row, head group)
   const int ng = a.H / HG;
+  // XCD-aware order: workgroups go round-robin over the 8 XCDs, and XCD x
+  // takes key blocks x, x + 8, ... with all (batch row, head group) pairs of
+  // a key block back to back, so that the key block's rotation table rows
+  // are fetched into that XCD's L2 once
+  const int nbg = a.B * ng;                      // (batch row, head group) pairs
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int kb = (slot / nbg) * 8 + xcd;
+  const int bg = slot % nbg;                     // (batch row, head group)
+  if (kb >= nkb) return;
+  const int k0 = kb * PK;
   const int b = bg / ng, h0 = (bg % ng) * HG;
   const int64_t bh0 = (int64_t)b * a.H + h0;
 
@@ -87,7 +104,7 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
         x = prologue_chunk_bf16(x, 0.0, nullptr, cs);
       }
       *reinterpret_cast<u32x4 *>(a.kr + ((bh0 + g) * a.S_pad + key) * D + 8 * c) = x;
-      *reinterpret_cast<u32x4 *>(vs + (g * PK + r) * VSTR + 8 * c) = vw[g];
+      *reinterpret_cast<u32x4 *>(vs + (g * PK + r) * D + 8 * (c ^ vchunk_swz<CH>(r))) = vw[g];
     }
   }
   __syncthreads();
@@ -99,7 +116,7 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
   for (int idx = tid; idx < HG * (D / 2) * (PK / 8); idx += PT) {
     const int g = idx / ((D / 2) * (PK / 8));
     const int d = 2 * ((idx / (PK / 8)) % (D / 2)), j = idx % (PK / 8);
-    const bf16 *vsg = vs + g * PK * VSTR;
+    const bf16 *vsg = vs + g * PK * D;
     bf16 *vtb = a.vt + (bh0 + g) * D * a.S_pad;
     uint32_t w[4], x[4];
 #pragma unroll
@@ -107,8 +124,10 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
       const int p0 = 8 * j + 2 * e, p1 = p0 + 1;
       const int r0 = 16 * (p0 / 16) + vt_key_of_slot(p0 % 16);
       const int r1 = 16 * (p1 / 16) + vt_key_of_slot(p1 % 16);
-      const uint32_t v0 = *reinterpret_cast<const uint32_t *>(vsg + r0 * VSTR + d);
-      const uint32_t v1 = *reinterpret_cast<const uint32_t *>(vsg + r1 * VSTR + d);
+      const uint32_t v0 = *reinterpret_cast<const uint32_t *>(
+          vsg + r0 * D + 8 * ((d / 8) ^ vchunk_swz<CH>(r0)) + d % 8);
+      const uint32_t v1 = *reinterpret_cast<const uint32_t *>(
+          vsg + r1 * D + 8 * ((d / 8) ^ vchunk_swz<CH>(r1)) + d % 8);
       w[e] = __builtin_amdgcn_perm(v1, v0, 0x05040100u);    // row d:   key r0 | key r1
       x[e] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);    // row d+1: key r0 | key r1
     }
@@ -120,9 +139,7 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
 
 template <int D, bool ROPE>
 void launch_rope(const PrepArgs &a, dim3 grid, int hg, hipStream_t st) {
-  if (hg == 4)
-    hipLaunchKernelGGL((prep_kv_bf16_kernel<D, ROPE, 4>), grid, dim3(PT), 0, st, a);
-  else if (hg == 2)
+  if (hg == 2)
     hipLaunchKernelGGL((prep_kv_bf16_kernel<D, ROPE, 2>), grid, dim3(PT), 0, st, a);
   else
     hipLaunchKernelGGL((prep_kv_bf16_kernel<D, ROPE, 1>), grid, dim3(PT), 0, st, a);
@@ -159,8 +176,11 @@ hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v
   a.S = L.S;
   a.S_pad = prep_pad(L.S);
   a.H = L.H;
-  const int hg = L.H % 4 == 0 ? 4 : L.H % 2 == 0 ? 2 : 1;
-  const dim3 grid((unsigned)((int64_t)(a.S_pad / PK) * L.B * (L.H / hg)));
+  a.B = L.B;
+  const int hg = L.H % 2 == 0 ? 2 : 1;
+  // every XCD gets ceil(nkb / 8) key blocks (the excess workgroups exit)
+  const int64_t nkb8 = (a.S_pad / PK + 7) / 8 * 8;
+  const dim3 grid((unsigned)(nkb8 * L.B * (L.H / hg)));
   if (L.D == 64)
     launch_group<64>(a, grid, rope != nullptr, hg, st);
   else

@@ -44,11 +44,16 @@ struct Prep8Args {
   int S, S_pad, H;
 };
 
+// Staged V row r keeps its 16-byte chunk c at c ^ vrow_swz(r): the 16 rows
+// 4m + e (m = 0..15) that one transpose read touches then spread over the
+// bank groups.
+template <int CH>
+__device__ __forceinline__ int vrow_swz(int r) { return (r >> 2) & (CH - 1); }
+
 template <int D>
 __global__ __launch_bounds__(PT) void prep_kv_fp8_kernel(Prep8Args a) {
   constexpr int CH = D / 16;          // 16-byte chunks per row
-  constexpr int VSTR = D + 16;        // bytes per staged V row (16-byte pad)
-  __shared__ __attribute__((aligned(16))) uint8_t vs[PK * VSTR];
+  __shared__ __attribute__((aligned(16))) uint8_t vs[PK * D];
   const int tid = threadIdx.x;
   const int nt = a.S_pad / PK;
   const int tile = blockIdx.x % nt;
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(PT) void prep_kv_fp8_kernel(Prep8Args a) {
       vw = *reinterpret_cast<const u32x4 *>(vb + key * row + 16 * ch);
     }
     *reinterpret_cast<u32x4 *>(krb + (int64_t)key * D + 16 * ch) = kw;
-    *reinterpret_cast<u32x4 *>(vs + r * VSTR + 16 * ch) = vw;
+    *reinterpret_cast<u32x4 *>(vs + r * D + 16 * (ch ^ vrow_swz<CH>(r))) = vw;
   }
 
   // per-key values
@@ -108,7 +113,11 @@ __global__ __launch_bounds__(PT) void prep_kv_fp8_kernel(Prep8Args a) {
     const int m = idx % (PK / 4), dq = idx / (PK / 4);
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint32_t *>(vs + (4 * m + e) * VSTR + 4 * dq);
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * m + e;
+      w[e] = *reinterpret_cast<const uint32_t *>(vs + r * D + 16 * ((dq / 4) ^ vrow_swz<CH>(r)) +
+                                                 4 * (dq % 4));
+    }
     // w[e] holds columns 4dq..+3 of key 4m+e; u[j] gets keys 4m..+3 of column 4dq+j
     const uint32_t t01l = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
     const uint32_t t01h = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);

@@ -61,6 +61,33 @@ def test_quantizer_zero_vectors_and_no_rope():
     assert got[5][0, 0, 10] == 1.0 and np.all(got[2][0, 10] == 0)
 
 
+def test_quantizer_every_bf16_magnitude():
+    # one head vector per positive finite bf16 value m (both signs, at varying
+    # head-dimension positions) over a random background below m: every V
+    # scale fl32(m / 448), every Q/K power-of-two scale and their codes,
+    # bit for bit against the oracle
+    mags = (np.arange(1, 0x7f80, dtype=np.uint32) << 16).view(np.float32)
+    n = mags.size
+    h, d = 2, 64
+    s = (n + h - 1) // h
+    rng = np.random.default_rng(11)
+    x = rng.uniform(-1, 1, size=(1, s, h, d)).astype(np.float32)
+    x = x * np.resize(mags, s * h).reshape(1, s, h, 1)
+    flat = x.reshape(s * h, d)
+    cols = rng.integers(0, d, size=s * h)
+    sign = np.where(rng.integers(0, 2, size=s * h) == 1, 1.0, -1.0).astype(np.float32)
+    flat[np.arange(s * h), cols] = np.resize(mags, s * h) * sign
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    _say(f"quant every bf16 magnitude ({n} values)")
+    got = _quant_gpu(t, t, t, None)
+    ref = oracle.quant_rope_fp8(t, t, t, None)
+    for name, g, r in zip(("q8", "k8", "v8", "sq", "sk", "sv"), got, ref):
+        g, r = np.asarray(g), np.asarray(r)
+        gv = g.view(np.uint8) if g.dtype == np.uint8 else g.view(np.uint32)
+        rv = r.view(np.uint8) if r.dtype == np.uint8 else r.astype(np.float32).view(np.uint32)
+        assert np.array_equal(gv, rv), name
+
+
 def _dev(*xs):
     return [torch.from_numpy(np.ascontiguousarray(x)).to(DEV) for x in xs]
 
