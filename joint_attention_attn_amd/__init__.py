@@ -25,7 +25,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libjoint_attn.so")
+# JA_LIBRARY names another build of the same library (the host-sanitizer
+# build of the C ABI tests); by default the in-tree libjoint_attn.so
+_LIB_PATH = os.environ.get("JA_LIBRARY") or os.path.join(_HERE, "libjoint_attn.so")
 _LIB = None
 
 JA_OK, JA_ERR_INVALID_ARG, JA_ERR_UNSUPPORTED, JA_ERR_HIP = 0, 1, 2, 3

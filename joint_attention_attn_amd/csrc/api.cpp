@@ -394,7 +394,11 @@ ja_status scratch_address(void **out) {
 extern "C" {
 
 const char *joint_attn_status_string(ja_status s) {
-  switch (s) {
+  // a C caller may pass any int; read it as one (an out-of-range value of
+  // the enum type is not a valid C++ value)
+  int code;
+  std::memcpy(&code, &s, sizeof code);
+  switch (code) {
     case JA_OK: return "JA_OK";
     case JA_ERR_INVALID_ARG: return "JA_ERR_INVALID_ARG: invalid argument";
     case JA_ERR_UNSUPPORTED: return "JA_ERR_UNSUPPORTED: unsupported shape";

@@ -57,5 +57,44 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI
+# layer (api.cpp: argument validation, planning, workspace carving), linked
+# with the kernel objects of the regular build.  Device code is not
+# instrumented (-Xarch_host).  Loading it needs the ASan runtime preloaded.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    base = os.path.join(rocm, "lib", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(base), reverse=True):
+        path = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(path):
+            return path
+    raise RuntimeError("no libclang_rt.asan-x86_64.so under " + base)
+
+
+def build_sanitized() -> str:
+    out_dir = os.path.join(PKG, "_build")
+    objs = [os.path.join(out_dir, os.path.splitext(src)[0] + ".o") for src in SOURCES
+            if src != "api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    cc = hipcc()
+    api_o = os.path.join(out_dir, "api_san.o")
+    r = subprocess.run([cc, "-x", "hip", *FLAGS, *SAN_FLAGS, "-c", os.path.join(HERE, "api.cpp"),
+                        "-o", api_o], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized api.cpp failed:\n{r.stdout}\n{r.stderr}")
+    lib = os.path.join(out_dir, "libjoint_attn_san.so")
+    r = subprocess.run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", api_o, *objs,
+                        "-o", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stdout}\n{r.stderr}")
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
