@@ -185,8 +185,9 @@ def main() -> int:
     table_avg = sum(tms) / len(tms)
     # the benchmarked output comes from the one-call path
     ja.fwd_bf16(qd, kd, vd, pos_d, w.theta, out=out)
-    # algorithmic bytes of the preparation: read K, V and the table, write both
-    prep_bytes = 4 * B * S * H * D * 2 + S * (D // 2) * 8
+    # algorithmic bytes of the preparation: read K, V and the table (fp64
+    # cos, sin per pair), write both
+    prep_bytes = 4 * B * S * H * D * 2 + S * (D // 2) * 16
     achieved = flops / (k_avg * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -226,7 +227,7 @@ def main() -> int:
         fms = _time_launches(lambda: ja.fwd_fp8_prepared(q8, sq, kv8, out=out8), n)
         q_avg, pp_avg, f_avg = sum(qms) / n, sum(pp8) / n, sum(fms) / n
         elems = B * S * H * D
-        q_bytes = 3 * elems * 2 + S * (D // 2) * 8 + 3 * elems + 3 * B * H * S * 4
+        q_bytes = 3 * elems * 2 + S * (D // 2) * 16 + 3 * elems + 3 * B * H * S * 4
         # preparation: read K and V codes and two scales, write the prepared
         # K, V^T and 16 bytes of per-key values per key (64-key padding aside)
         pp_bytes = 2 * elems + 2 * B * H * S * 4 + 2 * elems + B * H * S * 16
