@@ -1,10 +1,10 @@
 // Repair set of the FP8 path: the tokens with the largest quantization error.
 //
-// The pages configure VC-Attention FP8 with a repair budget that selects the
-// fraction of tokens with the highest quantization error for residual
-// correction ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
-// Blackwell GPUs", section "Quantized and sparse attention",
-// vc_repair_budget).  Here, per (batch, head):
+// In the pages' VC-Attention FP8 setting, a budget (vc_repair_budget) sets
+// what share of the tokens gets corrected: those whose quantization hurt
+// most ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
+// Blackwell GPUs", section "Quantized and sparse attention").  Here, per
+// (batch, head):
 //   e[token] = max_d |k - k^| + max_d |v - v^|   (k the rotated key that was
 //              quantized, from the fp64 prologue; k^ = value(code) * scale,
 //              exact in fp64; the differences, maxima and sum in fp64, the

@@ -149,10 +149,10 @@ def fp8_attention(q8, k8, v8, sq, sk, sv, scale=None, rows=None):
 # ---------------------------------------------------------------------------
 # Repair of the tokens with the largest quantization error (VC-Attention FP8)
 #
-# The pages configure VC-Attention FP8 with a repair budget rho = 0.005 that
-# selects the fraction of tokens with the highest quantization error for
-# residual correction (same page, section "Quantized and sparse attention",
-# vc_repair_budget).  The mechanism is not given beyond that sentence.
+# In the pages' VC-Attention FP8 setting a budget rho = 0.005
+# (vc_repair_budget) sets the share of tokens that get a correction: the ones
+# whose quantization error is largest (same page, section "Quantized and
+# sparse attention").  The pages say nothing more about the mechanism.
 # Reading taken:
 #
 # * a token's error, per (batch, head), is the max-abs quantization error of

@@ -6,11 +6,12 @@ position of every token.  It holds none of the attention, RoPE or
 quantization arithmetic, so both the fp64 oracle and the HIP path can take
 their inputs from here without sharing any of the method.
 
-Token order of the joint sequence is [text | target image | reference image],
-the plainest reading of "text, noisy target-image, and optional
-reference-image streams ... combined through joint attention" ("Speed Up Image
-Generation with FLUX 3 Image Klein on NVIDIA Blackwell GPUs", section "FLUX 3
-inference with TensorRT LLM VisualGen").  The pages give no shapes; the sizes
+Token order of the joint sequence is [text | target image | reference image]:
+the pages list the text stream, the noisy image being generated and the
+optional reference images, processed separately and then merged by joint
+attention ("Speed Up Image Generation with FLUX 3 Image Klein on NVIDIA
+Blackwell GPUs", section "FLUX 3 inference with TensorRT LLM VisualGen"); the
+order follows that listing.  The pages give no shapes; the sizes
 below are the 1024x1024 / 2048x2048 DiT step shapes (16 pixels per latent
 token, 512 text tokens, 24 heads of 128) the build is measured on.
 """
