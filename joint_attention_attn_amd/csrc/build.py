@@ -54,7 +54,22 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(cc, out_dir)
     return LIB
+
+
+# Stand-alone microbenchmark of the bf16 forward's per-tile instruction chain
+# (mfma_chain_probe.hip): the rate the chip sustains for that mix of matrix,
+# vector and LDS work under its power limit.  Not part of the library.
+PROBE = os.path.join(PKG, "_build", "mfma_chain_probe")
+
+
+def build_probe(cc: str, out_dir: str) -> str:
+    r = subprocess.run([cc, *FLAGS, os.path.join(HERE, "mfma_chain_probe.hip"), "-o", PROBE],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on mfma_chain_probe.hip:\n{r.stdout}\n{r.stderr}")
+    return PROBE
 
 
 # Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the C ABI
