@@ -186,6 +186,31 @@ __device__ __forceinline__ void prologue_chunk_f64_regs(u32x4 w, double r, const
   }
 }
 
+// The same with the chunk's 8 norm weights already in registers (used if
+// norm).
+__device__ __forceinline__ void prologue_chunk_f64_w(u32x4 w, double r, bool norm,
+                                                     const float (&gv)[8], bool rope,
+                                                     const double2 (&cs)[4], double (&y)[8]) {
+#pragma clang fp contract(off)
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[2 * e] = bf16_lo(ws[e]);
+    y[2 * e + 1] = bf16_hi(ws[e]);
+  }
+  if (norm) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * r * (double)gv[e];
+  }
+  if (rope) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double x0 = y[2 * e], x1 = y[2 * e + 1];
+      rope_pair_f64(x0, x1, cs[e], y[2 * e], y[2 * e + 1]);
+    }
+  }
+}
+
 // The same with the chunk's 4 table entries read from cs (if cs).
 __device__ __forceinline__ void prologue_chunk_f64(u32x4 w, double r, const float *g,
                                                    const double2 *cs, double (&y)[8]) {

@@ -52,8 +52,10 @@ __device__ __forceinline__ int vchunk_swz(int r) {
 }
 
 template <int D, bool ROPE, int HG>
-__global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
+__global__ __launch_bounds__(PT, 3) void prep_kv_bf16_kernel(PrepArgs a) {
   constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int IT = PK * CH / PT;   // chunk positions per thread
+  static_assert(PK * CH % PT == 0 && PT % CH == 0, "whole rows per pass");
   __shared__ __attribute__((aligned(16))) bf16 vs[HG * PK * D];
   const int tid = threadIdx.x;
   const int nkb = a.S_pad / PK;
@@ -71,40 +73,77 @@ __global__ __launch_bounds__(PT) void prep_kv_bf16_kernel(PrepArgs a) {
   const int b = bg / ng, h0 = (bg % ng) * HG;
   const int64_t bh0 = (int64_t)b * a.H + h0;
 
-  // K: (normalize,) rotate and copy; V: stage row-major in LDS.  The CH
-  // chunks of a row are CH consecutive lanes, so the norm's butterfly runs
-  // inside each lane group (every lane takes part; rows past S are zeros).
-  // All loads of a chunk position are issued before any of them is used.
+  // A thread holds chunk c of keys r0, r0 + PT/CH, ... (IT of them) in each
+  // of the HG heads.  Every load of the workgroup's share of K, V and the
+  // rotation table is issued before any of them is used: the pass is bound
+  // by the bytes it keeps in flight, and stores in between would keep the
+  // compiler from hoisting later loads above them.
+  const int c = tid % CH, r0 = tid / CH;
+  // the chunk's norm weights (the same for every key and head of the thread;
+  // loaded first, so that waiting for them waits for nothing else)
+  float gw[8];
+  if (a.kn) {
+    const float4 g0 = reinterpret_cast<const float4 *>(a.kn + 8 * c)[0];
+    const float4 g1 = reinterpret_cast<const float4 *>(a.kn + 8 * c)[1];
+    gw[0] = g0.x; gw[1] = g0.y; gw[2] = g0.z; gw[3] = g0.w;
+    gw[4] = g1.x; gw[5] = g1.y; gw[6] = g1.z; gw[7] = g1.w;
+  }
+  // Loads are unconditional (a key past S reads key S-1; its V and its
+  // rotated K are replaced by zeros), so the compiler keeps them together.
+  u32x4 kw[IT][HG], vw[IT][HG];
 #pragma unroll
-  for (int idx = tid; idx < PK * CH; idx += PT) {
-    const int r = idx / CH, c = idx % CH;
-    const int key = k0 + r;
-    u32x4 kw[HG], vw[HG];
+  for (int it = 0; it < IT; ++it) {
+    const int ks = min(k0 + r0 + it * (PT / CH), a.S - 1);
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
-      kw[g] = u32x4{0, 0, 0, 0};
-      vw[g] = u32x4{0, 0, 0, 0};
-      if (key < a.S) {
-        kw[g] = *reinterpret_cast<const u32x4 *>(a.k + b * a.k_sb + (h0 + g) * a.k_sh +
-                                                 (int64_t)key * a.k_ss + 8 * c);
-        vw[g] = *reinterpret_cast<const u32x4 *>(a.v + b * a.v_sb + (h0 + g) * a.v_sh +
-                                                 (int64_t)key * a.v_ss + 8 * c);
-      }
+      kw[it][g] = *reinterpret_cast<const u32x4 *>(a.k + b * a.k_sb + (h0 + g) * a.k_sh +
+                                                   (int64_t)ks * a.k_ss + 8 * c);
+      vw[it][g] = *reinterpret_cast<const u32x4 *>(a.v + b * a.v_sb + (h0 + g) * a.v_sh +
+                                                   (int64_t)ks * a.v_ss + 8 * c);
     }
-    // the key's 4 table entries (a global pointer: the loads stay in
-    // registers across the HG heads)
-    const double2 *cs = ROPE && key < a.S ? a.rope + (int64_t)key * (D / 2) + 4 * c : nullptr;
+  }
+  // the 4 table entries of each of the thread's keys (pairs 4c .. 4c+3)
+  double2 cs[IT][4];
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int ks = min(k0 + r0 + it * (PT / CH), a.S - 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cs[it][e] = a.rope[(int64_t)ks * (D / 2) + 4 * c + e];
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it)
+    if (k0 + r0 + it * (PT / CH) >= a.S)
+#pragma unroll
+      for (int g = 0; g < HG; ++g) vw[it][g] = u32x4{0, 0, 0, 0};
+
+  // V: staged row-major in LDS for the transpose below
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int r = r0 + it * (PT / CH);
+#pragma unroll
+    for (int g = 0; g < HG; ++g)
+      *reinterpret_cast<u32x4 *>(vs + (g * PK + r) * D + 8 * (c ^ vchunk_swz<CH>(r))) = vw[it][g];
+  }
+  // K: (normalize,) rotate, round once, store.  The CH chunks of a row are
+  // CH consecutive lanes, so the norm's butterfly runs inside each lane group
+  // (every lane takes part; rows past S are zeros).
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int key = k0 + r0 + it * (PT / CH);
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
-      u32x4 x = kw[g];
-      if (a.kn) {
-        const double ss = chunk_sum_lanes_f64<CH>(chunk_sumsq_f64(x));
-        x = prologue_chunk_bf16(x, rms_scale_f64<D>(ss, a.eps), a.kn + 8 * c, cs);
-      } else if (cs) {
-        x = prologue_chunk_bf16(x, 0.0, nullptr, cs);
+      u32x4 x = kw[it][g];
+      if (a.kn || ROPE) {
+        double rn = 0.0;
+        if (a.kn) rn = rms_scale_f64<D>(chunk_sum_lanes_f64<CH>(chunk_sumsq_f64(x)), a.eps);
+        double y[8];
+        prologue_chunk_f64_w(x, rn, a.kn != nullptr, gw, ROPE, cs[it], y);
+        x = pack8_bf16_f64(y);
       }
+      if (key >= a.S) x = u32x4{0, 0, 0, 0};
       *reinterpret_cast<u32x4 *>(a.kr + ((bh0 + g) * a.S_pad + key) * D + 8 * c) = x;
-      *reinterpret_cast<u32x4 *>(vs + (g * PK + r) * D + 8 * (c ^ vchunk_swz<CH>(r))) = vw[g];
     }
   }
   __syncthreads();
