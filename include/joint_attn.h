@@ -260,7 +260,7 @@ ja_status joint_attn_fwd_bf16_block_sparse_prepared(const ja_params *p, const vo
  * share that array, so two calls that overlap on one device race.  The call
  * allocates nothing.
  */
-#define JA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define JA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
 ja_status joint_attn_fwd_bf16_prepared_noalloc(const ja_params *p, const void *q,
                                                const void *kv, size_t kv_bytes, void *o,
                                                float *lse, void *stream);

@@ -8,9 +8,13 @@
 // (K in the preparation pass) and the rotated values are rounded once to
 // bf16 for the MFMA.
 //
-// Work decomposition: one workgroup per (384-query block, head, batch row),
-// twelve wave64s of 32 query rows each, three per SIMD.  Both products are
-// computed transposed so that a lane owns one query row throughout:
+// Work decomposition: one workgroup per (512-query block, head, batch row),
+// eight wave64s of 64 query rows each (two 32-row blocks), two per SIMD.
+// The two blocks of a wave share every K and V^T fragment read from LDS,
+// which halves the LDS bytes per MFMA flop against 32-row waves; under the
+// chip's power limit that energy is what sets the clock.  Both products are
+// computed transposed so that a lane owns one query row of each block
+// throughout:
 //   S^T[key][q]  = K . Q^T      (v_mfma_f32_32x32x16_bf16, A = rotated K from
 //                                LDS, B = rotated Q kept in registers)
 //   O^T[d][q]   += V^T . P^T    (A = V^T from LDS, B = P straight from the S^T
@@ -29,12 +33,12 @@
 // would fill a pad load a dummy chunk) and V^T rows are XOR-swizzled, so that
 // the 16 lanes served together by a fragment read hit distinct banks.
 //
-// Each wave runs Q K^T, softmax and P.V of a tile in turn; the three waves of
+// Each wave runs Q K^T, softmax and P.V of a tile in turn; the two waves of
 // a SIMD overlap one another's MFMA, VALU and memory waits (a wave fits in
-// 168 VGPRs this way, which a wave that also overlapped the next tile's Q K^T
-// with its own softmax would not).  Inside Q K^T and P.V the LDS fragment
-// reads run four MFMAs ahead.  One barrier per tile; it waits only for the
-// loads of the next tile, never for the ones still in flight behind it.
+// 256 VGPRs this way: 128 for O, 64 for Q, 32 for S).  Inside Q K^T and P.V
+// the LDS fragment reads run four fragments ahead.  One barrier per tile; it
+// waits only for the loads of the next tile, never for the ones still in
+// flight behind it.
 //
 // Block-sparse variant (the kernel half of the pages' sparse attention,
 // section "Quantized and sparse attention": attention restricted to the
@@ -54,7 +58,6 @@ namespace ja {
 
 namespace {
 
-constexpr int RW = 1;               // 32-row query blocks per wave
 constexpr int BN = 32;              // keys per K/V tile
 
 // Block-mask granularity of the block-sparse variant.
@@ -62,16 +65,17 @@ constexpr int kQueryBlock = 128;
 constexpr int kKeyBlock = 64;
 constexpr int KB_TILES = kKeyBlock / BN;              // key tiles per key block
 
-// Workgroup shape.  Dense: one workgroup of 12 waves per CU, three per SIMD
-// at most 168 VGPRs each, over a 4-stage ring; latency is hidden by the three
-// waves of a SIMD rather than by deeper software pipelining inside a wave
+// Workgroup shape.  Dense: one workgroup of 8 waves of 64 rows per CU, two
+// per SIMD at most 256 VGPRs each, over a 4-stage ring; latency is hidden by
+// the two waves of a SIMD rather than by software pipelining inside a wave
 // (which needs more registers).  Block-sparse: one 128-row query block per
-// workgroup of 4 waves, three workgroups per CU over 3-stage rings, so that a
-// workgroup stages only the key tiles its own query block keeps and no wave
-// waits on a tile it does not use.
+// workgroup of 4 waves of 32 rows, three workgroups per CU over 3-stage
+// rings, so that a workgroup stages only the key tiles its own query block
+// keeps and no wave waits on a tile it does not use.
 template <bool SPARSE>
 struct Cfg {
-  static constexpr int NW = SPARSE ? 4 : 12;          // waves per workgroup
+  static constexpr int RW = SPARSE ? 1 : 2;           // 32-row query blocks per wave
+  static constexpr int NW = SPARSE ? 4 : 8;           // waves per workgroup
   static constexpr int NSTAGE = SPARSE ? 3 : 4;       // K/V tiles in the LDS ring
   static constexpr int WG_PER_CU = SPARSE ? 3 : 1;
   static constexpr int BM = 32 * RW * NW;             // query rows per workgroup
@@ -165,7 +169,8 @@ struct Lds {
 template <int D, bool ROPE, bool SPARSE>
 __global__ __launch_bounds__(Cfg<SPARSE>::NT, Cfg<SPARSE>::WG_PER_CU)
 void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NW = Cfg<SPARSE>::NW, NT = Cfg<SPARSE>::NT, BM = Cfg<SPARSE>::BM;
+  constexpr int RW = Cfg<SPARSE>::RW, NW = Cfg<SPARSE>::NW, NT = Cfg<SPARSE>::NT,
+                BM = Cfg<SPARSE>::BM;
   constexpr int NSTAGE = Cfg<SPARSE>::NSTAGE, QB_PER_WG = Cfg<SPARSE>::QB_PER_WG;
   using L = Lds<D, NSTAGE>;
   constexpr int CH = L::CH;
@@ -435,11 +440,13 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
   const uint32_t ones_bf16x2 = 0x3f803f80u;
 
   // ---- online softmax of one tile (accumulator row i is key
-  //      8*(i/4) + 4*hf + i%4).  P is first computed against the running max
-  //      m_run: that is exact and bounded by 2^24 unless some row's tile max
-  //      exceeds m_run by the threshold, which is rare after the first tile.
-  //      Then the slow path rescales O and l and recomputes P against the new
-  //      max. ----
+  //      8*(i/4) + 4*hf + i%4).  The tile's row maxima come first; P is then
+  //      computed against the running max m_run, which is exact and bounded
+  //      by 2^24 unless some row's tile max exceeds m_run by the threshold
+  //      (rare after the first tile).  Only then are O and l rescaled and
+  //      m_run moved to the new max, before P is computed.  Taking the max
+  //      first keeps S alone alive up to the decision, not S and a
+  //      speculative P. ----
   auto exp_tile = [&](const f32x16 &sacc, float mref, bf16x8 (&pb)[2]) JA_INLINE -> float {
     const float mc = mref * c;
     float lt = 0.f;
@@ -460,7 +467,7 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
     return lt;
   };
   auto softmax = [&]<bool TAIL>(f32x16 (&sacc)[RW], int j0, bf16x8 (&pb)[RW][2]) JA_INLINE {
-    float mx[RW], lt[RW];
+    float mx[RW];
     bool grow[RW], any = false;
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
@@ -475,15 +482,8 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
       mx[r] = half_max(mx[r]);
       grow[r] = mx[r] > m_run[r] + thresh;
       any = any || grow[r];
-      lt[r] = exp_tile(sacc[r], m_run[r], pb[r]);
     }
     if (__builtin_amdgcn_ballot_w64(any)) {
-      // keep the speculative P computed before the branch (it is the result
-      // on the common path); here it is replaced
-#pragma unroll
-      for (int r = 0; r < RW; ++r)
-#pragma unroll
-        for (int g = 0; g < 2; ++g) asm volatile("" ::"v"(pb[r][g]));
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         const float m_new = grow[r] ? mx[r] : m_run[r];
@@ -494,11 +494,10 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[r][db][i] *= alpha;
-        lt[r] = exp_tile(sacc[r], m_new, pb[r]);
       }
     }
 #pragma unroll
-    for (int r = 0; r < RW; ++r) l_run[r] += lt[r];
+    for (int r = 0; r < RW; ++r) l_run[r] += exp_tile(sacc[r], m_run[r], pb[r]);
   };
 
   // ---- loop over the workgroup's tiles (local index i, list position

@@ -17,7 +17,7 @@ namespace ja {
 
 namespace {
 
-constexpr int kMaxParts = 8;
+constexpr int kMaxParts = 16;
 constexpr int kMinTilesPerPart = 4;
 
 struct MergeArgs {
