@@ -90,16 +90,19 @@ __global__ __launch_bounds__(PT, 3) void prep_kv_bf16_kernel(PrepArgs a) {
   }
   // Loads are unconditional (a key past S reads key S-1; its V and its
   // rotated K are replaced by zeros), so the compiler keeps them together.
+  // K and V are read once: non-temporal loads keep them from displacing
+  // cache lines that are reused (the table; the prepared buffer, which the
+  // forward reads right after).
   u32x4 kw[IT][HG], vw[IT][HG];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int ks = min(k0 + r0 + it * (PT / CH), a.S - 1);
 #pragma unroll
     for (int g = 0; g < HG; ++g) {
-      kw[it][g] = *reinterpret_cast<const u32x4 *>(a.k + b * a.k_sb + (h0 + g) * a.k_sh +
-                                                   (int64_t)ks * a.k_ss + 8 * c);
-      vw[it][g] = *reinterpret_cast<const u32x4 *>(a.v + b * a.v_sb + (h0 + g) * a.v_sh +
-                                                   (int64_t)ks * a.v_ss + 8 * c);
+      kw[it][g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+          a.k + b * a.k_sb + (h0 + g) * a.k_sh + (int64_t)ks * a.k_ss + 8 * c));
+      vw[it][g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+          a.v + b * a.v_sb + (h0 + g) * a.v_sh + (int64_t)ks * a.v_ss + 8 * c));
     }
   }
   // the 4 table entries of each of the thread's keys (pairs 4c .. 4c+3)
