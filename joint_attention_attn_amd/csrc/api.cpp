@@ -151,7 +151,12 @@ int device_cu_count() {
 // Split plan of a forward, or no split when the flags say so.
 ja::SplitPlan no_split(const ja::SplitPlan &plan) {
   if (plan.n_units == 0) return plan;
-  return ja::SplitPlan{plan.n_direct + plan.n_units / plan.parts, 1, 0, 0};
+  ja::SplitPlan p = plan;
+  p.n_direct = plan.n_direct + plan.n_units / plan.parts;
+  p.parts = 1;
+  p.n_units = 0;
+  p.ws_bytes = 0;
+  return p;
 }
 ja::SplitPlan plan_bf16(const ja_params *p, bool sparse) {
   const ja::SplitPlan plan = ja::plan_fwd_bf16(layout(p), device_cu_count(), sparse);

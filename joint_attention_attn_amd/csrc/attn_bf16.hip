@@ -120,6 +120,7 @@ struct FwdArgs {
   // remaining ones are `parts` workgroups per item, each over a contiguous
   // range of key tiles, writing unnormalised partial results to `ws`.
   int n_direct, parts;
+  int qgroup;               // work-item order (item_coords)
   SplitWorkspace ws;
   // block-sparse variant: mask [B][H][nqb][nkb] (nonzero = keep)
   const uint8_t *mask;
@@ -205,8 +206,8 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
     part = unit % a.parts;
     item = a.n_direct + unit / a.parts;
   }
-  const int qblk = item % a.n_qblk;
-  const int bh = item / a.n_qblk;
+  int qblk, bh;
+  item_coords(item, a.n_qblk, a.B * a.H, a.qgroup, bh, qblk);
   const int h = bh % a.H, b = bh / a.H;
 
   // ---- block-sparse variant: compact the key blocks kept by any of this
@@ -630,7 +631,10 @@ SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse) {
   const int bm = fwd_bf16_block_rows(sparse);
   const int wg = sparse ? Cfg<true>::WG_PER_CU : Cfg<false>::WG_PER_CU;
   const int n_items = ((L.S + bm - 1) / bm) * L.H * L.B;
-  return plan_split(n_items, (L.S + BN - 1) / BN, n_cu * wg, bm, L.D);
+  SplitPlan p = plan_split(n_items, (L.S + BN - 1) / BN, n_cu * wg, bm, L.D);
+  // dense: the query blocks of a head run together on the CUs of one XCD
+  p.qgroup = sparse ? 0 : (n_cu >= 8 ? n_cu / 8 : 1);
+  return p;
 }
 
 int fwd_bf16_sparse_max_seq() { return kSparseMaxSeq; }
@@ -662,6 +666,7 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   a.scale_log2 = L.scale_log2;
   a.n_direct = plan.n_direct;
   a.parts = plan.parts;
+  a.qgroup = plan.qgroup;
   a.ws = split_workspace(plan, workspace, bm, L.D);
   a.mask = mask;
   a.nqb = (L.S + kQueryBlock - 1) / kQueryBlock;

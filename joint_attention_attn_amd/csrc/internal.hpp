@@ -32,7 +32,29 @@ struct SplitPlan {
   int parts = 1;        // key ranges per split item
   int n_units = 0;      // workgroups over key ranges (split items x parts)
   int64_t ws_bytes = 0; // workspace the split needs
+  int qgroup = 0;       // work-item order, see item_coords
 };
+
+// (batch x head, query block) of work item `item`.  qgroup = 0: head-major.
+// qgroup = G > 0: the first floor(n_qblk / G) * G query blocks of every
+// head, head-major, then the remaining blocks of every head.  With G the
+// CUs of one XCD and the forward's XCD-aware placement, a round of an XCD's
+// workgroups then covers G blocks of one head, which stream the same K/V
+// through that XCD's L2 together, and the leftover blocks gather in the
+// last round (the one the split cuts into key ranges).
+__host__ __device__ inline void item_coords(int item, int n_qblk, int n_bh, int qgroup, int &bh,
+                                            int &qblk) {
+  const int full_blocks = qgroup > 0 ? n_qblk / qgroup * qgroup : 0;
+  const int full_items = n_bh * full_blocks;
+  if (item < full_items) {
+    bh = item / full_blocks;
+    qblk = item % full_blocks;
+  } else {
+    const int j = item - full_items, rest = n_qblk - full_blocks;
+    bh = j / rest;
+    qblk = full_blocks + j % rest;
+  }
+}
 // Partial results of the split workgroups: O rows [n_units][block_rows][D]
 // (fp32, unnormalised) and (row max, row sum) [n_units][block_rows][2]; the
 // row max times the merge's m_scale is in the exp2 domain.

@@ -25,7 +25,7 @@ struct MergeArgs {
   bf16 *o;
   float *lse;
   int64_t o_sb, o_ss, o_sh;
-  int S, H, n_qblk, block_rows, n_direct, parts, n_split;
+  int S, H, B, n_qblk, block_rows, n_direct, parts, n_split, qgroup;
   float scale_log2;   // factor from stored row maxima to the exp2 domain
 };
 
@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void merge_split_kernel(MergeArgs m) {
   const int row = (int)(rr % m.block_rows);
   const int sidx = (int)(rr / m.block_rows);
   const int item = m.n_direct + sidx;
-  const int qblk = item % m.n_qblk, bh = item / m.n_qblk;
+  int qblk, bh;
+  item_coords(item, m.n_qblk, m.B * m.H, m.qgroup, bh, qblk);
   const int h = bh % m.H, b = bh / m.H;
   const int qi = qblk * m.block_rows + row;
   if (qi >= m.S) return;
@@ -124,7 +125,9 @@ hipError_t launch_merge_split(const AttnLayout &L, const SplitPlan &plan,
   m.o_sb = L.o_sb; m.o_ss = L.o_ss; m.o_sh = L.o_sh;
   m.S = L.S;
   m.H = L.H;
+  m.B = L.B;
   m.n_qblk = (L.S + block_rows - 1) / block_rows;
+  m.qgroup = plan.qgroup;
   m.block_rows = block_rows;
   m.n_direct = plan.n_direct;
   m.parts = plan.parts;
