@@ -20,10 +20,11 @@
 //   repair_err_kernel     one lane group per (b, token, head) vector, as in the
 //                         quantizer; writes e into kbias [B][H][S].
 //   repair_select_kernel  one workgroup per (b, h): finds the n-th largest e by
-//                         a bitwise search over its fp32 pattern (e >= 0, so
-//                         the patterns order like the values), ranks ties by
-//                         index with block scans, writes the ascending index
-//                         list and kbias = 0 / -inf, then gathers kr / vr.
+//                         a radix select over its fp32 pattern, four 8-bit
+//                         digits (e >= 0, so the patterns order like the
+//                         values), ranks ties by index with block scans,
+//                         writes the ascending index list and kbias = 0 /
+//                         -inf, then gathers kr / vr.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -146,6 +147,8 @@ template <int D>
 __global__ __launch_bounds__(SEL_NT) void repair_select_kernel(SelArgs a) {
   extern __shared__ uint32_t ekey[];        // [S] fp32 patterns of e
   __shared__ int red[SEL_NT / 64];
+  __shared__ int hist[256];                 // radix-select histogram
+  __shared__ int sel_digit[2];              // chosen digit, rank within it
   const int tid = threadIdx.x;
   const int h = blockIdx.x % a.H, b = blockIdx.x / a.H;
   const int64_t bh = (int64_t)b * a.H + h;
@@ -158,13 +161,51 @@ __global__ __launch_bounds__(SEL_NT) void repair_select_kernel(SelArgs a) {
   const int per = (S + SEL_NT - 1) / SEL_NT;
   const int s0 = min(S, tid * per), s1 = min(S, s0 + per);
 
-  uint32_t thr = 0;   // n-th largest pattern
+  // n-th largest pattern, by a radix select over four 8-bit digits from the
+  // top: each pass histograms the next digit of the patterns that match the
+  // digits fixed so far, and keeps the digit whose bin holds the target rank
+  // (counted from the largest)
+  uint32_t thr = 0;
   if (n > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      int c = 0;
-      for (int s = s0; s < s1; ++s) c += ekey[s] >= cand;
-      if (block_sum(c, red) >= n) thr = cand;
+    uint32_t mask = 0;
+    int rank = n;       // rank of the target among the patterns matching thr
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int s = s0; s < s1; ++s) {
+        const uint32_t key = ekey[s];
+        if ((key & mask) == thr) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // lane l holds bins 255-4l, ..., 252-4l (descending); counts above
+        // each bin by an inclusive scan over the lanes
+        int c[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = hist[255 - 4 * tid - j];
+          tot += c[j];
+        }
+        int incl = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(incl, off);
+          if (tid >= off) incl += y;
+        }
+        int above = incl - tot;   // patterns in the bins above this lane's
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (above < rank && rank <= above + c[j]) {
+            sel_digit[0] = 255 - 4 * tid - j;
+            sel_digit[1] = rank - above;
+          }
+          above += c[j];
+        }
+      }
+      __syncthreads();
+      thr |= (uint32_t)sel_digit[0] << shift;
+      rank = sel_digit[1];
+      mask |= 255u << shift;
     }
   }
   int gt = 0, eq = 0;
