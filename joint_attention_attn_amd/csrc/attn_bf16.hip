@@ -142,10 +142,14 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS ring: NSTAGE stages of [K tile | V^T tile].  A K row is D bf16 plus a
-// 16-byte pad; the K part is rounded up to whole 1 KB loads (one wave's 64
-// lanes x 16 bytes), the slack taking the dummy chunks.  A V^T row is the 32
-// keys of one head-dimension column, 64 bytes, granule g stored at g ^ vswz.
+// LDS ring: NSTAGE stages of [K tile | V^T tile].  The K tile is stored in
+// the order in which the Q K^T fragment reads consume it: for each 16-column
+// block kk of the head dimension, 1 KB holding, at position 16 lane, the
+// 8 bf16 that `lane` reads (key lane % 32, columns 16 kk + 8 (lane / 32) ..
+// + 7).  A fragment read is then one 1 KB block read contiguously by the
+// wave's lanes (conflict-free, immediate offsets), and the tile is whole
+// 1 KB loads without padding.  A V^T row is the 32 keys of one
+// head-dimension column, 64 bytes, granule g stored at g ^ vswz.
 // Granule position of V^T row d's granule g is g ^ vswz(d): the 16 rows read
 // together by a fragment read then cover all 16 bank groups of 16 bytes.
 __host__ __device__ constexpr int vswz(int d) { return (d / 4) % 4; }
@@ -153,9 +157,7 @@ __host__ __device__ constexpr int vswz(int d) { return (d / 4) % 4; }
 template <int D, int NSTAGE>
 struct Lds {
   static constexpr int CH = D / 8;                    // 16-byte chunks per K row
-  static constexpr int KSTR = D + 8;                  // bf16 per K row
-  static constexpr int K_GRANULES = BN * (CH + 1);    // K part incl. pads
-  static constexpr int K_LOADS = (K_GRANULES + 63) / 64;
+  static constexpr int K_LOADS = D / 16;              // K part: one 1 KB block per kk
   static constexpr int V_LOADS = D * (BN / 8) / 64;   // V^T part: 4 granules per row
   static constexpr int LOADS = K_LOADS + V_LOADS;     // 1 KB loads per tile
   static constexpr int KBYTES = K_LOADS * 1024;
@@ -174,8 +176,6 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
                 BM = Cfg<SPARSE>::BM;
   constexpr int NSTAGE = Cfg<SPARSE>::NSTAGE, QB_PER_WG = Cfg<SPARSE>::QB_PER_WG;
   using L = Lds<D, NSTAGE>;
-  constexpr int CH = L::CH;
-  constexpr int KSTR = L::KSTR;
   constexpr int LOADS = L::LOADS, K_LOADS = L::K_LOADS;
   constexpr int JW = (LOADS + NW - 1) / NW;           // tile loads per wave, at most
   static_assert(JW <= 5, "at most five tile loads per wave");
@@ -311,9 +311,9 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
 
   // ---- tile loads: load j (0 <= j < LOADS) of a tile fills LDS bytes
   //      [j KB, (j+1) KB) of its stage, lane i the 16 bytes at 16 i.  Loads
-  //      below K_LOADS carry the K rows: granule G = 64 j + i is chunk
-  //      G % (CH+1) of row G / (CH+1), and pad or slack granules take a dummy
-  //      chunk.  The others carry V^T rows, 16 per load: row
+  //      below K_LOADS carry the K tile's column block kk = j: lane i the
+  //      chunk 2 j + i / 32 of key i % 32.  The others carry V^T rows, 16
+  //      per load: row
   //      d = 16 (j - K_LOADS) + i / 4, position i % 4 holding granule
   //      (i % 4) ^ vswz(d) of the row.  Wave w issues loads w, w + NW, ...
   //      The lane offsets are fixed (scalars: an array element as the
@@ -324,11 +324,7 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16 *>(a.vt + (int64_t)bh * D * a.S_pad), 0, a.S_pad * D * 2, kBufferFlags);
   auto load_offset = [&](int j) JA_INLINE -> int {
-    if (j < K_LOADS) {
-      const int g = 64 * j + lane;
-      const int r = g / (CH + 1), c = g % (CH + 1);
-      return (r < BN && c < CH) ? (r * D + 8 * c) * 2 : 0;
-    }
+    if (j < K_LOADS) return ((lane % 32) * D + 8 * (2 * j + lane / 32)) * 2;
     const int d = 16 * (j - K_LOADS) + lane / 4;
     return (d * a.S_pad + 8 * ((lane % 4) ^ vswz(d))) * 2;
   };
@@ -378,11 +374,11 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[r][i] = 0.f;
     }
-    const bf16 *krow = Kst(buf) + l32 * KSTR + 8 * hf;
+    const bf16 *krow = Kst(buf) + 8 * lane;
     bf16x8 kf[kPrefetch];
 #pragma unroll
     for (int j = 0; j < kPrefetch && KK0 + j < KK1; ++j)
-      kf[j] = *reinterpret_cast<const bf16x8 *>(krow + 16 * (KK0 + j));
+      kf[j] = *reinterpret_cast<const bf16x8 *>(krow + 512 * (KK0 + j));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = KK0; kk < KK1; ++kk) {
@@ -391,7 +387,7 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
         sacc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[(kk - KK0) % kPrefetch], qreg[r][kk],
                                                           sacc[r], 0, 0, 0);
       if (kk + kPrefetch < KK1)
-        kf[(kk - KK0) % kPrefetch] = *reinterpret_cast<const bf16x8 *>(krow + 16 * (kk + kPrefetch));
+        kf[(kk - KK0) % kPrefetch] = *reinterpret_cast<const bf16x8 *>(krow + 512 * (kk + kPrefetch));
       __builtin_amdgcn_sched_barrier(0);
     }
   };
