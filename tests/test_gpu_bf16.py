@@ -214,6 +214,33 @@ def test_split_last_round_parity():
     assert max_abs(lse, lse_ns) <= 1e-2
 
 
+def test_split_round_mixing_whole_and_leftover_query_blocks():
+    # 16500 tokens make 33 query blocks of 512 rows per head, the last one
+    # partial (116 rows).  The work items are the first 32 blocks of every
+    # head, head by head, then the 33rd block of every head; with 26 heads on
+    # 256 CUs the last round (90 items, split over key ranges) holds the
+    # first 32 blocks of heads 24 and 25 and all 26 partial blocks.  Sampled
+    # rows cover early blocks, the split heads and the partial last block;
+    # the unsplit launch is the second reference.
+    w = synth.Workload("mixed_split", 1, 26, 128, n_text=116, grid=128, outlier_frac=0.01)
+    ws = (ja.fwd_bf16_workspace_bytes(1, w.seq_len, w.heads, 128)
+          - ja.fwd_bf16_workspace_bytes(1, w.seq_len, w.heads, 128, split=False))
+    q, k, v, idx, pos = _gpu_inputs(w, 11)
+    _say(f"bf16 mixed split round: S={w.seq_len} H={w.heads} workspace={ws} B")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    out_ns, lse_ns = _run_bf16(q, k, v, pos, return_lse=True, split=False)
+    rows = np.unique(np.concatenate([sample_rows(w.seq_len, w.n_text, idx, 96, seed=3),
+                                     np.arange(16384, w.seq_len, 5), [15871, 15872, 16383]]))
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos, rows=rows)
+    got, got_lse = out.cpu()[:, rows], lse.cpu()[:, :, rows]
+    _say(f"  rel_l2={rel_l2(got, ref):.3e} vs unsplit {rel_l2(out.cpu(), out_ns.cpu()):.3e}")
+    assert rel_l2(got, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(got, ref) <= BF16_MAX_ABS
+    assert max_abs(got_lse, ref_lse) <= 2e-2
+    assert rel_l2(out.cpu(), out_ns.cpu()) <= 2e-3
+    assert max_abs(lse, lse_ns) <= 1e-2
+
+
 def _slot_key(p):
     # key of P-operand slot p in a 16-key group (the V^T order the header documents)
     return 4 * (p // 8) + (p % 8 if p % 8 < 4 else p % 8 + 4)
