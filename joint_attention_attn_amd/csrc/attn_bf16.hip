@@ -29,9 +29,10 @@
 // go from HBM straight into an LDS ring (four stages; three for the
 // block-sparse variant's smaller workgroups) with buffer loads to LDS: no
 // registers, no VALU work, and the loads of a tile are issued a ring's depth
-// minus one tiles ahead of its use.  K rows are padded by one 16-byte granule (the lanes that
-// would fill a pad load a dummy chunk) and V^T rows are XOR-swizzled, so that
-// the 16 lanes served together by a fragment read hit distinct banks.
+// minus one tiles ahead of its use.  A K tile is stored in fragment order
+// (1 KB per 16-column step: lane l's 16 bytes of row l%32 at byte 16 l) and
+// V^T rows are XOR-swizzled, so that the 16 lanes served together by a
+// fragment read hit distinct banks.
 //
 // Each wave runs Q K^T, softmax and P.V of a tile in turn; the two waves of
 // a SIMD overlap one another's MFMA, VALU and memory waits (a wave fits in
