@@ -66,19 +66,22 @@ constexpr int kQueryBlock = 128;
 constexpr int kKeyBlock = 64;
 constexpr int KB_TILES = kKeyBlock / BN;              // key tiles per key block
 
-// Workgroup shape.  Dense: one workgroup of 8 waves of 64 rows per CU, two
-// per SIMD at most 256 VGPRs each, over a 4-stage ring; latency is hidden by
-// the two waves of a SIMD rather than by software pipelining inside a wave
-// (which needs more registers).  Block-sparse: one 128-row query block per
+// Workgroup shapes.  Wide (the dense forward when its items fill the CUs):
+// one workgroup of 8 waves of 64 rows per CU, two per SIMD at most 256
+// VGPRs each, over a 4-stage ring; latency is hidden by the two waves of a
+// SIMD rather than by software pipelining inside a wave (which needs more
+// registers).  Small (the block-sparse variant, and the dense forward when
+// the wide items would fill at most half of the CUs): one 128-row query block per
 // workgroup of 4 waves of 32 rows, three workgroups per CU over 3-stage
-// rings, so that a workgroup stages only the key tiles its own query block
-// keeps and no wave waits on a tile it does not use.
-template <bool SPARSE>
+// rings, so that a block-sparse workgroup stages only the key tiles its own
+// query block keeps, and a short dense launch has four times as many items
+// to spread over the CUs.
+template <bool SMALL>
 struct Cfg {
-  static constexpr int RW = SPARSE ? 1 : 2;           // 32-row query blocks per wave
-  static constexpr int NW = SPARSE ? 4 : 8;           // waves per workgroup
-  static constexpr int NSTAGE = SPARSE ? 3 : 4;       // K/V tiles in the LDS ring
-  static constexpr int WG_PER_CU = SPARSE ? 3 : 1;
+  static constexpr int RW = SMALL ? 1 : 2;            // 32-row query blocks per wave
+  static constexpr int NW = SMALL ? 4 : 8;            // waves per workgroup
+  static constexpr int NSTAGE = SMALL ? 3 : 4;        // K/V tiles in the LDS ring
+  static constexpr int WG_PER_CU = SMALL ? 3 : 1;
   static constexpr int BM = 32 * RW * NW;             // query rows per workgroup
   static constexpr int NT = 64 * NW;                  // threads per workgroup
   static constexpr int QB_PER_WG = BM / kQueryBlock;  // query blocks per workgroup
@@ -170,12 +173,13 @@ struct Lds {
 };
 
 
-template <int D, bool ROPE, bool SPARSE>
-__global__ __launch_bounds__(Cfg<SPARSE>::NT, Cfg<SPARSE>::WG_PER_CU)
+template <int D, bool ROPE, bool SPARSE, bool SMALL>
+__global__ __launch_bounds__(Cfg<SMALL>::NT, Cfg<SMALL>::WG_PER_CU)
 void attn_fwd_bf16_kernel(FwdArgs a) {
-  constexpr int RW = Cfg<SPARSE>::RW, NW = Cfg<SPARSE>::NW, NT = Cfg<SPARSE>::NT,
-                BM = Cfg<SPARSE>::BM;
-  constexpr int NSTAGE = Cfg<SPARSE>::NSTAGE, QB_PER_WG = Cfg<SPARSE>::QB_PER_WG;
+  static_assert(SMALL || !SPARSE, "the block-sparse variant has the small shape");
+  constexpr int RW = Cfg<SMALL>::RW, NW = Cfg<SMALL>::NW, NT = Cfg<SMALL>::NT,
+                BM = Cfg<SMALL>::BM;
+  constexpr int NSTAGE = Cfg<SMALL>::NSTAGE, QB_PER_WG = Cfg<SMALL>::QB_PER_WG;
   using L = Lds<D, NSTAGE>;
   constexpr int LOADS = L::LOADS, K_LOADS = L::K_LOADS;
   constexpr int JW = (LOADS + NW - 1) / NW;           // tile loads per wave, at most
@@ -589,9 +593,9 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
 
 // Dynamic LDS of one instantiation; its limit is raised once per device (the
 // attribute is set with the device current).
-template <int D, bool ROPE, bool SPARSE>
+template <int D, bool ROPE, bool SPARSE, bool SMALL>
 hipError_t launch_instance(const FwdArgs &a, dim3 grid, hipStream_t st) {
-  using L = Lds<D, Cfg<SPARSE>::NSTAGE>;
+  using L = Lds<D, Cfg<SMALL>::NSTAGE>;
   const int bytes = SPARSE ? L::sparse_bytes(a.nkb) : L::BYTES;
   constexpr int kMaxDevices = 64;
   static std::atomic<bool> done[kMaxDevices];
@@ -600,37 +604,48 @@ hipError_t launch_instance(const FwdArgs &a, dim3 grid, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices || !done[dev].load(std::memory_order_acquire)) {
     e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<D, ROPE, SPARSE>),
+        reinterpret_cast<const void *>(&attn_fwd_bf16_kernel<D, ROPE, SPARSE, SMALL>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
         SPARSE ? L::sparse_bytes((kSparseMaxSeq + kKeyBlock - 1) / kKeyBlock) : L::BYTES);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) done[dev].store(true, std::memory_order_release);
   }
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, ROPE, SPARSE>), grid, dim3(Cfg<SPARSE>::NT), bytes,
-                     st, a);
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, ROPE, SPARSE, SMALL>), grid, dim3(Cfg<SMALL>::NT),
+                     bytes, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dim(const FwdArgs &a, dim3 grid, bool rope_on, hipStream_t st) {
+hipError_t launch_dim(const FwdArgs &a, dim3 grid, bool rope_on, bool small, hipStream_t st) {
   if (a.mask)
-    return rope_on ? launch_instance<D, true, true>(a, grid, st)
-                   : launch_instance<D, false, true>(a, grid, st);
-  return rope_on ? launch_instance<D, true, false>(a, grid, st)
-                 : launch_instance<D, false, false>(a, grid, st);
+    return rope_on ? launch_instance<D, true, true, true>(a, grid, st)
+                   : launch_instance<D, false, true, true>(a, grid, st);
+  if (small)
+    return rope_on ? launch_instance<D, true, false, true>(a, grid, st)
+                   : launch_instance<D, false, false, true>(a, grid, st);
+  return rope_on ? launch_instance<D, true, false, false>(a, grid, st)
+                 : launch_instance<D, false, false, false>(a, grid, st);
 }
 
 }  // namespace
 
-int fwd_bf16_block_rows(bool sparse) { return sparse ? Cfg<true>::BM : Cfg<false>::BM; }
+int fwd_bf16_block_rows(bool small) { return small ? Cfg<true>::BM : Cfg<false>::BM; }
 
 SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse) {
-  const int bm = fwd_bf16_block_rows(sparse);
-  const int wg = sparse ? Cfg<true>::WG_PER_CU : Cfg<false>::WG_PER_CU;
+  // The dense forward takes the small shape when the wide items would leave
+  // at least half of the CUs idle.  (Between half and one round the wide
+  // shape stays ahead: at 16896 tokens and 6 heads, 198 wide items, it is
+  // 5 % faster than 792 small ones; at 3 heads the small shape is 30 %
+  // faster.)
+  const int64_t wide_items = (int64_t)((L.S + Cfg<false>::BM - 1) / Cfg<false>::BM) * L.H * L.B;
+  const bool small = sparse || 2 * wide_items <= n_cu;
+  const int bm = fwd_bf16_block_rows(small);
+  const int wg = small ? Cfg<true>::WG_PER_CU : Cfg<false>::WG_PER_CU;
   const int n_items = ((L.S + bm - 1) / bm) * L.H * L.B;
   SplitPlan p = plan_split(n_items, (L.S + BN - 1) / BN, n_cu * wg, bm, L.D);
+  p.small = small;
   // dense: the query blocks of a head run together on the CUs of one XCD
-  p.qgroup = sparse ? 0 : (n_cu >= 8 ? n_cu / 8 : 1);
+  p.qgroup = sparse ? 0 : (n_cu >= 8 ? n_cu / 8 * wg : 1);
   return p;
 }
 
@@ -658,7 +673,8 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   a.S_pad = prep_pad(L.S);
   a.H = L.H;
   a.B = L.B;
-  const int bm = fwd_bf16_block_rows(mask != nullptr);
+  const bool small = mask != nullptr || plan.small;
+  const int bm = fwd_bf16_block_rows(small);
   a.n_qblk = (L.S + bm - 1) / bm;
   a.scale_log2 = L.scale_log2;
   a.n_direct = plan.n_direct;
@@ -669,8 +685,8 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   a.nqb = (L.S + kQueryBlock - 1) / kQueryBlock;
   a.nkb = (L.S + kKeyBlock - 1) / kKeyBlock;
   const dim3 grid((unsigned)(plan.n_direct + plan.n_units));
-  const hipError_t e = L.D == 64 ? launch_dim<64>(a, grid, rope != nullptr, st)
-                                 : launch_dim<128>(a, grid, rope != nullptr, st);
+  const hipError_t e = L.D == 64 ? launch_dim<64>(a, grid, rope != nullptr, small, st)
+                                 : launch_dim<128>(a, grid, rope != nullptr, small, st);
   if (e != hipSuccess || plan.n_units == 0) return e;
   return launch_merge_split(L, plan, a.ws, bm, L.scale_log2, o, lse, st);
 }

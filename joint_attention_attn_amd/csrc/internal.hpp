@@ -33,6 +33,7 @@ struct SplitPlan {
   int n_units = 0;      // workgroups over key ranges (split items x parts)
   int64_t ws_bytes = 0; // workspace the split needs
   int qgroup = 0;       // work-item order, see item_coords
+  bool small = false;   // bf16 dense forward: the 128-row workgroup shape
 };
 
 // (batch x head, query block) of work item `item`.  qgroup = 0: head-major.
@@ -124,7 +125,7 @@ int fwd_fp8_sparse_max_seq();    // longest sequence of the block-sparse variant
 
 // Query rows per workgroup of each forward kernel (the grid's x extent is
 // ceil(S / rows)).
-int fwd_bf16_block_rows(bool sparse);
+int fwd_bf16_block_rows(bool small);
 int fwd_fp8_block_rows(bool sparse);
 
 }  // namespace ja

@@ -80,6 +80,27 @@ def test_ragged_lengths(s, d):
     assert max_abs(lse, ref_lse) <= 1e-2
 
 
+@pytest.mark.parametrize("s,d,b,h", [(1, 64, 4, 64), (65, 128, 4, 64), (700, 128, 2, 64),
+                                     (1037, 64, 2, 64)])
+def test_ragged_lengths_wide_shape(s, d, b, h):
+    # Enough (512-query block, head, batch row) items to fill the CUs, so the
+    # forward runs its wide shape (eight 64-row waves per workgroup) on
+    # ragged lengths; the shapes above, whose wide items would fill at most
+    # half of the CUs, run the small one (four 32-row waves).
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert -(-s // 512) * h * b >= n_cu
+    w = synth.Workload("ragged_wide", b, h, d, n_text=s, grid=0, outlier_frac=0.02)
+    q, k, v, _ = synth.make_qkv(w, seed=s)
+    rng = np.random.default_rng(s)
+    pos = rng.integers(0, 200, size=(s, 2)).astype(np.int32)
+    _say(f"bf16 ragged wide S={s} D={d} B={b} H={h}")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos)
+    assert rel_l2(out, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
+    assert max_abs(lse, ref_lse) <= 1e-2
+
+
 def test_no_rope_and_custom_scale():
     w = synth.Workload("norope", 1, 2, 128, n_text=300, grid=0)
     q, k, v, _ = synth.make_qkv(w, seed=11)
@@ -178,6 +199,25 @@ def test_2048_sampled_parity(name, n_rows):
     else:
         assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
     assert max_abs(lse, ref_lse) <= 2e-2
+
+
+@pytest.mark.parametrize("heads", [6, 3])
+def test_sequence_parallel_shard_shapes(heads):
+    # The per-GPU share of 16896 tokens under sequence parallelism over 4 or
+    # 8 GPUs: all tokens, 24/u heads.  Six heads give 198 wide items (the
+    # wide shape, one partial round); three give 99, which the small shape
+    # (396 items of 128 rows) covers.
+    w = synth.WORKLOADS["t2i_2048"].replace(heads=heads)
+    q, k, v, idx, pos = _gpu_inputs(w, 7)
+    rows = sample_rows(w.seq_len, w.n_text, idx, 128, seed=heads)
+    _say(f"bf16 shard shape S={w.seq_len} H={heads} sampled rows={len(rows)}")
+    out, lse = _run_bf16(q, k, v, pos, return_lse=True)
+    ref, ref_lse = oracle.joint_attention(q, k, v, pos, rows=rows)
+    got, got_lse = out.cpu()[:, rows], lse.cpu()[:, :, rows]
+    _say(f"  rel_l2={rel_l2(got, ref):.3e}")
+    assert rel_l2(got, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(got, ref) <= BF16_MAX_ABS
+    assert max_abs(got_lse, ref_lse) <= 2e-2
 
 
 def test_split_last_round_parity():
