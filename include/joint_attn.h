@@ -212,9 +212,11 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len, int32_t 
  *   kv       device buffer (16-byte aligned) of kv_bytes >=
  *            joint_attn_prep_kv_bf16_bytes(p), written with
  *              Kr [batch*heads][S_pad][head_dim]  rotated K (bf16),
- *              Vt [batch*heads][head_dim][S_pad]  V transposed, the keys of
- *                   every 16-key group in the order p -> 4*(p/8) + (p%8 < 4 ?
- *                   p%8 : p%8 + 4) (the P operand order of the forward),
+ *              Vt [batch*heads][S_pad/32][head_dim][32]  V transposed in
+ *                   tiles of 32 keys (per tile one row of 32 keys for each
+ *                   head-dimension column), the keys of every 16-key group
+ *                   in the order p -> 4*(p/8) + (p%8 < 4 ? p%8 : p%8 + 4)
+ *                   (the P operand order of the forward),
  *              and, when p gives pos without rope_table, the RoPE table of
  *              pos (fp64 [seq_len][head_dim/2][2]),
  *            S_pad = seq_len rounded up to 64, zeros past seq_len.

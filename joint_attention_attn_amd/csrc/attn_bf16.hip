@@ -60,6 +60,7 @@ namespace ja {
 namespace {
 
 constexpr int BN = 32;              // keys per K/V tile
+static_assert(BN == kVtTile, "a V^T tile of the prepared buffer is one K/V tile");
 
 // Block-mask granularity of the block-sparse variant.
 constexpr int kQueryBlock = 128;
@@ -331,7 +332,7 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
   auto load_offset = [&](int j) JA_INLINE -> int {
     if (j < K_LOADS) return ((lane % 32) * D + 8 * (2 * j + lane / 32)) * 2;
     const int d = 16 * (j - K_LOADS) + lane / 4;
-    return (d * a.S_pad + 8 * ((lane % 4) ^ vswz(d))) * 2;
+    return (d * BN + 8 * ((lane % 4) ^ vswz(d))) * 2;
   };
   auto voff_of = [&](int m) JA_INLINE -> int {
     return wave + m * NW < LOADS ? load_offset(wave + m * NW) : 0;
@@ -344,7 +345,7 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
     if (j < K_LOADS)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, JA_LDS_PTR(dst), 16, voff, t * (BN * D * 2), 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, JA_LDS_PTR(dst), 16, voff, t * (BN * 2), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, JA_LDS_PTR(dst), 16, voff, t * (BN * D * 2), 0, 0);
   };
   // loads of key tile t into stage st
   auto issue = [&](int t, int st) JA_INLINE {

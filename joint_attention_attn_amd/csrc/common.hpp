@@ -274,6 +274,9 @@ __device__ __forceinline__ u32x4 prologue_chunk_bf16(u32x4 w, double r, const fl
 __host__ __device__ constexpr int vt_key_of_slot(int p) {
   return 4 * (p / 8) + (p % 8 < 4 ? p % 8 : p % 8 + 4);
 }
+// BF16 path: keys per tile of the prepared V^T (one 64-byte row per
+// head-dimension column and tile).
+constexpr int kVtTile = 32;
 
 // FP8 forward: position of key r (0..63) of a tile inside a V^T row: the P' operand of
 // lane half hf holds, in slot kb*16 + g*4 + i, key kb*32 + g*8 + hf*4 + i

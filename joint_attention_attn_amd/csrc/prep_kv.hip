@@ -19,10 +19,13 @@
 // Layout of the prepared buffer, Kr then Vt (S_pad = S rounded up to 64
 // keys; rows and columns past S are 0):
 //   Kr [B*H][S_pad][D]  rotated K, one row per key;
-//   Vt [B*H][D][S_pad]  V transposed, one row per head-dimension column; in
-//                       every 16-key group the keys are stored in the order
-//                       in which the attention kernel's P operand holds them
-//                       (position p holds key vt_key_of_slot(p)).
+//   Vt [B*H][S_pad/32][D][32]  V transposed in tiles of 32 keys: per tile
+//                       one 64-byte row per head-dimension column, so that a
+//                       tile of the attention kernel is one contiguous 8 KB
+//                       (D = 128) block; in every 16-key group the keys are
+//                       stored in the order in which the attention kernel's
+//                       P operand holds them (position p holds key
+//                       vt_key_of_slot(p)).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -173,9 +176,10 @@ __global__ __launch_bounds__(PT, 3) void prep_kv_bf16_kernel(PrepArgs a) {
       w[e] = __builtin_amdgcn_perm(v1, v0, 0x05040100u);    // row d:   key r0 | key r1
       x[e] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);    // row d+1: key r0 | key r1
     }
-    *reinterpret_cast<u32x4 *>(vtb + (int64_t)d * a.S_pad + k0 + 8 * j) = u32x4{w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u32x4 *>(vtb + (int64_t)(d + 1) * a.S_pad + k0 + 8 * j) =
-        u32x4{x[0], x[1], x[2], x[3]};
+    const int kk = k0 + 8 * j;           // first key of the chunk
+    bf16 *vtt = vtb + (int64_t)(kk / kVtTile) * (D * kVtTile) + kk % kVtTile;
+    *reinterpret_cast<u32x4 *>(vtt + d * kVtTile) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4 *>(vtt + (d + 1) * kVtTile) = u32x4{x[0], x[1], x[2], x[3]};
   }
 }
 

@@ -292,7 +292,8 @@ def _slot_key(p):
                                            (130, 64, True, 6)])
 def test_prep_kv_bit_exact(s, d, strided, h):
     # rotated K equals the oracle's bf16-rounded rotation bit for bit; V^T is
-    # V transposed in the documented key order; padding is zero
+    # V transposed in 32-key tiles in the documented key order; padding is
+    # zero
     w = synth.Workload("prep", 2, h, d, n_text=s, grid=0)
     q, k, v, _ = synth.make_qkv(w, seed=21)
     pos = np.random.default_rng(s).integers(0, 300, size=(s, 2)).astype(np.int32)
@@ -308,7 +309,7 @@ def test_prep_kv_bit_exact(s, d, strided, h):
     s_pad = (s + 63) // 64 * 64
     n = 2 * h * s_pad * d
     kr = kv[: 2 * n].view(torch.bfloat16).view(2, h, s_pad, d)
-    vt = kv[2 * n:4 * n].view(torch.bfloat16).view(2, h, d, s_pad)
+    vt = kv[2 * n:4 * n].view(torch.bfloat16).view(2, h, s_pad // 32, d, 32)
     assert torch.equal(kv_pos[:kv.numel()], kv)
     table = kv_pos[kv.numel():kv.numel() + s * d * 8].numpy().view(np.float64)
     assert np.array_equal(table, rope.cpu().numpy().ravel())
@@ -319,6 +320,7 @@ def test_prep_kv_bit_exact(s, d, strided, h):
     vpad = torch.zeros((2, s_pad, h, d), dtype=torch.bfloat16)
     vpad[:, :s] = v
     vref = vpad[:, order].permute(0, 2, 3, 1)            # [B, H, D, S_pad]
+    vref = vref.reshape(2, h, d, s_pad // 32, 32).permute(0, 1, 3, 2, 4)   # 32-key tiles
     assert torch.equal(vt.view(torch.int16), vref.contiguous().view(torch.int16))
 
 
