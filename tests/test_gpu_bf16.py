@@ -80,20 +80,22 @@ def test_ragged_lengths(s, d):
     assert max_abs(lse, ref_lse) <= 1e-2
 
 
-@pytest.mark.parametrize("s,d,b,h", [(1, 64, 4, 64), (65, 128, 4, 64), (700, 128, 2, 64),
-                                     (1037, 64, 2, 64)])
-def test_ragged_lengths_wide_shape(s, d, b, h):
+@pytest.mark.parametrize("s,d,b,h,rope", [(1, 64, 4, 64, True), (65, 128, 4, 64, True),
+                                          (700, 128, 2, 64, True), (1037, 64, 2, 64, True),
+                                          (520, 128, 2, 64, False)])
+def test_ragged_lengths_wide_shape(s, d, b, h, rope):
     # Enough (512-query block, head, batch row) items to fill the CUs, so the
     # forward runs its wide shape (eight 64-row waves per workgroup) on
-    # ragged lengths; the shapes above, whose wide items would fill at most
-    # half of the CUs, run the small one (four 32-row waves).
+    # ragged lengths, with and without RoPE; the shapes above, whose wide
+    # items would fill at most half of the CUs, run the small one (four
+    # 32-row waves).
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     assert -(-s // 512) * h * b >= n_cu
     w = synth.Workload("ragged_wide", b, h, d, n_text=s, grid=0, outlier_frac=0.02)
     q, k, v, _ = synth.make_qkv(w, seed=s)
     rng = np.random.default_rng(s)
-    pos = rng.integers(0, 200, size=(s, 2)).astype(np.int32)
-    _say(f"bf16 ragged wide S={s} D={d} B={b} H={h}")
+    pos = rng.integers(0, 200, size=(s, 2)).astype(np.int32) if rope else None
+    _say(f"bf16 ragged wide S={s} D={d} B={b} H={h} rope={rope}")
     out, lse = _run_bf16(q, k, v, pos, return_lse=True)
     ref, ref_lse = oracle.joint_attention(q, k, v, pos)
     assert rel_l2(out, ref) <= BF16_REL_L2
