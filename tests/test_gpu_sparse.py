@@ -172,3 +172,30 @@ def test_longest_sequence_sampled_rows():
     _say(f"  rel_l2={rel_l2(got, ref):.3e}")
     assert rel_l2(got, ref) <= BF16_REL_L2 and max_abs(got, ref) <= BF16_MAX_ABS
     _lse_close(lse.cpu()[:, :, rows], ref_lse)
+
+
+@pytest.mark.parametrize("use_table", [True, False])
+def test_prepared_matches_one_call(use_table):
+    # The two-phase form (K/V prepared once, then the masked forward) gives
+    # the one-call result bit for bit, with a prebuilt RoPE table or with
+    # the positions (the table then built by the preparation call).
+    w = synth.Workload("sparse_prep", 2, 3, 128, n_text=1100, grid=0, outlier_frac=0.01)
+    q, k, v, _ = synth.make_qkv(w, seed=9)
+    pos = np.random.default_rng(9).integers(0, 200, size=(w.seq_len, 2)).astype(np.int32)
+    mask = synth.make_block_mask(w, 0.5, seed=10)
+    mask[1, 2, 0] = 0
+    _say(f"sparse prepared table={use_table}")
+    out, lse = _run(q, k, v, mask, pos)
+    qd, kd, vd, md = q.to(DEV), k.to(DEV), v.to(DEV), mask.to(DEV)
+    if use_table:
+        rope = _rope(pos, 128)
+        kv = ja.prep_kv_bf16(kd, vd, rope=rope)
+        out2, lse2 = ja.fwd_bf16_block_sparse_prepared(qd, kv, md, rope=rope, return_lse=True)
+    else:
+        kv = ja.prep_kv_bf16(kd, vd, pos)
+        out2, lse2 = ja.fwd_bf16_block_sparse_prepared(qd, kv, md, pos, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    ref, ref_lse = oracle.block_sparse_attention(q, k, v, mask, pos)
+    _check(out2.cpu(), lse2, ref, ref_lse, scaled=True)
