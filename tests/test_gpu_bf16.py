@@ -103,6 +103,28 @@ def test_ragged_lengths_wide_shape(s, d, b, h, rope):
     assert max_abs(lse, ref_lse) <= 1e-2
 
 
+def test_rope_base_500():
+    # another RoPE base than the default, through the one-call forward (its
+    # table built from the positions) and the preparation pass (rotated K
+    # bit for bit)
+    w = synth.Workload("theta500", 2, 3, 128, n_text=77, grid=11, outlier_frac=0.03)
+    q, k, v, _ = synth.make_qkv(w, 4)
+    pos = synth.positions(w)
+    _say("bf16 theta=500")
+    out = _run_bf16(q, k, v, pos, theta=500.0)
+    ref, _ = oracle.joint_attention(q, k, v, pos, theta=500.0)
+    assert rel_l2(out, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
+    ref_default, _ = oracle.joint_attention(q, k, v, pos)
+    assert rel_l2(out, ref_default) > 10 * BF16_REL_L2    # the base matters here
+    kv = ja.prep_kv_bf16(k.to(DEV), v.to(DEV), pos, 500.0).cpu()
+    s_pad = (w.seq_len + 63) // 64 * 64
+    kr = kv[: 2 * 2 * 3 * s_pad * 128].view(torch.bfloat16).view(2, 3, s_pad, 128)
+    kref = oracle.rotated_qk(k, pos, theta=500.0).to(torch.bfloat16)
+    assert torch.equal(kr[:, :, :w.seq_len].view(torch.int16),
+                       kref.permute(0, 2, 1, 3).contiguous().view(torch.int16))
+
+
 def test_no_rope_and_custom_scale():
     w = synth.Workload("norope", 1, 2, 128, n_text=300, grid=0)
     q, k, v, _ = synth.make_qkv(w, seed=11)

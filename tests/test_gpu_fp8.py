@@ -47,6 +47,25 @@ def test_quantizer_bit_exact(w):
         assert mism == 0, f"{name}: {mism} of {g.size} differ"
 
 
+def test_quantizer_rope_base_500():
+    # another RoPE base than the default: the table the call builds from the
+    # positions follows it, and the codes and scales stay bit-exact
+    w = synth.Workload("theta500", 2, 3, 128, n_text=77, grid=11, outlier_frac=0.03)
+    q, k, v, _ = synth.make_qkv(w, 4)
+    pos = synth.positions(w)
+    _say("quant theta=500")
+    res = ja.quant_rope_fp8(q.to(DEV), k.to(DEV), v.to(DEV), pos, 500.0)
+    torch.cuda.synchronize()
+    got = [t.cpu().numpy() for t in res]
+    ref = oracle.quant_rope_fp8(q, k, v, pos, theta=500.0)
+    for name, g, r in zip(("q8", "k8", "v8", "sq", "sk", "sv"), got, ref):
+        if g.dtype == np.float32:
+            g, r = g.view(np.uint32), r.view(np.uint32)
+        assert np.array_equal(g, r), name
+    # and the base matters: the default base gives other K codes
+    assert not np.array_equal(got[1], oracle.quant_rope_fp8(q, k, v, pos)[1])
+
+
 def test_quantizer_zero_vectors_and_no_rope():
     w = synth.Workload("zeros", 1, 2, 128, n_text=70, grid=0)
     q, k, v, _ = synth.make_qkv(w, 5)
