@@ -180,11 +180,13 @@ def main() -> int:
     _log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
     # dominant kernel: the attention forward (RoPE fused into the Q load),
-    # timed per launch on K/V prepared once; the preparation beside it
+    # timed per launch on K/V prepared once from the positions (prepared K/V,
+    # RoPE table and coordinate table in one buffer, as the one-call path
+    # builds them); the preparation kernel beside it, on a prebuilt table
     rope = ja.rope_table_2d(pos_d, D, w.theta)
-    kv = ja.prep_kv_bf16(kd, vd, rope=rope)
+    kv_pos = ja.prep_kv_bf16(kd, vd, pos_d, w.theta)
     n_t = max(args.steps, 5)
-    kms = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope=rope, out=out), n_t)
+    kms = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv_pos, pos_d, w.theta, out=out), n_t)
     k_avg = sum(kms) / len(kms)
     pms = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope=rope), n_t, short=True)
     prep_avg = sum(pms) / len(pms)
@@ -279,13 +281,13 @@ def main() -> int:
 
     qk_norm = None
     if not args.no_norm:
-        qk_norm = _norm_leg(ja, w, qd, kd, vd, rope, out, k_avg, prep_avg,
+        qk_norm = _norm_leg(ja, w, qd, kd, vd, rope, pos_d, out, k_avg, prep_avg,
                             fp8["quant_ms"] if fp8 else None, max(args.steps, 5), args.seed)
 
     sparse = None
     if not args.no_sparse:
         fp8_in = (q8, sq, kv8, fp8["fwd_ms"]) if fp8 else None
-        sparse = _sparse_leg(ja, w, qd, kv, rope, out, k_avg, max(args.steps, 5), args.seed,
+        sparse = _sparse_leg(ja, w, qd, kv_pos, pos_d, out, k_avg, max(args.steps, 5), args.seed,
                              fp8_in)
 
     cpu = None
@@ -333,22 +335,23 @@ def _gemm_context(fwd_tflops, n):
             "fwd_over_gemm": round(fwd_tflops / tf, 4)}
 
 
-def _norm_leg(ja, w, qd, kd, vd, rope, out, fwd_ms, prep_ms, quant_ms, n, seed):
+def _norm_leg(ja, w, qd, kd, vd, rope, pos_d, out, fwd_ms, prep_ms, quant_ms, n, seed):
     """Query/key RMS normalization fused into the passes that apply RoPE:
     their times with it, beside the times without (same run)."""
     import torch
     import synth
     B, S, H, D = w.shape
     gq, gk = (torch.from_numpy(g).to(qd.device) for g in synth.make_norm_weights(D, seed))
-    kv = ja.prep_kv_bf16(kd, vd, rope=rope, k_norm=gk)
+    kv = ja.prep_kv_bf16(kd, vd, pos_d, w.theta, k_norm=gk)
     # its own output buffer: `out` keeps the plain forward's result, which
     # the CPU baseline checks
     outn = torch.empty_like(out)
     for _ in range(3):
-        ja.fwd_bf16_prepared(qd, kv, rope=rope, out=outn, q_norm=gq)
+        ja.fwd_bf16_prepared(qd, kv, pos_d, w.theta, out=outn, q_norm=gq)
     torch.cuda.synchronize()
     pm = _time_launches(lambda: ja.prep_kv_bf16(kd, vd, rope=rope, k_norm=gk), n, short=True)
-    fm = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, rope=rope, out=outn, q_norm=gq), n)
+    fm = _time_launches(lambda: ja.fwd_bf16_prepared(qd, kv, pos_d, w.theta, out=outn, q_norm=gq),
+                        n)
     p_avg, f_avg = sum(pm) / n, sum(fm) / n
     rec = {"weights": "seeded g = 1 + 0.1 N(0,1), eps 1e-6",
            "prep_kv_ms": round(p_avg, 4), "prep_kv_ms_without": round(prep_ms, 4),
@@ -364,7 +367,7 @@ def _norm_leg(ja, w, qd, kd, vd, rope, out, fwd_ms, prep_ms, quant_ms, n, seed):
     return rec
 
 
-def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed, fp8_in=None):
+def _sparse_leg(ja, w, qd, kv, pos_d, out, dense_ms, n, seed, fp8_in=None):
     """Block-sparse forwards on the seeded mask of the workload: kernel time,
     the flops of the kept blocks per second, and the fraction of the key
     blocks staged (a workgroup covers one query block and stages the key
@@ -384,9 +387,9 @@ def _sparse_leg(ja, w, qd, kv, rope, out, dense_ms, n, seed, fp8_in=None):
     mask_d = mask.to(qd.device)
     outs = torch.empty_like(out)
     for _ in range(3):
-        ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope=rope, out=outs)
+        ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, pos_d, w.theta, out=outs)
     torch.cuda.synchronize()
-    ms = _time_launches(lambda: ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, rope=rope,
+    ms = _time_launches(lambda: ja.fwd_bf16_block_sparse_prepared(qd, kv, mask_d, pos_d, w.theta,
                                                                   out=outs), n)
     avg = sum(ms) / n
     tf = kept_flops / (avg * 1e-3) / 1e12

@@ -141,8 +141,9 @@ typedef struct {
  *              log-sum-exp of each query row's scaled scores.
  *   workspace, workspace_bytes   at least
  *              joint_attn_fwd_bf16_workspace_bytes(p) bytes: the prepared
- *              K/V of joint_attn_prep_kv_bf16 (RoPE table included when only
- *              pos is given) and the partial results of the split below.
+ *              K/V of joint_attn_prep_kv_bf16 (RoPE and coordinate tables
+ *              included when only pos is given) and the partial results of
+ *              the split below.
  * Q and K are normalized and rotated in fp64 and rounded once to bf16 before
  * Q K^T.  Softmax
  * statistics and both products accumulate in fp32; P is rounded to bf16 for
@@ -218,7 +219,12 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len, int32_t 
  *                   in the order p -> 4*(p/8) + (p%8 < 4 ? p%8 : p%8 + 4)
  *                   (the P operand order of the forward),
  *              and, when p gives pos without rope_table, the RoPE table of
- *              pos (fp64 [seq_len][head_dim/2][2]),
+ *              pos (fp64 [seq_len][head_dim/2][2]), then the coordinate
+ *              table (fp64 [1024][head_dim/4][2]: cos and sin of c * w_k
+ *              for every grid coordinate c < 1024), each starting on a
+ *              256-byte boundary; the forward rotates Q from the coordinate
+ *              table where a token's coordinates lie in it (the same values
+ *              bit for bit),
  *            S_pad = seq_len rounded up to 64, zeros past seq_len.
  * The buffer depends only on K, V and the positions: when several calls
  * share them, prepare once.

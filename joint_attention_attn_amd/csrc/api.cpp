@@ -188,10 +188,12 @@ ja_status check_bf16(const ja_params *p, bool q, bool kv) {
 }
 
 // Prepared K/V of the BF16 path: rotated K and V^T, then (when the call
-// builds it) the RoPE table.
+// builds them from pos) the RoPE table and the coordinate table.
 int64_t prep_kv_bf16_core(const ja_params *p) { return align256(ja::prep_kv_bytes(layout(p))); }
 int64_t prep_kv_bf16_total(const ja_params *p) {
-  return prep_kv_bf16_core(p) + (rope_build(p) ? align256(rope_bytes(p)) : 0);
+  return prep_kv_bf16_core(p) +
+         (rope_build(p) ? align256(rope_bytes(p)) + align256(ja::coord_table_bytes(p->head_dim))
+                        : 0);
 }
 // Table a BF16 call on prepared K/V rotates Q with (NULL = no RoPE).
 const double *prepared_table(const ja_params *p, const void *kv) {
@@ -200,17 +202,25 @@ const double *prepared_table(const ja_params *p, const void *kv) {
       static_cast<const char *>(kv) + prep_kv_bf16_core(p));
   return nullptr;
 }
+// The coordinate table built beside it (NULL with a caller's table).
+const double *prepared_coord_table(const ja_params *p, const void *kv) {
+  if (!rope_build(p)) return nullptr;
+  return reinterpret_cast<const double *>(static_cast<const char *>(kv) + prep_kv_bf16_core(p) +
+                                          align256(rope_bytes(p)));
+}
 
-ja_status launch_table(const ja_params *p, double *table, hipStream_t st) {
+ja_status launch_table(const ja_params *p, double *table, double *ctab, hipStream_t st) {
   return hip_status(ja::launch_rope_table_2d(p->pos, p->seq_len, p->head_dim, rope_theta(p),
-                                             table, st));
+                                             table, ctab, st));
 }
 
 ja_status prep_bf16(const ja_params *p, const void *k, const void *v, void *kv, hipStream_t st) {
   const double *table = p->rope_table;
   if (rope_build(p)) {
     double *built = reinterpret_cast<double *>(byte_ptr(kv, prep_kv_bf16_core(p)));
-    JA_TRY(launch_table(p, built, st));
+    double *ctab = reinterpret_cast<double *>(
+        byte_ptr(kv, prep_kv_bf16_core(p) + align256(rope_bytes(p))));
+    JA_TRY(launch_table(p, built, ctab, st));
     table = built;
   }
   return hip_status(ja::launch_prep_kv_bf16(layout(p), k, v, table, kv, st));
@@ -223,8 +233,9 @@ ja_status fwd_bf16_launch(const ja_params *p, const void *q, const void *kv,
   if (plan.n_units > 0 && (size_t)plan.ws_bytes > ws_bytes)
     return fail(JA_ERR_INVALID_ARG, "workspace of %zu bytes is less than the %lld needed",
                 ws_bytes, (long long)plan.ws_bytes);
-  return hip_status(ja::launch_fwd_bf16(layout(p), q, kv, prepared_table(p, kv), mask, o, lse,
-                                        plan, ws, st));
+  const double *ctab = prepared_coord_table(p, kv);
+  return hip_status(ja::launch_fwd_bf16(layout(p), q, kv, prepared_table(p, kv), ctab,
+                                        ctab ? p->pos : nullptr, mask, o, lse, plan, ws, st));
 }
 
 ja_status check_sparse(const ja_params *p, const uint8_t *mask, int max_seq) {
@@ -426,7 +437,7 @@ ja_status joint_attn_rope_table_2d(const int32_t *pos, int32_t seq_len, int32_t 
     return fail(JA_ERR_INVALID_ARG, "table must be 16-byte and pos 4-byte aligned");
   if ((int64_t)seq_len * (head_dim / 2) > 0x7fffffffLL * 256)
     return fail(JA_ERR_UNSUPPORTED, "table too large for one launch");
-  return hip_status(ja::launch_rope_table_2d(pos, seq_len, head_dim, theta, table,
+  return hip_status(ja::launch_rope_table_2d(pos, seq_len, head_dim, theta, table, nullptr,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -531,7 +542,7 @@ ja_status joint_attn_quant_rope_fp8(const ja_params *p, const void *q, const voi
     if (!workspace || workspace_bytes < (size_t)rope_bytes(p))
       return fail(JA_ERR_INVALID_ARG, "workspace of %zu bytes is less than the %lld needed",
                   workspace_bytes, (long long)rope_bytes(p));
-    JA_TRY(launch_table(p, static_cast<double *>(workspace), st));
+    JA_TRY(launch_table(p, static_cast<double *>(workspace), nullptr, st));
     table = static_cast<const double *>(workspace);
   }
   return hip_status(ja::launch_quant_rope_fp8(layout(p), q, k, v, table, q8, k8, v8, sq, sk, sv,
@@ -575,7 +586,7 @@ ja_status joint_attn_fp8_repair_plan(const ja_params *p, const void *k, const vo
     if (!workspace || workspace_bytes < (size_t)rope_bytes(p))
       return fail(JA_ERR_INVALID_ARG, "workspace of %zu bytes is less than the %lld needed",
                   workspace_bytes, (long long)rope_bytes(p));
-    JA_TRY(launch_table(p, static_cast<double *>(workspace), st));
+    JA_TRY(launch_table(p, static_cast<double *>(workspace), nullptr, st));
     table = static_cast<const double *>(workspace);
   }
   return hip_status(ja::launch_repair_plan(layout(p), k, v, table, k8, v8, sk, sv, n_rep, idx,

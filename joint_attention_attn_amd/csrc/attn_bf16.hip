@@ -115,6 +115,10 @@ struct FwdArgs {
   float eps;
   const bf16 *kr, *vt;      // prepared K and V^T (prep_kv.hip), S_pad keys
   const double2 *rope;      // RoPE table [S][D/2] (cos, sin) in fp64
+  // the coordinate table of the same positions, [kCoordTableN][D/4] (cos,
+  // sin), and the positions [S][2] (both NULL = per-token table only)
+  const double2 *ctab;
+  const int32_t *pos;
   bf16 *o;
   float *lse;
   int64_t q_sb, q_ss, q_sh, o_sb, o_ss, o_sh;
@@ -303,13 +307,34 @@ void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int kk = 0; kk < NK; ++kk) ss += chunk_sumsq_f64(w[kk]);
       rn = rms_scale_f64<D>(ss + __shfl_xor(ss, 32), a.eps);
     }
+    // (cos, sin) of the row's pairs: pairs below D/4 turn by the token's
+    // grid row, the others by its column.  When every lane of the wave has
+    // both coordinates inside the coordinate table, read them there (the
+    // same values bit for bit; a 512-row block of an image spans a few grid
+    // rows, so most of its reads hit lines another row already brought into
+    // the vector L1), else from the token's row of the per-token table.
+    const double2 *row_cs = nullptr, *col_cs = nullptr;
+    if (ROPE) {
+      row_cs = a.rope + (int64_t)qs * (D / 2);
+      col_cs = row_cs + D / 4;
+      if (a.ctab) {
+        const int32_t pr = a.pos[2 * (int64_t)qs], pc = a.pos[2 * (int64_t)qs + 1];
+        const bool inside = (uint32_t)pr < (uint32_t)kCoordTableN &&
+                            (uint32_t)pc < (uint32_t)kCoordTableN;
+        if (__builtin_amdgcn_ballot_w64(!inside) == 0) {
+          row_cs = a.ctab + pr * (D / 4);
+          col_cs = a.ctab + pc * (D / 4);
+        }
+      }
+    }
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int d0 = 16 * kk + 8 * hf;
       u32x4 x = w[kk];
       if (ROPE || a.qn)
         x = prologue_chunk_bf16(x, rn, a.qn ? a.qn + d0 : nullptr,
-                                ROPE ? a.rope + (int64_t)qs * (D / 2) + d0 / 2 : nullptr);
+                                !ROPE ? nullptr
+                                : kk < D / 32 ? row_cs + d0 / 2 : col_cs + (d0 / 2 - D / 4));
       if (qi[r] >= S) x = u32x4{0, 0, 0, 0};
       qreg[r][kk] = bit_cast<bf16x8>(x);
     }
@@ -653,8 +678,9 @@ SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse) {
 int fwd_bf16_sparse_max_seq() { return kSparseMaxSeq; }
 
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
-                           const double *rope, const uint8_t *mask, void *o, float *lse,
-                           const SplitPlan &plan, void *workspace, hipStream_t st) {
+                           const double *rope, const double *ctab, const int32_t *pos,
+                           const uint8_t *mask, void *o, float *lse, const SplitPlan &plan,
+                           void *workspace, hipStream_t st) {
   // kv: prepared K | prepared V^T (prep_kv.hip)
   const int64_t prep_elems = (int64_t)L.B * L.H * prep_pad(L.S) * L.D;
   const bf16 *kr = static_cast<const bf16 *>(kv);
@@ -666,6 +692,8 @@ hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
   a.kr = kr;
   a.vt = vt;
   a.rope = reinterpret_cast<const double2 *>(rope);
+  a.ctab = rope && pos ? reinterpret_cast<const double2 *>(ctab) : nullptr;
+  a.pos = a.ctab ? pos : nullptr;
   a.o = static_cast<bf16 *>(o);
   a.lse = lse;
   a.q_sb = L.q_sb; a.q_ss = L.q_ss; a.q_sh = L.q_sh;

@@ -19,8 +19,14 @@ struct AttnLayout {
 };
 
 // RoPE table: (cos, sin) in fp64 per (token, pair), [S][D/2][2] doubles.
+// ctab (NULL = not built): the coordinate table, (cos, sin) of c * w_k for
+// every grid coordinate c < kCoordTableN and k < D/4, [kCoordTableN][D/4][2]
+// doubles.  A token's entry for pair p < D/4 equals ctab[row][p], for
+// p >= D/4 ctab[col][p - D/4], bit for bit (the same product and sincos).
+constexpr int kCoordTableN = 1024;
+inline int64_t coord_table_bytes(int D) { return (int64_t)kCoordTableN * (D / 4) * 16; }
 hipError_t launch_rope_table_2d(const int32_t *pos, int S, int D, float theta,
-                                double *table, hipStream_t st);
+                                double *table, double *ctab, hipStream_t st);
 
 // Split of the last partial round of workgroups over key ranges.  A forward
 // launch has n_items (query block, head, batch row) work items for `slots`
@@ -78,12 +84,15 @@ hipError_t launch_prep_kv_bf16(const AttnLayout &L, const void *k, const void *v
                                const double *rope, void *kv, hipStream_t st);
 
 SplitPlan plan_fwd_bf16(const AttnLayout &L, int n_cu, bool sparse);
-// kv: the prepared K/V buffer; mask: NULL = dense, else the block mask of the
-// block-sparse variant, uint8 [B][H][ceil(S/128)][ceil(S/64)] (nonzero =
-// keep).  workspace: the split's partial results (plan.ws_bytes).
+// kv: the prepared K/V buffer; rope: the RoPE table (NULL = no RoPE); ctab,
+// pos: the coordinate table of the same positions and the positions (both
+// NULL when the table came without them); mask: NULL = dense, else the block
+// mask of the block-sparse variant, uint8 [B][H][ceil(S/128)][ceil(S/64)]
+// (nonzero = keep).  workspace: the split's partial results (plan.ws_bytes).
 hipError_t launch_fwd_bf16(const AttnLayout &L, const void *q, const void *kv,
-                           const double *rope, const uint8_t *mask, void *o, float *lse,
-                           const SplitPlan &plan, void *workspace, hipStream_t st);
+                           const double *rope, const double *ctab, const int32_t *pos,
+                           const uint8_t *mask, void *o, float *lse, const SplitPlan &plan,
+                           void *workspace, hipStream_t st);
 int fwd_bf16_sparse_max_seq();   // longest sequence of the block-sparse variant
 
 hipError_t launch_quant_rope_fp8(const AttnLayout &L, const void *q,

@@ -15,33 +15,48 @@ namespace ja {
 
 // The D/4 frequencies are computed once per workgroup (fp64 pow is the most
 // expensive step); every entry then takes one fp64 product and one sincos
-// (a shared argument reduction for the cosine and the sine).
+// (a shared argument reduction for the cosine and the sine).  The threads
+// past the per-token table fill the coordinate table (ctab), where the
+// coordinate c takes the place of the token's position.
 __global__ __launch_bounds__(256) void rope_table_2d_kernel(
     const int32_t *__restrict__ pos, int S, int D, double theta,
-    double2 *__restrict__ table) {
+    double2 *__restrict__ table, double2 *__restrict__ ctab) {
   __shared__ double freq[32];                 // D/4 <= 32
   const int half = D / 2, quarter = D / 4;
   if ((int)threadIdx.x < quarter) freq[threadIdx.x] = pow(theta, (double)(-4 * (int)threadIdx.x) / (double)D);
   __syncthreads();
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)S * half) return;
-  const int p = (int)(idx % half);
-  const int64_t s = idx / half;
-  const int axis = p / quarter;
-  const int k = p - axis * quarter;
-  const double ang = (double)pos[2 * s + axis] * freq[k];
+  const int64_t n_tok = (int64_t)S * half;
+  int32_t coord;
+  int k;
+  if (idx < n_tok) {
+    const int p = (int)(idx % half);
+    const int64_t s = idx / half;
+    const int axis = p / quarter;
+    k = p - axis * quarter;
+    coord = pos[2 * s + axis];
+  } else {
+    const int64_t j = idx - n_tok;
+    if (!ctab || j >= (int64_t)kCoordTableN * quarter) return;
+    k = (int)(j % quarter);
+    coord = (int32_t)(j / quarter);
+  }
+  const double ang = (double)coord * freq[k];
   double sn, cs;
   sincos(ang, &sn, &cs);
-  table[idx] = make_double2(cs, sn);
+  if (idx < n_tok)
+    table[idx] = make_double2(cs, sn);
+  else
+    ctab[idx - n_tok] = make_double2(cs, sn);
 }
 
 hipError_t launch_rope_table_2d(const int32_t *pos, int S, int D, float theta,
-                                double *table, hipStream_t st) {
-  const int64_t n = (int64_t)S * (D / 2);
+                                double *table, double *ctab, hipStream_t st) {
+  const int64_t n = (int64_t)S * (D / 2) + (ctab ? (int64_t)kCoordTableN * (D / 4) : 0);
   const int64_t blocks = (n + 255) / 256;
   hipLaunchKernelGGL(rope_table_2d_kernel, dim3((unsigned)blocks), dim3(256), 0,
                      st, pos, S, D, (double)theta,
-                     reinterpret_cast<double2 *>(table));
+                     reinterpret_cast<double2 *>(table), reinterpret_cast<double2 *>(ctab));
   return hipGetLastError();
 }
 

@@ -152,10 +152,12 @@ def test_fwd_bf16_rejects_bad_pointers(lib):
 def test_workspace_sizes(lib):
     p = _p(s=300, h=2, d=64)
     kv = 2 * 1 * 2 * 320 * 64 * 2             # rotated K and V^T, S_pad = 320
-    # no RoPE, or a table given: K/V only; positions alone: K/V plus the table
+    # no RoPE, or a table given: K/V only; positions alone: K/V plus the
+    # table and the coordinate table (1024 coordinates x D/4 pairs x 16 B)
     assert lib.joint_attn_prep_kv_bf16_bytes(ctypes.byref(p)) == kv
     p.pos = FAKE
-    assert lib.joint_attn_prep_kv_bf16_bytes(ctypes.byref(p)) == kv + (300 * 64 * 8 + 255) // 256 * 256
+    assert lib.joint_attn_prep_kv_bf16_bytes(ctypes.byref(p)) == \
+        kv + (300 * 64 * 8 + 255) // 256 * 256 + 1024 * 16 * 16
     assert lib.joint_attn_quant_rope_fp8_workspace_bytes(ctypes.byref(p)) == 300 * 64 * 8
     assert lib.joint_attn_fp8_repair_plan_workspace_bytes(ctypes.byref(p)) == 300 * 64 * 8
     p.rope_table, p.rope_table_bytes = FAKE + 0x1000, 300 * 64 * 8

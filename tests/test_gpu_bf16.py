@@ -125,6 +125,34 @@ def test_rope_base_500():
                        kref.permute(0, 2, 1, 3).contiguous().view(torch.int16))
 
 
+@pytest.mark.parametrize("lo,hi", [(0, 300), (-40, 3000), (1024, 5000)])
+def test_positions_path_equals_table_path(lo, hi):
+    # The forward given positions reads Q's cos/sin from the coordinate table
+    # when a wave's coordinates all lie in [0, 1024), else from the per-token
+    # table; either way the output equals the one from a prebuilt per-token
+    # table bit for bit.  (-40, 3000): waves of both kinds; (1024, 5000):
+    # none inside.
+    w = synth.Workload("coords", 1, 64, 128, n_text=1100, grid=0, outlier_frac=0.01)
+    q, k, v, _ = synth.make_qkv(w, 13)
+    pos = np.random.default_rng(lo + 77).integers(lo, hi, size=(w.seq_len, 2)).astype(np.int32)
+    if lo == -40:
+        pos[:600] = np.abs(pos[:600]) % 1024            # the first waves inside
+    _say(f"bf16 positions path vs table path, coordinates in [{lo}, {hi})")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    pos_d = torch.from_numpy(pos).to(DEV)
+    out_pos, lse_pos = ja.fwd_bf16(qd, kd, vd, pos_d, return_lse=True)
+    out_tab, lse_tab = ja.fwd_bf16(qd, kd, vd, rope=ja.rope_table_2d(pos_d, 128),
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out_pos.view(torch.int16), out_tab.view(torch.int16))
+    assert torch.equal(lse_pos, lse_tab)
+    rows = np.unique(np.concatenate([np.arange(0, w.seq_len, 37), [w.seq_len - 1]]))
+    ref, _ = oracle.joint_attention(q, k, v, pos, rows=rows)
+    got = out_pos.cpu()[:, rows]
+    assert rel_l2(got, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(got, ref) <= BF16_MAX_ABS
+
+
 def test_no_rope_and_custom_scale():
     w = synth.Workload("norope", 1, 2, 128, n_text=300, grid=0)
     q, k, v, _ = synth.make_qkv(w, seed=11)
@@ -337,6 +365,16 @@ def test_prep_kv_bit_exact(s, d, strided, h):
     assert torch.equal(kv_pos[:kv.numel()], kv)
     table = kv_pos[kv.numel():kv.numel() + s * d * 8].numpy().view(np.float64)
     assert np.array_equal(table, rope.cpu().numpy().ravel())
+    # then the coordinate table: (cos, sin) of c * w_k for c < 1024, whose
+    # entries equal the per-token table's bit for bit (pairs below D/4 by
+    # the token's row, the others by its column)
+    align = lambda x: (x + 255) // 256 * 256
+    c0 = kv.numel() + align(s * d * 8)
+    assert kv_pos.numel() == c0 + align(1024 * (d // 4) * 16)
+    ctab = kv_pos[c0:c0 + 1024 * (d // 4) * 16].numpy().view(np.float64).reshape(1024, d // 4, 2)
+    tab = table.reshape(s, d // 2, 2)
+    assert np.array_equal(tab[:, :d // 4].view(np.uint64), ctab[pos[:, 0]].view(np.uint64))
+    assert np.array_equal(tab[:, d // 4:].view(np.uint64), ctab[pos[:, 1]].view(np.uint64))
     kref = oracle.rotated_qk(k, pos).to(torch.bfloat16)
     assert torch.equal(kr[:, :, :s].view(torch.int16), kref.permute(0, 2, 1, 3).contiguous().view(torch.int16))
     assert not kr[:, :, s:].view(torch.int16).any()
