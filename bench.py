@@ -80,11 +80,11 @@ def _parse():
     return ap.parse_args()
 
 
-def _traffic_for_current_kernel(record: str, source: str):
+def _traffic_for_current_kernel(kernel: str, workload: str, source: str):
     """HBM bytes per launch from a committed rocprofv3 counter record
-    (profiles/<record>), only if it was taken on the kernel source as it is
-    now; None otherwise."""
-    path = os.path.join(PROFILES, record)
+    (profiles/<kernel>_<workload>_traffic.txt), only if it was taken on this
+    workload and on the kernel source as it is now; None otherwise."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -200,16 +200,14 @@ def main() -> int:
     achieved = flops / (k_avg * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic_for_current_kernel("attn_fwd_bf16_t2i_2048_traffic.txt",
-                                                       "attn_bf16.hip"),
+                "traffic": _traffic_for_current_kernel("attn_fwd_bf16", w.name, "attn_bf16.hip"),
                 "kernel": "attn_fwd_bf16_kernel<128, true, false, false> (+ merge_split_kernel of the "
                           "split last round); K/V preparation in prep_kv",
                 "kernel_ms": round(k_avg, 4), "kernel_ms_min": round(min(kms), 4),
                 "kernel_ms_median": round(sorted(kms)[len(kms) // 2], 4),
                 "rope_table_ms": round(table_avg, 4),
                 "prep_kv": {"ms": round(prep_avg, 4),
-                            "traffic": _traffic_for_current_kernel(
-                                "prep_kv_bf16_t2i_2048_traffic.txt", "prep_kv.hip"),
+                            "traffic": _traffic_for_current_kernel("prep_kv_bf16", w.name, "prep_kv.hip"),
                             "gbs": round(prep_bytes / (prep_avg * 1e-3) / 1e9, 1),
                             "frac_of_hbm": round(prep_bytes / (prep_avg * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                                  4)}}
@@ -243,18 +241,15 @@ def main() -> int:
         f_tf = flops / (f_avg * 1e-3) / 1e12
         fp8 = {"fwd_ms": round(f_avg, 4), "fwd_tflops": round(f_tf, 2),
                "fwd_frac_of_fp8_peak": round(f_tf / PEAK_FP8_TFLOPS, 4),
-               "fwd_traffic": _traffic_for_current_kernel("attn_fwd_fp8_t2i_2048_traffic.txt",
-                                                          "attn_fp8.hip"),
+               "fwd_traffic": _traffic_for_current_kernel("attn_fwd_fp8", w.name, "attn_fp8.hip"),
                "quant_ms": round(q_avg, 4),
                "quant_gbs": round(q_bytes / (q_avg * 1e-3) / 1e9, 1),
                "quant_frac_of_hbm": round(q_bytes / (q_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-               "quant_traffic": _traffic_for_current_kernel("quant_rope_fp8_t2i_2048_traffic.txt",
-                                                            "quant_fp8.hip"),
+               "quant_traffic": _traffic_for_current_kernel("quant_rope_fp8", w.name, "quant_fp8.hip"),
                "prep_ms": round(pp_avg, 4),
                "prep_gbs": round(pp_bytes / (pp_avg * 1e-3) / 1e9, 1),
                "prep_frac_of_hbm": round(pp_bytes / (pp_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-               "prep_traffic": _traffic_for_current_kernel("prep_kv_fp8_t2i_2048_traffic.txt",
-                                                           "prep_kv_fp8.hip"),
+               "prep_traffic": _traffic_for_current_kernel("prep_kv_fp8", w.name, "prep_kv_fp8.hip"),
                "path_tflops": round(flops / ((f_avg + q_avg + pp_avg) * 1e-3) / 1e12, 2)}
         _log(f"[bench] fp8: fwd {f_avg:.3f} ms ({f_tf:.1f} TFLOP/s), quant {q_avg:.3f} ms "
              f"({fp8['quant_gbs']} GB/s), K/V prep {pp_avg:.3f} ms ({fp8['prep_gbs']} GB/s)")
