@@ -103,6 +103,32 @@ def test_ragged_lengths_wide_shape(s, d, b, h, rope):
     assert max_abs(lse, ref_lse) <= 1e-2
 
 
+@pytest.mark.parametrize("b,h", [(4, 64), (1, 2)])
+def test_running_max_growth_across_tiles(b, h):
+    # Scores built so that a row's running max climbs by about 56 (exp2
+    # domain) per 32-key tile (query magnitude 64 on a key ramp over
+    # [-64, 64]), by 28 or 14 per tile (32, 16: the max moves every few
+    # tiles, P up to the rescale threshold in between), or sits at the first
+    # key (negative magnitudes): the rescale path of the forward, in the wide
+    # shape (4 x 64 heads) and the small one (2 heads), no RoPE.
+    s, d = 600, 128
+    rng = np.random.default_rng(11)
+    q = 0.05 * rng.standard_normal((b, s, h, d))
+    k = 0.05 * rng.standard_normal((b, s, h, d))
+    v = rng.standard_normal((b, s, h, d))
+    mags = np.array([64.0, 32.0, 16.0, 8.0, -64.0, -8.0, 0.0, 1.0])
+    q[..., 0] = mags[np.arange(s) % len(mags)][None, :, None]
+    k[..., 0] = np.linspace(-64.0, 64.0, s)[None, :, None]
+    q, k, v = (torch.from_numpy(t.astype(np.float32)).to(torch.bfloat16) for t in (q, k, v))
+    _say(f"bf16 running-max growth S={s} D={d} B={b} H={h}")
+    out, lse = _run_bf16(q, k, v, None, return_lse=True)
+    ref, ref_lse = oracle.joint_attention(q, k, v, None)
+    assert torch.isfinite(out.float()).all()
+    assert rel_l2(out, ref) <= BF16_REL_L2
+    assert row_scaled_max_abs(out, ref) <= BF16_MAX_ABS
+    assert max_abs(lse, ref_lse) <= 1e-2
+
+
 def test_rope_base_500():
     # another RoPE base than the default, through the one-call forward (its
     # table built from the positions) and the preparation pass (rotated K
